@@ -1,0 +1,273 @@
+"""Plain float64 oracle of one block-diffusion denoising step and of the block loop.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the benchmark's
+CPU baseline; never by the product path.
+
+What is computed, and where it comes from:
+
+* Reverse process.  A network reads a block in which some positions hold the
+  special [MASK] token and predicts a token for every masked position in parallel
+  (PredNext, "人工知能は拡散言語モデルの夢を見るか？", section
+  "拡散言語モデルのLLMへの応用").  The [MASK] id is V, an extra embedding row; the
+  LM head has V outputs so it can never emit [MASK].
+* Network.  The denoiser tower attends bidirectionally inside the block and
+  cross-attends to the frozen, causal context tower through that tower's cached
+  keys/values (poko-everyday.com Nemotron-TwoTower news item, section
+  技術/ビジネス面).  Read here as ONE softmax per query over [prefix keys ; block
+  keys] with no mask; layer l of the denoiser reads prefix K/V layer l; query head
+  j uses K/V head floor(j / (H / Hkv)).  Pre-norm residual layers with RMSNorm
+  (eps 1e-6), an ungated GELU MLP (erf form) of width F, a final RMSNorm, no biases.
+  A learned per-block-position row Pos[p] is added to the token embedding; without
+  it every masked position would see identical inputs and produce identical
+  predictions.
+* Confidence.  conf_p is the largest softmax probability of the logits of position
+  p scaled by that position's inverse temperature tau_p; the prediction is the
+  lowest vocabulary id among the maximal scaled logits.
+* Commit rule and loop (PredNext, same article, section
+  "拡散言語モデルで推論するには", steps 1-5; dzen.guru "NVIDIA Nemotron 70B
+  генерирует текст…", section "Что нового": blocks of 16 refined over several
+  iterations, threshold gamma trades quality for speed).  Start from an all-[MASK]
+  block; run the network; adopt every masked position whose confidence is at
+  least gamma; if none is, adopt the single most confident masked position
+  (lowest position on ties); the rest stay [MASK]; repeat until no [MASK] is left.
+  Adopted tokens never change.  Every step adopts at least one position, so a
+  block of B ends in at most B steps.
+
+Precision.  Everything is float64.  Mode "bf16" additionally rounds to the nearest
+bfloat16 (ties to even) exactly at the points where the GPU stores bfloat16: the
+normed GEMM inputs (h, h2, hf), q/k/v, the attention output o and the MLP
+activation u.  Logits are never rounded.  Decisions that turn floats into
+integers (argmax, conf >= gamma, the fallback choice) are taken on float32
+roundings of the float64 values, the precision the kernels decide in.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+from scipy.special import erf
+
+
+# ----------------------------------------------------------------------------- elementwise
+
+
+def round_bf16(x) -> np.ndarray:
+    """Nearest bfloat16 value of each float64 element, ties to even (finite inputs).
+
+    bfloat16 keeps 8 significant bits and float32's exponent range.  For
+    x = m * 2**e with 0.5 <= |m| < 1 the representable neighbours are multiples of
+    2**(e-8); below 2**-126 the spacing stays 2**-133 (subnormals).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    e = np.maximum(e, -125)
+    return np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x**2) + eps) * g over the last axis."""
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """Exact GELU: 0.5 * x * (1 + erf(x / sqrt(2)))."""
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def joint_attention(q: np.ndarray, k_pre: np.ndarray, v_pre: np.ndarray, k_blk: np.ndarray,
+                    v_blk: np.ndarray) -> np.ndarray:
+    """Block queries against [prefix keys ; block keys], one softmax per query row, no mask.
+
+    q [B][H][hd]; k_pre, v_pre [P][Hkv][hd] (P may be 0); k_blk, v_blk [B][Hkv][hd].
+    Returns o [B][H][hd].  Query head j reads K/V head j // (H // Hkv).
+    """
+    Bq, H, hd = q.shape
+    Hkv = k_blk.shape[1]
+    G = H // Hkv
+    o = np.empty((Bq, H, hd), dtype=np.float64)
+    for j in range(H):
+        g = j // G
+        K = np.concatenate([k_pre[:, g, :], k_blk[:, g, :]], axis=0)
+        Vv = np.concatenate([v_pre[:, g, :], v_blk[:, g, :]], axis=0)
+        s = (q[:, j, :] @ K.T) / np.sqrt(hd)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        o[:, j, :] = p @ Vv
+    return o
+
+
+# ----------------------------------------------------------------------------- tower
+
+KVProvider = Callable[[int, int], Tuple[np.ndarray, np.ndarray]]   # (layer, seq) -> (K, V) [P][Hkv][hd]
+
+
+class OracleTower:
+    """The denoiser tower with its weights held as float64.
+
+    `weights` maps names to arrays holding the stored values exactly (float32, or
+    bfloat16 widened to float32): tok_emb [V+1][d], pos_emb [B][d], final_norm [d],
+    lm_head [V][d], and per-layer lists wq [H*hd][d], wk/wv [Hkv*hd][d],
+    wo [d][H*hd], w1 [F][d], w2 [d][F], attn_norm [d], mlp_norm [d].
+    """
+
+    def __init__(self, weights: Dict[str, object], *, H: int, Hkv: int, hd: int, eps: float = 1e-6,
+                 mode: str = "plain"):
+        if mode not in ("plain", "bf16"):
+            raise ValueError(mode)
+        self.W = weights
+        self.H, self.Hkv, self.hd, self.eps, self.mode = H, Hkv, hd, eps, mode
+        self.L = len(weights["wq"])
+        self.V = weights["lm_head"].shape[0]
+        self.d = weights["lm_head"].shape[1]
+        self._f64: Dict[Tuple[str, int], np.ndarray] = {}
+
+    def _w(self, name: str, layer: int = -1) -> np.ndarray:
+        key = (name, layer)
+        if key not in self._f64:
+            a = self.W[name] if layer < 0 else self.W[name][layer]
+            self._f64[key] = np.asarray(a, dtype=np.float64)
+        return self._f64[key]
+
+    def _rnd(self, a: np.ndarray) -> np.ndarray:
+        return round_bf16(a) if self.mode == "bf16" else a
+
+    def hidden(self, tok: np.ndarray, kv: KVProvider, seqs: Sequence[int],
+               capture: Optional[dict] = None) -> np.ndarray:
+        """Final-normed hidden states hf [S][B][d] for token blocks tok [S][B].
+
+        `seqs[s]` is the batch index of row-block s, passed to `kv` to fetch its prefix.
+        """
+        S, B = tok.shape
+        H, Hkv, hd = self.H, self.Hkv, self.hd
+        E = self.W["tok_emb"]
+        x = np.asarray(E[tok.reshape(-1)], dtype=np.float64).reshape(S, B, self.d)
+        x = x + self._w("pos_emb")[None, :B, :]
+        for l in range(self.L):
+            h = self._rnd(rmsnorm(x, self._w("attn_norm", l), self.eps))
+            q = self._rnd(h @ self._w("wq", l).T).reshape(S, B, H, hd)
+            k = self._rnd(h @ self._w("wk", l).T).reshape(S, B, Hkv, hd)
+            v = self._rnd(h @ self._w("wv", l).T).reshape(S, B, Hkv, hd)
+            o = np.empty((S, B, H, hd))
+            for s in range(S):
+                kp, vp = kv(l, seqs[s])
+                o[s] = joint_attention(q[s], np.asarray(kp, np.float64), np.asarray(vp, np.float64),
+                                       k[s], v[s])
+            o = self._rnd(o.reshape(S, B, H * hd))
+            x = x + o @ self._w("wo", l).T
+            h2 = self._rnd(rmsnorm(x, self._w("mlp_norm", l), self.eps))
+            u = self._rnd(gelu(h2 @ self._w("w1", l).T))
+            x = x + u @ self._w("w2", l).T
+            if capture is not None:
+                capture.setdefault("x", []).append(x.copy())
+        return self._rnd(rmsnorm(x, self._w("final_norm"), self.eps))
+
+    def logits(self, hf_rows: np.ndarray) -> np.ndarray:
+        """z = hf Wlm^T for rows hf_rows [R][d] (float64, never rounded)."""
+        return hf_rows @ self._w("lm_head").T
+
+
+# ----------------------------------------------------------------------------- reduction + commit
+
+
+def vocab_reduce(z: np.ndarray, tau: np.ndarray):
+    """Per row: conf = max softmax prob of tau*z, arg = lowest id of the max, gap = p1 - p2.
+
+    z [R][V] float64, tau [R].  arg is decided on the float32 rounding of tau*z.
+    """
+    s = np.asarray(tau, np.float64)[:, None] * z
+    arg = np.argmax(s.astype(np.float32), axis=1)          # first maximum = lowest id
+    m = s.max(axis=1, keepdims=True)
+    Z = np.exp(s - m).sum(axis=1)
+    conf = 1.0 / Z
+    s2 = np.partition(s, s.shape[1] - 2, axis=1)[:, -2]
+    p2 = np.exp(s2 - m[:, 0]) / Z
+    return conf, arg.astype(np.int64), conf - p2
+
+
+def commit_rule(conf: np.ndarray, masked: np.ndarray, gamma: float) -> np.ndarray:
+    """Positions adopted this step: masked with conf >= gamma, else the single most confident.
+
+    Decided in float32.  Ties in the fallback go to the lowest position.  A block with
+    no masked position adopts nothing.
+    """
+    c32 = np.asarray(conf, np.float64).astype(np.float32)
+    U = masked & (c32 >= np.float32(gamma))
+    if not U.any() and masked.any():
+        cand = np.where(masked, c32, np.float32(-np.inf))
+        U = np.zeros_like(masked)
+        U[int(np.argmax(cand))] = True
+    return U
+
+
+@dataclasses.dataclass
+class StepResult:
+    conf: np.ndarray        # [S][B] float64 (nan where committed on entry)
+    arg: np.ndarray         # [S][B] int64 (-1 where committed on entry)
+    gap: np.ndarray         # [S][B] p1 - p2 (nan where committed on entry)
+    U: np.ndarray           # [S][B] bool, adopted this step
+    tok: np.ndarray         # [S][B] tokens after the step
+    committed: np.ndarray   # [S][B] bool after the step
+    z: Optional[np.ndarray] = None   # [S][B][V] logits of masked rows (nan elsewhere) if kept
+
+
+def oracle_step(tower: OracleTower, tok: np.ndarray, committed: np.ndarray, tau: np.ndarray,
+                gamma: float, kv: KVProvider, seqs: Optional[Sequence[int]] = None,
+                keep_logits: bool = False) -> StepResult:
+    """One denoising step for S independent sequences from state (tok, committed)."""
+    S, B = tok.shape
+    seqs = list(range(S)) if seqs is None else list(seqs)
+    masked = ~committed.astype(bool)
+    assert np.array_equal(tok == tower.V, masked), "state must hold [MASK] exactly at uncommitted positions"
+    hf = tower.hidden(tok, kv, seqs)
+    rows = np.nonzero(masked.reshape(-1))[0]
+    conf = np.full(S * B, np.nan)
+    arg = np.full(S * B, -1, dtype=np.int64)
+    gap = np.full(S * B, np.nan)
+    z_all = None
+    if rows.size:
+        z = tower.logits(hf.reshape(S * B, -1)[rows])
+        c, a, g = vocab_reduce(z, tau.reshape(-1)[rows])
+        conf[rows], arg[rows], gap[rows] = c, a, g
+        if keep_logits:
+            z_all = np.full((S * B, tower.V), np.nan)
+            z_all[rows] = z
+            z_all = z_all.reshape(S, B, tower.V)
+    conf, arg, gap = conf.reshape(S, B), arg.reshape(S, B), gap.reshape(S, B)
+    U = np.zeros((S, B), dtype=bool)
+    for s in range(S):
+        U[s] = commit_rule(conf[s], masked[s], gamma)
+    new_tok = np.where(U, arg, tok)
+    new_c = committed.astype(bool) | U
+    return StepResult(conf, arg, gap, U, new_tok, new_c, z_all)
+
+
+def oracle_generate(tower: OracleTower, S: int, B: int, tau: np.ndarray, gamma: float, kv: KVProvider,
+                    seqs: Optional[Sequence[int]] = None, keep_trace: bool = True):
+    """Run the block loop from an all-[MASK] block until every position is adopted.
+
+    Returns (tok [S][B], commit_step [S][B], steps [S], trace: list of StepResult).
+    steps[s] counts the steps in which sequence s still had a masked position.
+    """
+    tok = np.full((S, B), tower.V, dtype=np.int64)
+    committed = np.zeros((S, B), dtype=bool)
+    commit_step = np.full((S, B), -1, dtype=np.int64)
+    steps = np.zeros(S, dtype=np.int64)
+    trace: List[StepResult] = []
+    t = 0
+    while not committed.all():
+        active = ~committed.all(axis=1)
+        r = oracle_step(tower, tok, committed, tau, gamma, kv, seqs)
+        assert (r.U.sum(axis=1)[active] >= 1).all(), "an active sequence must adopt at least one position"
+        commit_step[r.U] = t
+        steps += active
+        tok, committed = r.tok, r.committed
+        if keep_trace:
+            trace.append(r)
+        t += 1
+        assert t <= B, "the loop must end within B steps"
+    return tok, commit_step, steps, trace
