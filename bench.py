@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-diffusion denoising loop on one MI355X.
+
+A bench "step" is one pass of the whole hot path over one batch: td_generate_block, i.e.
+the device-driven loop of denoising steps (embedding, L layers of fused QKV / split-K
+attention / output / MLP projections, LM head with fused vocab reduction, on-device
+commit) that starts from an all-[MASK] block and ends when every position is adopted.
+
+Default workload: bf16 tower at batch 1 (prefix 4096, d 2048, 16 x 128 heads, 8 layers,
+MLP 8192, vocab 131072, block 16, gamma 0.8), inputs synthetic and resident in HBM
+before the timed region.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "committed tokens/s + denoise steps/s, 1 GPU; % of HBM / MFMA roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50, help="timed blocks")
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="b1_p4096")
+    p.add_argument("--gamma", type=float, default=None)
+    p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--breakdown", action="store_true", help="also time each kernel class (extra blocks)")
+    return p.parse_args()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_diffusion_lm_step_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel_src: str, per_launch_bytes_alg: float):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", "lmhead_b1_p4096_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it stands, on this host's cores, on a bounded sample of the workload."""
+    from oracle import OracleTower, oracle_step
+    from synth import draw_inv_temp, draw_prefix_lengths, draw_tower, f32_from_bf16_bits
+    from synth.gen import draw_prefix_kv
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    tw = draw_tower(w)
+    f = tw.as_f32
+    W = dict(tok_emb=f(tw.tok_emb), pos_emb=f(tw.pos_emb), final_norm=f(tw.final_norm), lm_head=f(tw.lm_head),
+             wq=[f(a) for a in tw.wq], wk=[f(a) for a in tw.wk], wv=[f(a) for a in tw.wv], wo=[f(a) for a in tw.wo],
+             w1=[f(a) for a in tw.w1], w2=[f(a) for a in tw.w2], attn_norm=[f(a) for a in tw.attn_norm],
+             mlp_norm=[f(a) for a in tw.mlp_norm])
+    del tw
+    orc = OracleTower(W, H=w.H, Hkv=w.Hkv, hd=w.hd, eps=w.rms_eps, mode="bf16" if w.dtype == "bf16" else "plain")
+    plens = draw_prefix_lengths(w)
+    tau = draw_inv_temp(w)
+    n_s = min(w.n, 4)   # sequences of the sample (all of a batch-1 workload)
+    cache = {}
+
+    def kv(l, s):
+        if (l, s) not in cache:
+            k = draw_prefix_kv(w, l, s, int(plens[s]), "k")
+            v = draw_prefix_kv(w, l, s, int(plens[s]), "v")
+            if w.dtype == "bf16":
+                k, v = f32_from_bf16_bits(k), f32_from_bf16_bits(v)
+            cache[(l, s)] = (k, v)
+        return cache[(l, s)]
+
+    for l in range(w.L):   # inputs staged and weights widened before timing, as td_create is untimed
+        for s in range(n_s):
+            kv(l, s)
+        for name in ("wq", "wk", "wv", "wo", "w1", "w2", "attn_norm", "mlp_norm"):
+            orc._w(name, l)
+    for name in ("lm_head", "pos_emb", "final_norm"):
+        orc._w(name)
+    tok = np.full((n_s, w.B), w.V, dtype=np.int64)
+    c = np.zeros((n_s, w.B), bool)
+    t0 = time.perf_counter()
+    steps, committed = 0, 0
+    while not c.all() and time.perf_counter() - t0 < budget_s:
+        r = oracle_step(orc, tok, c, tau[:n_s], w.gamma, kv)
+        committed += int(r.U.sum())
+        steps += 1
+        tok, c = r.tok, r.committed
+    dt = time.perf_counter() - t0
+    sample = (f"{steps} oracle steps of the block loop from all-[MASK] on sequences 0..{n_s - 1} of {w.name} "
+              f"(float64, {'bf16-faithful' if w.dtype == 'bf16' else 'plain'}), {committed} positions adopted"
+              f"{', block complete' if c.all() else ', stopped at the time budget'}")
+    return dict(value=committed / dt, unit="committed tokens/s", cores=int(threads), kind="oracle", sample=sample,
+                denoise_steps_per_s=steps / dt, seconds=dt)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from block_diffusion_lm_step_amd import TD_PROF_ATTENTION, TD_PROF_GEMM, TD_PROF_LMHEAD, TD_PROF_STEP, Denoiser
+    from synth import draw_inv_temp, draw_prefix_lengths, draw_tower, get_workload
+    from synth.device import prefix_to_device, tower_config, tower_to_device
+
+    w = get_workload(args.workload)
+    if args.gamma is not None:
+        w = w.with_(gamma=args.gamma)
+    log(f"[bench] workload {w.name}: n={w.n} B={w.B} d={w.d} H={w.H}/{w.Hkv}x{w.hd} L={w.L} F={w.F} V={w.V} "
+        f"gamma={w.gamma}")
+    t = time.time()
+    tw = draw_tower(w)
+    dW = tower_to_device(tw)
+    del tw
+    plens = draw_prefix_lengths(w)
+    offsets, ks, vs = prefix_to_device(w, plens)
+    tau = torch.from_numpy(draw_inv_temp(w)).cuda()
+    dev = Denoiser(tower_config(w, max_batch=w.n, max_prefix_tokens=max(1, offsets[-1])), dW)
+    dev.set_prefix(offsets, ks, vs)
+    del dW
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.time() - t:.1f} s)")
+
+    tok = torch.zeros((w.n, w.B), dtype=torch.int32, device="cuda")
+    com = torch.zeros((w.n, w.B), dtype=torch.uint8, device="cuda")
+    steps = torch.zeros(w.n, dtype=torch.int32, device="cuda")
+
+    def block():
+        dev.generate_block(tok, com, tau, w.gamma, steps=steps)
+
+    for _ in range(args.warmup):
+        block()
+    dev.sync()
+    log("[bench] warmup done")
+
+    dev.profile_begin(TD_PROF_LMHEAD)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        block()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lm_ms = dev.profile_end()
+    dev.sync()
+    elapsed = t1 - t0
+    st = steps.cpu().numpy()
+    S = int(st.max())
+    assert com.cpu().numpy().all(), "block not fully committed"
+    log(f"[bench] {args.steps} blocks in {elapsed * 1e3:.2f} ms; steps per block {st.tolist()}")
+
+    tokens_per_s = args.steps * w.n * w.B / elapsed
+    steps_per_s = args.steps * S / elapsed
+    # LM-head launches that did work: the first S of every block's B launches.
+    lm = np.array(lm_ms).reshape(args.steps, w.B)[:, :S]
+    lm_avg_ms = float(lm.mean())
+    elt = 2 if w.dtype == "bf16" else 4
+    lm_bytes = w.V * w.d * elt
+    achieved = lm_bytes / (lm_avg_ms * 1e-3) / 1e9
+    traffic = traffic_record("k_lmhead.hip", lm_bytes)
+
+    breakdown = {}
+    if args.breakdown:
+        for name, kind in (("gemm", TD_PROF_GEMM), ("attention", TD_PROF_ATTENTION), ("step", TD_PROF_STEP)):
+            dev.profile_begin(kind)
+            for _ in range(3):
+                block()
+            ms = np.array(dev.profile_end())
+            per = len(ms) // (3 * w.B)
+            ms = ms.reshape(3, w.B, per)[:, :S, :]
+            breakdown[name] = dict(ms_per_step=float(ms.sum(axis=2).mean()), launches_per_step=per)
+        step_bytes = w.weight_params() * elt + int(plens.sum()) * w.L * 2 * w.Hkv * w.hd * elt
+        breakdown["step_alg_bytes"] = step_bytes
+        breakdown["step_hbm_frac"] = step_bytes / (breakdown["step"]["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 3),
+        "unit": "committed tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; random-init tower weights N(0,0.02), prefix K/V N(0,1))",
+        "config": {"workload": w.name, "batch": w.n, "prefix_tokens": int(plens.sum()), "block": w.B, "gamma": w.gamma,
+                   "d_model": w.d, "heads": w.H, "kv_heads": w.Hkv, "head_dim": w.hd, "layers": w.L, "d_ff": w.F,
+                   "vocab": w.V},
+        "denoise_steps_per_s": round(steps_per_s, 3),
+        "denoise_steps_per_block": S,
+        "roofline": {"kernel": "lmhead_kernel (LM head GEMM + fused tau-scaled vocab max/sumexp/argmax)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": lm_bytes, "avg_launch_ms": round(lm_avg_ms, 5),
+                     "launches_averaged": int(lm.size)},
+    }
+    if breakdown:
+        out["breakdown"] = breakdown
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle sample")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    dev.close()
+
+
+if __name__ == "__main__":
+    main()

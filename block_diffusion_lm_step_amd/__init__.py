@@ -1,0 +1,162 @@
+"""Python binding of libtd, the MI355X block-diffusion denoising step (C ABI in include/td.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind the C
+ABI.  torch tensors provide device memory and the HIP stream.  Importing this package
+raises if libtd.so has not been built (build with `python -m block_diffusion_lm_step_amd.build`
+or `__graft_entry__.build()`); there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int, c_int8, c_int32, c_int64, c_uint8, c_void_p
+from typing import Dict, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtd.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m block_diffusion_lm_step_amd.build` first")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+TD_OK, TD_EINVAL, TD_ENOMEM, TD_EDEVICE, TD_EUNSUPPORTED = range(5)
+TD_F32, TD_BF16 = 0, 1
+STATUS_NAMES = {0: "TD_OK", 1: "TD_EINVAL", 2: "TD_ENOMEM", 3: "TD_EDEVICE", 4: "TD_EUNSUPPORTED"}
+
+
+class TdConfig(ctypes.Structure):
+    _fields_ = [("n_layers", c_int32), ("d_model", c_int32), ("n_heads", c_int32), ("n_kv_heads", c_int32),
+                ("head_dim", c_int32), ("d_ff", c_int32), ("vocab", c_int32), ("block_size", c_int32),
+                ("max_batch", c_int32), ("max_prefix_tokens", c_int64), ("dtype", c_int32), ("rms_eps", c_float)]
+
+
+class TdWeights(ctypes.Structure):
+    _fields_ = [("tok_emb", c_void_p), ("pos_emb", c_void_p), ("attn_norm", POINTER(c_void_p)),
+                ("wq", POINTER(c_void_p)), ("wk", POINTER(c_void_p)), ("wv", POINTER(c_void_p)),
+                ("wo", POINTER(c_void_p)), ("mlp_norm", POINTER(c_void_p)), ("w1", POINTER(c_void_p)),
+                ("w2", POINTER(c_void_p)), ("final_norm", c_void_p), ("lm_head", c_void_p)]
+
+
+_CTX = c_void_p
+lib.td_create.argtypes = [POINTER(TdConfig), POINTER(TdWeights), c_void_p, POINTER(_CTX)]
+lib.td_set_prefix.argtypes = [_CTX, c_int32, POINTER(c_int64), POINTER(c_void_p), POINTER(c_void_p)]
+lib.td_denoise_step.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_void_p]
+lib.td_generate_block.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
+lib.td_debug_attention.argtypes = [_CTX, c_int32, c_void_p, c_void_p]
+lib.td_sync.argtypes = [_CTX]
+lib.td_profile_begin.argtypes = [_CTX, c_int32]
+lib.td_profile_begin.restype = c_int
+lib.td_profile_end.argtypes = [_CTX, POINTER(c_float), c_int32]
+lib.td_profile_end.restype = c_int32
+lib.td_kernels_per_step.argtypes = [_CTX]
+lib.td_kernels_per_step.restype = c_int32
+lib.td_destroy.argtypes = [_CTX]
+lib.td_destroy.restype = None
+lib.td_last_error.argtypes = [_CTX]
+lib.td_last_error.restype = c_char_p
+lib.td_version.restype = c_char_p
+for _f in ("td_create", "td_set_prefix", "td_denoise_step", "td_generate_block", "td_debug_attention", "td_sync"):
+    getattr(lib, _f).restype = c_int
+
+# Every symbol the C header declares.
+EXPORTED = ("td_create", "td_set_prefix", "td_denoise_step", "td_generate_block", "td_debug_attention", "td_sync",
+            "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_destroy", "td_last_error", "td_version")
+TD_PROF_OFF, TD_PROF_LMHEAD, TD_PROF_GEMM, TD_PROF_ATTENTION, TD_PROF_STEP = range(5)
+
+
+class TdError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _ptr_array(ts: Sequence) -> ctypes.Array:
+    return (c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+class Denoiser:
+    """One libtd context: a denoiser tower bound to one device and one HIP stream.
+
+    cfg keys: n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ff, vocab, block_size,
+    max_batch, max_prefix_tokens, dtype ("f32"/"bf16"), rms_eps.
+    weights: torch tensors on the GPU in the config's dtype (bf16 as torch.bfloat16),
+    keys as in td_weights; per-layer entries are lists.
+    """
+
+    def __init__(self, cfg: Dict, weights: Dict, stream=None):
+        import torch
+
+        self._torch = torch
+        self.cfg = dict(cfg)
+        c = TdConfig(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"],
+                     cfg["d_ff"], cfg["vocab"], cfg["block_size"], cfg["max_batch"], cfg["max_prefix_tokens"],
+                     TD_BF16 if cfg["dtype"] == "bf16" else TD_F32, cfg.get("rms_eps", 1e-6))
+        self._keep = {k: _ptr_array(weights[k]) for k in
+                      ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w1", "w2")}
+        w = TdWeights(weights["tok_emb"].data_ptr(), weights["pos_emb"].data_ptr(), self._keep["attn_norm"],
+                      self._keep["wq"], self._keep["wk"], self._keep["wv"], self._keep["wo"],
+                      self._keep["mlp_norm"], self._keep["w1"], self._keep["w2"], weights["final_norm"].data_ptr(),
+                      weights["lm_head"].data_ptr())
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        ctx = _CTX()
+        st = lib.td_create(ctypes.byref(c), ctypes.byref(w), c_void_p(self.stream.cuda_stream), ctypes.byref(ctx))
+        if st != TD_OK:
+            raise TdError(st, lib.td_last_error(None).decode())
+        self._ctx = ctx
+        self._prefix_refs = None
+
+    def _check(self, st: int):
+        if st != TD_OK:
+            raise TdError(st, lib.td_last_error(self._ctx).decode())
+
+    @property
+    def kernels_per_step(self) -> int:
+        return lib.td_kernels_per_step(self._ctx)
+
+    def set_prefix(self, offsets: Sequence[int], k_caches: Sequence, v_caches: Sequence) -> None:
+        n = len(offsets) - 1
+        off = (c_int64 * (n + 1))(*[int(v) for v in offsets])
+        ka, va = _ptr_array(k_caches), _ptr_array(v_caches)
+        self._check(lib.td_set_prefix(self._ctx, n, off, ka, va))
+        self._prefix_refs = (list(k_caches), list(v_caches))   # borrowed by the ctx
+
+    def denoise_step(self, tokens, committed, inv_temp, gamma: float, newly=None, conf=None, argmax=None,
+                     logits=None) -> None:
+        self._check(lib.td_denoise_step(self._ctx, _ptr(tokens), _ptr(committed), _ptr(inv_temp), float(gamma),
+                                        _ptr(newly), _ptr(conf), _ptr(argmax), _ptr(logits)))
+
+    def generate_block(self, tokens, committed, inv_temp, gamma: float, steps=None, commit_step=None) -> None:
+        self._check(lib.td_generate_block(self._ctx, _ptr(tokens), _ptr(committed), _ptr(inv_temp), float(gamma),
+                                          _ptr(steps), _ptr(commit_step)))
+
+    def debug_attention(self, layer: int, qkv, o) -> None:
+        self._check(lib.td_debug_attention(self._ctx, int(layer), _ptr(qkv), _ptr(o)))
+
+    def profile_begin(self, kind: int) -> None:
+        self._check(lib.td_profile_begin(self._ctx, int(kind)))
+
+    def profile_end(self, max_launches: int = 65536):
+        buf = (c_float * max_launches)()
+        n = lib.td_profile_end(self._ctx, buf, max_launches)
+        if n < 0:
+            raise TdError(TD_EDEVICE, lib.td_last_error(self._ctx).decode())
+        return [buf[i] for i in range(min(n, max_launches))]
+
+    def sync(self) -> None:
+        self._check(lib.td_sync(self._ctx))
+
+    def close(self) -> None:
+        if getattr(self, "_ctx", None):
+            lib.td_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,133 @@
+// Weight packing, loop-state kernels and the token + block-position embedding.
+#include "td_device.h"
+#include "td_kernels.h"
+
+namespace td {
+
+namespace {
+
+// W [N][K] -> MFMA tile order; one thread per 8-element lane fragment.
+template <typename T>
+__global__ void pack_weight_kernel(const T *__restrict__ W, T *__restrict__ Wp, int N, int K) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int KT = K / 32;
+  const int64_t total = (int64_t)N * K / 8;
+  if (idx >= total) return;
+  const int64_t tile = idx >> 6;
+  const int lane = (int)(idx & 63);
+  const int nt = (int)(tile / KT), kt = (int)(tile % KT);
+  const T *src = W + (int64_t)(nt * 16 + (lane & 15)) * K + kt * 32 + (lane >> 4) * 8;
+  T *dst = Wp + idx * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = src[e];
+}
+
+__global__ __launch_bounds__(1024) void prep_kernel(const int *tokens, const uint8_t *committed, int M, int V,
+                                                    StepState st) {
+  __shared__ int s_wave[16];
+  int base = 0, err = 0;
+  for (int r0 = 0; r0 < M; r0 += 1024) {
+    const int r = r0 + threadIdx.x;
+    bool masked = false;
+    if (r < M) {
+      const int tok = tokens[r];
+      masked = committed[r] == 0;
+      const bool bad = tok < 0 || tok > V || masked != (tok == V);
+      if (bad) {
+        err = 1;
+        masked = false;    // an invalid row is left untouched
+      }
+    }
+    base = block_compact(masked, base, st.rowlist, st.rowpos, r < M ? r : -1, s_wave);
+  }
+  if (err) atomicOr(st.err, 1);
+  if (threadIdx.x == 0) {
+    *st.n_rows = base;
+    *st.done = base == 0 ? 1 : 0;
+  }
+}
+
+__global__ __launch_bounds__(1024) void init_block_kernel(int *tokens, uint8_t *committed, int8_t *commit_step,
+                                                          int *steps, int n, int B, int V, StepState st) {
+  const int M = n * B;
+  for (int r = threadIdx.x; r < M; r += blockDim.x) {
+    tokens[r] = V;
+    committed[r] = 0;
+    if (commit_step) commit_step[r] = -1;
+    st.rowlist[r] = r;
+    st.rowpos[r] = r;
+  }
+  if (steps)
+    for (int i = threadIdx.x; i < n; i += blockDim.x) steps[i] = 0;
+  if (threadIdx.x == 0) {
+    *st.n_rows = M;
+    *st.done = M == 0 ? 1 : 0;
+    *st.t = 0;
+  }
+}
+
+// x[r] = E[tok[r]] + Pos[r % B] (fp32) and the partial sums of squares of every 16-column
+// group, [d/16][M], which the next GEMM prologue turns into the RMSNorm row scale.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int *tokens, const T *E, const T *Pos, float *x,
+                                                    float *ssq, int M, int B, int d, int V, StepState st) {
+  if (*st.done) return;
+  const int r = blockIdx.x;
+  int tok = tokens[r];
+  if (tok < 0 || tok > V) {
+    if (threadIdx.x == 0) atomicOr(st.err, 2);
+    tok = V;
+  }
+  const T *e = E + (size_t)tok * d;
+  const T *p = Pos + (size_t)(r % B) * d;
+  for (int grp = threadIdx.x; grp < d / 16; grp += blockDim.x) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int k = grp * 16 + c;
+      const float v = to_f32<T>(e[k]) + to_f32<T>(p[k]);
+      x[(size_t)r * d + k] = v;
+      s += v * v;
+    }
+    ssq[(size_t)grp * M + r] = s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_weight(int dtype, const void *W, void *Wp, int N, int K, hipStream_t s) {
+  if (N % 16 || K % 32) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)N * K / 8;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(pack_weight_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t *)W, (bf16_t *)Wp, N, K);
+  else
+    hipLaunchKernelGGL(pack_weight_kernel<float>, grid, dim3(256), 0, s, (const float *)W, (float *)Wp, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const int *tokens, const uint8_t *committed, int M, int V, StepState st, hipStream_t s) {
+  hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, s, tokens, committed, M, V, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_block(int *tokens, uint8_t *committed, int8_t *commit_step, int *steps, int n, int B,
+                             int V, StepState st, hipStream_t s) {
+  hipLaunchKernelGGL(init_block_kernel, dim3(1), dim3(1024), 0, s, tokens, committed, commit_step, steps, n, B, V,
+                     st);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(int dtype, const int *tokens, const void *E, const void *Pos, float *x, float *ssq, int M,
+                        int B, int d, int V, StepState st, hipStream_t s) {
+  if (d % 16) return hipErrorInvalidValue;
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, s, tokens, (const bf16_t *)E,
+                       (const bf16_t *)Pos, x, ssq, M, B, d, V, st);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, s, tokens, (const float *)E, (const float *)Pos,
+                       x, ssq, M, B, d, V, st);
+  return hipGetLastError();
+}
+
+}  // namespace td

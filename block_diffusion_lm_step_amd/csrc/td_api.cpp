@@ -1,0 +1,603 @@
+// Host runtime behind td.h: validation, workspace, weight packing, split-K planning,
+// and the launch sequence of one denoising step / one block loop on the ctx's stream.
+#include "../../include/td.h"
+#include "td_kernels.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+using namespace td;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct GemmPlan {
+  int ktw = 1, ksplit = 1;
+};
+
+struct VStatHost {   // mirror of the device VStat (max, sumexp, argmax)
+  float m, s;
+  int a;
+};
+
+}  // namespace
+
+struct td_ctx {
+  td_config cfg{};
+  int dev = 0;
+  hipStream_t stream = nullptr;
+  std::string err;
+  int elt = 4;
+
+  // weights (ctx-owned, packed)
+  void *tok_emb = nullptr, *pos_emb = nullptr, *final_norm = nullptr, *lm_head = nullptr;
+  std::vector<void *> attn_norm, mlp_norm, wqkv, wo, w1, w2;
+
+  // workspace
+  int Mmax = 0, Nqkv = 0;
+  float *x = nullptr, *ssq = nullptr, *part = nullptr, *conf_row = nullptr, *vpart = nullptr;
+  void *qkv = nullptr, *o = nullptr, *u = nullptr;
+  unsigned *counters = nullptr;
+  int *arg_row = nullptr;
+  int *state_ints = nullptr;    // rowlist | rowpos | n_rows, done, t, err, counter
+  StepState st{};
+  GemmPlan p_qkv, p_wo, p_w1, p_w2;
+
+  // prefix binding
+  int n_seqs = 0;
+  std::vector<int64_t> offsets;
+  int64_t *offsets_d = nullptr;
+  std::vector<const void *> kc, vc;
+  AttnItem *items_d = nullptr;
+  int *pair_first_d = nullptr, *pair_count_d = nullptr;
+  int n_items = 0, n_pairs = 0;
+  size_t items_cap = 0, pairs_cap = 0;
+  float *att_o = nullptr, *att_ml = nullptr;
+  size_t att_cap_rows = 0;   // capacity in partial rows (items * R)
+  size_t part_cap = 0;       // split-K partial capacity (floats)
+
+  // profiling: event pairs around the launches of one kernel class
+  int prof_kind = TD_PROF_OFF;
+  std::vector<hipEvent_t> ev_start, ev_stop;
+  size_t prof_n = 0;
+};
+
+namespace {
+
+td_status fail(td_ctx *c, td_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  else g_create_error = buf;
+  return s;
+}
+
+#define TD_HIP(c, expr)                                                                        \
+  do {                                                                                         \
+    hipError_t e_ = (expr);                                                                    \
+    if (e_ != hipSuccess) return fail((c), TD_EDEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+template <typename P>
+td_status dmalloc(td_ctx *c, P **p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipMalloc((void **)p, bytes);
+  if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+    return fail(c, TD_ENOMEM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+  if (e != hipSuccess) return fail(c, TD_EDEVICE, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+  return TD_OK;
+}
+
+#define TD_TRY(expr)            \
+  do {                          \
+    td_status s_ = (expr);      \
+    if (s_ != TD_OK) return s_; \
+  } while (0)
+
+bool finite(float v) { return std::isfinite(v); }
+
+td_status validate_config(const td_config *cfg) {
+  if (!cfg) return fail(nullptr, TD_EINVAL, "cfg is NULL");
+  const td_config &c = *cfg;
+  if (c.dtype != TD_F32 && c.dtype != TD_BF16) return fail(nullptr, TD_EINVAL, "dtype must be TD_F32 or TD_BF16");
+  if (c.n_layers < 1 || c.n_layers > 1024) return fail(nullptr, TD_EINVAL, "n_layers must be in [1, 1024]");
+  if (c.d_model < 64 || c.d_model % 64) return fail(nullptr, TD_EINVAL, "d_model must be a positive multiple of 64");
+  if (c.d_ff < 64 || c.d_ff % 64) return fail(nullptr, TD_EINVAL, "d_ff must be a positive multiple of 64");
+  if (c.vocab < 64 || c.vocab % 64) return fail(nullptr, TD_EINVAL, "vocab must be a positive multiple of 64");
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(nullptr, TD_EINVAL, "head_dim must be 64 or 128");
+  if (c.n_heads < 1 || c.n_kv_heads < 1 || c.n_heads % c.n_kv_heads)
+    return fail(nullptr, TD_EINVAL, "n_heads must be a positive multiple of n_kv_heads");
+  if (c.block_size != 8 && c.block_size != 16 && c.block_size != 32)
+    return fail(nullptr, TD_EINVAL, "block_size must be 8, 16 or 32");
+  if (c.max_batch < 1 || (int64_t)c.max_batch * c.block_size > (1 << 20))
+    return fail(nullptr, TD_EINVAL, "max_batch must be in [1, 2^20 / block_size]");
+  if (c.max_prefix_tokens < 0 || c.max_prefix_tokens > ((int64_t)1 << 40))
+    return fail(nullptr, TD_EINVAL, "max_prefix_tokens out of range");
+  if (!finite(c.rms_eps) || c.rms_eps <= 0.f) return fail(nullptr, TD_EINVAL, "rms_eps must be finite and > 0");
+  if ((int64_t)c.n_heads * c.head_dim > (1 << 20)) return fail(nullptr, TD_EINVAL, "n_heads * head_dim too large");
+  return TD_OK;
+}
+
+td_status validate_weights(const td_config &c, const td_weights *w) {
+  if (!w) return fail(nullptr, TD_EINVAL, "weights is NULL");
+  if (!w->tok_emb || !w->pos_emb || !w->final_norm || !w->lm_head)
+    return fail(nullptr, TD_EINVAL, "a global weight pointer is NULL");
+  const void *const *lists[] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w1, w->w2};
+  for (auto *l : lists) {
+    if (!l) return fail(nullptr, TD_EINVAL, "a per-layer weight array is NULL");
+    for (int i = 0; i < c.n_layers; ++i)
+      if (!l[i]) return fail(nullptr, TD_EINVAL, "per-layer weight pointer %d is NULL", i);
+  }
+  return TD_OK;
+}
+
+GemmPlan plan_gemm(int M, int N, int K) {
+  GemmPlan p;
+  const int KT = K / 32;
+  const int mblocks = M <= 16 ? 1 : (M + 63) / 64;
+  const long tiles = (long)(N / 16) * mblocks;
+  int ks = 1;
+  while (tiles * ks < 640 && KT / (4 * ks * 2) >= 4) ks *= 2;
+  int ktw = (KT + 4 * ks - 1) / (4 * ks);
+  if (ktw > 16) {
+    ks = (KT + 63) / 64;
+    ktw = (KT + 4 * ks - 1) / (4 * ks);
+  }
+  p.ksplit = ks;
+  p.ktw = std::max(1, ktw);
+  return p;
+}
+
+int chunk_keys(int R) {
+  int tc = 128;
+  while (tc < 8 * R && tc < 4096) tc *= 2;
+  return tc;
+}
+
+constexpr size_t PROF_MAX = 65536;
+
+td_status prof_mark(td_ctx *c, int kind, bool start) {
+  if (c->prof_kind != kind || c->prof_n >= PROF_MAX) return TD_OK;
+  if (start) {
+    if (c->ev_start.size() <= c->prof_n) {
+      hipEvent_t a, b;
+      TD_HIP(c, hipEventCreate(&a));
+      TD_HIP(c, hipEventCreate(&b));
+      c->ev_start.push_back(a);
+      c->ev_stop.push_back(b);
+    }
+    TD_HIP(c, hipEventRecord(c->ev_start[c->prof_n], c->stream));
+  } else {
+    TD_HIP(c, hipEventRecord(c->ev_stop[c->prof_n], c->stream));
+    ++c->prof_n;
+  }
+  return TD_OK;
+}
+
+td_status enqueue_attention(td_ctx *c, int layer, const void *qkv, void *o, const int *done) {
+  const td_config &g = c->cfg;
+  AttnArgs a{};
+  a.B = g.block_size;
+  a.H = g.n_heads;
+  a.Hkv = g.n_kv_heads;
+  a.hd = g.head_dim;
+  a.Nqkv = c->Nqkv;
+  a.G = g.n_heads / g.n_kv_heads;
+  a.R = a.G * a.B;
+  a.qkv = qkv;
+  a.kc = c->kc[layer];
+  a.vc = c->vc[layer];
+  a.offsets = c->offsets_d;
+  a.items = c->items_d;
+  a.n_items = c->n_items;
+  a.pair_first = c->pair_first_d;
+  a.pair_count = c->pair_count_d;
+  a.n_pairs = c->n_pairs;
+  a.part_o = c->att_o;
+  a.part_ml = c->att_ml;
+  a.o = o;
+  a.ldo = g.n_heads * g.head_dim;
+  a.scale = 1.0f / std::sqrt((float)g.head_dim);
+  a.done = done;
+  TD_TRY(prof_mark(c, TD_PROF_ATTENTION, true));
+  TD_HIP(c, launch_attention(g.dtype, a, c->stream));
+  TD_TRY(prof_mark(c, TD_PROF_ATTENTION, false));
+  return TD_OK;
+}
+
+NormIn norm_in(td_ctx *c, const void *gain) {
+  NormIn n{};
+  n.x = c->x;
+  n.ssq = c->ssq;
+  n.nparts = c->cfg.d_model / 16;
+  n.gain = gain;
+  n.eps = c->cfg.rms_eps;
+  return n;
+}
+
+td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const void *A, int lda,
+                       const void *gain, const void *Wp, const GemmPlan &p, void *out, int ldo) {
+  GemmArgs a{};
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.A = A;
+  a.lda = lda;
+  if (norm) a.norm = norm_in(c, gain);
+  a.Wp = Wp;
+  a.ktw = p.ktw;
+  a.ksplit = p.ksplit;
+  a.part = c->part;
+  a.counters = c->counters;
+  a.out = out;
+  a.ldo = ldo;
+  a.ssq_out = c->ssq;
+  a.done = c->st.done;
+  TD_TRY(prof_mark(c, TD_PROF_GEMM, true));
+  TD_HIP(c, launch_gemm(c->cfg.dtype, epi, norm, a, c->stream));
+  TD_TRY(prof_mark(c, TD_PROF_GEMM, false));
+  return TD_OK;
+}
+
+td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *inv_temp, float gamma,
+                       uint8_t *newly, float *conf_out, int *argmax_out, float *logits, int *steps,
+                       int8_t *commit_step) {
+  const td_config &g = c->cfg;
+  const int M = c->n_seqs * g.block_size;
+  const int d = g.d_model, Hd = g.n_heads * g.head_dim;
+  TD_TRY(prof_mark(c, TD_PROF_STEP, true));
+  TD_HIP(c, launch_embed(g.dtype, tokens, c->tok_emb, c->pos_emb, c->x, c->ssq, M, g.block_size, d, g.vocab, c->st,
+                         c->stream));
+  for (int l = 0; l < g.n_layers; ++l) {
+    TD_TRY(enqueue_gemm(c, EPI_STORE, true, M, c->Nqkv, d, nullptr, 0, c->attn_norm[l], c->wqkv[l], c->p_qkv, c->qkv,
+                        c->Nqkv));
+    TD_TRY(enqueue_attention(c, l, c->qkv, c->o, c->st.done));
+    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, Hd, c->o, Hd, nullptr, c->wo[l], c->p_wo, c->x, d));
+    TD_TRY(enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, nullptr, 0, c->mlp_norm[l], c->w1[l], c->p_w1, c->u,
+                        g.d_ff));
+    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->u, g.d_ff, nullptr, c->w2[l], c->p_w2, c->x, d));
+  }
+  LmArgs la{};
+  la.V = g.vocab;
+  la.d = d;
+  la.B = g.block_size;
+  la.n = c->n_seqs;
+  la.norm = norm_in(c, c->final_norm);
+  la.Wp = c->lm_head;
+  la.inv_temp = inv_temp;
+  la.vpart = c->vpart;
+  la.logits = logits;
+  la.st = c->st;
+  TD_TRY(prof_mark(c, TD_PROF_LMHEAD, true));
+  TD_HIP(c, launch_lmhead(g.dtype, la, c->stream));
+  TD_TRY(prof_mark(c, TD_PROF_LMHEAD, false));
+  CommitArgs ca{};
+  ca.V = g.vocab;
+  ca.B = g.block_size;
+  ca.n = c->n_seqs;
+  ca.nslices = g.vocab / 64;
+  ca.vpart = c->vpart;
+  ca.conf_row = c->conf_row;
+  ca.arg_row = c->arg_row;
+  ca.tokens = tokens;
+  ca.committed = committed;
+  ca.gamma = gamma;
+  ca.newly = newly;
+  ca.conf_out = conf_out;
+  ca.argmax_out = argmax_out;
+  ca.steps = steps;
+  ca.commit_step = commit_step;
+  ca.st = c->st;
+  TD_HIP(c, launch_merge_commit(ca, M, c->stream));
+  TD_TRY(prof_mark(c, TD_PROF_STEP, false));
+  return TD_OK;
+}
+
+td_status check_ctx(td_ctx *c) {
+  if (!c) return fail(nullptr, TD_EINVAL, "ctx is NULL");
+  return TD_OK;
+}
+
+td_status check_bound(td_ctx *c) {
+  if (c->n_seqs <= 0) return fail(c, TD_EINVAL, "no prefix bound: call td_set_prefix first");
+  TD_HIP(c, hipSetDevice(c->dev));
+  return TD_OK;
+}
+
+void free_all(td_ctx *c) {
+  auto f = [](void *p) {
+    if (p) (void)hipFree(p);
+  };
+  f(c->tok_emb); f(c->pos_emb); f(c->final_norm); f(c->lm_head);
+  for (auto *v : {&c->attn_norm, &c->mlp_norm, &c->wqkv, &c->wo, &c->w1, &c->w2})
+    for (void *p : *v) f(p);
+  f(c->x); f(c->ssq); f(c->part); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->o); f(c->u);
+  f(c->counters); f(c->arg_row); f(c->state_ints); f(c->offsets_d); f(c->items_d); f(c->pair_first_d);
+  f(c->pair_count_d); f(c->att_o); f(c->att_ml);
+  for (hipEvent_t e : c->ev_start) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->ev_stop) (void)hipEventDestroy(e);
+}
+
+td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
+  TD_HIP(c, hipGetDevice(&c->dev));
+  c->elt = g.dtype == TD_BF16 ? 2 : 4;
+  const size_t e = c->elt;
+  const size_t d = g.d_model, F = g.d_ff, V = g.vocab, L = g.n_layers;
+  const size_t Hd = (size_t)g.n_heads * g.head_dim, KVd = (size_t)g.n_kv_heads * g.head_dim;
+  c->Nqkv = (int)(Hd + 2 * KVd);
+  c->Mmax = g.max_batch * g.block_size;
+  const size_t M = c->Mmax;
+
+  // Packed weights.
+  TD_TRY(dmalloc(c, &c->tok_emb, (V + 1) * d * e));
+  TD_TRY(dmalloc(c, &c->pos_emb, (size_t)g.block_size * d * e));
+  TD_TRY(dmalloc(c, &c->final_norm, d * e));
+  TD_TRY(dmalloc(c, &c->lm_head, V * d * e));
+  TD_HIP(c, hipMemcpyAsync(c->tok_emb, w.tok_emb, (V + 1) * d * e, hipMemcpyDeviceToDevice, c->stream));
+  TD_HIP(c, hipMemcpyAsync(c->pos_emb, w.pos_emb, (size_t)g.block_size * d * e, hipMemcpyDeviceToDevice, c->stream));
+  TD_HIP(c, hipMemcpyAsync(c->final_norm, w.final_norm, d * e, hipMemcpyDeviceToDevice, c->stream));
+  TD_HIP(c, launch_pack_weight(g.dtype, w.lm_head, c->lm_head, (int)V, (int)d, c->stream));
+  c->attn_norm.assign(L, nullptr); c->mlp_norm.assign(L, nullptr); c->wqkv.assign(L, nullptr);
+  c->wo.assign(L, nullptr); c->w1.assign(L, nullptr); c->w2.assign(L, nullptr);
+  for (size_t l = 0; l < L; ++l) {
+    TD_TRY(dmalloc(c, &c->attn_norm[l], d * e));
+    TD_TRY(dmalloc(c, &c->mlp_norm[l], d * e));
+    TD_TRY(dmalloc(c, &c->wqkv[l], (size_t)c->Nqkv * d * e));
+    TD_TRY(dmalloc(c, &c->wo[l], d * Hd * e));
+    TD_TRY(dmalloc(c, &c->w1[l], F * d * e));
+    TD_TRY(dmalloc(c, &c->w2[l], d * F * e));
+    TD_HIP(c, hipMemcpyAsync(c->attn_norm[l], w.attn_norm[l], d * e, hipMemcpyDeviceToDevice, c->stream));
+    TD_HIP(c, hipMemcpyAsync(c->mlp_norm[l], w.mlp_norm[l], d * e, hipMemcpyDeviceToDevice, c->stream));
+    char *qkv = (char *)c->wqkv[l];
+    TD_HIP(c, launch_pack_weight(g.dtype, w.wq[l], qkv, (int)Hd, (int)d, c->stream));
+    TD_HIP(c, launch_pack_weight(g.dtype, w.wk[l], qkv + Hd * d * e, (int)KVd, (int)d, c->stream));
+    TD_HIP(c, launch_pack_weight(g.dtype, w.wv[l], qkv + (Hd + KVd) * d * e, (int)KVd, (int)d, c->stream));
+    TD_HIP(c, launch_pack_weight(g.dtype, w.wo[l], c->wo[l], (int)d, (int)Hd, c->stream));
+    TD_HIP(c, launch_pack_weight(g.dtype, w.w1[l], c->w1[l], (int)F, (int)d, c->stream));
+    TD_HIP(c, launch_pack_weight(g.dtype, w.w2[l], c->w2[l], (int)d, (int)F, c->stream));
+  }
+
+  // Workspace sized for max_batch (split-K partials are sized per batch in td_set_prefix).
+  const size_t Nmax = std::max({(size_t)c->Nqkv, d, F});
+  TD_TRY(dmalloc(c, &c->x, M * d * 4));
+  TD_TRY(dmalloc(c, &c->ssq, (d / 16) * M * 4));
+  TD_TRY(dmalloc(c, &c->counters, ((M + 15) / 16) * (Nmax / 16) * sizeof(unsigned)));
+  TD_TRY(dmalloc(c, &c->qkv, M * c->Nqkv * e));
+  TD_TRY(dmalloc(c, &c->o, M * Hd * e));
+  TD_TRY(dmalloc(c, &c->u, M * F * e));
+  TD_TRY(dmalloc(c, &c->conf_row, M * 4));
+  TD_TRY(dmalloc(c, &c->arg_row, M * 4));
+  TD_TRY(dmalloc(c, &c->vpart, M * (V / 64) * sizeof(VStatHost)));
+  TD_TRY(dmalloc(c, &c->state_ints, (2 * M + 8) * sizeof(int)));
+  TD_HIP(c, hipMemsetAsync(c->counters, 0, ((M + 15) / 16) * (Nmax / 16) * sizeof(unsigned), c->stream));
+  TD_HIP(c, hipMemsetAsync(c->state_ints, 0, (2 * M + 8) * sizeof(int), c->stream));
+  int *si = c->state_ints;
+  c->st.rowlist = si;
+  c->st.rowpos = si + M;
+  c->st.n_rows = si + 2 * M;
+  c->st.done = si + 2 * M + 1;
+  c->st.t = si + 2 * M + 2;
+  c->st.err = si + 2 * M + 3;
+  c->st.counter = (unsigned *)(si + 2 * M + 4);
+  TD_HIP(c, hipStreamSynchronize(c->stream));
+  return TD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+td_status td_create(const td_config *cfg, const td_weights *w, void *stream, td_ctx **out) {
+  g_create_error.clear();
+  if (!out) return fail(nullptr, TD_EINVAL, "out is NULL");
+  *out = nullptr;
+  TD_TRY(validate_config(cfg));
+  TD_TRY(validate_weights(*cfg, w));
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev <= 0)
+    return fail(nullptr, TD_EDEVICE, "no HIP device available (%s)", hipGetErrorString(e));
+  td_ctx *c = new (std::nothrow) td_ctx();
+  if (!c) return fail(nullptr, TD_ENOMEM, "host allocation failed");
+  c->cfg = *cfg;
+  c->stream = (hipStream_t)stream;
+  td_status s = create_impl(c, *cfg, *w);
+  if (s != TD_OK) {
+    g_create_error = c->err;
+    (void)hipStreamSynchronize(c->stream);
+    free_all(c);
+    delete c;
+    return s;
+  }
+  *out = c;
+  return TD_OK;
+}
+
+td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const void *const *k_cache_host,
+                        const void *const *v_cache_host) {
+  TD_TRY(check_ctx(c));
+  const td_config &g = c->cfg;
+  if (n_seqs < 1 || n_seqs > g.max_batch) return fail(c, TD_EINVAL, "n_seqs must be in [1, max_batch=%d]", g.max_batch);
+  if (!off || !k_cache_host || !v_cache_host) return fail(c, TD_EINVAL, "NULL offsets or cache array");
+  if (off[0] != 0) return fail(c, TD_EINVAL, "prefix_offsets[0] must be 0");
+  for (int i = 0; i < n_seqs; ++i)
+    if (off[i + 1] < off[i]) return fail(c, TD_EINVAL, "prefix_offsets must be non-decreasing");
+  if (off[n_seqs] > g.max_prefix_tokens)
+    return fail(c, TD_ENOMEM, "sum of prefix lengths %lld exceeds max_prefix_tokens %lld", (long long)off[n_seqs],
+                (long long)g.max_prefix_tokens);
+  for (int l = 0; l < g.n_layers; ++l)
+    if (off[n_seqs] > 0 && (!k_cache_host[l] || !v_cache_host[l]))
+      return fail(c, TD_EINVAL, "cache pointer of layer %d is NULL", l);
+  TD_HIP(c, hipSetDevice(c->dev));
+  TD_HIP(c, hipStreamSynchronize(c->stream));   // previous work may still read the old binding
+
+  const int G = g.n_heads / g.n_kv_heads, R = G * g.block_size, tc = chunk_keys(R);
+  std::vector<AttnItem> items;
+  std::vector<int> pfirst, pcount;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int64_t P = off[i + 1] - off[i];
+    if (P > (int64_t)1 << 30) return fail(c, TD_EINVAL, "prefix of sequence %d too long", i);
+    for (int h = 0; h < g.n_kv_heads; ++h) {
+      const int pair = i * g.n_kv_heads + h;
+      pfirst.push_back((int)items.size());
+      for (int64_t k0 = 0; k0 < P; k0 += tc)
+        items.push_back(AttnItem{i, h, (int)k0, (int)std::min<int64_t>(P, k0 + tc), 0, pair});
+      items.push_back(AttnItem{i, h, 0, g.block_size, 1, pair});
+      pcount.push_back((int)items.size() - pfirst.back());
+    }
+  }
+  if (items.size() > ((size_t)1 << 28)) return fail(c, TD_EINVAL, "too many attention work items");
+  auto grow = [&](auto **p, size_t &cap, size_t need, size_t elt) -> td_status {
+    if (need <= cap) return TD_OK;
+    if (*p) TD_HIP(c, hipFree(*p));
+    *p = nullptr;
+    cap = 0;
+    TD_TRY(dmalloc(c, p, need * elt));
+    cap = need;
+    return TD_OK;
+  };
+  size_t cap_items = c->items_cap;
+  TD_TRY(grow(&c->items_d, cap_items, items.size(), sizeof(AttnItem)));
+  c->items_cap = cap_items;
+  size_t cap_pairs = c->pairs_cap, cap_pairs2 = c->pairs_cap;
+  TD_TRY(grow(&c->pair_first_d, cap_pairs, pfirst.size(), sizeof(int)));
+  TD_TRY(grow(&c->pair_count_d, cap_pairs2, pcount.size(), sizeof(int)));
+  c->pairs_cap = std::min(cap_pairs, cap_pairs2);
+  const size_t rows = items.size() * (size_t)R;
+  size_t cap_o = c->att_cap_rows, cap_ml = c->att_cap_rows;
+  TD_TRY(grow(&c->att_o, cap_o, rows, (size_t)g.head_dim * 4));
+  TD_TRY(grow(&c->att_ml, cap_ml, rows, 8));
+  c->att_cap_rows = std::min(cap_o, cap_ml);
+  if (!c->offsets_d) TD_TRY(dmalloc(c, &c->offsets_d, (size_t)(g.max_batch + 1) * sizeof(int64_t)));
+  TD_HIP(c, hipMemcpy(c->items_d, items.data(), items.size() * sizeof(AttnItem), hipMemcpyHostToDevice));
+  TD_HIP(c, hipMemcpy(c->pair_first_d, pfirst.data(), pfirst.size() * sizeof(int), hipMemcpyHostToDevice));
+  TD_HIP(c, hipMemcpy(c->pair_count_d, pcount.data(), pcount.size() * sizeof(int), hipMemcpyHostToDevice));
+  TD_HIP(c, hipMemcpy(c->offsets_d, off, (size_t)(n_seqs + 1) * sizeof(int64_t), hipMemcpyHostToDevice));
+  {  // split-K plans for this batch size and their partial buffer
+    const int M = n_seqs * g.block_size;
+    const int d = g.d_model, F = g.d_ff, Hd = g.n_heads * g.head_dim;
+    c->p_qkv = plan_gemm(M, c->Nqkv, d);
+    c->p_wo = plan_gemm(M, d, Hd);
+    c->p_w1 = plan_gemm(M, F, d);
+    c->p_w2 = plan_gemm(M, d, F);
+    size_t part = 0;
+    for (auto pr : {std::make_pair(c->p_qkv, c->Nqkv), std::make_pair(c->p_wo, d), std::make_pair(c->p_w1, F),
+                    std::make_pair(c->p_w2, d)})
+      if (pr.first.ksplit > 1) part = std::max(part, (size_t)pr.first.ksplit * M * pr.second);
+    size_t cap = c->part_cap;
+    TD_TRY(grow(&c->part, cap, part, 4));
+    c->part_cap = cap;
+  }
+  c->offsets.assign(off, off + n_seqs + 1);
+  c->kc.assign(k_cache_host, k_cache_host + g.n_layers);
+  c->vc.assign(v_cache_host, v_cache_host + g.n_layers);
+  c->n_items = (int)items.size();
+  c->n_pairs = (int)pfirst.size();
+  c->n_seqs = n_seqs;
+  return TD_OK;
+}
+
+td_status td_denoise_step(td_ctx *c, int32_t *tokens, uint8_t *committed, const float *inv_temp, float gamma,
+                          uint8_t *newly, float *conf_out, int32_t *argmax_out, float *logits_out) {
+  TD_TRY(check_ctx(c));
+  if (!tokens || !committed) return fail(c, TD_EINVAL, "tokens and committed must not be NULL");
+  if (!finite(gamma)) return fail(c, TD_EINVAL, "gamma must be finite");
+  TD_TRY(check_bound(c));
+  const int M = c->n_seqs * c->cfg.block_size;
+  TD_HIP(c, launch_prep(tokens, committed, M, c->cfg.vocab, c->st, c->stream));
+  return enqueue_step(c, tokens, committed, inv_temp, gamma, newly, conf_out, argmax_out, logits_out, nullptr,
+                      nullptr);
+}
+
+td_status td_generate_block(td_ctx *c, int32_t *tokens, uint8_t *committed, const float *inv_temp, float gamma,
+                            int32_t *steps, int8_t *commit_step) {
+  TD_TRY(check_ctx(c));
+  if (!tokens || !committed) return fail(c, TD_EINVAL, "tokens and committed must not be NULL");
+  if (!finite(gamma)) return fail(c, TD_EINVAL, "gamma must be finite");
+  TD_TRY(check_bound(c));
+  const td_config &g = c->cfg;
+  TD_HIP(c, launch_init_block(tokens, committed, commit_step, steps, c->n_seqs, g.block_size, g.vocab, c->st,
+                              c->stream));
+  for (int s = 0; s < g.block_size; ++s)
+    TD_TRY(enqueue_step(c, tokens, committed, inv_temp, gamma, nullptr, nullptr, nullptr, nullptr, steps,
+                        commit_step));
+  return TD_OK;
+}
+
+td_status td_debug_attention(td_ctx *c, int32_t layer, const void *qkv, void *o) {
+  TD_TRY(check_ctx(c));
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, TD_EINVAL, "layer out of range");
+  if (!qkv || !o) return fail(c, TD_EINVAL, "qkv and o must not be NULL");
+  TD_TRY(check_bound(c));
+  return enqueue_attention(c, layer, qkv, o, nullptr);
+}
+
+td_status td_sync(td_ctx *c) {
+  TD_TRY(check_ctx(c));
+  TD_HIP(c, hipSetDevice(c->dev));
+  TD_HIP(c, hipStreamSynchronize(c->stream));
+  int err = 0;
+  TD_HIP(c, hipMemcpy(&err, c->st.err, sizeof(int), hipMemcpyDeviceToHost));
+  if (err) {
+    const int zero = 0;
+    TD_HIP(c, hipMemcpy(c->st.err, &zero, sizeof(int), hipMemcpyHostToDevice));
+    return fail(c, TD_EDEVICE, "device-side input error %d: %s", err,
+                (err & 1) ? "token/committed state invalid (a token outside [0, vocab], or [MASK] not exactly at "
+                            "uncommitted positions)"
+                          : "token id outside [0, vocab]");
+  }
+  return TD_OK;
+}
+
+td_status td_profile_begin(td_ctx *c, int32_t kind) {
+  TD_TRY(check_ctx(c));
+  if (kind < TD_PROF_OFF || kind > TD_PROF_STEP) return fail(c, TD_EINVAL, "unknown profiling kind %d", kind);
+  c->prof_kind = kind;
+  return TD_OK;
+}
+
+int32_t td_profile_end(td_ctx *c, float *ms_out, int32_t max) {
+  if (!c) return -1;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return -1;
+  const size_t n = c->prof_n;
+  for (size_t i = 0; i < n && (int64_t)i < max && ms_out; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, c->ev_start[i], c->ev_stop[i]) != hipSuccess) return -1;
+    ms_out[i] = ms;
+  }
+  c->prof_n = 0;
+  c->prof_kind = TD_PROF_OFF;
+  return (int32_t)n;
+}
+
+int32_t td_kernels_per_step(const td_ctx *c) {
+  if (!c) return -1;
+  return 1 + 1 + 6 * c->cfg.n_layers + 2;   // prep/init, embed, per layer 6, LM head, merge+commit
+}
+
+void td_destroy(td_ctx *c) {
+  if (!c) return;
+  (void)hipSetDevice(c->dev);
+  (void)hipStreamSynchronize(c->stream);
+  free_all(c);
+  delete c;
+}
+
+const char *td_last_error(const td_ctx *c) { return c ? c->err.c_str() : g_create_error.c_str(); }
+
+const char *td_version(void) { return "td 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+// Device helpers for the gfx950 kernels: bf16 conversion, MFMA fragments, wave reductions.
+//
+// MFMA fragment convention (16x16 output tiles, 64-wide wavefront).  For a product
+// D[16][16] += A[16][K] * B[K][16], lane l holds the 8 contraction elements
+// {8*(l/16) .. 8*(l/16)+7} of A row (l % 16) and of B column (l % 16), and receives
+// D rows 4*(l/16) + r (r = 0..3) of column (l % 16).  Because A and B always use the
+// same lane/slot -> k assignment, any bijection between (lane group, slot) and the 32
+// contraction indices of one step gives the same sum; the kernels exploit this to pick
+// k (or key) orders that make their loads contiguous.
+//   bf16: one v_mfma_f32_16x16x32_bf16 per 32-wide step.
+//   fp32: eight v_mfma_f32_16x16x4f32, slot j of every lane group forming step j.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+#define TD_DEV __device__ __forceinline__
+
+TD_DEV float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bfloat16, round to nearest, ties to even (finite inputs).
+TD_DEV bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> TD_DEV float to_f32(T v);
+template <> TD_DEV float to_f32<float>(float v) { return v; }
+template <> TD_DEV float to_f32<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> TD_DEV T from_f32(float v);
+template <> TD_DEV float from_f32<float>(float v) { return v; }
+template <> TD_DEV bf16_t from_f32<bf16_t>(float v) { return f2bf(v); }
+
+// Eight consecutive contraction elements held by one lane.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+  uint4 raw;   // 8 bf16
+  TD_DEV void zero() { raw = make_uint4(0, 0, 0, 0); }
+  TD_DEV void load(const bf16_t *p) { raw = *reinterpret_cast<const uint4 *>(p); }
+  TD_DEV float get(int j) const {
+    uint32_t w = (&raw.x)[j >> 1];
+    return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+  TD_DEV void set8(const float *v) {
+    raw.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    raw.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    raw.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+    raw.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  }
+  TD_DEV bf16x8_t vec() const { return __builtin_bit_cast(bf16x8_t, raw); }
+};
+template <> struct Frag<float> {
+  float4 lo, hi;
+  TD_DEV void zero() { lo = hi = make_float4(0.f, 0.f, 0.f, 0.f); }
+  TD_DEV void load(const float *p) {
+    lo = reinterpret_cast<const float4 *>(p)[0];
+    hi = reinterpret_cast<const float4 *>(p)[1];
+  }
+  TD_DEV float get(int j) const { return j < 4 ? (&lo.x)[j] : (&hi.x)[j - 4]; }
+  TD_DEV void set8(const float *v) {
+    lo = make_float4(v[0], v[1], v[2], v[3]);
+    hi = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+// acc += A(frag a) * B(frag b) over one 32-wide contraction step.
+TD_DEV f32x4_t mma(const Frag<bf16_t> &a, const Frag<bf16_t> &b, f32x4_t acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.vec(), b.vec(), acc, 0, 0, 0);
+}
+TD_DEV f32x4_t mma(const Frag<float> &a, const Frag<float> &b, f32x4_t acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+  return acc;
+}
+
+TD_DEV f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// Butterfly reductions over the 16 lanes that share l / 16 (offsets 1..8) or over the
+// four lane groups that share l % 16 (offsets 16, 32).
+TD_DEV float sum16(float v) {
+  v += __shfl_xor(v, 1); v += __shfl_xor(v, 2); v += __shfl_xor(v, 4); v += __shfl_xor(v, 8);
+  return v;
+}
+TD_DEV float max_groups(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16)); v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+TD_DEV float sum_groups(float v) {
+  v += __shfl_xor(v, 16); v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Softmax-statistics triple of a set of scaled logits: max, sum of exp(s - max), lowest
+// index of the max.  Merging is exact for (max, index) and fixed-order for the sum.
+struct VStat {
+  float m, s;
+  int a;
+};
+TD_DEV VStat vstat_merge(VStat x, VStat y) {
+  VStat r;
+  r.m = fmaxf(x.m, y.m);
+  // exp(m - max) is 1 for the side that holds the max (also when both are -inf, the
+  // empty set, so that the empty set stays the identity).
+  float ex = (x.m == r.m) ? 1.0f : __expf(x.m - r.m);
+  float ey = (y.m == r.m) ? 1.0f : __expf(y.m - r.m);
+  r.s = x.s * ex + y.s * ey;
+  r.a = (x.m > y.m) ? x.a : (y.m > x.m ? y.a : min(x.a, y.a));
+  return r;
+}
+
+TD_DEV float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+// Exclusive position of each flagged row among the flagged rows, in row order.
+// Called by every thread of one workgroup, once per chunk of blockDim.x rows; `row` < 0
+// marks a thread past the end.  s_wave holds blockDim.x / 64 ints of LDS.
+TD_DEV int block_compact(bool flag, int base, int *rowlist, int *rowpos, int row, int *s_wave) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long mask = __ballot(flag);
+  const int before = __popcll(mask & ((1ull << lane) - 1ull));
+  if (lane == 0) s_wave[wave] = __popcll(mask);
+  __syncthreads();
+  int off = base;
+  for (int w = 0; w < wave; ++w) off += s_wave[w];
+  int total = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) total += s_wave[w];
+  if (flag) {
+    rowlist[off + before] = row;
+    rowpos[row] = off + before;
+  } else if (row >= 0) {
+    rowpos[row] = -1;
+  }
+  __syncthreads();
+  return base + total;
+}

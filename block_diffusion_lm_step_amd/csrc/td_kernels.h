@@ -1,0 +1,106 @@
+// Host-side launch interface of the gfx950 kernels (internal to libtd).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace td {
+
+enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
+enum Epi { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2 };
+
+// ---------------------------------------------------------------- packing
+// W [N][K] row-major -> 16x32 MFMA tiles, tile (nt, kt) at ((nt * K/32 + kt) * 64 + lane) * 8,
+// lane l holding W[16 nt + l%16][32 kt + 8 (l/16) .. +8].
+hipError_t launch_pack_weight(int dtype, const void *W, void *Wp, int N, int K, hipStream_t s);
+hipError_t launch_copy_convert(int dtype, const void *src, void *dst, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM (weight streaming)
+struct NormIn {            // A = bf16/f32(rmsnorm(x) * gain) formed in the GEMM prologue
+  const float *x;          // [M][K] residual stream (fp32)
+  const float *ssq;        // [nparts][M] partial sums of squares of each x row
+  int nparts;
+  const void *gain;        // [K] config dtype
+  float eps;
+};
+
+struct GemmArgs {
+  int M, N, K;
+  const void *A;  int lda; // plain A [M][lda] (config dtype) when norm is off
+  NormIn norm;
+  const void *Wp;          // packed weight [N][K]
+  int ktw;                 // 32-wide k-tiles per wave (<= 16)
+  int ksplit;              // workgroups along K
+  float *part;             // [ksplit][M][N] split-K partials (fp32)
+  unsigned *counters;      // [ceil(M/64)][N/16], zero on entry, left zero
+  void *out; int ldo;      // STORE/GELU: config dtype [M][ldo]; RESID: fp32 x [M][ldo], updated in place
+  float *ssq_out;          // RESID: [N/16][M] partial sums of squares of the updated rows
+  const int *done;         // skip the launch when *done != 0 (nullable)
+};
+hipError_t launch_gemm(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+// One split-K work item: keys [k_begin, k_end) of a prefix chunk, or the block's own keys.
+struct AttnItem {
+  int seq, kvh;            // sequence and key/value head
+  int k_begin, k_end;      // key range (prefix token index within the sequence; or 0..B)
+  int is_block;            // 1: keys/values are the block's own k/v from the projections
+  int pair;                // seq * Hkv + kvh
+};
+struct AttnArgs {
+  int B, H, Hkv, hd, Nqkv, G, R;   // R = G * B query rows per (seq, kv head)
+  const void *qkv;                 // [n*B][Nqkv]: q | k_block | v_block (config dtype)
+  const void *kc, *vc;             // prefix caches [sumP][Hkv][hd]
+  const int64_t *offsets;          // [n+1] prefix offsets (device)
+  const AttnItem *items; int n_items;
+  const int *pair_first, *pair_count;   // item range of each (seq, kv head) pair
+  int n_pairs;
+  float *part_o;                   // [n_items][R][hd]
+  float *part_ml;                  // [n_items][R][2]
+  void *o; int ldo;                // output [n*B][H*hd] (config dtype)
+  float scale;                     // 1 / sqrt(hd)
+  const int *done;
+};
+hipError_t launch_attention(int dtype, const AttnArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- embedding, step control
+struct StepState {                 // device-resident loop state owned by the ctx
+  int *rowlist;                    // [M] rows (seq*B + p) still masked, ascending
+  int *rowpos;                     // [M] index of each row in rowlist, or -1
+  int *n_rows;                     // number of masked rows
+  int *done;                       // 1 when no row is masked
+  int *t;                          // step counter of td_generate_block
+  int *err;                        // device-side input error flags
+  unsigned *counter;               // last-workgroup counter of the vocab merge
+};
+hipError_t launch_prep(const int *tokens, const uint8_t *committed, int M, int V, StepState st, hipStream_t s);
+hipError_t launch_init_block(int *tokens, uint8_t *committed, int8_t *commit_step, int *steps, int n, int B,
+                             int V, StepState st, hipStream_t s);
+hipError_t launch_embed(int dtype, const int *tokens, const void *E, const void *Pos, float *x, float *ssq,
+                        int M, int B, int d, int V, StepState st, hipStream_t s);
+
+// ---------------------------------------------------------------- LM head + vocab reduction + commit
+struct LmArgs {
+  int V, d, B, n;
+  NormIn norm;                     // hf = rmsnorm(x) * g_final
+  const void *Wp;                  // packed LM head [V][d]
+  const float *inv_temp;           // [n*B] or nullptr
+  float *vpart;                    // [M][V/64][3] (max, sumexp, argmax) per row and vocab slice
+  float *logits;                   // debug capture [n*B][V] or nullptr
+  StepState st;
+};
+hipError_t launch_lmhead(int dtype, const LmArgs &a, hipStream_t s);
+
+struct CommitArgs {
+  int V, B, n, nslices;
+  const float *vpart;
+  float *conf_row; int *arg_row;   // [M] per-row results (indexed by position in rowlist)
+  int *tokens; uint8_t *committed;
+  float gamma;
+  uint8_t *newly;                  // nullable [n*B]
+  float *conf_out; int *argmax_out;   // nullable [n*B]
+  int *steps; int8_t *commit_step; // nullable
+  StepState st;
+};
+hipError_t launch_merge_commit(const CommitArgs &a, int max_rows, hipStream_t s);
+
+}  // namespace td

@@ -1,0 +1,163 @@
+/*
+ * td.h — C ABI of the block-diffusion denoising step on MI355X (gfx950).
+ *
+ * The operation.  A block of B positions, each holding a vocabulary token or the
+ * [MASK] token (id == vocab), is refined by a denoiser tower whose block queries
+ * attend, in one softmax, over the frozen context tower's cached prefix keys/values
+ * and bidirectionally over the block's own keys (poko-everyday.com Nemotron-TwoTower
+ * news item, section 技術/ビジネス面).  An LM head and a vocabulary softmax give each
+ * masked position a confidence (largest probability of its logits scaled by the
+ * position's inverse temperature) and a prediction (lowest id of the largest logit).
+ * Masked positions whose confidence is at least gamma are adopted; if none is, the
+ * single most confident masked position is; the rest stay [MASK], and the loop
+ * repeats until the block has no [MASK] left (PredNext "人工知能は拡散言語モデルの夢を
+ * 見るか？", section 拡散言語モデルで推論するには, steps 1-5; dzen.guru "NVIDIA
+ * Nemotron 70B генерирует текст…", section "Как попробовать?": block 16, threshold 0.8).
+ *
+ * Conventions.
+ *  - Every buffer pointer is a DEVICE pointer unless its name ends in _host.
+ *  - All calls enqueue work on the stream given to td_create and return without
+ *    waiting; results are valid once that stream has synchronised (td_sync).
+ *  - A ctx is bound to one device and one stream and is not thread-safe.
+ *  - Every call returns td_status; no C++ exception crosses the ABI.  Arguments are
+ *    validated on the host before anything is enqueued (TD_EINVAL, nothing runs).
+ *    Asynchronous device faults and device-side input errors (a token id outside
+ *    [0, vocab]) surface as TD_EDEVICE from td_sync or a later call; the message is
+ *    in td_last_error.
+ *  - Layouts are row-major.  bf16 is stored as IEEE bfloat16 (uint16 bit pattern).
+ */
+#ifndef TD_H
+#define TD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct td_ctx td_ctx;
+
+typedef enum {
+  TD_OK = 0,
+  TD_EINVAL = 1,        /* bad argument; nothing was enqueued */
+  TD_ENOMEM = 2,        /* device allocation failed or capacity exceeded */
+  TD_EDEVICE = 3,       /* HIP runtime / device error, or a device-side input error */
+  TD_EUNSUPPORTED = 4   /* valid but unsupported shape */
+} td_status;
+
+typedef enum { TD_F32 = 0, TD_BF16 = 1 } td_dtype;
+
+/* Tower shape and capacity.  Supported: head_dim in {64, 128}; block_size in {8, 16, 32};
+ * n_heads % n_kv_heads == 0; d_model, d_ff, vocab multiples of 64; n_heads*head_dim a
+ * multiple of 64.  dtype is the storage type of weights and prefix K/V; accumulators,
+ * the residual stream and all softmax statistics are fp32 either way. */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ff, vocab;
+  int32_t block_size;          /* B, positions per block */
+  int32_t max_batch;           /* capacity: sequences per call */
+  int64_t max_prefix_tokens;   /* capacity: sum of prefix lengths over the batch */
+  int32_t dtype;               /* td_dtype */
+  float rms_eps;               /* RMSNorm epsilon (1e-6 in the synthetic towers) */
+} td_config;
+
+/* Tower weights, DEVICE pointers in the config's dtype, row-major [out][in].
+ * Per-layer entries are HOST arrays of n_layers device pointers.  td_create copies
+ * and repacks every weight into ctx-owned memory; the caller may free its copies once
+ * the stream has synchronised after td_create. */
+typedef struct {
+  const void *tok_emb;                 /* [vocab+1][d]; row `vocab` embeds [MASK] */
+  const void *pos_emb;                 /* [B][d]; learned row per block position */
+  const void *const *attn_norm;        /* L x [d] RMSNorm gains before attention */
+  const void *const *wq;               /* L x [n_heads*head_dim][d] */
+  const void *const *wk;               /* L x [n_kv_heads*head_dim][d] */
+  const void *const *wv;               /* L x [n_kv_heads*head_dim][d] */
+  const void *const *wo;               /* L x [d][n_heads*head_dim] */
+  const void *const *mlp_norm;         /* L x [d] RMSNorm gains before the MLP */
+  const void *const *w1;               /* L x [d_ff][d]   (u = gelu_erf(h W1^T)) */
+  const void *const *w2;               /* L x [d][d_ff]   (x += u W2^T) */
+  const void *final_norm;              /* [d] */
+  const void *lm_head;                 /* [vocab][d], untied; never predicts [MASK] */
+} td_weights;
+
+/* Create a ctx on the current HIP device.  `stream` is a hipStream_t (NULL = default
+ * stream).  Validates cfg/w (TD_EINVAL), allocates the workspace for max_batch and
+ * max_prefix_tokens (TD_ENOMEM), packs the weights (TD_EDEVICE on runtime failure,
+ * e.g. no device).  On failure *out is NULL and the message is in td_last_error(NULL). */
+td_status td_create(const td_config *cfg, const td_weights *w, void *stream, td_ctx **out);
+
+/* Bind the frozen context tower's prefix K/V for a batch of n_seqs sequences.
+ * prefix_offsets_host[n_seqs+1]: sequence i owns tokens [off[i], off[i+1]) of every
+ * layer's cache; off[0] == 0, non-decreasing, off[n] <= max_prefix_tokens; a prefix
+ * may be empty.  k_cache_host / v_cache_host: HOST arrays of n_layers DEVICE pointers,
+ * layer l of the context tower feeding denoiser layer l, each [off[n]][n_kv_heads]
+ * [head_dim] in the config's dtype.  The caches are BORROWED: they must stay valid and
+ * unchanged until the next td_set_prefix or td_destroy.  Builds the split-K work list
+ * (host) and may grow the ctx's attention workspace. */
+td_status td_set_prefix(td_ctx *ctx, int32_t n_seqs, const int64_t *prefix_offsets_host,
+                        const void *const *k_cache_host, const void *const *v_cache_host);
+
+/* One denoising step over the bound batch.
+ *  tokens     int32 [n][B] in/out: a token id, or vocab ([MASK]) exactly where
+ *             committed == 0.
+ *  committed  uint8 [n][B] in/out.
+ *  inv_temp   fp32 [n][B] per-position logit inverse temperature, or NULL (all 1).
+ *  gamma      adoption threshold (finite; <= 0 adopts every masked position, > 1 adopts
+ *             exactly one per sequence with a masked position).
+ *  newly_committed  uint8 [n][B] or NULL: 1 where this step adopted the position.
+ *  conf_out   fp32 [n][B] or NULL: confidence of each position masked on entry
+ *             (unchanged elsewhere).
+ *  argmax_out int32 [n][B] or NULL: prediction of each position masked on entry.
+ *  logits_out fp32 [n][B][vocab] or NULL: debug capture of the raw logits (before the
+ *             inverse temperature) of positions masked on entry. */
+td_status td_denoise_step(td_ctx *ctx, int32_t *tokens, uint8_t *committed, const float *inv_temp,
+                          float gamma, uint8_t *newly_committed, float *conf_out, int32_t *argmax_out,
+                          float *logits_out);
+
+/* The whole block loop on the device, without host round-trips: sets tokens to [MASK]
+ * and committed to 0, then runs at most B steps; each sequence's loop ends when its
+ * block is fully committed (a finished sequence is left unchanged).
+ *  steps        int32 [n] or NULL: steps in which the sequence still had a masked position.
+ *  commit_step  int8 [n][B] or NULL: step index at which each position was adopted. */
+td_status td_generate_block(td_ctx *ctx, int32_t *tokens, uint8_t *committed, const float *inv_temp,
+                            float gamma, int32_t *steps, int8_t *commit_step);
+
+/* Debug hook: run the layer-`layer` attention (prefix split-K + in-block keys + merge)
+ * on caller-provided projections qkv [n*B][(n_heads + 2*n_kv_heads)*head_dim] (q, then
+ * k, then v of the block, config dtype) and write o [n*B][n_heads*head_dim]. */
+td_status td_debug_attention(td_ctx *ctx, int32_t layer, const void *qkv, void *o);
+
+/* Wait for the ctx's stream; report asynchronous device errors and device-side input
+ * errors recorded since the last td_sync. */
+td_status td_sync(td_ctx *ctx);
+
+/* Kernel classes for td_profile_begin. */
+typedef enum {
+  TD_PROF_OFF = 0,
+  TD_PROF_LMHEAD = 1,     /* LM head + fused vocab statistics (one launch per step) */
+  TD_PROF_GEMM = 2,       /* the 4 L layer projections of a step */
+  TD_PROF_ATTENTION = 3,  /* split-K attention + merge, L per step */
+  TD_PROF_STEP = 4        /* one whole step, embedding to commit */
+} td_prof_kind;
+
+/* Profiling: from now on bracket every launch of kernel class `kind` with a pair of HIP
+ * events on the ctx's stream (at most 65536 launches are recorded; later ones are not).
+ * TD_PROF_OFF stops recording. */
+td_status td_profile_begin(td_ctx *ctx, int32_t kind);
+
+/* Wait for the stream, write the duration in ms of each bracketed launch, in launch order,
+ * to ms_out_host[0 .. min(count, max)) and return the number recorded (or -1 on error);
+ * then clear the record.  Launches skipped on the device because the block was already
+ * committed are included (they take a few microseconds). */
+int32_t td_profile_end(td_ctx *ctx, float *ms_out_host, int32_t max);
+
+/* Number of kernels one td_denoise_step enqueues (for profiling and launch accounting). */
+int32_t td_kernels_per_step(const td_ctx *ctx);
+
+void td_destroy(td_ctx *ctx);                  /* NULL-safe; waits for the stream */
+const char *td_last_error(const td_ctx *ctx);  /* ctx == NULL: this thread's last create error */
+const char *td_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TD_H */

@@ -1,0 +1,122 @@
+"""Shared pieces of the GPU parity tests: building a case, running steps, comparing.
+
+Parity rules (from the problem statement, with the readings stated in the design doc):
+* logits: per row, max_v |z_gpu - z_oracle| / max_v |z_oracle| <= 1e-4 (fp32 towers) or
+  2e-2 (bf16 towers, against the bf16-faithful oracle);
+* token ids and commit masks, each step from the oracle's state, are bit-exact except at
+  positions whose oracle confidence is within 1e-3 of gamma or whose oracle top-2 gap
+  (p1 - p2) is below 1e-3; a fallback choice is also exempt when the oracle's two most
+  confident masked positions differ by less than 1e-3.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+import sys
+from typing import List, Optional
+
+import numpy as np
+
+EXEMPT = 1e-3
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@dataclasses.dataclass
+class Case:
+    w: object
+    orc: object
+    plens: np.ndarray
+    tau: np.ndarray
+    kv: object
+    dev: object          # Denoiser
+    tau_d: object
+    torch: object
+    keep: object = None
+
+
+def build_case(w, plens=None, mode=None, device="cuda") -> Case:
+    import torch
+
+    from block_diffusion_lm_step_amd import Denoiser
+    from synth import draw_inv_temp, draw_prefix_lengths, draw_tower
+    from synth.device import prefix_to_device, tower_config, tower_to_device
+    from tests.helpers import kv_provider, oracle_weights
+    from oracle import OracleTower
+
+    log(f"[case] building {w.name}: n={w.n} B={w.B} d={w.d} L={w.L} V={w.V} dtype={w.dtype}")
+    tw = draw_tower(w)
+    plens = draw_prefix_lengths(w) if plens is None else np.asarray(plens, dtype=np.int64)
+    tau = draw_inv_temp(w)
+    mode = mode or ("bf16" if w.dtype == "bf16" else "plain")
+    orc = OracleTower(oracle_weights(tw), H=w.H, Hkv=w.Hkv, hd=w.hd, eps=w.rms_eps, mode=mode)
+    kv = kv_provider(w, plens)
+    dW = tower_to_device(tw, device)
+    offsets, ks, vs = prefix_to_device(w, plens, device)
+    dev = Denoiser(tower_config(w, max_batch=w.n, max_prefix_tokens=max(1, offsets[-1])), dW)
+    dev.set_prefix(offsets, ks, vs)
+    del dW
+    torch.cuda.synchronize()
+    tau_d = torch.from_numpy(tau).to(device)
+    return Case(w, orc, plens, tau, kv, dev, tau_d, torch, keep=(ks, vs))
+
+
+def gpu_step(case: Case, tok: np.ndarray, committed: np.ndarray, gamma: float, want_logits=False):
+    """One td_denoise_step from state (tok, committed); returns host arrays."""
+    torch = case.torch
+    w = case.w
+    t_tok = torch.from_numpy(tok.astype(np.int32)).cuda()
+    t_c = torch.from_numpy(committed.astype(np.uint8)).cuda()
+    newly = torch.zeros_like(t_c)
+    conf = torch.full(tok.shape, float("nan"), dtype=torch.float32, device="cuda")
+    arg = torch.full(tok.shape, -1, dtype=torch.int32, device="cuda")
+    logits = torch.full(tok.shape + (w.V,), float("nan"), dtype=torch.float32, device="cuda") if want_logits else None
+    case.dev.denoise_step(t_tok, t_c, case.tau_d, gamma, newly=newly, conf=conf, argmax=arg, logits=logits)
+    case.dev.sync()
+    out = dict(tok=t_tok.cpu().numpy(), committed=t_c.cpu().numpy().astype(bool), U=newly.cpu().numpy().astype(bool),
+               conf=conf.cpu().numpy(), arg=arg.cpu().numpy())
+    if want_logits:
+        out["z"] = logits.cpu().numpy()
+    return out
+
+
+def logits_rel_err(z_gpu: np.ndarray, z_orc: np.ndarray) -> np.ndarray:
+    """Per-row max |dz| / max |z_oracle| over the vocabulary (rows = masked positions)."""
+    return np.abs(z_gpu.astype(np.float64) - z_orc).max(axis=-1) / np.abs(z_orc).max(axis=-1)
+
+
+def decision_mismatches(g: dict, r, committed_in: np.ndarray, gamma: float) -> List[str]:
+    """Non-exempt differences between the GPU step `g` and the oracle StepResult `r`."""
+    bad = []
+    masked = ~committed_in.astype(bool)
+    S, B = masked.shape
+    for s in range(S):
+        conf_o = r.conf[s]
+        gap_o = r.gap[s]
+        mc = np.where(masked[s], conf_o, -np.inf)
+        top = np.sort(mc)[::-1]
+        fallback_possible = not (mc >= gamma + EXEMPT).any()
+        for p in range(B):
+            if not masked[s, p]:
+                continue
+            near_gamma = abs(conf_o[p] - gamma) < EXEMPT
+            if g["arg"][s, p] != r.arg[s, p] and not (gap_o[p] < EXEMPT or near_gamma):
+                bad.append(f"seq {s} pos {p}: arg gpu {g['arg'][s, p]} oracle {r.arg[s, p]} "
+                           f"(conf {conf_o[p]:.6f}, gap {gap_o[p]:.2e})")
+            if g["U"][s, p] != r.U[s, p]:
+                fb_tie = fallback_possible and conf_o[p] >= top[0] - EXEMPT and (top[0] - top[1] < EXEMPT
+                                                                               if B > 1 else False)
+                if not (near_gamma or fb_tie):
+                    bad.append(f"seq {s} pos {p}: commit gpu {g['U'][s, p]} oracle {r.U[s, p]} "
+                               f"(conf {conf_o[p]:.6f}, gamma {gamma}, top2 {top[:2]})")
+    return bad
+
+
+def conf_abs_err(g: dict, r, committed_in: np.ndarray) -> float:
+    masked = ~committed_in.astype(bool)
+    if not masked.any():
+        return 0.0
+    return float(np.abs(g["conf"][masked].astype(np.float64) - r.conf[masked]).max())
