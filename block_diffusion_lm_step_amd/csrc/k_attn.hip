@@ -20,9 +20,12 @@
 //   O^T[hd][row] += V^T . P^T    (MFMA, A = V^T from LDS, B = P straight from S^T's
 //                                 accumulator layout; the keys are stored in LDS in
 //                                 the permuted order that makes this possible)
-// In bf16 the probabilities are split into a bf16 high part and a bf16 remainder so
-// the P.V product keeps ~16 bits of the fp32 probability.
-// The merge kernel combines an item's partial (m, l, O) rows in item order.
+// Queries are fp32 activations; with bf16 keys each query fragment enters the MFMA as a
+// bf16 high part plus a bf16 remainder, and the probabilities are split the same way
+// for P.V, so q and P keep ~16 significant bits.  The block's own keys and values are
+// fp32 activations as well: the (few) block keys of each pair are handled by a
+// separate fp32 VALU kernel that writes the same (m, l, O) partial.
+// The merge kernel combines a pair's partial (m, l, O) rows in item order.
 #include "td_device.h"
 #include "td_kernels.h"
 
@@ -57,28 +60,20 @@ __global__ __launch_bounds__(64 * NW) void attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T s_vt[2][HD * VP];
 
   const AttnItem it = a.items[blockIdx.x];
+  if (it.is_block) return;   // block keys: attn_block_kernel
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int nkeys = it.k_end - it.k_begin;
   const int nsub = (nkeys + SUB - 1) / SUB;
 
   // Key/value row pointers of this item.
-  const T *kbase, *vbase;
-  size_t kstride;
-  if (it.is_block) {
-    const T *q = reinterpret_cast<const T *>(a.qkv) + (size_t)it.seq * a.B * a.Nqkv;
-    kbase = q + (size_t)(a.H + it.kvh) * HD;
-    vbase = q + (size_t)(a.H + a.Hkv + it.kvh) * HD;
-    kstride = a.Nqkv;
-  } else {
-    const size_t off = (size_t)(a.offsets[it.seq] + it.k_begin) * a.Hkv + it.kvh;
-    kbase = reinterpret_cast<const T *>(a.kc) + off * HD;
-    vbase = reinterpret_cast<const T *>(a.vc) + off * HD;
-    kstride = (size_t)a.Hkv * HD;
-  }
+  const size_t off = (size_t)(a.offsets[it.seq] + it.k_begin) * a.Hkv + it.kvh;
+  const T *kbase = reinterpret_cast<const T *>(a.kc) + off * HD;
+  const T *vbase = reinterpret_cast<const T *>(a.vc) + off * HD;
+  const size_t kstride = (size_t)a.Hkv * HD;
 
   // Query fragments (B operand of S^T = K Q^T) of this wave's row tiles.
-  Frag<T> qf[RT][HC];
+  AFrag<T> qf[RT][HC];
   const int rt0 = (blockIdx.y * NW + wave) * RT;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -87,8 +82,9 @@ __global__ __launch_bounds__(64 * NW) void attn_split_kernel(AttnArgs a) {
     for (int c = 0; c < HC; ++c) {
       if (rho < a.R) {
         const int j = rho / a.B, p = rho % a.B;
-        qf[rt][c].load(reinterpret_cast<const T *>(a.qkv) + (size_t)(it.seq * a.B + p) * a.Nqkv +
-                       (size_t)(it.kvh * a.G + j) * HD + c * 32 + g * 8);
+        float v[8];
+        load8f(a.qkv + (size_t)(it.seq * a.B + p) * a.Nqkv + (size_t)(it.kvh * a.G + j) * HD + c * 32 + g * 8, v);
+        qf[rt][c].set8(v);
       } else {
         qf[rt][c].zero();
       }
@@ -163,7 +159,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < HC; ++c) {
           const Frag<T> kf = *reinterpret_cast<const Frag<T> *>(&ks[(16 * h + l16) * KP + c * 32 + g * 8]);
-          st[h] = mma(kf, qf[rt][c], st[h]);
+          st[h] = mma_b(kf, qf[rt][c], st[h]);
         }
       float sc[8];
       float mx = -INFINITY;
@@ -234,6 +230,67 @@ __global__ __launch_bounds__(64 * NW) void attn_split_kernel(AttnArgs a) {
   }
 }
 
+// The block's own B keys of one (seq, kv head) pair, in fp32: one workgroup per pair,
+// 16 threads per query row (each owning HD/16 head dimensions), partial (m, l, O) into
+// the slot of the pair's block item.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_block_kernel(AttnArgs a) {
+  if (a.done && *a.done) return;
+  constexpr int EPT = HD / 16;
+  constexpr int BMAX = 32;
+  __shared__ float s_k[BMAX][HD + 1], s_v[BMAX][HD + 1];
+  const int pair = blockIdx.x;
+  const int item = a.pair_first[pair] + a.pair_count[pair] - 1;
+  const AttnItem it = a.items[item];
+  const float *base = a.qkv + (size_t)it.seq * a.B * a.Nqkv;
+  for (int i = threadIdx.x; i < a.B * HD; i += blockDim.x) {
+    const int key = i / HD, e = i % HD;
+    s_k[key][e] = base[(size_t)key * a.Nqkv + (size_t)(a.H + it.kvh) * HD + e];
+    s_v[key][e] = base[(size_t)key * a.Nqkv + (size_t)(a.H + a.Hkv + it.kvh) * HD + e];
+  }
+  __syncthreads();
+  const int sub = threadIdx.x & 15, e0 = sub * EPT;
+  for (int rho = threadIdx.x >> 4; rho < a.R; rho += blockDim.x >> 4) {
+    const int j = rho / a.B, p = rho % a.B;
+    const float *q = base + (size_t)p * a.Nqkv + (size_t)(it.kvh * a.G + j) * HD + e0;
+    float qv[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) qv[e] = q[e];
+    float sc[BMAX];
+    float m = -INFINITY;
+#pragma unroll
+    for (int key = 0; key < BMAX; ++key) {
+      if (key < a.B) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) d += qv[e] * s_k[key][e0 + e];
+        d = sum16(d) * a.scale;
+        sc[key] = d;
+        m = fmaxf(m, d);
+      }
+    }
+    float l = 0.f, o[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int key = 0; key < BMAX; ++key) {
+      if (key < a.B) {
+        const float pk = __expf(sc[key] - m);
+        l += pk;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) o[e] += pk * s_v[key][e0 + e];
+      }
+    }
+    const size_t prow = (size_t)item * a.R + rho;
+    if (sub == 0) {
+      a.part_ml[prow * 2 + 0] = m;
+      a.part_ml[prow * 2 + 1] = l;
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) a.part_o[prow * HD + e0 + e] = o[e];
+  }
+}
+
 // One workgroup per (pair, 16 query rows): 16 threads per row, HD/16 outputs each.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
@@ -260,9 +317,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const float inv = 1.0f / L;
   const AttnItem it = a.items[first];
   const int j = rho / a.B, p = rho % a.B;
-  T *out = reinterpret_cast<T *>(a.o) + (size_t)(it.seq * a.B + p) * a.ldo + (size_t)(it.kvh * a.G + j) * HD + e0;
+  float *out = a.o + (size_t)(it.seq * a.B + p) * a.ldo + (size_t)(it.kvh * a.G + j) * HD + e0;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) out[e] = from_f32<T>(acc[e] * inv);
+  for (int e = 0; e < EPT; ++e) out[e] = acc[e] * inv;
 }
 
 template <typename T, int HD, int RT, int NW>
@@ -278,9 +335,10 @@ hipError_t launch_hd(const AttnArgs &a, hipStream_t s) {
   hipError_t e;
   if (a.R <= 16) e = launch_split<T, HD, 1, 1>(a, s);
   else if (a.R <= 32) e = launch_split<T, HD, 2, 1>(a, s);
-  else if (a.R <= 64) e = launch_split<T, HD, 4, 1>(a, s);
+  else if (a.R <= 64) e = launch_split<T, HD, 1, 4>(a, s);
   else e = launch_split<T, HD, 4, 4>(a, s);
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_block_kernel<HD>), dim3(a.n_pairs), dim3(256), 0, s, a);
   dim3 grid(a.n_pairs, (a.R + 15) / 16);
   hipLaunchKernelGGL((attn_merge_kernel<T, HD>), grid, dim3(256), 0, s, a);
   return hipGetLastError();

@@ -12,11 +12,13 @@
 //   * when N/16 tiles cannot fill the chip, K is also split across workgroups; the last
 //     workgroup of a tile (integer counter) adds the split partials in split order, so
 //     results are deterministic and no float atomics are used;
+//   * activations are fp32; for bf16 weights each activation fragment enters the MFMA
+//     as a bf16 high part plus a bf16 remainder (two MFMAs per weight fragment, free
+//     while the weight stream is the bound), so no activation is ever rounded to bf16;
 //   * prologue: RMSNorm of the fp32 residual stream (row scale from the partial sums of
-//     squares left by the producer) fused into the A-fragment load, rounded to the
-//     storage type exactly where the reference rounds;
-//   * epilogue: store (q/k/v), GELU (MLP up), or residual add + partial sums of squares
-//     for the next RMSNorm (output projection, MLP down).
+//     squares left by the producer) fused into the A-fragment load;
+//   * epilogue (fp32 out): store (q/k/v), GELU (MLP up), or residual add + partial sums
+//     of squares for the next RMSNorm (output projection, MLP down).
 #include "td_device.h"
 #include "td_kernels.h"
 
@@ -27,38 +29,38 @@ namespace td {
 namespace {
 
 constexpr int KTW_MAX = 16;   // k-tiles per wave
-constexpr int CH = 4;         // k-tiles per pipeline chunk
 
-template <typename T, int MT, bool NORM>
+// A fragment of rows m0 + 16 mt + (lane % 16), k-tile kt: fp32 activations (or the RMSNorm
+// of the residual stream), split for the bf16 MFMA.
+template <typename T, bool NORM>
 struct AOperand {
   const GemmArgs &a;
   const float *rs;   // LDS row scales (NORM)
   int m0, lane;
-  TD_DEV Frag<T> load(int mt, int kt) const {
-    Frag<T> f;
+  TD_DEV AFrag<T> load(int mt, int kt) const {
+    AFrag<T> f;
     const int row = m0 + mt * 16 + (lane & 15);
     const int k = kt * 32 + (lane >> 4) * 8;
     if (row >= a.M) { f.zero(); return f; }
+    float v[8];
     if constexpr (NORM) {
-      const float *xp = a.norm.x + (size_t)row * a.K + k;
-      float4 x0 = reinterpret_cast<const float4 *>(xp)[0];
-      float4 x1 = reinterpret_cast<const float4 *>(xp)[1];
+      load8f(a.norm.x + (size_t)row * a.K + k, v);
       Frag<T> g;
       g.load(reinterpret_cast<const T *>(a.norm.gain) + k);
       const float r = rs[mt * 16 + (lane & 15)];
-      float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = v[j] * r * g.get(j);
-      f.set8(v);
     } else {
-      f.load(reinterpret_cast<const T *>(a.A) + (size_t)row * a.lda + k);
+      load8f(a.A + (size_t)row * a.lda + k, v);
     }
+    f.set8(v);
     return f;
   }
 };
 
 template <typename T, int MT, int EPI, bool NORM>
 __global__ __launch_bounds__(256) void gemm_ws_kernel(GemmArgs a) {
+  constexpr int CH = MT == 1 ? 4 : 2;   // k-tiles per pipeline chunk
   if (a.done && *a.done) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nt = blockIdx.x, ks = blockIdx.y;
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(256) void gemm_ws_kernel(GemmArgs a) {
     __syncthreads();
   }
 
-  AOperand<T, MT, NORM> A{a, s_rs, m0, lane};
+  AOperand<T, NORM> A{a, s_rs, m0, lane};
   const T *Wp = reinterpret_cast<const T *>(a.Wp) + ((size_t)nt * KT) * 512 + (size_t)lane * 8;
 
   f32x4_t acc[MT];
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void gemm_ws_kernel(GemmArgs a) {
   // Wave `wave` owns k-tiles kbeg + wave + 4*i; chunks of CH tiles, next chunk in flight.
   const int nk = (kend - kbeg - wave + 3) / 4;   // tiles of this wave (may be <= 0)
   Frag<T> wb[2][CH];
-  Frag<T> ab[2][CH][MT];
+  AFrag<T> ab[2][CH][MT];
   // Buffer indices are literals after inlining, so both buffers stay in registers.
   auto issue = [&](auto buf, int c) __attribute__((always_inline)) {
     constexpr int b = decltype(buf)::value;
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void gemm_ws_kernel(GemmArgs a) {
     for (int j = 0; j < CH; ++j) {
       if (c * CH + j < nk) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = mma(ab[b][j][mt], wb[b][j], acc[mt]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = mma_a(ab[b][j][mt], wb[b][j], acc[mt]);
       }
     }
   };
@@ -181,16 +183,16 @@ __global__ __launch_bounds__(256) void gemm_ws_kernel(GemmArgs a) {
       const int row = m0 + mt * 16 + 4 * g + r;
       const bool ok = row < a.M;
       const float y = acc[mt][r];
+      float *op = a.out + (size_t)row * a.ldo + col;
       if constexpr (EPI == EPI_STORE) {
-        if (ok) reinterpret_cast<T *>(a.out)[(size_t)row * a.ldo + col] = from_f32<T>(y);
+        if (ok) *op = y;
       } else if constexpr (EPI == EPI_GELU) {
-        if (ok) reinterpret_cast<T *>(a.out)[(size_t)row * a.ldo + col] = from_f32<T>(gelu_erf(y));
+        if (ok) *op = gelu_erf(y);
       } else {
-        float *xp = reinterpret_cast<float *>(a.out) + (size_t)row * a.ldo + col;
         float xv = 0.f;
         if (ok) {
-          xv = *xp + y;
-          *xp = xv;
+          xv = *op + y;
+          *op = xv;
         }
         const float sq = sum16(xv * xv);
         if (ok && (lane & 15) == 0) a.ssq_out[(size_t)nt * a.M + row] = sq;

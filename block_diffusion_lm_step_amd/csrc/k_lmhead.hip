@@ -2,7 +2,8 @@
 //
 // Confidence of a masked position = largest softmax probability of its logits scaled by
 // the position's inverse temperature; prediction = lowest vocabulary id of the largest
-// scaled logit.  Each 16-column logit tile stays in the MFMA accumulators: the epilogue
+// scaled logit.  The final-normed hidden state is fp32 (hi + lo bf16 parts against the
+// bf16 head).  Each 16-column logit tile stays in the MFMA accumulators: the epilogue
 // scales it by tau and reduces it to (max, sum exp(s - max), argmax) per row, merges the
 // four waves' tiles, and writes one 12-byte triple per (row, 64-column slice).  The
 // [rows x V] logit matrix never reaches HBM (except in the optional debug capture).
@@ -24,134 +25,119 @@ namespace td {
 namespace {
 
 constexpr int CH = 4;
-constexpr int LM_MT = 4;   // row tiles per pass (64 rows)
 
+// Grid: x = 64-column vocabulary slices (one 16-column tile per wave), y = groups of 16
+// still-masked rows (a group past the live row count exits at once).
 template <typename T>
 __global__ __launch_bounds__(256) void lmhead_kernel(LmArgs a) {
   if (*a.st.done) return;
+  const int n_rows = *a.st.n_rows;
+  const int m0 = blockIdx.y * 16;
+  if (m0 >= n_rows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int nt = blockIdx.x * 4 + wave;
   const int KT = a.d >> 5;
-  const int n_rows = *a.st.n_rows;
   const T *Wp = reinterpret_cast<const T *>(a.Wp) + ((size_t)nt * KT) * 512 + (size_t)lane * 8;
   const int col = nt * 16 + l16;
 
-  __shared__ float s_rs[16 * LM_MT];
-  __shared__ int s_row[16 * LM_MT];
-  __shared__ VStat s_stat[4][16 * LM_MT];
+  __shared__ float s_rs[16];
+  __shared__ int s_row[16];
+  __shared__ VStat s_stat[4][16];
 
-  for (int m0 = 0; m0 < n_rows; m0 += 16 * LM_MT) {
-    {  // rows of this pass and their RMSNorm scales
-      const int r = threadIdx.x >> 2, sub = threadIdx.x & 3;
-      float acc = 0.f;
-      int row = -1;
-      if (r < 16 * LM_MT && m0 + r < n_rows) {
-        row = a.st.rowlist[m0 + r];
-        for (int p = sub; p < a.norm.nparts; p += 4) acc += a.norm.ssq[(size_t)p * (a.n * a.B) + row];
-      }
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (r < 16 * LM_MT && sub == 0) {
-        s_rs[r] = 1.0f / sqrtf(acc / (float)a.d + a.norm.eps);
-        s_row[r] = row;
-      }
-      __syncthreads();
+  {  // rows of this group and their RMSNorm scales
+    const int r = threadIdx.x >> 2, sub = threadIdx.x & 3;
+    float acc = 0.f;
+    int row = -1;
+    if (r < 16 && m0 + r < n_rows) {
+      row = a.st.rowlist[m0 + r];
+      for (int p = sub; p < a.norm.nparts; p += 4) acc += a.norm.ssq[(size_t)p * (a.n * a.B) + row];
     }
-
-    auto load_a = [&](int mt, int kt) __attribute__((always_inline)) {
-      Frag<T> f;
-      const int row = s_row[mt * 16 + l16];
-      if (row < 0) { f.zero(); return f; }
-      const int k = kt * 32 + g * 8;
-      const float *xp = a.norm.x + (size_t)row * a.d + k;
-      const float4 x0 = reinterpret_cast<const float4 *>(xp)[0];
-      const float4 x1 = reinterpret_cast<const float4 *>(xp)[1];
-      Frag<T> gg;
-      gg.load(reinterpret_cast<const T *>(a.norm.gain) + k);
-      const float rs = s_rs[mt * 16 + l16];
-      float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = v[j] * rs * gg.get(j);
-      f.set8(v);
-      return f;
-    };
-
-    f32x4_t acc[LM_MT];
-#pragma unroll
-    for (int i = 0; i < LM_MT; ++i) acc[i] = zero4();
-    const int mts = min(LM_MT, (n_rows - m0 + 15) / 16);   // live row tiles this pass
-    Frag<T> wb[2][CH];
-    Frag<T> ab[2][CH][LM_MT];
-    auto issue = [&](auto buf, int c) __attribute__((always_inline)) {
-      constexpr int b = decltype(buf)::value;
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const int kt = c * CH + j;
-        if (kt < KT) {
-          wb[b][j].load(Wp + (size_t)kt * 512);
-#pragma unroll
-          for (int mt = 0; mt < LM_MT; ++mt)
-            if (mt < mts) ab[b][j][mt] = load_a(mt, kt);
-        }
-      }
-    };
-    auto compute = [&](auto buf, int c) __attribute__((always_inline)) {
-      constexpr int b = decltype(buf)::value;
-#pragma unroll
-      for (int j = 0; j < CH; ++j)
-        if (c * CH + j < KT) {
-#pragma unroll
-          for (int mt = 0; mt < LM_MT; ++mt)
-            if (mt < mts) acc[mt] = mma(ab[b][j][mt], wb[b][j], acc[mt]);
-        }
-    };
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    const int nchunks = (KT + CH - 1) / CH;
-    issue(B0{}, 0);
-    for (int c = 0; c < nchunks; c += 2) {
-      if (c + 1 < nchunks) issue(B1{}, c + 1);
-      compute(B0{}, c);
-      if (c + 1 < nchunks) {
-        if (c + 2 < nchunks) issue(B0{}, c + 2);
-        compute(B1{}, c + 1);
-      }
-    }
-
-    // Epilogue: tau-scaled statistics of each row over this wave's 16 columns.
-#pragma unroll
-    for (int mt = 0; mt < LM_MT; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = mt * 16 + 4 * g + r;      // row slot within the pass
-        const int row = s_row[rr];
-        const float z = acc[mt][r];
-        float sv = -INFINITY;
-        if (row >= 0) {
-          if (a.logits) a.logits[(size_t)row * a.V + col] = z;
-          sv = (a.inv_temp ? a.inv_temp[row] : 1.0f) * z;
-        }
-        float mx = sv;
-        mx = fmaxf(mx, __shfl_xor(mx, 1)); mx = fmaxf(mx, __shfl_xor(mx, 2));
-        mx = fmaxf(mx, __shfl_xor(mx, 4)); mx = fmaxf(mx, __shfl_xor(mx, 8));
-        const float e = (row >= 0) ? __expf(sv - mx) : 0.f;
-        const float se = sum16(e);
-        int am = (row >= 0 && sv == mx) ? col : 0x7FFFFFFF;
-        am = min(am, __shfl_xor(am, 1)); am = min(am, __shfl_xor(am, 2));
-        am = min(am, __shfl_xor(am, 4)); am = min(am, __shfl_xor(am, 8));
-        if (l16 == 0) s_stat[wave][rr] = VStat{mx, se, am};
-      }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (r < 16 && sub == 0) {
+      s_rs[r] = 1.0f / sqrtf(acc / (float)a.d + a.norm.eps);
+      s_row[r] = row;
     }
     __syncthreads();
-    if (threadIdx.x < 16 * LM_MT && s_row[threadIdx.x] >= 0) {
-      VStat v = s_stat[0][threadIdx.x];
+  }
+  const int arow = s_row[l16];
+  const float ars = s_rs[l16];
+
+  auto load_a = [&](int kt) __attribute__((always_inline)) {
+    AFrag<T> f;
+    if (arow < 0) { f.zero(); return f; }
+    const int k = kt * 32 + g * 8;
+    float v[8];
+    load8f(a.norm.x + (size_t)arow * a.d + k, v);
+    Frag<T> gg;
+    gg.load(reinterpret_cast<const T *>(a.norm.gain) + k);
 #pragma unroll
-      for (int w = 1; w < 4; ++w) v = vstat_merge(v, s_stat[w][threadIdx.x]);
-      const int nslices = gridDim.x;
-      reinterpret_cast<VStat *>(a.vpart)[(size_t)(m0 + threadIdx.x) * nslices + blockIdx.x] = v;
+    for (int j = 0; j < 8; ++j) v[j] = v[j] * ars * gg.get(j);
+    f.set8(v);
+    return f;
+  };
+
+  f32x4_t acc = zero4();
+  Frag<T> wb[2][CH];
+  AFrag<T> ab[2][CH];
+  auto issue = [&](auto buf, int c) __attribute__((always_inline)) {
+    constexpr int b = decltype(buf)::value;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int kt = c * CH + j;
+      if (kt < KT) {
+        wb[b][j].load(Wp + (size_t)kt * 512);
+        ab[b][j] = load_a(kt);
+      }
     }
-    __syncthreads();
+  };
+  auto compute = [&](auto buf, int c) __attribute__((always_inline)) {
+    constexpr int b = decltype(buf)::value;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (c * CH + j < KT) acc = mma_a(ab[b][j], wb[b][j], acc);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  const int nchunks = (KT + CH - 1) / CH;
+  issue(B0{}, 0);
+  for (int c = 0; c < nchunks; c += 2) {
+    if (c + 1 < nchunks) issue(B1{}, c + 1);
+    compute(B0{}, c);
+    if (c + 1 < nchunks) {
+      if (c + 2 < nchunks) issue(B0{}, c + 2);
+      compute(B1{}, c + 1);
+    }
+  }
+
+  // Epilogue: tau-scaled statistics of each row over this wave's 16 columns.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rr = 4 * g + r;      // row slot within the group
+    const int row = s_row[rr];
+    const float z = acc[r];
+    float sv = -INFINITY;
+    if (row >= 0) {
+      if (a.logits) a.logits[(size_t)row * a.V + col] = z;
+      sv = (a.inv_temp ? a.inv_temp[row] : 1.0f) * z;
+    }
+    float mx = sv;
+    mx = fmaxf(mx, __shfl_xor(mx, 1)); mx = fmaxf(mx, __shfl_xor(mx, 2));
+    mx = fmaxf(mx, __shfl_xor(mx, 4)); mx = fmaxf(mx, __shfl_xor(mx, 8));
+    const float e = (row >= 0) ? __expf(sv - mx) : 0.f;
+    const float se = sum16(e);
+    int am = (row >= 0 && sv == mx) ? col : 0x7FFFFFFF;
+    am = min(am, __shfl_xor(am, 1)); am = min(am, __shfl_xor(am, 2));
+    am = min(am, __shfl_xor(am, 4)); am = min(am, __shfl_xor(am, 8));
+    if (l16 == 0) s_stat[wave][rr] = VStat{mx, se, am};
+  }
+  __syncthreads();
+  if (threadIdx.x < 16 && s_row[threadIdx.x] >= 0) {
+    VStat v = s_stat[0][threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v = vstat_merge(v, s_stat[w][threadIdx.x]);
+    reinterpret_cast<VStat *>(a.vpart)[(size_t)(m0 + threadIdx.x) * gridDim.x + blockIdx.x] = v;
   }
 }
 
@@ -236,7 +222,7 @@ __global__ __launch_bounds__(256) void merge_commit_kernel(CommitArgs a) {
 
 hipError_t launch_lmhead(int dtype, const LmArgs &a, hipStream_t s) {
   if (a.V % 64 || a.d % 32) return hipErrorInvalidValue;
-  dim3 grid(a.V / 64);
+  dim3 grid(a.V / 64, (a.n * a.B + 15) / 16);
   if (dtype == DT_BF16) hipLaunchKernelGGL(lmhead_kernel<bf16_t>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(lmhead_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

@@ -45,7 +45,7 @@ struct td_ctx {
   // workspace
   int Mmax = 0, Nqkv = 0;
   float *x = nullptr, *ssq = nullptr, *part = nullptr, *conf_row = nullptr, *vpart = nullptr;
-  void *qkv = nullptr, *o = nullptr, *u = nullptr;
+  float *qkv = nullptr, *o = nullptr, *u = nullptr;   // fp32 activations
   unsigned *counters = nullptr;
   int *arg_row = nullptr;
   int *state_ints = nullptr;    // rowlist | rowpos | n_rows, done, t, err, counter
@@ -187,7 +187,7 @@ td_status prof_mark(td_ctx *c, int kind, bool start) {
   return TD_OK;
 }
 
-td_status enqueue_attention(td_ctx *c, int layer, const void *qkv, void *o, const int *done) {
+td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, const int *done) {
   const td_config &g = c->cfg;
   AttnArgs a{};
   a.B = g.block_size;
@@ -228,8 +228,8 @@ NormIn norm_in(td_ctx *c, const void *gain) {
   return n;
 }
 
-td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const void *A, int lda,
-                       const void *gain, const void *Wp, const GemmPlan &p, void *out, int ldo) {
+td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const float *A, int lda,
+                       const void *gain, const void *Wp, const GemmPlan &p, float *out, int ldo) {
   GemmArgs a{};
   a.M = M;
   a.N = N;
@@ -375,9 +375,9 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   TD_TRY(dmalloc(c, &c->x, M * d * 4));
   TD_TRY(dmalloc(c, &c->ssq, (d / 16) * M * 4));
   TD_TRY(dmalloc(c, &c->counters, ((M + 15) / 16) * (Nmax / 16) * sizeof(unsigned)));
-  TD_TRY(dmalloc(c, &c->qkv, M * c->Nqkv * e));
-  TD_TRY(dmalloc(c, &c->o, M * Hd * e));
-  TD_TRY(dmalloc(c, &c->u, M * F * e));
+  TD_TRY(dmalloc(c, &c->qkv, M * c->Nqkv * 4));
+  TD_TRY(dmalloc(c, &c->o, M * Hd * 4));
+  TD_TRY(dmalloc(c, &c->u, M * F * 4));
   TD_TRY(dmalloc(c, &c->conf_row, M * 4));
   TD_TRY(dmalloc(c, &c->arg_row, M * 4));
   TD_TRY(dmalloc(c, &c->vpart, M * (V / 64) * sizeof(VStatHost)));
@@ -542,7 +542,7 @@ td_status td_debug_attention(td_ctx *c, int32_t layer, const void *qkv, void *o)
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, TD_EINVAL, "layer out of range");
   if (!qkv || !o) return fail(c, TD_EINVAL, "qkv and o must not be NULL");
   TD_TRY(check_bound(c));
-  return enqueue_attention(c, layer, qkv, o, nullptr);
+  return enqueue_attention(c, layer, (const float *)qkv, (float *)o, nullptr);
 }
 
 td_status td_sync(td_ctx *c) {

@@ -21,12 +21,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 TD_DEV float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// float -> bfloat16, round to nearest, ties to even (finite inputs).
-TD_DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// float -> bfloat16, round to nearest, ties to even (gfx950 converts in hardware).
+TD_DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 template <typename T> TD_DEV float to_f32(T v);
 template <> TD_DEV float to_f32<float>(float v) { return v; }
@@ -84,7 +80,48 @@ TD_DEV f32x4_t mma(const Frag<float> &a, const Frag<float> &b, f32x4_t acc) {
   return acc;
 }
 
+// Activation fragment.  Activations are carried at fp32 precision: for the bf16 MFMA
+// they are split into a bf16 high part and the bf16 rounding of the remainder
+// (hi + lo keeps ~16 significant bits, relative error <= 2^-17), and both parts are
+// multiplied into the same fp32 accumulator; the fp32 MFMA takes them as they are.
+template <typename T> struct AFrag;
+template <> struct AFrag<bf16_t> {
+  Frag<bf16_t> hi, lo;
+  TD_DEV void zero() { hi.zero(); lo.zero(); }
+  TD_DEV void set8(const float *v) {
+    hi.set8(v);
+    float r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = v[j] - hi.get(j);
+    lo.set8(r);
+  }
+};
+template <> struct AFrag<float> {
+  Frag<float> f;
+  TD_DEV void zero() { f.zero(); }
+  TD_DEV void set8(const float *v) { f.set8(v); }
+};
+
+// acc += activation(rows) x weight(columns)
+TD_DEV f32x4_t mma_a(const AFrag<bf16_t> &a, const Frag<bf16_t> &w, f32x4_t acc) {
+  acc = mma(a.hi, w, acc);
+  return mma(a.lo, w, acc);
+}
+TD_DEV f32x4_t mma_a(const AFrag<float> &a, const Frag<float> &w, f32x4_t acc) { return mma(a.f, w, acc); }
+// acc += weight-like(rows) x activation(columns)
+TD_DEV f32x4_t mma_b(const Frag<bf16_t> &k, const AFrag<bf16_t> &q, f32x4_t acc) {
+  acc = mma(k, q.hi, acc);
+  return mma(k, q.lo, acc);
+}
+TD_DEV f32x4_t mma_b(const Frag<float> &k, const AFrag<float> &q, f32x4_t acc) { return mma(k, q.f, acc); }
+
 TD_DEV f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+TD_DEV void load8f(const float *p, float *v) {
+  const float4 a = reinterpret_cast<const float4 *>(p)[0];
+  const float4 b = reinterpret_cast<const float4 *>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
 
 // Butterfly reductions over the 16 lanes that share l / 16 (offsets 1..8) or over the
 // four lane groups that share l % 16 (offsets 16, 32).

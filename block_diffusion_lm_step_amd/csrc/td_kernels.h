@@ -12,10 +12,9 @@ enum Epi { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2 };
 // W [N][K] row-major -> 16x32 MFMA tiles, tile (nt, kt) at ((nt * K/32 + kt) * 64 + lane) * 8,
 // lane l holding W[16 nt + l%16][32 kt + 8 (l/16) .. +8].
 hipError_t launch_pack_weight(int dtype, const void *W, void *Wp, int N, int K, hipStream_t s);
-hipError_t launch_copy_convert(int dtype, const void *src, void *dst, int64_t n, hipStream_t s);
 
 // ---------------------------------------------------------------- GEMM (weight streaming)
-struct NormIn {            // A = bf16/f32(rmsnorm(x) * gain) formed in the GEMM prologue
+struct NormIn {            // A = rmsnorm(x) * gain, formed in the GEMM prologue
   const float *x;          // [M][K] residual stream (fp32)
   const float *ssq;        // [nparts][M] partial sums of squares of each x row
   int nparts;
@@ -25,14 +24,14 @@ struct NormIn {            // A = bf16/f32(rmsnorm(x) * gain) formed in the GEMM
 
 struct GemmArgs {
   int M, N, K;
-  const void *A;  int lda; // plain A [M][lda] (config dtype) when norm is off
+  const float *A; int lda; // plain A [M][lda] (fp32 activations) when norm is off
   NormIn norm;
   const void *Wp;          // packed weight [N][K]
   int ktw;                 // 32-wide k-tiles per wave (<= 16)
   int ksplit;              // workgroups along K
   float *part;             // [ksplit][M][N] split-K partials (fp32)
   unsigned *counters;      // [ceil(M/64)][N/16], zero on entry, left zero
-  void *out; int ldo;      // STORE/GELU: config dtype [M][ldo]; RESID: fp32 x [M][ldo], updated in place
+  float *out; int ldo;     // STORE/GELU: fp32 [M][ldo]; RESID: x [M][ldo], updated in place
   float *ssq_out;          // RESID: [N/16][M] partial sums of squares of the updated rows
   const int *done;         // skip the launch when *done != 0 (nullable)
 };
@@ -40,6 +39,7 @@ hipError_t launch_gemm(int dtype, int epi, bool norm, const GemmArgs &a, hipStre
 
 // ---------------------------------------------------------------- attention
 // One split-K work item: keys [k_begin, k_end) of a prefix chunk, or the block's own keys.
+// The items of a (seq, kv head) pair are consecutive; the block item is the pair's last.
 struct AttnItem {
   int seq, kvh;            // sequence and key/value head
   int k_begin, k_end;      // key range (prefix token index within the sequence; or 0..B)
@@ -48,7 +48,7 @@ struct AttnItem {
 };
 struct AttnArgs {
   int B, H, Hkv, hd, Nqkv, G, R;   // R = G * B query rows per (seq, kv head)
-  const void *qkv;                 // [n*B][Nqkv]: q | k_block | v_block (config dtype)
+  const float *qkv;                // [n*B][Nqkv]: q | k_block | v_block (fp32)
   const void *kc, *vc;             // prefix caches [sumP][Hkv][hd]
   const int64_t *offsets;          // [n+1] prefix offsets (device)
   const AttnItem *items; int n_items;
@@ -56,7 +56,7 @@ struct AttnArgs {
   int n_pairs;
   float *part_o;                   // [n_items][R][hd]
   float *part_ml;                  // [n_items][R][2]
-  void *o; int ldo;                // output [n*B][H*hd] (config dtype)
+  float *o; int ldo;               // output [n*B][H*hd] (fp32)
   float scale;                     // 1 / sqrt(hd)
   const int *done;
 };

@@ -49,8 +49,10 @@ typedef enum { TD_F32 = 0, TD_BF16 = 1 } td_dtype;
 
 /* Tower shape and capacity.  Supported: head_dim in {64, 128}; block_size in {8, 16, 32};
  * n_heads % n_kv_heads == 0; d_model, d_ff, vocab multiples of 64; n_heads*head_dim a
- * multiple of 64.  dtype is the storage type of weights and prefix K/V; accumulators,
- * the residual stream and all softmax statistics are fp32 either way. */
+ * multiple of 64.  dtype is the storage type of weights and prefix K/V.  Activations
+ * (the residual stream, normed inputs, q/k/v, attention output, MLP activation) and all
+ * accumulators and softmax statistics are fp32 either way; against bf16 weights an
+ * activation enters the bf16 matrix cores as a bf16 high part plus a bf16 remainder. */
 typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ff, vocab;
   int32_t block_size;          /* B, positions per block */
@@ -123,7 +125,8 @@ td_status td_generate_block(td_ctx *ctx, int32_t *tokens, uint8_t *committed, co
 
 /* Debug hook: run the layer-`layer` attention (prefix split-K + in-block keys + merge)
  * on caller-provided projections qkv [n*B][(n_heads + 2*n_kv_heads)*head_dim] (q, then
- * k, then v of the block, config dtype) and write o [n*B][n_heads*head_dim]. */
+ * k, then v of the block; fp32, the precision the step carries activations in) and
+ * write o [n*B][n_heads*head_dim] (fp32). */
 td_status td_debug_attention(td_ctx *ctx, int32_t layer, const void *qkv, void *o);
 
 /* Wait for the ctx's stream; report asynchronous device errors and device-side input

@@ -15,7 +15,7 @@ def _run(dtype, H, Hkv, hd, B, plens, seed=0, qscale=1.0):
     import torch
 
     from block_diffusion_lm_step_amd import Denoiser
-    from oracle import joint_attention, round_bf16
+    from oracle import joint_attention
     from synth import Workload, draw_tower, f32_from_bf16_bits
     from synth.device import prefix_to_device, tower_config, tower_to_device
 
@@ -29,18 +29,12 @@ def _run(dtype, H, Hkv, hd, B, plens, seed=0, qscale=1.0):
     dev.set_prefix(offsets, ks, vs)
     rng = np.random.default_rng(seed)
     Nqkv = (H + 2 * Hkv) * hd
-    qkv = (rng.standard_normal((n * B, Nqkv)) * qscale).astype(np.float32)
-    if dtype == "bf16":
-        qkv_t = torch.from_numpy(qkv).to(torch.bfloat16)
-        qkv = qkv_t.float().numpy()
-        qkv_d = qkv_t.cuda()
-        o_d = torch.zeros((n * B, H * hd), dtype=torch.bfloat16, device="cuda")
-    else:
-        qkv_d = torch.from_numpy(qkv).cuda()
-        o_d = torch.zeros((n * B, H * hd), dtype=torch.float32, device="cuda")
+    qkv = (rng.standard_normal((n * B, Nqkv)) * qscale).astype(np.float32)   # fp32 activations
+    qkv_d = torch.from_numpy(qkv).cuda()
+    o_d = torch.zeros((n * B, H * hd), dtype=torch.float32, device="cuda")
     dev.debug_attention(0, qkv_d, o_d)
     dev.sync()
-    o = o_d.float().cpu().numpy().reshape(n, B, H, hd)
+    o = o_d.cpu().numpy().reshape(n, B, H, hd)
     q3 = qkv.reshape(n, B, Nqkv).astype(np.float64)
     worst = 0.0
     for s in range(n):
@@ -50,17 +44,11 @@ def _run(dtype, H, Hkv, hd, B, plens, seed=0, qscale=1.0):
         kb = q3[s, :, H * hd:(H + Hkv) * hd].reshape(B, Hkv, hd)
         vb = q3[s, :, (H + Hkv) * hd:].reshape(B, Hkv, hd)
         ref = joint_attention(q, k_pre, v_pre, kb, vb)
-        if dtype == "bf16":
-            ref_r = round_bf16(ref)
-            # one bf16 rounding of the output plus fp32 accumulation: within 2 bf16 ulps
-            tol = 2.0 ** -7 * np.abs(ref) + 1e-6
-            err = np.abs(o[s] - ref_r)
-            assert (err <= tol).all(), f"seq {s}: max err {err.max():.3e}"
-            worst = max(worst, float((np.abs(o[s] - ref) / (np.abs(ref) + 1e-3)).max()))
-        else:
-            err = np.abs(o[s] - ref).max() / np.abs(ref).max()
-            worst = max(worst, float(err))
-            assert err < 1e-5, f"seq {s}: rel err {err:.3e}"
+        # fp32 accumulation; with bf16 keys the fp32 queries and probabilities enter the
+        # MFMA as hi + lo bf16 parts (relative error <= 2^-17 each)
+        err = float(np.abs(o[s] - ref).max() / np.abs(ref).max())
+        worst = max(worst, err)
+        assert err < (3e-5 if dtype == "bf16" else 1e-5), f"seq {s}: rel err {err:.3e}"
     log(f"[attn] worst relative error {worst:.3e}")
     dev.close()
 
