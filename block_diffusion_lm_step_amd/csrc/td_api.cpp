@@ -21,12 +21,7 @@ namespace {
 thread_local std::string g_create_error;
 
 struct GemmPlan {
-  int ktw = 1, ksplit = 1;
-};
-
-struct VStatHost {   // mirror of the device VStat (max, sumexp, argmax)
-  float m, s;
-  int a;
+  int nt = 1, nw = 4;
 };
 
 }  // namespace
@@ -44,13 +39,13 @@ struct td_ctx {
 
   // workspace
   int Mmax = 0, Nqkv = 0;
-  float *x = nullptr, *ssq = nullptr, *part = nullptr, *conf_row = nullptr, *vpart = nullptr;
+  float *x = nullptr, *ssq = nullptr, *conf_row = nullptr;
+  VStat *vpart = nullptr;
   float *qkv = nullptr, *o = nullptr, *u = nullptr;   // fp32 activations
-  unsigned *counters = nullptr;
   int *arg_row = nullptr;
   int *state_ints = nullptr;    // rowlist | rowpos | n_rows, done, t, err, counter
   StepState st{};
-  GemmPlan p_qkv, p_wo, p_w1, p_w2;
+  GemmPlan p_qkv, p_wo, p_w1, p_w2, p_lm;
 
   // prefix binding
   int n_seqs = 0;
@@ -59,11 +54,10 @@ struct td_ctx {
   std::vector<const void *> kc, vc;
   AttnItem *items_d = nullptr;
   int *pair_first_d = nullptr, *pair_count_d = nullptr;
-  int n_items = 0, n_pairs = 0;
+  int n_items = 0, n_pairs = 0, max_pair_items = 0;
   size_t items_cap = 0, pairs_cap = 0;
   float *att_o = nullptr, *att_ml = nullptr;
   size_t att_cap_rows = 0;   // capacity in partial rows (items * R)
-  size_t part_cap = 0;       // split-K partial capacity (floats)
 
   // profiling: event pairs around the launches of one kernel class
   int prof_kind = TD_PROF_OFF;
@@ -144,26 +138,31 @@ td_status validate_weights(const td_config &c, const td_weights *w) {
   return TD_OK;
 }
 
-GemmPlan plan_gemm(int M, int N, int K) {
+// The LM head (vocabulary statistics): 4 column tiles per wave, 256 columns per
+// workgroup.  Layer projections: one 16-column tile per workgroup and enough waves
+// along K that each holds at most 16 k-tiles (16 KiB of bf16 weights) in flight.
+GemmPlan plan_gemm(int M, int N, int K, bool vstat) {
+  (void)M;
   GemmPlan p;
-  const int KT = K / 32;
-  const int mblocks = M <= 16 ? 1 : (M + 63) / 64;
-  const long tiles = (long)(N / 16) * mblocks;
-  int ks = 1;
-  while (tiles * ks < 640 && KT / (4 * ks * 2) >= 4) ks *= 2;
-  int ktw = (KT + 4 * ks - 1) / (4 * ks);
-  if (ktw > 16) {
-    ks = (KT + 63) / 64;
-    ktw = (KT + 4 * ks - 1) / (4 * ks);
+  if (vstat) {
+    p.nt = N % 256 == 0 ? 4 : (N % 128 == 0 ? 2 : 1);
+  } else {
+    const int KT = K / 32;
+    p.nw = 4;
+    while (p.nw < 16 && (KT + p.nw - 1) / p.nw > 16) p.nw *= 2;
   }
-  p.ksplit = ks;
-  p.ktw = std::max(1, ktw);
   return p;
 }
 
-int chunk_keys(int R) {
-  int tc = 128;
-  while (tc < 8 * R && tc < 4096) tc *= 2;
+// Prefix keys per split-K item.  Few query rows per K/V head (R <= 32): 256 keys, which
+// the four waves of a workgroup stream 64 each; grouped-query heads: the partial state
+// per item (R rows x (hd + 2) floats) is large, so items grow with R.  Items also grow
+// so that a prefix of P keys has at most 256 of them (the merge's capacity).
+int chunk_keys(int R, int64_t Pmax) {
+  int tc = 256;
+  if (R > 32)
+    while (tc < 4 * R && tc < 4096) tc *= 2;
+  while ((Pmax + tc - 1) / tc > 256) tc *= 2;
   return tc;
 }
 
@@ -206,6 +205,7 @@ td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, co
   a.pair_first = c->pair_first_d;
   a.pair_count = c->pair_count_d;
   a.n_pairs = c->n_pairs;
+  a.max_pair_items = c->max_pair_items;
   a.part_o = c->att_o;
   a.part_ml = c->att_ml;
   a.o = o;
@@ -229,26 +229,31 @@ NormIn norm_in(td_ctx *c, const void *gain) {
 }
 
 td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const float *A, int lda,
-                       const void *gain, const void *Wp, const GemmPlan &p, float *out, int ldo) {
+                       const void *gain, const void *Wp, const GemmPlan &p, float *out, int ldo,
+                       const GemmArgs *extra = nullptr) {
   GemmArgs a{};
+  if (extra) a = *extra;
   a.M = M;
   a.N = N;
   a.K = K;
   a.A = A;
   a.lda = lda;
   if (norm) a.norm = norm_in(c, gain);
+  a.ld_ssq = M;
   a.Wp = Wp;
-  a.ktw = p.ktw;
-  a.ksplit = p.ksplit;
-  a.part = c->part;
-  a.counters = c->counters;
+  a.nt = p.nt;
+  a.nw = p.nw;
   a.out = out;
   a.ldo = ldo;
   a.ssq_out = c->ssq;
   a.done = c->st.done;
-  TD_TRY(prof_mark(c, TD_PROF_GEMM, true));
-  TD_HIP(c, launch_gemm(c->cfg.dtype, epi, norm, a, c->stream));
-  TD_TRY(prof_mark(c, TD_PROF_GEMM, false));
+  if (epi == EPI_VSTAT) {
+    TD_HIP(c, launch_gemm(c->cfg.dtype, epi, norm, a, c->stream));
+  } else {
+    TD_TRY(prof_mark(c, TD_PROF_GEMM, true));
+    TD_HIP(c, launch_gemm_wk(c->cfg.dtype, epi, norm, a, c->stream));
+    TD_TRY(prof_mark(c, TD_PROF_GEMM, false));
+  }
   return TD_OK;
 }
 
@@ -270,25 +275,21 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
                         g.d_ff));
     TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->u, g.d_ff, nullptr, c->w2[l], c->p_w2, c->x, d));
   }
-  LmArgs la{};
-  la.V = g.vocab;
-  la.d = d;
-  la.B = g.block_size;
-  la.n = c->n_seqs;
-  la.norm = norm_in(c, c->final_norm);
-  la.Wp = c->lm_head;
-  la.inv_temp = inv_temp;
-  la.vpart = c->vpart;
-  la.logits = logits;
-  la.st = c->st;
+  GemmArgs lm{};
+  lm.rowlist = c->st.rowlist;
+  lm.n_rows = c->st.n_rows;
+  lm.inv_temp = inv_temp;
+  lm.vpart = c->vpart;
+  lm.logits = logits;
   TD_TRY(prof_mark(c, TD_PROF_LMHEAD, true));
-  TD_HIP(c, launch_lmhead(g.dtype, la, c->stream));
+  TD_TRY(enqueue_gemm(c, EPI_VSTAT, true, M, g.vocab, d, nullptr, 0, c->final_norm, c->lm_head, c->p_lm, nullptr, 0,
+                      &lm));
   TD_TRY(prof_mark(c, TD_PROF_LMHEAD, false));
   CommitArgs ca{};
   ca.V = g.vocab;
   ca.B = g.block_size;
   ca.n = c->n_seqs;
-  ca.nslices = g.vocab / 64;
+  ca.nslices = g.vocab / (64 * c->p_lm.nt);
   ca.vpart = c->vpart;
   ca.conf_row = c->conf_row;
   ca.arg_row = c->arg_row;
@@ -324,8 +325,8 @@ void free_all(td_ctx *c) {
   f(c->tok_emb); f(c->pos_emb); f(c->final_norm); f(c->lm_head);
   for (auto *v : {&c->attn_norm, &c->mlp_norm, &c->wqkv, &c->wo, &c->w1, &c->w2})
     for (void *p : *v) f(p);
-  f(c->x); f(c->ssq); f(c->part); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->o); f(c->u);
-  f(c->counters); f(c->arg_row); f(c->state_ints); f(c->offsets_d); f(c->items_d); f(c->pair_first_d);
+  f(c->x); f(c->ssq); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->o); f(c->u);
+  f(c->arg_row); f(c->state_ints); f(c->offsets_d); f(c->items_d); f(c->pair_first_d);
   f(c->pair_count_d); f(c->att_o); f(c->att_ml);
   for (hipEvent_t e : c->ev_start) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->ev_stop) (void)hipEventDestroy(e);
@@ -370,19 +371,16 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
     TD_HIP(c, launch_pack_weight(g.dtype, w.w2[l], c->w2[l], (int)d, (int)F, c->stream));
   }
 
-  // Workspace sized for max_batch (split-K partials are sized per batch in td_set_prefix).
-  const size_t Nmax = std::max({(size_t)c->Nqkv, d, F});
+  // Workspace sized for max_batch.
   TD_TRY(dmalloc(c, &c->x, M * d * 4));
   TD_TRY(dmalloc(c, &c->ssq, (d / 16) * M * 4));
-  TD_TRY(dmalloc(c, &c->counters, ((M + 15) / 16) * (Nmax / 16) * sizeof(unsigned)));
   TD_TRY(dmalloc(c, &c->qkv, M * c->Nqkv * 4));
   TD_TRY(dmalloc(c, &c->o, M * Hd * 4));
   TD_TRY(dmalloc(c, &c->u, M * F * 4));
   TD_TRY(dmalloc(c, &c->conf_row, M * 4));
   TD_TRY(dmalloc(c, &c->arg_row, M * 4));
-  TD_TRY(dmalloc(c, &c->vpart, M * (V / 64) * sizeof(VStatHost)));
+  TD_TRY(dmalloc(c, &c->vpart, M * (V / 64) * sizeof(VStat)));
   TD_TRY(dmalloc(c, &c->state_ints, (2 * M + 8) * sizeof(int)));
-  TD_HIP(c, hipMemsetAsync(c->counters, 0, ((M + 15) / 16) * (Nmax / 16) * sizeof(unsigned), c->stream));
   TD_HIP(c, hipMemsetAsync(c->state_ints, 0, (2 * M + 8) * sizeof(int), c->stream));
   int *si = c->state_ints;
   c->st.rowlist = si;
@@ -444,7 +442,9 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
   TD_HIP(c, hipSetDevice(c->dev));
   TD_HIP(c, hipStreamSynchronize(c->stream));   // previous work may still read the old binding
 
-  const int G = g.n_heads / g.n_kv_heads, R = G * g.block_size, tc = chunk_keys(R);
+  int64_t Pmax = 0;
+  for (int i = 0; i < n_seqs; ++i) Pmax = std::max(Pmax, off[i + 1] - off[i]);
+  const int G = g.n_heads / g.n_kv_heads, R = G * g.block_size, tc = chunk_keys(R, Pmax);
   std::vector<AttnItem> items;
   std::vector<int> pfirst, pcount;
   for (int i = 0; i < n_seqs; ++i) {
@@ -486,25 +486,20 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
   TD_HIP(c, hipMemcpy(c->pair_first_d, pfirst.data(), pfirst.size() * sizeof(int), hipMemcpyHostToDevice));
   TD_HIP(c, hipMemcpy(c->pair_count_d, pcount.data(), pcount.size() * sizeof(int), hipMemcpyHostToDevice));
   TD_HIP(c, hipMemcpy(c->offsets_d, off, (size_t)(n_seqs + 1) * sizeof(int64_t), hipMemcpyHostToDevice));
-  {  // split-K plans for this batch size and their partial buffer
+  {  // GEMM plans for this batch size
     const int M = n_seqs * g.block_size;
     const int d = g.d_model, F = g.d_ff, Hd = g.n_heads * g.head_dim;
-    c->p_qkv = plan_gemm(M, c->Nqkv, d);
-    c->p_wo = plan_gemm(M, d, Hd);
-    c->p_w1 = plan_gemm(M, F, d);
-    c->p_w2 = plan_gemm(M, d, F);
-    size_t part = 0;
-    for (auto pr : {std::make_pair(c->p_qkv, c->Nqkv), std::make_pair(c->p_wo, d), std::make_pair(c->p_w1, F),
-                    std::make_pair(c->p_w2, d)})
-      if (pr.first.ksplit > 1) part = std::max(part, (size_t)pr.first.ksplit * M * pr.second);
-    size_t cap = c->part_cap;
-    TD_TRY(grow(&c->part, cap, part, 4));
-    c->part_cap = cap;
+    c->p_qkv = plan_gemm(M, c->Nqkv, d, false);
+    c->p_wo = plan_gemm(M, d, Hd, false);
+    c->p_w1 = plan_gemm(M, F, d, false);
+    c->p_w2 = plan_gemm(M, d, F, false);
+    c->p_lm = plan_gemm(M, g.vocab, d, true);
   }
   c->offsets.assign(off, off + n_seqs + 1);
   c->kc.assign(k_cache_host, k_cache_host + g.n_layers);
   c->vc.assign(v_cache_host, v_cache_host + g.n_layers);
   c->n_items = (int)items.size();
+  c->max_pair_items = *std::max_element(pcount.begin(), pcount.end());
   c->n_pairs = (int)pfirst.size();
   c->n_seqs = n_seqs;
   return TD_OK;

@@ -13,6 +13,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "td_kernels.h"
+
+using td::VStat;
+
 typedef uint16_t bf16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
@@ -138,12 +142,7 @@ TD_DEV float sum_groups(float v) {
   return v;
 }
 
-// Softmax-statistics triple of a set of scaled logits: max, sum of exp(s - max), lowest
-// index of the max.  Merging is exact for (max, index) and fixed-order for the sum.
-struct VStat {
-  float m, s;
-  int a;
-};
+// Merge of two softmax-statistics triples: exact for (max, index), fixed-order for the sum.
 TD_DEV VStat vstat_merge(VStat x, VStat y) {
   VStat r;
   r.m = fmaxf(x.m, y.m);

@@ -6,7 +6,14 @@
 namespace td {
 
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
-enum Epi { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2 };
+enum Epi { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2, EPI_VSTAT = 3 };
+
+// Softmax statistics of a set of scaled logits: max, sum of exp(s - max), lowest index
+// of the max.
+struct VStat {
+  float m, s;
+  int a;
+};
 
 // ---------------------------------------------------------------- packing
 // W [N][K] row-major -> 16x32 MFMA tiles, tile (nt, kt) at ((nt * K/32 + kt) * 64 + lane) * 8,
@@ -23,19 +30,28 @@ struct NormIn {            // A = rmsnorm(x) * gain, formed in the GEMM prologue
 };
 
 struct GemmArgs {
-  int M, N, K;
+  int M, N, K;             // M: row capacity (grid); the live count is *n_rows when n_rows != nullptr
   const float *A; int lda; // plain A [M][lda] (fp32 activations) when norm is off
   NormIn norm;
+  int ld_ssq;              // row stride of norm.ssq (the M of the GEMM that produced it)
+  const int *rowlist;      // optional row gather: GEMM row r reads/writes activation row rowlist[r]
+  const int *n_rows;       // optional live row count (device)
   const void *Wp;          // packed weight [N][K]
-  int ktw;                 // 32-wide k-tiles per wave (<= 16)
-  int ksplit;              // workgroups along K
-  float *part;             // [ksplit][M][N] split-K partials (fp32)
-  unsigned *counters;      // [ceil(M/64)][N/16], zero on entry, left zero
+  int nt;                  // launch_gemm: 16-column tiles per wave (1, 2, 4)
+  int nw;                  // launch_gemm_wk: waves per workgroup (4, 8, 16)
   float *out; int ldo;     // STORE/GELU: fp32 [M][ldo]; RESID: x [M][ldo], updated in place
   float *ssq_out;          // RESID: [N/16][M] partial sums of squares of the updated rows
+  const float *inv_temp;   // VSTAT: [rows] inverse temperature, or nullptr (1)
+  VStat *vpart;            // VSTAT: [row index][grid.x] statistics of each column group
+  float *logits;           // VSTAT: optional capture [rows][N] of the raw logits
   const int *done;         // skip the launch when *done != 0 (nullable)
 };
+// Column-split layout with 4 waves x nt tiles per workgroup, activations staged in LDS;
+// used for the LM head (EPI_VSTAT).
 hipError_t launch_gemm(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s);
+// One 16-column tile per workgroup, its nw waves splitting K with all weights in flight;
+// used for the layer projections (STORE, GELU, RESID).
+hipError_t launch_gemm_wk(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 // One split-K work item: keys [k_begin, k_end) of a prefix chunk, or the block's own keys.
@@ -54,6 +70,7 @@ struct AttnArgs {
   const AttnItem *items; int n_items;
   const int *pair_first, *pair_count;   // item range of each (seq, kv head) pair
   int n_pairs;
+  int max_pair_items;              // largest pair_count (<= 257)
   float *part_o;                   // [n_items][R][hd]
   float *part_ml;                  // [n_items][R][2]
   float *o; int ldo;               // output [n*B][H*hd] (fp32)
@@ -78,21 +95,10 @@ hipError_t launch_init_block(int *tokens, uint8_t *committed, int8_t *commit_ste
 hipError_t launch_embed(int dtype, const int *tokens, const void *E, const void *Pos, float *x, float *ssq,
                         int M, int B, int d, int V, StepState st, hipStream_t s);
 
-// ---------------------------------------------------------------- LM head + vocab reduction + commit
-struct LmArgs {
-  int V, d, B, n;
-  NormIn norm;                     // hf = rmsnorm(x) * g_final
-  const void *Wp;                  // packed LM head [V][d]
-  const float *inv_temp;           // [n*B] or nullptr
-  float *vpart;                    // [M][V/64][3] (max, sumexp, argmax) per row and vocab slice
-  float *logits;                   // debug capture [n*B][V] or nullptr
-  StepState st;
-};
-hipError_t launch_lmhead(int dtype, const LmArgs &a, hipStream_t s);
-
+// ---------------------------------------------------------------- vocab merge + commit
 struct CommitArgs {
   int V, B, n, nslices;
-  const float *vpart;
+  const VStat *vpart;              // [row index][nslices]
   float *conf_row; int *arg_row;   // [M] per-row results (indexed by position in rowlist)
   int *tokens; uint8_t *committed;
   float gamma;
