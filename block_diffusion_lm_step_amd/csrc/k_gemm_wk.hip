@@ -1,20 +1,29 @@
-// Layer projections at block-sized M: Y[M][N] = A[M][K] * W[N][K]^T, weights in flight
-// all at once.
+// Layer projections at block-sized M: Y[M][N] = A[M][K] * W[N][K]^T with the weight
+// stream kept in flight.
 //
 // With B = 16 rows per sequence the fused QKV, output and MLP projections read every
 // weight once per step and do only ~2*M FLOP per weight element: the time is the
 // latency and bandwidth of the weight stream.  Each workgroup owns one 16-column tile
-// and the whole K range; its NW waves split K, and every wave issues the loads of its
-// whole weight slice (pre-packed 16x32 MFMA tiles: one contiguous KiB per load) before
-// it touches the activations, so that chip-wide most of the matrix is in flight at
-// once.  Activation fragments (fp32 rows of the residual stream through the fused
-// RMSNorm, or fp32 attention output / MLP activation) are loaded from L2 in groups
-// while the weights arrive, split into a bf16 high part and a bf16 remainder against
-// bf16 weights (kept fp32 against fp32 weights), and multiplied into one accumulator
-// per 16-row tile.  The waves' accumulators are summed through LDS in wave order (no
-// cross-workgroup reduction, no device-scope fence, deterministic), and wave 0 applies
-// the epilogue: store (q/k/v), exact GELU (MLP up), or residual add + partial sums of
-// squares of the new residual rows for the next RMSNorm (output projection, MLP down).
+// and the whole K range; its NW waves split K.  Every wave keeps PASS k-tiles of
+// weights (pre-packed 16x32 MFMA tiles: one contiguous KiB per load) and of activation
+// fragments in flight: a slot is refilled right after its MFMA, so the loads stream
+// without bubbles, and all loads are unconditional (clamped addresses) so that the
+// waits the compiler places before each MFMA are exact.
+//
+// The activations arrive in fragment layout, written by their producer: fp32 values
+// split into a bf16 high part and a bf16 remainder against bf16 weights (fp32 as is
+// against fp32 weights); a lane's operand is one 32-byte load, no conversion.  A normed
+// input is stored by its producer as x * gain (this GEMM's RMSNorm gain); the per-row
+// scale 1/sqrt(mean(x^2) + eps) factors out of the sum over K and multiplies the
+// accumulator.  It is formed from the producer's partial sums of squares, which are
+// loaded before the weights so that waiting for them never waits for the weights.
+//
+// The waves' accumulators are summed through LDS in wave order (no cross-workgroup
+// reduction, no device-scope fence, deterministic) and wave 0 applies the epilogue:
+//   STORE  q/k/v (fp32, row-major),
+//   GELU   u = gelu_erf(y), written in fragment layout for the MLP down projection,
+//   RESID  x += y (fp32 residual stream), partial sums of squares of the new rows per
+//          16 columns, and x * (next RMSNorm gain) in fragment layout.
 #include "td_device.h"
 #include "td_kernels.h"
 
@@ -22,105 +31,89 @@ namespace td {
 
 namespace {
 
+// k-tiles in flight per wave: the VGPRs per k-tile (activation fragments of MT row
+// tiles + one weight fragment) into a budget that keeps two workgroups per CU
+// (1024-thread workgroups: one workgroup, 128 VGPRs).
+template <typename T, int MT, int NW> constexpr int wk_pass() {
+  constexpr int per = MT * 8 + (sizeof(T) == 2 ? 4 : 8);
+  constexpr int budget = NW == 16 ? 72 : 192;
+  constexpr int p = budget / per;
+  return p > 16 ? 16 : (p < 1 ? 1 : p);
+}
+
 template <typename T, int MT, int NW, int EPI, bool NORM>
 __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
-  // k-tiles of weights a wave holds in flight at once, and k-tiles of activations per
-  // load group, sized to the register file (1024-thread workgroups get 128 VGPRs).
-  constexpr int PASS = NW < 16 ? 16 : (MT == 4 ? 4 : (NORM ? 8 : 16));
-  constexpr int AG = MT == 4 ? 1 : (NW == 16 ? 2 : 4);
+  constexpr int PASS = wk_pass<T, MT, NW>();
+  constexpr int ROWS = 16 * MT;
+  constexpr int TPR = (64 * NW / ROWS) < 64 ? 64 * NW / ROWS : 64;   // threads per row (row scales)
+  constexpr int SQB = 16;                                             // partial sums loaded per batch
   if (a.done && *a.done) return;
   const int M = a.M;
-  const int m0 = blockIdx.z * 16 * MT;
+  const int m0 = blockIdx.z * ROWS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int nt = blockIdx.x;
   const int KT = a.K >> 5;
-  const int kwt = (KT + NW - 1) / NW;          // k-tiles per wave
-  const int kw0 = wave * kwt, kw1 = min(KT, kw0 + kwt);
+  const int kwt = (KT + NW - 1) / NW;            // k-tiles per wave
+  const int kw0 = min(KT, wave * kwt), kw1 = min(KT, kw0 + kwt);
 
-  __shared__ float s_rs[16 * MT];
+  __shared__ float s_rs[ROWS];
   __shared__ f32x4_t s_red[NW - 1][MT][64];
 
+  const T *Wl = reinterpret_cast<const T *>(a.Wp) + ((size_t)nt * KT) * 512 + (size_t)lane * 8;
+  const char *Al = reinterpret_cast<const char *>(a.A) + ((size_t)(m0 >> 4) * KT) * 2048 + (size_t)lane * 32;
+  auto clampk = [&](int kt) { return max(0, min(kt, KT - 1)); };
+  AFrag<T> xa[PASS][MT];
+  Frag<T> wb[PASS];
+  auto fill = [&](int i, int kt) __attribute__((always_inline)) {
+    const int k = clampk(kt);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xa[i][mt] = afl_get<T>(Al + ((size_t)mt * KT + k) * 2048);
+    wb[i].load(Wl + (size_t)k * 512);
+  };
+
+  // Partial sums of squares of this thread's row first (TPR threads per row).
+  const int rr = threadIdx.x / TPR, sub = threadIdx.x % TPR;
+  const int srow = min(m0 + rr, M - 1);
+  float sq[SQB];
   if constexpr (NORM) {
-    // Row scale 1/sqrt(mean(x^2) + eps) from the producer's partial sums of squares:
-    // 16 threads per row, fixed order.
-    for (int r0 = 0; r0 < 16 * MT; r0 += 4 * NW) {
-      const int r = r0 + (threadIdx.x >> 4), sub = threadIdx.x & 15;
-      float acc = 0.f;
-      if (r < 16 * MT && m0 + r < M)
-        for (int p = sub; p < a.norm.nparts; p += 16) acc += a.norm.ssq[(size_t)p * a.ld_ssq + m0 + r];
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      acc += __shfl_xor(acc, 4);
-      acc += __shfl_xor(acc, 8);
-      if (r < 16 * MT && sub == 0) s_rs[r] = 1.0f / sqrtf(acc / (float)a.K + a.norm.eps);
-    }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SQB; ++j)
+      sq[j] = a.ssq[(size_t)min(sub + TPR * j, a.norm_nparts - 1) * a.ld_ssq + srow];
   }
-
-  const T *Wp = reinterpret_cast<const T *>(a.Wp) + ((size_t)nt * KT) * 512 + (size_t)lane * 8;
-  const float *Abase = NORM ? a.norm.x : a.A;
-  const int lda = NORM ? a.K : a.lda;
-
-  // Raw activation fragments (8 fp32) of rows m0 + 16 mt + lane%16 for k-tile kt.
-  auto load_a = [&](float (&v)[8], int mt, int kt) __attribute__((always_inline)) {
-    const int row = m0 + mt * 16 + l16;
-    if (row < M && kt < kw1) {
-      load8f(Abase + (size_t)row * lda + kt * 32 + g * 8, v);
-    } else {
+  // First PASS k-tiles of activations and weights.
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.f;
-    }
-  };
-  auto to_frag = [&](const float (&v)[8], int mt, int kt) __attribute__((always_inline)) {
-    AFrag<T> f;
-    if constexpr (NORM) {
-      float u[8];
-      Frag<T> gg;
-      gg.load(reinterpret_cast<const T *>(a.norm.gain) + kt * 32 + g * 8);
-      const float r = s_rs[mt * 16 + l16];
+  for (int i = 0; i < PASS; ++i) fill(i, kw0 + i);
+  if constexpr (NORM) {
+    float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) u[j] = v[j] * r * gg.get(j);
-      f.set8(u);
-    } else {
-      f.set8(v);
-    }
-    return f;
-  };
+    for (int j = 0; j < SQB; ++j) s += (sub + TPR * j < a.norm_nparts) ? sq[j] : 0.f;
+    for (int p = sub + TPR * SQB; p < a.norm_nparts; p += TPR) s += a.ssq[(size_t)p * a.ld_ssq + srow];
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o);
+    if (sub == 0) s_rs[rr] = 1.0f / sqrtf(s / (float)a.K + a.norm_eps);
+  }
 
   f32x4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = zero4();
-
-  for (int p0 = kw0; p0 < kw1; p0 += PASS) {
-    // Whole pass of weights in flight first.
-    Frag<T> wb[PASS];
+  int p0 = kw0;
+  for (; p0 + PASS < kw1; p0 += PASS) {
 #pragma unroll
-    for (int i = 0; i < PASS; ++i)
-      if (p0 + i < kw1) wb[i].load(Wp + (size_t)(p0 + i) * 512);
-    // Activations in groups of AG k-tiles, one group ahead.
-    float xa[2][AG][MT][8];
+    for (int i = 0; i < PASS; ++i) {
 #pragma unroll
-    for (int i = 0; i < AG; ++i)
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mma_a(xa[i][mt], wb[i], acc[mt]);
+      fill(i, p0 + PASS + i);
+      // Keep each refill right behind its MFMA: left alone, the scheduler sinks all
+      // refills below the pass's MFMAs and the stream stalls once per pass.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) load_a(xa[0][i][mt], mt, p0 + i);
+  for (int i = 0; i < PASS; ++i) {
+    if (p0 + i < kw1) {
 #pragma unroll
-    for (int gi = 0; gi < PASS / AG; ++gi) {
-      const int cur = gi & 1;
-      if (p0 + (gi + 1) * AG < kw1 && gi + 1 < PASS / AG) {
-#pragma unroll
-        for (int i = 0; i < AG; ++i)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) load_a(xa[cur ^ 1][i][mt], mt, p0 + (gi + 1) * AG + i);
-      }
-#pragma unroll
-      for (int i = 0; i < AG; ++i) {
-        const int kt = p0 + gi * AG + i;
-        if (kt < kw1) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = mma_a(to_frag(xa[cur][i][mt], mt, kt), wb[gi * AG + i], acc[mt]);
-        }
-      }
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mma_a(xa[i][mt], wb[i], acc[mt]);
     }
   }
 
@@ -137,26 +130,41 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
     for (int mt = 0; mt < MT; ++mt) acc[mt] += s_red[w][mt][lane];
 
   const int col = nt * 16 + l16;
+  const int KTo = a.N >> 5;   // k-tiles of a fragment-layout output (its K is this GEMM's N)
+  // Residual rows and the next gain, all loaded before any store (the outputs may alias
+  // nothing here, but the compiler cannot know that and would serialise the loads).
+  float xold[MT][4], gnext = 1.0f;
+  if constexpr (EPI == EPI_RESID) {
+    gnext = to_f32<T>(reinterpret_cast<const T *>(a.gain_next)[col]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = min(m0 + mt * 16 + 4 * g + r, M - 1);
+        xold[mt][r] = a.out[(size_t)row * a.ldo + col];
+      }
+  }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = m0 + mt * 16 + 4 * g + r;
+      const int ri = mt * 16 + 4 * g + r;
+      const int row = m0 + ri;
       const bool ok = row < M;
-      const float y = acc[mt][r];
-      float *op = a.out + (size_t)row * a.ldo + col;
+      float y = acc[mt][r];
+      if constexpr (NORM) y *= s_rs[ri];
       if constexpr (EPI == EPI_STORE) {
-        if (ok) *op = y;
+        if (ok) a.out[(size_t)row * a.ldo + col] = y;
       } else if constexpr (EPI == EPI_GELU) {
-        if (ok) *op = gelu_erf(y);
+        if (ok) afl_put<T>(a.out_afl, KTo, row, col, gelu_erf(y));
       } else {
-        float xv = 0.f;
+        const float xv = ok ? xold[mt][r] + y : 0.f;
         if (ok) {
-          xv = *op + y;
-          *op = xv;
+          a.out[(size_t)row * a.ldo + col] = xv;
+          afl_put<T>(a.out_afl, KTo, row, col, xv * gnext);
         }
-        const float sq = sum16(xv * xv);
-        if (ok && l16 == 0) a.ssq_out[(size_t)nt * M + row] = sq;
+        const float sq16 = sum16(xv * xv);
+        if (ok && l16 == 0) a.ssq_out[(size_t)nt * M + row] = sq16;
       }
     }
   }
@@ -181,14 +189,17 @@ template <typename T, int MT>
 hipError_t launch_mt(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
   if (a.nw == 4) return launch_nw<T, MT, 4>(epi, norm, a, s);
   if (a.nw == 8) return launch_nw<T, MT, 8>(epi, norm, a, s);
-  if (a.nw == 16) return launch_nw<T, MT, 16>(epi, norm, a, s);
+  // Four row tiles with 16 waves would spill (128 VGPRs per lane): 8 waves instead.
+  if (a.nw == 16) return MT == 4 ? launch_nw<T, MT, 8>(epi, norm, a, s) : launch_nw<T, MT, 16>(epi, norm, a, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_gemm_wk(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s) {
-  if (a.N % 16 || a.K % 32 || a.M <= 0) return hipErrorInvalidValue;
+  if (a.N % 32 || a.K % 32 || a.M <= 0) return hipErrorInvalidValue;
+  if (norm && (a.ssq == nullptr || a.norm_nparts <= 0)) return hipErrorInvalidValue;
+  if ((epi == EPI_GELU || epi == EPI_RESID) && a.out_afl == nullptr) return hipErrorInvalidValue;
   const bool small = a.M <= 16;
   if (dtype == DT_BF16) return small ? launch_mt<bf16_t, 1>(epi, norm, a, s) : launch_mt<bf16_t, 4>(epi, norm, a, s);
   return small ? launch_mt<float, 1>(epi, norm, a, s) : launch_mt<float, 4>(epi, norm, a, s);

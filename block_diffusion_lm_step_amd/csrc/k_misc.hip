@@ -69,8 +69,9 @@ __global__ __launch_bounds__(1024) void init_block_kernel(int *tokens, uint8_t *
 // x[r] = E[tok[r]] + Pos[r % B] (fp32) and the partial sums of squares of every 16-column
 // group, [d/16][M], which the next GEMM prologue turns into the RMSNorm row scale.
 template <typename T>
-__global__ __launch_bounds__(256) void embed_kernel(const int *tokens, const T *E, const T *Pos, float *x,
-                                                    float *ssq, int M, int B, int d, int V, StepState st) {
+__global__ __launch_bounds__(256) void embed_kernel(const int *tokens, const T *E, const T *Pos, const T *gain,
+                                                    float *x, float *ssq, void *x_afl, int M, int B, int d, int V,
+                                                    StepState st) {
   if (*st.done) return;
   const int r = blockIdx.x;
   int tok = tokens[r];
@@ -81,15 +82,18 @@ __global__ __launch_bounds__(256) void embed_kernel(const int *tokens, const T *
   const T *e = E + (size_t)tok * d;
   const T *p = Pos + (size_t)(r % B) * d;
   for (int grp = threadIdx.x; grp < d / 16; grp += blockDim.x) {
-    float s = 0.f;
+    float s = 0.f, v[16], vg[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       const int k = grp * 16 + c;
-      const float v = to_f32<T>(e[k]) + to_f32<T>(p[k]);
-      x[(size_t)r * d + k] = v;
-      s += v * v;
+      v[c] = to_f32<T>(e[k]) + to_f32<T>(p[k]);
+      vg[c] = v[c] * to_f32<T>(gain[k]);
+      x[(size_t)r * d + k] = v[c];
+      s += v[c] * v[c];
     }
     ssq[(size_t)grp * M + r] = s;
+    afl_put8<T>(x_afl, d / 32, r, grp * 16, vg);
+    afl_put8<T>(x_afl, d / 32, r, grp * 16 + 8, vg + 8);
   }
 }
 
@@ -118,15 +122,15 @@ hipError_t launch_init_block(int *tokens, uint8_t *committed, int8_t *commit_ste
   return hipGetLastError();
 }
 
-hipError_t launch_embed(int dtype, const int *tokens, const void *E, const void *Pos, float *x, float *ssq, int M,
-                        int B, int d, int V, StepState st, hipStream_t s) {
-  if (d % 16) return hipErrorInvalidValue;
+hipError_t launch_embed(int dtype, const int *tokens, const void *E, const void *Pos, const void *gain, float *x,
+                        float *ssq, void *x_afl, int M, int B, int d, int V, StepState st, hipStream_t s) {
+  if (d % 32) return hipErrorInvalidValue;
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, s, tokens, (const bf16_t *)E,
-                       (const bf16_t *)Pos, x, ssq, M, B, d, V, st);
+                       (const bf16_t *)Pos, (const bf16_t *)gain, x, ssq, x_afl, M, B, d, V, st);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, s, tokens, (const float *)E, (const float *)Pos,
-                       x, ssq, M, B, d, V, st);
+                       (const float *)gain, x, ssq, x_afl, M, B, d, V, st);
   return hipGetLastError();
 }
 

@@ -41,7 +41,10 @@ struct td_ctx {
   int Mmax = 0, Nqkv = 0;
   float *x = nullptr, *ssq = nullptr, *conf_row = nullptr;
   VStat *vpart = nullptr;
-  float *qkv = nullptr, *o = nullptr, *u = nullptr;   // fp32 activations
+  float *qkv = nullptr;          // q | k | v of the block rows (fp32)
+  // GEMM inputs in fragment layout: ah = x * (gain of the next RMSNorm), ao = attention
+  // output, au = GELU output of the MLP up projection.
+  void *ah = nullptr, *ao = nullptr, *au = nullptr;
   int *arg_row = nullptr;
   int *state_ints = nullptr;    // rowlist | rowpos | n_rows, done, t, err, counter
   StepState st{};
@@ -50,7 +53,7 @@ struct td_ctx {
   // prefix binding
   int n_seqs = 0;
   std::vector<int64_t> offsets;
-  int64_t *offsets_d = nullptr;
+  int64_t *page_off_d = nullptr;
   std::vector<const void *> kc, vc;
   AttnItem *items_d = nullptr;
   int *pair_first_d = nullptr, *pair_count_d = nullptr;
@@ -139,17 +142,18 @@ td_status validate_weights(const td_config &c, const td_weights *w) {
 }
 
 // The LM head (vocabulary statistics): 4 column tiles per wave, 256 columns per
-// workgroup.  Layer projections: one 16-column tile per workgroup and enough waves
-// along K that each holds at most 16 k-tiles (16 KiB of bf16 weights) in flight.
+// workgroup.  Layer projections: one 16-column tile per workgroup.  At most 256 tiles
+// (one workgroup per CU): 16 waves along K (8 with four row tiles, for the register
+// file), so that one CU keeps many k-tiles in flight; more tiles: 4 waves, so that two
+// workgroups fit on a CU and 512 tiles run in one round.  Each wave keeps >= 2 k-tiles.
 GemmPlan plan_gemm(int M, int N, int K, bool vstat) {
-  (void)M;
   GemmPlan p;
   if (vstat) {
     p.nt = N % 256 == 0 ? 4 : (N % 128 == 0 ? 2 : 1);
   } else {
-    const int KT = K / 32;
-    p.nw = 4;
-    while (p.nw < 16 && (KT + p.nw - 1) / p.nw > 16) p.nw *= 2;
+    const int KT = K / 32, tiles = N / 16;
+    p.nw = tiles <= 256 ? (M <= 16 ? 16 : 8) : 4;
+    while (p.nw > 4 && KT / p.nw < 2) p.nw /= 2;
   }
   return p;
 }
@@ -186,7 +190,7 @@ td_status prof_mark(td_ctx *c, int kind, bool start) {
   return TD_OK;
 }
 
-td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, const int *done) {
+td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, void *o_afl, const int *done) {
   const td_config &g = c->cfg;
   AttnArgs a{};
   a.B = g.block_size;
@@ -199,7 +203,7 @@ td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, co
   a.qkv = qkv;
   a.kc = c->kc[layer];
   a.vc = c->vc[layer];
-  a.offsets = c->offsets_d;
+  a.page_off = c->page_off_d;
   a.items = c->items_d;
   a.n_items = c->n_items;
   a.pair_first = c->pair_first_d;
@@ -210,6 +214,7 @@ td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, co
   a.part_ml = c->att_ml;
   a.o = o;
   a.ldo = g.n_heads * g.head_dim;
+  a.o_afl = o_afl;
   a.scale = 1.0f / std::sqrt((float)g.head_dim);
   a.done = done;
   TD_TRY(prof_mark(c, TD_PROF_ATTENTION, true));
@@ -218,18 +223,10 @@ td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, co
   return TD_OK;
 }
 
-NormIn norm_in(td_ctx *c, const void *gain) {
-  NormIn n{};
-  n.x = c->x;
-  n.ssq = c->ssq;
-  n.nparts = c->cfg.d_model / 16;
-  n.gain = gain;
-  n.eps = c->cfg.rms_eps;
-  return n;
-}
-
-td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const float *A, int lda,
-                       const void *gain, const void *Wp, const GemmPlan &p, float *out, int ldo,
+// One weight-streaming GEMM.  A: fragment-layout input; norm: A holds x * gain of an
+// RMSNorm whose row scale comes from the partial sums of squares in c->ssq.
+td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const void *A, const void *Wp,
+                       const GemmPlan &p, float *out, void *out_afl, const void *gain_next,
                        const GemmArgs *extra = nullptr) {
   GemmArgs a{};
   if (extra) a = *extra;
@@ -237,14 +234,19 @@ td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const
   a.N = N;
   a.K = K;
   a.A = A;
-  a.lda = lda;
-  if (norm) a.norm = norm_in(c, gain);
-  a.ld_ssq = M;
+  if (norm) {
+    a.ssq = c->ssq;
+    a.norm_nparts = c->cfg.d_model / 16;
+    a.ld_ssq = M;
+    a.norm_eps = c->cfg.rms_eps;
+  }
   a.Wp = Wp;
   a.nt = p.nt;
   a.nw = p.nw;
   a.out = out;
-  a.ldo = ldo;
+  a.ldo = N;
+  a.out_afl = out_afl;
+  a.gain_next = gain_next;
   a.ssq_out = c->ssq;
   a.done = c->st.done;
   if (epi == EPI_VSTAT) {
@@ -264,16 +266,15 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   const int M = c->n_seqs * g.block_size;
   const int d = g.d_model, Hd = g.n_heads * g.head_dim;
   TD_TRY(prof_mark(c, TD_PROF_STEP, true));
-  TD_HIP(c, launch_embed(g.dtype, tokens, c->tok_emb, c->pos_emb, c->x, c->ssq, M, g.block_size, d, g.vocab, c->st,
-                         c->stream));
+  TD_HIP(c, launch_embed(g.dtype, tokens, c->tok_emb, c->pos_emb, c->attn_norm[0], c->x, c->ssq, c->ah, M,
+                         g.block_size, d, g.vocab, c->st, c->stream));
   for (int l = 0; l < g.n_layers; ++l) {
-    TD_TRY(enqueue_gemm(c, EPI_STORE, true, M, c->Nqkv, d, nullptr, 0, c->attn_norm[l], c->wqkv[l], c->p_qkv, c->qkv,
-                        c->Nqkv));
-    TD_TRY(enqueue_attention(c, l, c->qkv, c->o, c->st.done));
-    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, Hd, c->o, Hd, nullptr, c->wo[l], c->p_wo, c->x, d));
-    TD_TRY(enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, nullptr, 0, c->mlp_norm[l], c->w1[l], c->p_w1, c->u,
-                        g.d_ff));
-    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->u, g.d_ff, nullptr, c->w2[l], c->p_w2, c->x, d));
+    const void *gain_after = l + 1 < g.n_layers ? c->attn_norm[l + 1] : c->final_norm;
+    TD_TRY(enqueue_gemm(c, EPI_STORE, true, M, c->Nqkv, d, c->ah, c->wqkv[l], c->p_qkv, c->qkv, nullptr, nullptr));
+    TD_TRY(enqueue_attention(c, l, c->qkv, nullptr, c->ao, c->st.done));
+    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, Hd, c->ao, c->wo[l], c->p_wo, c->x, c->ah, c->mlp_norm[l]));
+    TD_TRY(enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, c->ah, c->w1[l], c->p_w1, nullptr, c->au, nullptr));
+    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->au, c->w2[l], c->p_w2, c->x, c->ah, gain_after));
   }
   GemmArgs lm{};
   lm.rowlist = c->st.rowlist;
@@ -282,8 +283,7 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   lm.vpart = c->vpart;
   lm.logits = logits;
   TD_TRY(prof_mark(c, TD_PROF_LMHEAD, true));
-  TD_TRY(enqueue_gemm(c, EPI_VSTAT, true, M, g.vocab, d, nullptr, 0, c->final_norm, c->lm_head, c->p_lm, nullptr, 0,
-                      &lm));
+  TD_TRY(enqueue_gemm(c, EPI_VSTAT, true, M, g.vocab, d, c->ah, c->lm_head, c->p_lm, nullptr, nullptr, nullptr, &lm));
   TD_TRY(prof_mark(c, TD_PROF_LMHEAD, false));
   CommitArgs ca{};
   ca.V = g.vocab;
@@ -325,8 +325,8 @@ void free_all(td_ctx *c) {
   f(c->tok_emb); f(c->pos_emb); f(c->final_norm); f(c->lm_head);
   for (auto *v : {&c->attn_norm, &c->mlp_norm, &c->wqkv, &c->wo, &c->w1, &c->w2})
     for (void *p : *v) f(p);
-  f(c->x); f(c->ssq); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->o); f(c->u);
-  f(c->arg_row); f(c->state_ints); f(c->offsets_d); f(c->items_d); f(c->pair_first_d);
+  f(c->x); f(c->ssq); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->ah); f(c->ao); f(c->au);
+  f(c->arg_row); f(c->state_ints); f(c->page_off_d); f(c->items_d); f(c->pair_first_d);
   f(c->pair_count_d); f(c->att_o); f(c->att_ml);
   for (hipEvent_t e : c->ev_start) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->ev_stop) (void)hipEventDestroy(e);
@@ -375,8 +375,13 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   TD_TRY(dmalloc(c, &c->x, M * d * 4));
   TD_TRY(dmalloc(c, &c->ssq, (d / 16) * M * 4));
   TD_TRY(dmalloc(c, &c->qkv, M * c->Nqkv * 4));
-  TD_TRY(dmalloc(c, &c->o, M * Hd * 4));
-  TD_TRY(dmalloc(c, &c->u, M * F * 4));
+  TD_TRY(dmalloc(c, &c->ah, afl_bytes((int)M, (int)d)));
+  TD_TRY(dmalloc(c, &c->ao, afl_bytes((int)M, (int)Hd)));
+  TD_TRY(dmalloc(c, &c->au, afl_bytes((int)M, (int)F)));
+  // Rows past the live count are read as padding by the GEMMs: keep them finite.
+  TD_HIP(c, hipMemsetAsync(c->ah, 0, afl_bytes((int)M, (int)d), c->stream));
+  TD_HIP(c, hipMemsetAsync(c->ao, 0, afl_bytes((int)M, (int)Hd), c->stream));
+  TD_HIP(c, hipMemsetAsync(c->au, 0, afl_bytes((int)M, (int)F), c->stream));
   TD_TRY(dmalloc(c, &c->conf_row, M * 4));
   TD_TRY(dmalloc(c, &c->arg_row, M * 4));
   TD_TRY(dmalloc(c, &c->vpart, M * (V / 64) * sizeof(VStat)));
@@ -481,11 +486,13 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
   TD_TRY(grow(&c->att_o, cap_o, rows, (size_t)g.head_dim * 4));
   TD_TRY(grow(&c->att_ml, cap_ml, rows, 8));
   c->att_cap_rows = std::min(cap_o, cap_ml);
-  if (!c->offsets_d) TD_TRY(dmalloc(c, &c->offsets_d, (size_t)(g.max_batch + 1) * sizeof(int64_t)));
+  if (!c->page_off_d) TD_TRY(dmalloc(c, &c->page_off_d, (size_t)(g.max_batch + 1) * sizeof(int64_t)));
   TD_HIP(c, hipMemcpy(c->items_d, items.data(), items.size() * sizeof(AttnItem), hipMemcpyHostToDevice));
   TD_HIP(c, hipMemcpy(c->pair_first_d, pfirst.data(), pfirst.size() * sizeof(int), hipMemcpyHostToDevice));
   TD_HIP(c, hipMemcpy(c->pair_count_d, pcount.data(), pcount.size() * sizeof(int), hipMemcpyHostToDevice));
-  TD_HIP(c, hipMemcpy(c->offsets_d, off, (size_t)(n_seqs + 1) * sizeof(int64_t), hipMemcpyHostToDevice));
+  std::vector<int64_t> page_off(n_seqs + 1, 0);
+  for (int i = 0; i < n_seqs; ++i) page_off[i + 1] = page_off[i] + (off[i + 1] - off[i] + KV_PAGE - 1) / KV_PAGE;
+  TD_HIP(c, hipMemcpy(c->page_off_d, page_off.data(), (size_t)(n_seqs + 1) * sizeof(int64_t), hipMemcpyHostToDevice));
   {  // GEMM plans for this batch size
     const int M = n_seqs * g.block_size;
     const int d = g.d_model, F = g.d_ff, Hd = g.n_heads * g.head_dim;
@@ -537,7 +544,7 @@ td_status td_debug_attention(td_ctx *c, int32_t layer, const void *qkv, void *o)
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, TD_EINVAL, "layer out of range");
   if (!qkv || !o) return fail(c, TD_EINVAL, "qkv and o must not be NULL");
   TD_TRY(check_bound(c));
-  return enqueue_attention(c, layer, (const float *)qkv, (float *)o, nullptr);
+  return enqueue_attention(c, layer, (const float *)qkv, (float *)o, nullptr, nullptr);
 }
 
 td_status td_sync(td_ctx *c) {

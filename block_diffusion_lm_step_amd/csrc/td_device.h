@@ -121,6 +121,52 @@ TD_DEV f32x4_t mma_b(const Frag<float> &k, const AFrag<float> &q, f32x4_t acc) {
 
 TD_DEV f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
+// ---------------------------------------------------------------- activation fragments in memory
+// Fragment layout ("AFL") of GEMM inputs, as described in td_kernels.h: a GEMM loads each
+// lane's MFMA operand with one 32-byte read and no conversion.
+// Byte offset of the fragment holding element (row, k) of a matrix with KT k-tiles.
+TD_DEV size_t afl_frag(int row, int k, int KT) {
+  return ((size_t)((row >> 4) * KT + (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (row & 15)) * 32;
+}
+template <typename T> TD_DEV void afl_put(void *buf, int KT, int row, int k, float v);
+template <> TD_DEV void afl_put<bf16_t>(void *buf, int KT, int row, int k, float v) {
+  char *f = reinterpret_cast<char *>(buf) + afl_frag(row, k, KT);
+  const bf16_t hi = f2bf(v);
+  const bf16_t lo = f2bf(v - bf2f(hi));
+  reinterpret_cast<bf16_t *>(f)[k & 7] = hi;
+  reinterpret_cast<bf16_t *>(f + 16)[k & 7] = lo;
+}
+template <> TD_DEV void afl_put<float>(void *buf, int KT, int row, int k, float v) {
+  reinterpret_cast<float *>(reinterpret_cast<char *>(buf) + afl_frag(row, k, KT))[k & 7] = v;
+}
+// Elements k .. k+7 (k a multiple of 8) of one row: one whole fragment.
+template <typename T> TD_DEV void afl_put8(void *buf, int KT, int row, int k, const float *v);
+template <> TD_DEV void afl_put8<bf16_t>(void *buf, int KT, int row, int k, const float *v) {
+  AFrag<bf16_t> f;
+  f.set8(v);
+  uint4 *p = reinterpret_cast<uint4 *>(reinterpret_cast<char *>(buf) + afl_frag(row, k, KT));
+  p[0] = f.hi.raw;
+  p[1] = f.lo.raw;
+}
+template <> TD_DEV void afl_put8<float>(void *buf, int KT, int row, int k, const float *v) {
+  float4 *p = reinterpret_cast<float4 *>(reinterpret_cast<char *>(buf) + afl_frag(row, k, KT));
+  p[0] = make_float4(v[0], v[1], v[2], v[3]);
+  p[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <typename T> TD_DEV AFrag<T> afl_get(const void *frag);
+template <> TD_DEV AFrag<bf16_t> afl_get<bf16_t>(const void *frag) {
+  AFrag<bf16_t> f;
+  f.hi.raw = reinterpret_cast<const uint4 *>(frag)[0];
+  f.lo.raw = reinterpret_cast<const uint4 *>(frag)[1];
+  return f;
+}
+template <> TD_DEV AFrag<float> afl_get<float>(const void *frag) {
+  AFrag<float> f;
+  f.f.lo = reinterpret_cast<const float4 *>(frag)[0];
+  f.f.hi = reinterpret_cast<const float4 *>(frag)[1];
+  return f;
+}
+
 TD_DEV void load8f(const float *p, float *v) {
   const float4 a = reinterpret_cast<const float4 *>(p)[0];
   const float4 b = reinterpret_cast<const float4 *>(p)[1];

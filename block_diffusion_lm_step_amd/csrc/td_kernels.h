@@ -20,26 +20,31 @@ struct VStat {
 // lane l holding W[16 nt + l%16][32 kt + 8 (l/16) .. +8].
 hipError_t launch_pack_weight(int dtype, const void *W, void *Wp, int N, int K, hipStream_t s);
 
-// ---------------------------------------------------------------- GEMM (weight streaming)
-struct NormIn {            // A = rmsnorm(x) * gain, formed in the GEMM prologue
-  const float *x;          // [M][K] residual stream (fp32)
-  const float *ssq;        // [nparts][M] partial sums of squares of each x row
-  int nparts;
-  const void *gain;        // [K] config dtype
-  float eps;
-};
+// ---------------------------------------------------------------- activations in fragment layout
+// Activation matrices that feed a GEMM are stored by their producer in MFMA A-fragment
+// order ("AFL"): fragment (mt, kt, lane) is 32 bytes at ((mt * K/32 + kt) * 64 + lane) * 32
+// and holds row 16 mt + lane % 16, columns 32 kt + 8 (lane / 16) .. +8, as 8 bf16 high
+// parts then 8 bf16 remainders (bf16 towers) or as 8 fp32 values (fp32 towers): 4 bytes
+// per element either way.  Rows are padded to a multiple of 64 (the widest row tile).
+inline size_t afl_bytes(int rows, int K) { return (size_t)((rows + 63) / 64 * 64) * K * 4; }
 
+// ---------------------------------------------------------------- GEMM (weight streaming)
 struct GemmArgs {
   int M, N, K;             // M: row capacity (grid); the live count is *n_rows when n_rows != nullptr
-  const float *A; int lda; // plain A [M][lda] (fp32 activations) when norm is off
-  NormIn norm;
-  int ld_ssq;              // row stride of norm.ssq (the M of the GEMM that produced it)
-  const int *rowlist;      // optional row gather: GEMM row r reads/writes activation row rowlist[r]
+  const void *A;           // activations [M][K] in fragment layout
+  // RMSNorm (NORM variants): A holds x * gain; the row scale 1/sqrt(mean(x^2) + eps)
+  // comes from the producer's partial sums of squares and multiplies the accumulator.
+  const float *ssq;        // [norm_nparts][ld_ssq]
+  int norm_nparts, ld_ssq;
+  float norm_eps;
+  const int *rowlist;      // optional row gather: GEMM row r is activation row rowlist[r]
   const int *n_rows;       // optional live row count (device)
   const void *Wp;          // packed weight [N][K]
   int nt;                  // launch_gemm: 16-column tiles per wave (1, 2, 4)
   int nw;                  // launch_gemm_wk: waves per workgroup (4, 8, 16)
-  float *out; int ldo;     // STORE/GELU: fp32 [M][ldo]; RESID: x [M][ldo], updated in place
+  float *out; int ldo;     // STORE: fp32 [M][ldo]; RESID: x [M][ldo], updated in place
+  void *out_afl;           // GELU: gelu(y) [M][N] in fragment layout; RESID: x * gain_next, same layout
+  const void *gain_next;   // RESID: [N] gain of the RMSNorm that consumes the updated x
   float *ssq_out;          // RESID: [N/16][M] partial sums of squares of the updated rows
   const float *inv_temp;   // VSTAT: [rows] inverse temperature, or nullptr (1)
   VStat *vpart;            // VSTAT: [row index][grid.x] statistics of each column group
@@ -54,8 +59,16 @@ hipError_t launch_gemm(int dtype, int epi, bool norm, const GemmArgs &a, hipStre
 hipError_t launch_gemm_wk(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
-// One split-K work item: keys [k_begin, k_end) of a prefix chunk, or the block's own keys.
-// The items of a (seq, kv head) pair are consecutive; the block item is the pair's last.
+// Prefix K/V cache pages: 32 tokens per page; page p of K/V head h is one contiguous
+// block, K as [32 tokens][hd] and V transposed as [hd][32 tokens]; element offsets
+//   K: ((p * Hkv + h) * 32 + slot) * hd + e        V: ((p * Hkv + h) * hd + e) * 32 + slot
+// Sequence i owns pages [page_off[i], page_off[i] + ceil(P_i / 32)); token t is in page
+// page_off[i] + t / 32, slot t % 32.
+constexpr int KV_PAGE = 32;
+
+// One split-K work item: prefix tokens [k_begin, k_end) (k_begin a multiple of the page
+// size), or the block's own keys.  The items of a (seq, kv head) pair are consecutive;
+// the block item is the pair's last.
 struct AttnItem {
   int seq, kvh;            // sequence and key/value head
   int k_begin, k_end;      // key range (prefix token index within the sequence; or 0..B)
@@ -65,15 +78,16 @@ struct AttnItem {
 struct AttnArgs {
   int B, H, Hkv, hd, Nqkv, G, R;   // R = G * B query rows per (seq, kv head)
   const float *qkv;                // [n*B][Nqkv]: q | k_block | v_block (fp32)
-  const void *kc, *vc;             // prefix caches [sumP][Hkv][hd]
-  const int64_t *offsets;          // [n+1] prefix offsets (device)
+  const void *kc, *vc;             // prefix cache pages (layout above)
+  const int64_t *page_off;         // [n+1] first page of each sequence (device)
   const AttnItem *items; int n_items;
   const int *pair_first, *pair_count;   // item range of each (seq, kv head) pair
   int n_pairs;
   int max_pair_items;              // largest pair_count (<= 257)
   float *part_o;                   // [n_items][R][hd]
   float *part_ml;                  // [n_items][R][2]
-  float *o; int ldo;               // output [n*B][H*hd] (fp32)
+  float *o; int ldo;               // optional output [n*B][ldo] (fp32, natural layout)
+  void *o_afl;                     // optional output [n*B][H*hd] in fragment layout
   float scale;                     // 1 / sqrt(hd)
   const int *done;
 };
@@ -92,8 +106,10 @@ struct StepState {                 // device-resident loop state owned by the ct
 hipError_t launch_prep(const int *tokens, const uint8_t *committed, int M, int V, StepState st, hipStream_t s);
 hipError_t launch_init_block(int *tokens, uint8_t *committed, int8_t *commit_step, int *steps, int n, int B,
                              int V, StepState st, hipStream_t s);
-hipError_t launch_embed(int dtype, const int *tokens, const void *E, const void *Pos, float *x, float *ssq,
-                        int M, int B, int d, int V, StepState st, hipStream_t s);
+// x = E[token] + Pos[position] (fp32), partial sums of squares per 16 columns, and
+// x * gain (the first RMSNorm's gain) in fragment layout.
+hipError_t launch_embed(int dtype, const int *tokens, const void *E, const void *Pos, const void *gain, float *x,
+                        float *ssq, void *x_afl, int M, int B, int d, int V, StepState st, hipStream_t s);
 
 // ---------------------------------------------------------------- vocab merge + commit
 struct CommitArgs {

@@ -87,14 +87,24 @@ typedef struct {
  * e.g. no device).  On failure *out is NULL and the message is in td_last_error(NULL). */
 td_status td_create(const td_config *cfg, const td_weights *w, void *stream, td_ctx **out);
 
+/* Prefix K/V cache layout (per layer, config dtype): pages of TD_KV_PAGE = 32 tokens.
+ * Page p of K/V head h is one contiguous block: K as [32 tokens][head_dim], V
+ * transposed as [head_dim][32 tokens]; element offsets
+ *   K: ((p * n_kv_heads + h) * 32 + slot) * head_dim + e
+ *   V: ((p * n_kv_heads + h) * head_dim + e) * 32 + slot.
+ * Sequence i owns ceil(P_i / 32) consecutive pages starting at page
+ * sum_{j<i} ceil(P_j / 32); its token t is in slot t % 32 of its page t / 32.  Slots
+ * past P_i in its last page are never used (they may hold anything). */
+#define TD_KV_PAGE 32
+
 /* Bind the frozen context tower's prefix K/V for a batch of n_seqs sequences.
- * prefix_offsets_host[n_seqs+1]: sequence i owns tokens [off[i], off[i+1]) of every
- * layer's cache; off[0] == 0, non-decreasing, off[n] <= max_prefix_tokens; a prefix
- * may be empty.  k_cache_host / v_cache_host: HOST arrays of n_layers DEVICE pointers,
- * layer l of the context tower feeding denoiser layer l, each [off[n]][n_kv_heads]
- * [head_dim] in the config's dtype.  The caches are BORROWED: they must stay valid and
- * unchanged until the next td_set_prefix or td_destroy.  Builds the split-K work list
- * (host) and may grow the ctx's attention workspace. */
+ * prefix_offsets_host[n_seqs+1]: P_i = off[i+1] - off[i] is sequence i's prefix length;
+ * off[0] == 0, non-decreasing, off[n] <= max_prefix_tokens; a prefix may be empty.
+ * k_cache_host / v_cache_host: HOST arrays of n_layers DEVICE pointers, layer l of the
+ * context tower feeding denoiser layer l, each holding sum_i ceil(P_i / 32) pages in the
+ * layout above.  The caches are BORROWED: they must stay valid and unchanged until the
+ * next td_set_prefix or td_destroy.  Builds the split-K work list (host) and may grow
+ * the ctx's attention workspace. */
 td_status td_set_prefix(td_ctx *ctx, int32_t n_seqs, const int64_t *prefix_offsets_host,
                         const void *const *k_cache_host, const void *const *v_cache_host);
 

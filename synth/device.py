@@ -41,27 +41,55 @@ def tower_config(w: Workload, max_batch: int = None, max_prefix_tokens: int = 0)
                 dtype=w.dtype, rms_eps=w.rms_eps)
 
 
+KV_PAGE = 32   # tokens per prefix-cache page
+
+
+def page_prefix(k: np.ndarray, v: np.ndarray, page: int = KV_PAGE):
+    """Natural [P][Hkv][hd] keys/values -> pages: K [pages][Hkv][page][hd], V [pages][Hkv][hd][page].
+
+    Pure data movement; slots past P in the last page are zero.
+    """
+    P, Hkv, hd = k.shape
+    npg = (P + page - 1) // page
+    kp = np.zeros((npg * page, Hkv, hd), dtype=k.dtype)
+    vp = np.zeros((npg * page, Hkv, hd), dtype=v.dtype)
+    kp[:P], vp[:P] = k, v
+    kp = kp.reshape(npg, page, Hkv, hd).transpose(0, 2, 1, 3)
+    vp = vp.reshape(npg, page, Hkv, hd).transpose(0, 2, 3, 1)
+    return np.ascontiguousarray(kp), np.ascontiguousarray(vp)
+
+
 def prefix_to_device(w: Workload, plens: Sequence[int], device="cuda", layers: int = None
                      ) -> Tuple[List[int], List, List]:
-    """Packed per-layer caches [sumP][Hkv][hd] for a batch with prefix lengths plens."""
+    """Per-layer paged prefix caches for a batch with prefix lengths plens.
+
+    Returns (token offsets [n+1], K caches, V caches); sequence s owns ceil(P_s / 32)
+    consecutive pages starting after the pages of sequences 0..s-1.
+    """
     torch = _torch()
     offsets = [0]
     for p in plens:
         offsets.append(offsets[-1] + int(p))
-    total = offsets[-1]
+    page_off = [0]
+    for p in plens:
+        page_off.append(page_off[-1] + (int(p) + KV_PAGE - 1) // KV_PAGE)
+    npages = max(page_off[-1], 1)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    bf = w.dtype == "bf16"
     L = w.L if layers is None else layers
     ks, vs = [], []
     with cf.ThreadPoolExecutor(_workers()) as pool:
         for l in range(L):
-            kt = torch.empty((max(total, 1), w.Hkv, w.hd), dtype=dt, device=device)
-            vt = torch.empty((max(total, 1), w.Hkv, w.hd), dtype=dt, device=device)
+            kt = torch.zeros((npages, w.Hkv, KV_PAGE, w.hd), dtype=dt, device=device)
+            vt = torch.zeros((npages, w.Hkv, w.hd, KV_PAGE), dtype=dt, device=device)
             for s, P in enumerate(plens):
                 if P == 0:
                     continue
-                for which, dst in (("k", kt), ("v", vt)):
-                    a = draw_prefix_kv(w, l, s, int(P), which, pool=pool)
-                    dst[offsets[s]:offsets[s + 1]] = host_to_device(a, w.dtype == "bf16", device)
+                k = draw_prefix_kv(w, l, s, int(P), "k", pool=pool)
+                v = draw_prefix_kv(w, l, s, int(P), "v", pool=pool)
+                kp, vp = page_prefix(k, v)
+                kt[page_off[s]:page_off[s + 1]] = host_to_device(kp, bf, device)
+                vt[page_off[s]:page_off[s + 1]] = host_to_device(vp, bf, device)
             ks.append(kt)
             vs.append(vt)
     return offsets, ks, vs

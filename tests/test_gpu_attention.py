@@ -17,7 +17,8 @@ def _run(dtype, H, Hkv, hd, B, plens, seed=0, qscale=1.0):
     from block_diffusion_lm_step_amd import Denoiser
     from oracle import joint_attention
     from synth import Workload, draw_tower, f32_from_bf16_bits
-    from synth.device import prefix_to_device, tower_config, tower_to_device
+    from synth.device import KV_PAGE, prefix_to_device, tower_config, tower_to_device
+    from synth.gen import draw_prefix_kv
 
     n = len(plens)
     w = Workload(name=f"attn_{dtype}_{H}_{Hkv}_{hd}_{B}", tower="attn_probe", n=n, plen=("fixed", 0), B=B, d=64,
@@ -25,6 +26,14 @@ def _run(dtype, H, Hkv, hd, B, plens, seed=0, qscale=1.0):
     log(f"[attn] dtype={dtype} H={H} Hkv={Hkv} hd={hd} B={B} plens={list(plens)[:8]}{'...' if n > 8 else ''}")
     dW = tower_to_device(draw_tower(w))
     offsets, ks, vs = prefix_to_device(w, plens)
+    # The cache contract leaves the slots past a prefix's end undefined: poison them.
+    page = 0
+    for P in plens:
+        npg = (P + KV_PAGE - 1) // KV_PAGE
+        if P % KV_PAGE:
+            ks[0][page + npg - 1, :, P % KV_PAGE:, :] = float("nan")
+            vs[0][page + npg - 1, :, :, P % KV_PAGE:] = float("nan")
+        page += npg
     dev = Denoiser(tower_config(w, max_batch=n, max_prefix_tokens=max(1, offsets[-1])), dW)
     dev.set_prefix(offsets, ks, vs)
     rng = np.random.default_rng(seed)
@@ -38,14 +47,19 @@ def _run(dtype, H, Hkv, hd, B, plens, seed=0, qscale=1.0):
     q3 = qkv.reshape(n, B, Nqkv).astype(np.float64)
     worst = 0.0
     for s in range(n):
-        k_pre = ks[0][offsets[s]:offsets[s + 1]].float().cpu().numpy().astype(np.float64)
-        v_pre = vs[0][offsets[s]:offsets[s + 1]].float().cpu().numpy().astype(np.float64)
+        P = int(plens[s])
+        k_pre = draw_prefix_kv(w, 0, s, P, "k")
+        v_pre = draw_prefix_kv(w, 0, s, P, "v")
+        if dtype == "bf16":
+            k_pre, v_pre = f32_from_bf16_bits(k_pre), f32_from_bf16_bits(v_pre)
+        k_pre, v_pre = k_pre.astype(np.float64), v_pre.astype(np.float64)
         q = q3[s, :, :H * hd].reshape(B, H, hd)
         kb = q3[s, :, H * hd:(H + Hkv) * hd].reshape(B, Hkv, hd)
         vb = q3[s, :, (H + Hkv) * hd:].reshape(B, Hkv, hd)
         ref = joint_attention(q, k_pre, v_pre, kb, vb)
         # fp32 accumulation; with bf16 keys the fp32 queries and probabilities enter the
         # MFMA as hi + lo bf16 parts (relative error <= 2^-17 each)
+        assert np.isfinite(o[s]).all(), f"seq {s}: non-finite output"
         err = float(np.abs(o[s] - ref).max() / np.abs(ref).max())
         worst = max(worst, err)
         assert err < (3e-5 if dtype == "bf16" else 1e-5), f"seq {s}: rel err {err:.3e}"

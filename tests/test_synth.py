@@ -76,3 +76,21 @@ def test_prefix_kv_token_slices():
     assert np.array_equal(full[40:77], draw_prefix_kv(w, 1, 0, 128, "k", tok_start=40, tok_stop=77))
     assert not np.array_equal(full, draw_prefix_kv(w, 1, 0, 128, "v"))
     assert abs(full.std() - 1.0) < 0.05
+
+
+def test_prefix_page_layout_matches_the_documented_offsets():
+    """K page p, head h: ((p*Hkv + h)*32 + slot)*hd + e; V: ((p*Hkv + h)*hd + e)*32 + slot."""
+    from synth.device import KV_PAGE, page_prefix
+    rng = np.random.default_rng(4)
+    P, Hkv, hd = 77, 3, 8
+    k = rng.standard_normal((P, Hkv, hd)).astype(np.float32)
+    v = rng.standard_normal((P, Hkv, hd)).astype(np.float32)
+    kp, vp = page_prefix(k, v)
+    npg = (P + KV_PAGE - 1) // KV_PAGE
+    assert kp.shape == (npg, Hkv, KV_PAGE, hd) and vp.shape == (npg, Hkv, hd, KV_PAGE)
+    kf, vf = kp.reshape(-1), vp.reshape(-1)
+    for t, h, e in [(0, 0, 0), (31, 2, 7), (32, 1, 3), (76, 2, 5), (40, 0, 1)]:
+        p_, slot = divmod(t, KV_PAGE)
+        assert kf[((p_ * Hkv + h) * KV_PAGE + slot) * hd + e] == k[t, h, e]
+        assert vf[((p_ * Hkv + h) * hd + e) * KV_PAGE + slot] == v[t, h, e]
+    assert (kp[-1, :, P % KV_PAGE:, :] == 0).all() and (vp[-1, :, :, P % KV_PAGE:] == 0).all()
