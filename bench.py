@@ -41,6 +41,12 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--breakdown", action="store_true", help="also time each kernel class (extra blocks)")
+    p.add_argument("--calibrate-copy-mb", type=int, default=0,
+                   help="before the timed region, one device-to-device copy of this many MiB (a plain copy "
+                        "kernel of known size, the scale of the HBM byte counters)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no benchmark: turn the counter CSVs of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; "
+                        "both with --calibrate-copy-mb) into the LM head's HBM traffic record under profiles/")
     return p.parse_args()
 
 
@@ -52,17 +58,74 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_record(kernel_src: str, per_launch_bytes_alg: float):
-    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current source."""
-    path = os.path.join(ROOT, "profiles", "lmhead_b1_p4096_traffic.json")
+LMHEAD_SOURCES = ("k_gemm.hip", "td_device.h", "td_kernels.h")
+LMHEAD_KERNEL = "lmhead_kernel"
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"lmhead_{workload}_traffic.json")
+
+
+def traffic_record(workload: str):
+    """HBM bytes per LM-head launch from the rocprofv3 counters, if taken on the current source."""
     try:
-        with open(path) as f:
+        with open(traffic_path(workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_hash(kernel_src):
+    if rec.get("source_sha256_16") != source_hash(*LMHEAD_SOURCES):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("hbm_bytes_per_launch")
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str, calib_mb: int) -> dict:
+    """Counter values per dispatch (KiB) -> bytes, scaled by the calibration copy.
+
+    The copy of calib_mb MiB reads and writes exactly that many bytes; the ratio of that
+    size to what FETCH_SIZE / WRITE_SIZE report for it scales the LM head's readings.
+    LM-head dispatches that exited early (the block was already adopted) read ~nothing
+    and are left out: the record is per working launch, like the bench's timing.
+    """
+    import csv
+
+    def per_dispatch(path, counter):
+        lm, blit, elem = [], [], []
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                v = float(row["Counter_Value"]) * 1024.0
+                k = row["Kernel_Name"]
+                if LMHEAD_KERNEL in k:
+                    lm.append(v)
+                elif "copyBuffer" in k:
+                    blit.append(v)
+                elif "MulFunctor" in k:
+                    elem.append(v)
+        return lm, blit, elem
+
+    calib = calib_mb * 1024 * 1024
+    out = {}
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        lm, blit, elem = per_dispatch(path, counter)
+        if not lm or not elem:
+            raise SystemExit(f"{path}: no {LMHEAD_KERNEL} or calibration dispatches with {counter}")
+        factor = calib / max(elem)
+        work = sorted(v for v in lm if v > 0.5 * max(lm)) if name == "fetch" else sorted(lm)
+        if name == "fetch":
+            fetch_work = len(work)
+        raw = float(np.median(work))
+        out[name] = dict(counter=counter, raw_bytes_per_launch=raw, calibration_kernel="elementwise (16 B per lane)",
+                         calibration_raw_bytes=max(elem), factor=factor, bytes_per_launch=raw * factor,
+                         dispatches=len(work), blit_copy_raw_bytes=max(blit) if blit else None)
+    rec = dict(kernel=LMHEAD_KERNEL, workload=workload, source_sha256_16=source_hash(*LMHEAD_SOURCES),
+               calibration_copy_bytes=calib, fetch=out["fetch"], write=out["write"],
+               hbm_bytes_per_launch=out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"],
+               working_launches=fetch_work)
+    os.makedirs(os.path.dirname(traffic_path(workload)), exist_ok=True)
+    with open(traffic_path(workload), "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
 
 
 def cpu_baseline(w, budget_s: float):
@@ -83,7 +146,7 @@ def cpu_baseline(w, budget_s: float):
              w1=[f(a) for a in tw.w1], w2=[f(a) for a in tw.w2], attn_norm=[f(a) for a in tw.attn_norm],
              mlp_norm=[f(a) for a in tw.mlp_norm])
     del tw
-    orc = OracleTower(W, H=w.H, Hkv=w.Hkv, hd=w.hd, eps=w.rms_eps, mode="bf16" if w.dtype == "bf16" else "plain")
+    orc = OracleTower(W, H=w.H, Hkv=w.Hkv, hd=w.hd, eps=w.rms_eps, mode="plain")
     plens = draw_prefix_lengths(w)
     tau = draw_inv_temp(w)
     n_s = min(w.n, 4)   # sequences of the sample (all of a batch-1 workload)
@@ -116,7 +179,7 @@ def cpu_baseline(w, budget_s: float):
         tok, c = r.tok, r.committed
     dt = time.perf_counter() - t0
     sample = (f"{steps} oracle steps of the block loop from all-[MASK] on sequences 0..{n_s - 1} of {w.name} "
-              f"(float64, {'bf16-faithful' if w.dtype == 'bf16' else 'plain'}), {committed} positions adopted"
+              f"(float64 numpy, BLAS on {threads} threads), {committed} positions adopted"
               f"{', block complete' if c.all() else ', stopped at the time budget'}")
     return dict(value=committed / dt, unit="committed tokens/s", cores=int(threads), kind="oracle", sample=sample,
                 denoise_steps_per_s=steps / dt, seconds=dt)
@@ -124,6 +187,11 @@ def cpu_baseline(w, budget_s: float):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        if args.calibrate_copy_mb <= 0:
+            raise SystemExit("--traffic-from needs the --calibrate-copy-mb the counter runs used")
+        print(json.dumps(write_traffic(args.workload, *args.traffic_from, args.calibrate_copy_mb)))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
@@ -162,6 +230,17 @@ def main():
     for _ in range(args.warmup):
         block()
     dev.sync()
+    if args.calibrate_copy_mb > 0:
+        # Two copies of known size: the runtime's blit copy, and an elementwise kernel
+        # whose lanes move 16 contiguous bytes each (1 KiB per wave instruction, the
+        # access pattern of the weight streams).
+        nb = args.calibrate_copy_mb * 1024 * 1024
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     log("[bench] warmup done")
 
     dev.profile_begin(TD_PROF_LMHEAD)
@@ -187,7 +266,7 @@ def main():
     elt = 2 if w.dtype == "bf16" else 4
     lm_bytes = w.V * w.d * elt
     achieved = lm_bytes / (lm_avg_ms * 1e-3) / 1e9
-    traffic = traffic_record("k_lmhead.hip", lm_bytes)
+    traffic = traffic_record(w.name)
 
     breakdown = {}
     if args.breakdown:

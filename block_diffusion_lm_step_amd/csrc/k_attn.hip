@@ -8,18 +8,21 @@
 // two towers; block-wise decoding keeps the prefix K/V read-only while the block is
 // refined).  Query head j reads K/V head j / (H / Hkv).
 //
-// Prefix keys, flash-decoding style.  An item is (sequence, K/V head, run of prefix
-// pages).  The cache is paged (32 tokens per page; per page and K/V head one contiguous
-// 8 KiB block of K as [token][hd] and one of V transposed as [hd][token]), so every
-// MFMA operand is a 16-byte load straight from HBM:
-//   S^T[key][row] = K . Q^T      (A = K rows, B = Q fragments held in registers; the
-//                                 two 16-key halves of a page take key rows in the
-//                                 order that leaves lane group g holding the scores
-//                                 of keys 8g .. 8g+7)
-//   O^T[hd][row] += V^T . P^T    (A = V^T rows of the page, B = P straight from the
-//                                 S^T accumulators)
-// with an online softmax (running max m, running sum l, unnormalised O) per query row.
-// Two shapes of work:
+// Work items (built on the host per prefix binding): runs of prefix pages of one
+// (sequence, K/V head) pair, and one item per pair for the block's own keys.  Every
+// item writes a partial state per query row: running max m, sum l of exp(s - m), and
+// the unnormalised output o; attn_merge_kernel combines a pair's partials in item order.
+//
+// Prefix items, flash-decoding style.  The cache is paged (32 tokens per page; per page
+// and K/V head one contiguous 8 KiB block of K and one of V for bf16), laid out so that
+// every MFMA operand is one contiguous KiB per wave instruction straight from HBM:
+//   S^T[key][row] = K . Q^T      (A = K rows, B = Q fragments held in registers).  The
+//                                 K block is stored as [hd / 32][2 halves][16 rows][32]:
+//                                 row i of half h is key krow(h, i), so that lane group g
+//                                 holds the scores of keys 8g .. 8g+7 of the page;
+//   O^T[hd][row] += V^T . P^T    (A = V^T rows of the page, stored [hd][32 keys]; B = P
+//                                 straight from the S^T accumulators)
+// with an online softmax per query row.  Two shapes of work:
 //   * few query rows per K/V head (R = G*B <= 32, multi-head attention): the four
 //     waves of a workgroup take alternate pages of the item with no LDS and no barrier
 //     in the key loop (the next page in flight while the current one is consumed), and
@@ -31,9 +34,8 @@
 // way for P.V, so q and P keep ~16 significant bits.  Key slots past the end of a
 // sequence's last page are masked (scores to -inf, values to 0).
 //
-// The block's own keys (attn_finish_kernel) are fp32 activations and few (B per pair):
-// they are attended in fp32 on the VALU by the kernel that then merges the prefix
-// partials of the pair, in item order, and writes o.
+// Block items: the B block keys/values are fp32 activations from the QKV projection and
+// few, so they are attended in fp32 on the VALU (16 threads per query row).
 #include "td_device.h"
 #include "td_kernels.h"
 
@@ -44,9 +46,12 @@ namespace td {
 namespace {
 
 constexpr int SUB = KV_PAGE;   // keys per page
+constexpr int BMAX = 32;       // largest block size
 
-// Key row of S^T tile h (0, 1) held by MFMA row i: keys 8g + 4h + r land in lane group g.
-TD_DEV int krow(int h, int i) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+// Element offset, within a K page block, of MFMA row i of S^T half h, hd chunk c (32
+// elements).  Row i of half h holds key 8 (i / 4) + 4 h + i % 4, so that lane group g
+// receives the scores of keys 8g .. 8g+7.
+TD_DEV int kpos(int c, int h, int i) { return ((c * 2 + h) * 16 + i) * 32; }
 
 template <typename T> struct Pad;
 template <> struct Pad<bf16_t> { static constexpr int K = 8, V = 8; };
@@ -145,24 +150,91 @@ TD_DEV void store_partial(const AttnArgs &a, int item, int rt0, int g, int l16, 
   }
 }
 
+template <int HD> constexpr int block_item_lds() { return 2 * BMAX * (HD + 1); }   // floats
+
+// The block's own keys of one (sequence, K/V head) pair, fp32 on the VALU: 16 threads
+// per query row (HD/16 dimensions each), 16 rows at a time.  sm: block_item_lds floats
+// of LDS.  Writes the pair's block partial (m, l, o) to the item's slot.
+template <int HD>
+TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *sm) {
+  constexpr int EPT = HD / 16, KPT = BMAX * HD / 256;
+  float *s_k = sm, *s_v = sm + BMAX * (HD + 1);
+  const float *base = a.qkv + (size_t)it.seq * a.B * a.Nqkv;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {   // all of the pair's block keys and values in flight at once
+    const int idx = threadIdx.x + 256 * i;
+    const int key = idx / HD, e = idx % HD;
+    if (key < a.B) {
+      s_k[key * (HD + 1) + e] = base[(size_t)key * a.Nqkv + (size_t)(a.H + it.kvh) * HD + e];
+      s_v[key * (HD + 1) + e] = base[(size_t)key * a.Nqkv + (size_t)(a.H + a.Hkv + it.kvh) * HD + e];
+    }
+  }
+  __syncthreads();
+  const int sub = threadIdx.x & 15, e0 = sub * EPT;
+  for (int rho0 = 0; rho0 < a.R; rho0 += 16) {
+    const int rho = rho0 + (threadIdx.x >> 4);
+    if (rho >= a.R) break;   // whole 16-lane groups leave together
+    const int j = rho / a.B, p = rho % a.B;
+    const float *q = base + (size_t)p * a.Nqkv + (size_t)(it.kvh * a.G + j) * HD + e0;
+    float qv[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) qv[e] = q[e];
+    float sc[BMAX];
+    float m = -INFINITY;
+#pragma unroll
+    for (int key = 0; key < BMAX; ++key) {
+      if (key < a.B) {
+        float dsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) dsum += qv[e] * s_k[key * (HD + 1) + e0 + e];
+        sc[key] = sum16(dsum) * a.scale;
+        m = fmaxf(m, sc[key]);
+      }
+    }
+    float l = 0.f, ov[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) ov[e] = 0.f;
+#pragma unroll
+    for (int key = 0; key < BMAX; ++key) {
+      if (key < a.B) {
+        const float pk = __expf(sc[key] - m);
+        l += pk;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) ov[e] += pk * s_v[key * (HD + 1) + e0 + e];
+      }
+    }
+    const size_t prow = (size_t)item * a.R + rho;
+    if (sub == 0) {
+      a.part_ml[prow * 2 + 0] = m;
+      a.part_ml[prow * 2 + 1] = l;
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4)
+      *reinterpret_cast<float4 *>(&a.part_o[prow * HD + e0 + e]) = make_float4(ov[e], ov[e + 1], ov[e + 2], ov[e + 3]);
+  }
+}
+
 // Multi-head shape (R <= 32): waves take alternate pages, operands straight from HBM.
 template <typename T, int HD, int RT>
 __global__ __launch_bounds__(256) void attn_direct_kernel(AttnArgs a) {
   if (a.done && *a.done) return;
   constexpr int NW = 4, HC = HD / 32, OT = HD / 16;
-  __shared__ float s_o[NW][RT * 16][HD];
-  __shared__ float s_ml[NW][RT * 16][2];
+  constexpr int MERGE = NW * RT * 16 * (HD + 2);
+  constexpr int LDS = MERGE > block_item_lds<HD>() ? MERGE : block_item_lds<HD>();
+  __shared__ float smem[LDS];
 
   const AttnItem it = a.items[blockIdx.x];
-  if (it.is_block) return;   // block keys: attn_finish_kernel
+  if (it.is_block) {
+    block_item<HD>(a, it, blockIdx.x, smem);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int nkeys = it.k_end - it.k_begin;
   const int npg = (nkeys + SUB - 1) / SUB;
-  const size_t page0 = (size_t)a.page_off[it.seq] + it.k_begin / SUB;
   const size_t pstride = (size_t)a.Hkv * SUB * HD;   // elements between pages
-  const T *Kp = reinterpret_cast<const T *>(a.kc) + (page0 * a.Hkv + it.kvh) * SUB * HD;
-  const T *Vp = reinterpret_cast<const T *>(a.vc) + (page0 * a.Hkv + it.kvh) * HD * SUB;
+  const T *Kp = reinterpret_cast<const T *>(a.kc) + ((size_t)it.page0 * a.Hkv + it.kvh) * SUB * HD;
+  const T *Vp = reinterpret_cast<const T *>(a.vc) + ((size_t)it.page0 * a.Hkv + it.kvh) * HD * SUB;
 
   AFrag<T> qf[RT][HC];
   load_q<T, HD, RT>(a, it, 0, g, l16, qf);
@@ -186,7 +258,7 @@ __global__ __launch_bounds__(256) void attn_direct_kernel(AttnArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int c = 0; c < HC; ++c) kf[b][h][c].load(kp + krow(h, l16) * HD + c * 32 + g * 8);
+        for (int c = 0; c < HC; ++c) kf[b][h][c].load(kp + kpos(c, h, l16) + g * 8);
 #pragma unroll
       for (int t = 0; t < OT; ++t) vf[b][t].load(vp + (16 * t + l16) * SUB + g * 8);
     }
@@ -219,14 +291,15 @@ __global__ __launch_bounds__(256) void attn_direct_kernel(AttnArgs a) {
   }
 
   // Merge the four waves' states (wave order) through LDS.
-  float l_tot[RT];
+  float(*s_o)[RT * 16][HD] = reinterpret_cast<float(*)[RT * 16][HD]>(smem);
+  float(*s_ml)[RT * 16][2] = reinterpret_cast<float(*)[RT * 16][2]>(smem + NW * RT * 16 * HD);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    l_tot[rt] = sum_groups(l_run[rt]);
+    const float l_tot = sum_groups(l_run[rt]);
     const int rr = rt * 16 + l16;
     if (g == 0) {
       s_ml[wave][rr][0] = m_run[rt];
-      s_ml[wave][rr][1] = l_tot[rt];
+      s_ml[wave][rr][1] = l_tot;
     }
 #pragma unroll
     for (int t = 0; t < OT; ++t) *reinterpret_cast<f32x4_t *>(&s_o[wave][rr][16 * t + 4 * g]) = o[rt][t];
@@ -260,29 +333,36 @@ __global__ __launch_bounds__(256) void attn_direct_kernel(AttnArgs a) {
   }
 }
 
-// Grouped-query shape (R > 32): each page is copied once into LDS (K rows and V^T rows,
-// 16-byte copies) and the four waves, RT 16-row tiles each, read it from there.
+// Grouped-query shape (R > 32): each page is copied once into LDS (16-byte copies, K in
+// its page layout with padded 32-element rows, V^T rows padded) and the four waves, RT
+// 16-row tiles each, read it from there.
 template <typename T, int HD, int RT>
 __global__ __launch_bounds__(256) void attn_shared_kernel(AttnArgs a) {
   if (a.done && *a.done) return;
   constexpr int NW = 4, HC = HD / 32, OT = HD / 16;
-  constexpr int KP = HD + Pad<T>::K;       // K row stride in LDS (elements)
+  constexpr int KR = 32 + Pad<T>::K;       // K row stride in LDS (elements)
   constexpr int VP = SUB + Pad<T>::V;      // V^T row stride in LDS (elements)
   constexpr int KCH = SUB * HD / 8;        // 8-element chunks of a K page (= of a V page)
   constexpr int PER_T = (KCH + 255) / 256;
-  __shared__ __attribute__((aligned(16))) T s_k[SUB * KP];
-  __shared__ __attribute__((aligned(16))) T s_vt[HD * VP];
+  constexpr int KBYTES = (HC * 2 * 16 * KR + HD * VP) * (int)sizeof(T);
+  constexpr int BBYTES = block_item_lds<HD>() * 4;
+  constexpr int BYTES = KBYTES > BBYTES ? KBYTES : BBYTES;
+  __shared__ __attribute__((aligned(16))) char smem[BYTES];
+  T *s_k = reinterpret_cast<T *>(smem);
+  T *s_vt = s_k + HC * 2 * 16 * KR;
 
   const AttnItem it = a.items[blockIdx.x];
-  if (it.is_block) return;
+  if (it.is_block) {
+    if (blockIdx.y == 0) block_item<HD>(a, it, blockIdx.x, reinterpret_cast<float *>(smem));
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int nkeys = it.k_end - it.k_begin;
   const int npg = (nkeys + SUB - 1) / SUB;
-  const size_t page0 = (size_t)a.page_off[it.seq] + it.k_begin / SUB;
   const size_t pstride = (size_t)a.Hkv * SUB * HD;
-  const T *Kp = reinterpret_cast<const T *>(a.kc) + (page0 * a.Hkv + it.kvh) * SUB * HD;
-  const T *Vp = reinterpret_cast<const T *>(a.vc) + (page0 * a.Hkv + it.kvh) * HD * SUB;
+  const T *Kp = reinterpret_cast<const T *>(a.kc) + ((size_t)it.page0 * a.Hkv + it.kvh) * SUB * HD;
+  const T *Vp = reinterpret_cast<const T *>(a.vc) + ((size_t)it.page0 * a.Hkv + it.kvh) * HD * SUB;
   const int rt0 = (blockIdx.y * NW + wave) * RT;
 
   AFrag<T> qf[RT][HC];
@@ -313,8 +393,8 @@ __global__ __launch_bounds__(256) void attn_shared_kernel(AttnArgs a) {
     for (int i = 0; i < PER_T; ++i) {
       const int c = threadIdx.x + 256 * i;
       if (c < KCH) {
-        const int krow_ = c / (HD / 8), kpart = c % (HD / 8);
-        *reinterpret_cast<Frag<T> *>(&s_k[krow_ * KP + kpart * 8]) = kreg[i];
+        // K: 32-element rows in page order ((hd chunk, half, MFMA row)), 4 chunks per row.
+        *reinterpret_cast<Frag<T> *>(&s_k[(c >> 2) * KR + (c & 3) * 8]) = kreg[i];
         const int vrow = c / (SUB / 8), vpart = c % (SUB / 8);
         Frag<T> v = vreg[i];
         mask_v<T>(v, vpart, kvalid);
@@ -333,7 +413,7 @@ __global__ __launch_bounds__(256) void attn_shared_kernel(AttnArgs a) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
       PageMath<T, HD>::run(
-          [&](int h, int c) { return *reinterpret_cast<const Frag<T> *>(&s_k[krow(h, l16) * KP + c * 32 + g * 8]); },
+          [&](int h, int c) { return *reinterpret_cast<const Frag<T> *>(&s_k[((c * 2 + h) * 16 + l16) * KR + g * 8]); },
           [&](int t) { return *reinterpret_cast<const Frag<T> *>(&s_vt[(16 * t + l16) * VP + g * 8]); }, qf[rt],
           a.scale, kvalid, g, m_run[rt], l_run[rt], o[rt]);
   }
@@ -343,127 +423,56 @@ __global__ __launch_bounds__(256) void attn_shared_kernel(AttnArgs a) {
   store_partial<HD, RT>(a, blockIdx.x, rt0, g, l16, m_run, l_tot, o);
 }
 
-// One workgroup per (pair, 16 query rows): the B block keys in fp32 (16 threads per row,
-// HD/16 head dimensions each), then the merge with the pair's prefix partials in item
-// order, and o.  The partial maxima and sums of the pair are first read in parallel
-// into LDS; the partial outputs are then read in independent batches.
-constexpr int FIN_ITEMS = 256;   // prefix items per pair the finish kernel merges
-
+// Merge of a pair's partials in item order (prefix runs, then the block), one thread
+// per (query row, 8 output dimensions): online log-sum-exp over batches of partials
+// loaded together.  Writes o (fp32, natural layout, optional) and the output
+// projection's input in fragment layout.
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_finish_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   if (a.done && *a.done) return;
-  constexpr int EPT = HD / 16;
-  constexpr int BMAX = 32;
   constexpr int BATCH = 8;
-  __shared__ float s_k[BMAX][HD + 1], s_v[BMAX][HD + 1];
-  __shared__ float s_m[FIN_ITEMS][16], s_l[FIN_ITEMS][16];
   const int pair = blockIdx.x;
   const int first = a.pair_first[pair], cnt = a.pair_count[pair];
-  const int npre = cnt - 1;                       // prefix items (the block item is last)
-  const AttnItem it = a.items[first + npre];
-  const int rho0 = blockIdx.y * 16;
-  const float *base = a.qkv + (size_t)it.seq * a.B * a.Nqkv;
-  for (int i = threadIdx.x; i < a.B * HD; i += blockDim.x) {
-    const int key = i / HD, e = i % HD;
-    s_k[key][e] = base[(size_t)key * a.Nqkv + (size_t)(a.H + it.kvh) * HD + e];
-    s_v[key][e] = base[(size_t)key * a.Nqkv + (size_t)(a.H + a.Hkv + it.kvh) * HD + e];
-  }
-  for (int i = threadIdx.x; i < npre * 16; i += blockDim.x) {
-    const int item = i >> 4, r = i & 15;
-    float m = -INFINITY, l = 0.f;
-    if (rho0 + r < a.R) {
-      const size_t prow = (size_t)(first + item) * a.R + rho0 + r;
-      m = a.part_ml[prow * 2];
-      l = a.part_ml[prow * 2 + 1];
-    }
-    s_m[item][r] = m;
-    s_l[item][r] = l;
-  }
-  __syncthreads();
-  const int sub = threadIdx.x & 15, e0 = sub * EPT;
-  const int r = threadIdx.x >> 4, rho = rho0 + r;
+  const int rho = blockIdx.y * 16 + (threadIdx.x >> 2);
+  const int e0 = blockIdx.z * 32 + (threadIdx.x & 3) * 8;
   if (rho >= a.R) return;
-  const int j = rho / a.B, p = rho % a.B;
-  const float *q = base + (size_t)p * a.Nqkv + (size_t)(it.kvh * a.G + j) * HD + e0;
-  float qv[EPT];
+  float M = -INFINITY, L = 0.f, acc[8];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) qv[e] = q[e];
-
-  // Block keys, fp32.
-  float sc[BMAX];
-  float mb = -INFINITY;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int i0 = 0; i0 < cnt; i0 += BATCH) {
+    float mi[BATCH], li[BATCH], oi[BATCH][8];
 #pragma unroll
-  for (int key = 0; key < BMAX; ++key) {
-    if (key < a.B) {
-      float d = 0.f;
+    for (int b = 0; b < BATCH; ++b) {
+      const size_t prow = (size_t)(first + min(i0 + b, cnt - 1)) * a.R + rho;
+      mi[b] = a.part_ml[prow * 2 + 0];
+      li[b] = a.part_ml[prow * 2 + 1];
+      load8f(a.part_o + prow * HD + e0, oi[b]);
+    }
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) d += qv[e] * s_k[key][e0 + e];
-      d = sum16(d) * a.scale;
-      sc[key] = d;
-      mb = fmaxf(mb, d);
+    for (int b = 0; b < BATCH; ++b) {
+      if (i0 + b < cnt && mi[b] != -INFINITY) {
+        const float Mn = fmaxf(M, mi[b]);
+        const float wo = (M == -INFINITY) ? 0.f : __expf(M - Mn);
+        const float wn = __expf(mi[b] - Mn);
+        L = L * wo + li[b] * wn;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] * wo + oi[b][e] * wn;
+        M = Mn;
+      }
     }
   }
-  float lb = 0.f, ob[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) ob[e] = 0.f;
-#pragma unroll
-  for (int key = 0; key < BMAX; ++key) {
-    if (key < a.B) {
-      const float pk = __expf(sc[key] - mb);
-      lb += pk;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) ob[e] += pk * s_v[key][e0 + e];
-    }
-  }
-
-  // Merge: prefix items in order, then the block keys.
-  float M = mb;
-  for (int i = 0; i < npre; ++i) M = fmaxf(M, s_m[i][r]);
-  float L = 0.f, acc[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
-  for (int i0 = 0; i0 < npre; i0 += BATCH) {
-    float po[BATCH][EPT];
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b)
-      if (i0 + b < npre) {
-        const float *src = a.part_o + ((size_t)(first + i0 + b) * a.R + rho) * HD + e0;
-#pragma unroll
-        for (int e = 0; e < EPT; e += 4) *reinterpret_cast<float4 *>(&po[b][e]) = *reinterpret_cast<const float4 *>(src + e);
-      }
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b)
-      if (i0 + b < npre) {
-        const float mi = s_m[i0 + b][r];
-        const float w = (mi == -INFINITY) ? 0.f : __expf(mi - M);
-        L += s_l[i0 + b][r] * w;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) acc[e] += po[b][e] * w;
-      }
-  }
-  const float wb = __expf(mb - M);
-  L += lb * wb;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) acc[e] += ob[e] * wb;
   const float inv = 1.0f / L;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) acc[e] *= inv;
-  const int orow = it.seq * a.B + p, ocol = (it.kvh * a.G + j) * HD + e0;
+  for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  const int seq = pair / a.Hkv, kvh = pair % a.Hkv;
+  const int j = rho / a.B, p = rho % a.B;
+  const int orow = seq * a.B + p, ocol = (kvh * a.G + j) * HD + e0;
   if (a.o) {
     float *out = a.o + (size_t)orow * a.ldo + ocol;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) out[e] = acc[e];
+    *reinterpret_cast<float4 *>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4 *>(out + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
-  if (a.o_afl) {   // input of the output projection
-    const int KTo = a.H * HD / 32;
-    if constexpr (EPT % 8 == 0) {
-#pragma unroll
-      for (int e = 0; e < EPT; e += 8) afl_put8<T>(a.o_afl, KTo, orow, ocol + e, acc + e);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) afl_put<T>(a.o_afl, KTo, orow, ocol + e, acc[e]);
-    }
-  }
+  if (a.o_afl) afl_put8<T>(a.o_afl, a.H * HD / 32, orow, ocol, acc);
 }
 
 template <typename T, int HD>
@@ -479,15 +488,14 @@ hipError_t launch_hd(const AttnArgs &a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid(a.n_pairs, (a.R + 15) / 16);
-  hipLaunchKernelGGL((attn_finish_kernel<T, HD>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3(a.n_pairs, (a.R + 15) / 16, HD / 32), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention(int dtype, const AttnArgs &a, hipStream_t s) {
-  if (a.n_items <= 0 || a.n_pairs <= 0 || a.B > 32 || a.max_pair_items > FIN_ITEMS + 1) return hipErrorInvalidValue;
+  if (a.n_items <= 0 || a.n_pairs <= 0 || a.B > BMAX) return hipErrorInvalidValue;
   if (dtype == DT_BF16) {
     if (a.hd == 128) return launch_hd<bf16_t, 128>(a, s);
     if (a.hd == 64) return launch_hd<bf16_t, 64>(a, s);

@@ -53,11 +53,10 @@ struct td_ctx {
   // prefix binding
   int n_seqs = 0;
   std::vector<int64_t> offsets;
-  int64_t *page_off_d = nullptr;
   std::vector<const void *> kc, vc;
   AttnItem *items_d = nullptr;
   int *pair_first_d = nullptr, *pair_count_d = nullptr;
-  int n_items = 0, n_pairs = 0, max_pair_items = 0;
+  int n_items = 0, n_pairs = 0;
   size_t items_cap = 0, pairs_cap = 0;
   float *att_o = nullptr, *att_ml = nullptr;
   size_t att_cap_rows = 0;   // capacity in partial rows (items * R)
@@ -158,16 +157,15 @@ GemmPlan plan_gemm(int M, int N, int K, bool vstat) {
   return p;
 }
 
-// Prefix keys per split-K item.  Few query rows per K/V head (R <= 32): 256 keys, which
-// the four waves of a workgroup stream 64 each; grouped-query heads: the partial state
-// per item (R rows x (hd + 2) floats) is large, so items grow with R.  Items also grow
-// so that a prefix of P keys has at most 256 of them (the merge's capacity).
-int chunk_keys(int R, int64_t Pmax) {
-  int tc = 256;
-  if (R > 32)
-    while (tc < 4 * R && tc < 4096) tc *= 2;
-  while ((Pmax + tc - 1) / tc > 256) tc *= 2;
-  return tc;
+// Prefix keys per split-K item: a multiple of the page size chosen so that the whole
+// batch (total prefix keys summed over K/V heads) makes about one workgroup per CU, and
+// at least four pages (one per wave).  Long prefixes then take long items (each wave
+// streams many pages) instead of many partials for the merge.
+int chunk_keys(int64_t total_pair_keys) {
+  constexpr int64_t kTargetItems = 256;
+  int64_t tc = (total_pair_keys + kTargetItems - 1) / kTargetItems;
+  tc = (tc + KV_PAGE - 1) / KV_PAGE * KV_PAGE;
+  return (int)std::min<int64_t>(std::max<int64_t>(tc, 4 * KV_PAGE), (int64_t)1 << 30);
 }
 
 constexpr size_t PROF_MAX = 65536;
@@ -176,9 +174,11 @@ td_status prof_mark(td_ctx *c, int kind, bool start) {
   if (c->prof_kind != kind || c->prof_n >= PROF_MAX) return TD_OK;
   if (start) {
     if (c->ev_start.size() <= c->prof_n) {
+      // Timing-only events: no system-scope fence, which would write back and invalidate
+      // the L2 around every timed launch and slow the next kernel.
       hipEvent_t a, b;
-      TD_HIP(c, hipEventCreate(&a));
-      TD_HIP(c, hipEventCreate(&b));
+      TD_HIP(c, hipEventCreateWithFlags(&a, hipEventDisableSystemFence));
+      TD_HIP(c, hipEventCreateWithFlags(&b, hipEventDisableSystemFence));
       c->ev_start.push_back(a);
       c->ev_stop.push_back(b);
     }
@@ -203,13 +203,11 @@ td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, vo
   a.qkv = qkv;
   a.kc = c->kc[layer];
   a.vc = c->vc[layer];
-  a.page_off = c->page_off_d;
   a.items = c->items_d;
   a.n_items = c->n_items;
   a.pair_first = c->pair_first_d;
   a.pair_count = c->pair_count_d;
   a.n_pairs = c->n_pairs;
-  a.max_pair_items = c->max_pair_items;
   a.part_o = c->att_o;
   a.part_ml = c->att_ml;
   a.o = o;
@@ -326,7 +324,7 @@ void free_all(td_ctx *c) {
   for (auto *v : {&c->attn_norm, &c->mlp_norm, &c->wqkv, &c->wo, &c->w1, &c->w2})
     for (void *p : *v) f(p);
   f(c->x); f(c->ssq); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->ah); f(c->ao); f(c->au);
-  f(c->arg_row); f(c->state_ints); f(c->page_off_d); f(c->items_d); f(c->pair_first_d);
+  f(c->arg_row); f(c->state_ints); f(c->items_d); f(c->pair_first_d);
   f(c->pair_count_d); f(c->att_o); f(c->att_ml);
   for (hipEvent_t e : c->ev_start) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->ev_stop) (void)hipEventDestroy(e);
@@ -447,22 +445,24 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
   TD_HIP(c, hipSetDevice(c->dev));
   TD_HIP(c, hipStreamSynchronize(c->stream));   // previous work may still read the old binding
 
-  int64_t Pmax = 0;
-  for (int i = 0; i < n_seqs; ++i) Pmax = std::max(Pmax, off[i + 1] - off[i]);
-  const int G = g.n_heads / g.n_kv_heads, R = G * g.block_size, tc = chunk_keys(R, Pmax);
+  for (int i = 0; i < n_seqs; ++i)
+    if (off[i + 1] - off[i] > (int64_t)1 << 30) return fail(c, TD_EINVAL, "prefix of sequence %d too long", i);
+  const int G = g.n_heads / g.n_kv_heads, R = G * g.block_size;
+  const int tc = chunk_keys(off[n_seqs] * g.n_kv_heads);
   std::vector<AttnItem> items;
   std::vector<int> pfirst, pcount;
+  int64_t page_base = 0;   // first cache page of sequence i
   for (int i = 0; i < n_seqs; ++i) {
     const int64_t P = off[i + 1] - off[i];
-    if (P > (int64_t)1 << 30) return fail(c, TD_EINVAL, "prefix of sequence %d too long", i);
     for (int h = 0; h < g.n_kv_heads; ++h) {
       const int pair = i * g.n_kv_heads + h;
       pfirst.push_back((int)items.size());
       for (int64_t k0 = 0; k0 < P; k0 += tc)
-        items.push_back(AttnItem{i, h, (int)k0, (int)std::min<int64_t>(P, k0 + tc), 0, pair});
-      items.push_back(AttnItem{i, h, 0, g.block_size, 1, pair});
+        items.push_back(AttnItem{i, h, (int)k0, (int)std::min<int64_t>(P, k0 + tc), 0, pair, page_base + k0 / KV_PAGE});
+      items.push_back(AttnItem{i, h, 0, g.block_size, 1, pair, 0});
       pcount.push_back((int)items.size() - pfirst.back());
     }
+    page_base += (P + KV_PAGE - 1) / KV_PAGE;
   }
   if (items.size() > ((size_t)1 << 28)) return fail(c, TD_EINVAL, "too many attention work items");
   auto grow = [&](auto **p, size_t &cap, size_t need, size_t elt) -> td_status {
@@ -486,13 +486,9 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
   TD_TRY(grow(&c->att_o, cap_o, rows, (size_t)g.head_dim * 4));
   TD_TRY(grow(&c->att_ml, cap_ml, rows, 8));
   c->att_cap_rows = std::min(cap_o, cap_ml);
-  if (!c->page_off_d) TD_TRY(dmalloc(c, &c->page_off_d, (size_t)(g.max_batch + 1) * sizeof(int64_t)));
   TD_HIP(c, hipMemcpy(c->items_d, items.data(), items.size() * sizeof(AttnItem), hipMemcpyHostToDevice));
   TD_HIP(c, hipMemcpy(c->pair_first_d, pfirst.data(), pfirst.size() * sizeof(int), hipMemcpyHostToDevice));
   TD_HIP(c, hipMemcpy(c->pair_count_d, pcount.data(), pcount.size() * sizeof(int), hipMemcpyHostToDevice));
-  std::vector<int64_t> page_off(n_seqs + 1, 0);
-  for (int i = 0; i < n_seqs; ++i) page_off[i + 1] = page_off[i] + (off[i + 1] - off[i] + KV_PAGE - 1) / KV_PAGE;
-  TD_HIP(c, hipMemcpy(c->page_off_d, page_off.data(), (size_t)(n_seqs + 1) * sizeof(int64_t), hipMemcpyHostToDevice));
   {  // GEMM plans for this batch size
     const int M = n_seqs * g.block_size;
     const int d = g.d_model, F = g.d_ff, Hd = g.n_heads * g.head_dim;
@@ -506,7 +502,6 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
   c->kc.assign(k_cache_host, k_cache_host + g.n_layers);
   c->vc.assign(v_cache_host, v_cache_host + g.n_layers);
   c->n_items = (int)items.size();
-  c->max_pair_items = *std::max_element(pcount.begin(), pcount.end());
   c->n_pairs = (int)pfirst.size();
   c->n_seqs = n_seqs;
   return TD_OK;

@@ -60,32 +60,35 @@ hipError_t launch_gemm_wk(int dtype, int epi, bool norm, const GemmArgs &a, hipS
 
 // ---------------------------------------------------------------- attention
 // Prefix K/V cache pages: 32 tokens per page; page p of K/V head h is one contiguous
-// block, K as [32 tokens][hd] and V transposed as [hd][32 tokens]; element offsets
-//   K: ((p * Hkv + h) * 32 + slot) * hd + e        V: ((p * Hkv + h) * hd + e) * 32 + slot
+// block of 32 * hd elements.  V is transposed, [hd][32 tokens]: element (slot, e) at
+//   ((p * Hkv + h) * hd + e) * 32 + slot.
+// K is [hd / 32][2][16][32]: element (slot, e) at
+//   ((p * Hkv + h) * 32 * hd) + ((e / 32) * 2 + hf) * 512 + i * 32 + e % 32,
+// with hf = (slot / 4) % 2 and i = (slot / 8) * 4 + slot % 4 (the row of the key in the
+// MFMA operand of its half of the page).
 // Sequence i owns pages [page_off[i], page_off[i] + ceil(P_i / 32)); token t is in page
 // page_off[i] + t / 32, slot t % 32.
 constexpr int KV_PAGE = 32;
 
 // One split-K work item: prefix tokens [k_begin, k_end) (k_begin a multiple of the page
-// size), or the block's own keys.  The items of a (seq, kv head) pair are consecutive;
-// the block item is the pair's last.
+// size, first page page0 of the cache), or the block's own keys.  The items of a
+// (seq, kv head) pair are consecutive; the block item is the pair's last.
 struct AttnItem {
   int seq, kvh;            // sequence and key/value head
   int k_begin, k_end;      // key range (prefix token index within the sequence; or 0..B)
   int is_block;            // 1: keys/values are the block's own k/v from the projections
   int pair;                // seq * Hkv + kvh
+  int64_t page0;           // cache page holding token k_begin (prefix items)
 };
 struct AttnArgs {
   int B, H, Hkv, hd, Nqkv, G, R;   // R = G * B query rows per (seq, kv head)
   const float *qkv;                // [n*B][Nqkv]: q | k_block | v_block (fp32)
   const void *kc, *vc;             // prefix cache pages (layout above)
-  const int64_t *page_off;         // [n+1] first page of each sequence (device)
   const AttnItem *items; int n_items;
   const int *pair_first, *pair_count;   // item range of each (seq, kv head) pair
   int n_pairs;
-  int max_pair_items;              // largest pair_count (<= 257)
-  float *part_o;                   // [n_items][R][hd]
-  float *part_ml;                  // [n_items][R][2]
+  float *part_o;                   // [n_items][R][hd] partial outputs (unnormalised)
+  float *part_ml;                  // [n_items][R][2] partial max and sum of exp
   float *o; int ldo;               // optional output [n*B][ldo] (fp32, natural layout)
   void *o_afl;                     // optional output [n*B][H*hd] in fragment layout
   float scale;                     // 1 / sqrt(hd)

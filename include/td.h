@@ -88,10 +88,14 @@ typedef struct {
 td_status td_create(const td_config *cfg, const td_weights *w, void *stream, td_ctx **out);
 
 /* Prefix K/V cache layout (per layer, config dtype): pages of TD_KV_PAGE = 32 tokens.
- * Page p of K/V head h is one contiguous block: K as [32 tokens][head_dim], V
- * transposed as [head_dim][32 tokens]; element offsets
- *   K: ((p * n_kv_heads + h) * 32 + slot) * head_dim + e
- *   V: ((p * n_kv_heads + h) * head_dim + e) * 32 + slot.
+ * Page p of K/V head h is one contiguous block of 32 * head_dim elements:
+ *   V, transposed [head_dim][32 tokens]: token slot s, dimension e at
+ *       ((p * n_kv_heads + h) * head_dim + e) * 32 + s
+ *   K, [head_dim / 32][2][16][32]: slot s, dimension e at
+ *       (p * n_kv_heads + h) * 32 * head_dim + ((e / 32) * 2 + (s / 4) % 2) * 512
+ *       + ((s / 8) * 4 + s % 4) * 32 + e % 32
+ *     (keys grouped by halves of the page in the row order of the attention kernel's
+ *     matrix-core operand, so every operand load is one contiguous KiB).
  * Sequence i owns ceil(P_i / 32) consecutive pages starting at page
  * sum_{j<i} ceil(P_j / 32); its token t is in slot t % 32 of its page t / 32.  Slots
  * past P_i in its last page are never used (they may hold anything). */

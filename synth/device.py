@@ -45,17 +45,21 @@ KV_PAGE = 32   # tokens per prefix-cache page
 
 
 def page_prefix(k: np.ndarray, v: np.ndarray, page: int = KV_PAGE):
-    """Natural [P][Hkv][hd] keys/values -> pages: K [pages][Hkv][page][hd], V [pages][Hkv][hd][page].
+    """Natural [P][Hkv][hd] keys/values -> cache pages (the layout of include/td.h).
 
-    Pure data movement; slots past P in the last page are zero.
+    V pages: [pages][Hkv][hd][page] (transposed).  K pages: [pages][Hkv][hd/32][2][16][32],
+    where slot s of a page sits in half (s // 4) % 2, row (s // 8) * 4 + s % 4.  Pure data
+    movement; slots past P in the last page are zero.
     """
     P, Hkv, hd = k.shape
     npg = (P + page - 1) // page
     kp = np.zeros((npg * page, Hkv, hd), dtype=k.dtype)
     vp = np.zeros((npg * page, Hkv, hd), dtype=v.dtype)
     kp[:P], vp[:P] = k, v
-    kp = kp.reshape(npg, page, Hkv, hd).transpose(0, 2, 1, 3)
     vp = vp.reshape(npg, page, Hkv, hd).transpose(0, 2, 3, 1)
+    # slot s = 8 * a + 4 * half + r  ->  (half, row = 4 * a + r)
+    kp = kp.reshape(npg, page // 8, 2, 4, Hkv, hd // 32, 32)          # [pg][a][half][r][h][c][e]
+    kp = kp.transpose(0, 4, 5, 2, 1, 3, 6).reshape(npg, Hkv, hd // 32, 2, 16, 32)
     return np.ascontiguousarray(kp), np.ascontiguousarray(vp)
 
 
@@ -80,7 +84,7 @@ def prefix_to_device(w: Workload, plens: Sequence[int], device="cuda", layers: i
     ks, vs = [], []
     with cf.ThreadPoolExecutor(_workers()) as pool:
         for l in range(L):
-            kt = torch.zeros((npages, w.Hkv, KV_PAGE, w.hd), dtype=dt, device=device)
+            kt = torch.zeros((npages, w.Hkv, w.hd // 32, 2, 16, 32), dtype=dt, device=device)
             vt = torch.zeros((npages, w.Hkv, w.hd, KV_PAGE), dtype=dt, device=device)
             for s, P in enumerate(plens):
                 if P == 0:

@@ -30,9 +30,10 @@ def _run(dtype, H, Hkv, hd, B, plens, seed=0, qscale=1.0):
     page = 0
     for P in plens:
         npg = (P + KV_PAGE - 1) // KV_PAGE
-        if P % KV_PAGE:
-            ks[0][page + npg - 1, :, P % KV_PAGE:, :] = float("nan")
-            vs[0][page + npg - 1, :, :, P % KV_PAGE:] = float("nan")
+        for slot in range(P % KV_PAGE if P % KV_PAGE else KV_PAGE, KV_PAGE):
+            # K page [Hkv][hd/32][half][row][32]: slot -> half (slot // 4) % 2, row (slot // 8) * 4 + slot % 4
+            ks[0][page + npg - 1, :, :, (slot // 4) % 2, (slot // 8) * 4 + slot % 4, :] = float("nan")
+            vs[0][page + npg - 1, :, :, slot] = float("nan")
         page += npg
     dev = Denoiser(tower_config(w, max_batch=n, max_prefix_tokens=max(1, offsets[-1])), dW)
     dev.set_prefix(offsets, ks, vs)

@@ -79,18 +79,30 @@ def test_prefix_kv_token_slices():
 
 
 def test_prefix_page_layout_matches_the_documented_offsets():
-    """K page p, head h: ((p*Hkv + h)*32 + slot)*hd + e; V: ((p*Hkv + h)*hd + e)*32 + slot."""
+    """Cache pages as include/td.h states them.  V: ((p*Hkv + h)*hd + e)*32 + s.
+    K: (p*Hkv + h)*32*hd + ((e//32)*2 + (s//4)%2)*512 + ((s//8)*4 + s%4)*32 + e%32."""
     from synth.device import KV_PAGE, page_prefix
     rng = np.random.default_rng(4)
-    P, Hkv, hd = 77, 3, 8
+    P, Hkv, hd = 77, 3, 64
     k = rng.standard_normal((P, Hkv, hd)).astype(np.float32)
     v = rng.standard_normal((P, Hkv, hd)).astype(np.float32)
     kp, vp = page_prefix(k, v)
     npg = (P + KV_PAGE - 1) // KV_PAGE
-    assert kp.shape == (npg, Hkv, KV_PAGE, hd) and vp.shape == (npg, Hkv, hd, KV_PAGE)
+    assert kp.size == npg * Hkv * KV_PAGE * hd and vp.shape == (npg, Hkv, hd, KV_PAGE)
     kf, vf = kp.reshape(-1), vp.reshape(-1)
-    for t, h, e in [(0, 0, 0), (31, 2, 7), (32, 1, 3), (76, 2, 5), (40, 0, 1)]:
-        p_, slot = divmod(t, KV_PAGE)
-        assert kf[((p_ * Hkv + h) * KV_PAGE + slot) * hd + e] == k[t, h, e]
-        assert vf[((p_ * Hkv + h) * hd + e) * KV_PAGE + slot] == v[t, h, e]
-    assert (kp[-1, :, P % KV_PAGE:, :] == 0).all() and (vp[-1, :, :, P % KV_PAGE:] == 0).all()
+
+    def koff(p_, h, s, e):
+        return (p_ * Hkv + h) * KV_PAGE * hd + ((e // 32) * 2 + (s // 4) % 2) * 512 + ((s // 8) * 4 + s % 4) * 32 + e % 32
+
+    for t in range(P):
+        p_, s_ = divmod(t, KV_PAGE)
+        for h in range(Hkv):
+            for e in (0, 5, 31, 32, 63):
+                assert kf[koff(p_, h, s_, e)] == k[t, h, e]
+                assert vf[((p_ * Hkv + h) * hd + e) * KV_PAGE + s_] == v[t, h, e]
+    # every element appears exactly once (the K map is a bijection on a page)
+    offs = {koff(0, 0, s_, e) for s_ in range(KV_PAGE) for e in range(hd)}
+    assert offs == set(range(KV_PAGE * hd))
+    for s_ in range(P % KV_PAGE, KV_PAGE):   # padding slots of the last page are zero
+        for e in range(hd):
+            assert kf[koff(npg - 1, 1, s_, e)] == 0 and vf[((npg - 1) * Hkv * hd + hd + e) * KV_PAGE + s_] == 0
