@@ -217,13 +217,13 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
 // Multi-head shape (R <= 32): waves take alternate pages, operands straight from HBM.
 template <typename T, int HD, int RT>
 __global__ __launch_bounds__(256) void attn_direct_kernel(AttnArgs a) {
-  if (a.done && *a.done) return;
   constexpr int NW = 4, HC = HD / 32, OT = HD / 16;
   constexpr int MERGE = NW * RT * 16 * (HD + 2);
   constexpr int LDS = MERGE > block_item_lds<HD>() ? MERGE : block_item_lds<HD>();
   __shared__ float smem[LDS];
 
-  const AttnItem it = a.items[blockIdx.x];
+  const AttnItem it = a.items[blockIdx.x];   // loaded together with the loop-exit flag
+  if (a.done && *a.done) return;
   if (it.is_block) {
     block_item<HD>(a, it, blockIdx.x, smem);
     return;
@@ -338,7 +338,6 @@ __global__ __launch_bounds__(256) void attn_direct_kernel(AttnArgs a) {
 // 16-row tiles each, read it from there.
 template <typename T, int HD, int RT>
 __global__ __launch_bounds__(256) void attn_shared_kernel(AttnArgs a) {
-  if (a.done && *a.done) return;
   constexpr int NW = 4, HC = HD / 32, OT = HD / 16;
   constexpr int KR = 32 + Pad<T>::K;       // K row stride in LDS (elements)
   constexpr int VP = SUB + Pad<T>::V;      // V^T row stride in LDS (elements)
@@ -351,7 +350,8 @@ __global__ __launch_bounds__(256) void attn_shared_kernel(AttnArgs a) {
   T *s_k = reinterpret_cast<T *>(smem);
   T *s_vt = s_k + HC * 2 * 16 * KR;
 
-  const AttnItem it = a.items[blockIdx.x];
+  const AttnItem it = a.items[blockIdx.x];   // loaded together with the loop-exit flag
+  if (a.done && *a.done) return;
   if (it.is_block) {
     if (blockIdx.y == 0) block_item<HD>(a, it, blockIdx.x, reinterpret_cast<float *>(smem));
     return;
@@ -429,10 +429,10 @@ __global__ __launch_bounds__(256) void attn_shared_kernel(AttnArgs a) {
 // projection's input in fragment layout.
 template <typename T, int HD>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
-  if (a.done && *a.done) return;
   constexpr int BATCH = 8;
   const int pair = blockIdx.x;
-  const int first = a.pair_first[pair], cnt = a.pair_count[pair];
+  const int first = a.pair_first[pair], cnt = a.pair_count[pair];   // loaded with the exit flag
+  if (a.done && *a.done) return;
   const int rho = blockIdx.y * 16 + (threadIdx.x >> 2);
   const int e0 = blockIdx.z * 32 + (threadIdx.x & 3) * 8;
   if (rho >= a.R) return;

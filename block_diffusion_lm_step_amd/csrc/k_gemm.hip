@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void lmhead_kernel(GemmArgs a) {
   constexpr int ROWS = 16 * MT;
   constexpr int TPR = 256 / ROWS;   // threads per row for the row scales
   constexpr int SQB = 16;
-  if (a.done && *a.done) return;
+  const int *done = a.done;
   const int nrows = a.n_rows ? *a.n_rows : a.M;
   const int m0 = blockIdx.z * ROWS;
   if (m0 >= nrows) return;
@@ -79,6 +79,8 @@ __global__ __launch_bounds__(256) void lmhead_kernel(GemmArgs a) {
   };
 #pragma unroll
   for (int i = 0; i < PASS; ++i) fill(i, i);
+  // The loop-exit flag is read only now, so that its latency overlaps the first loads.
+  if (done && *done) return;
   {
     float s = 0.f;
 #pragma unroll

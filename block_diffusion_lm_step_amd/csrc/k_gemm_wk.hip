@@ -3,12 +3,14 @@
 //
 // With B = 16 rows per sequence the fused QKV, output and MLP projections read every
 // weight once per step and do only ~2*M FLOP per weight element: the time is the
-// latency and bandwidth of the weight stream.  Each workgroup owns one 16-column tile
-// and the whole K range; its NW waves split K.  Every wave keeps PASS k-tiles of
-// weights (pre-packed 16x32 MFMA tiles: one contiguous KiB per load) and of activation
-// fragments in flight: a slot is refilled right after its MFMA, so the loads stream
-// without bubbles, and all loads are unconditional (clamped addresses) so that the
-// waits the compiler places before each MFMA are exact.
+// latency and bandwidth of the weight stream.  Each workgroup owns NT 16-column tiles
+// and the whole K range; its NW waves split K.  Every wave keeps PASS k-tiles of weights
+// (pre-packed 16x32 MFMA tiles: one contiguous KiB per load) and of activation fragments
+// in flight: a slot
+// is refilled right after its MFMAs, so the loads stream without bubbles, and all loads
+// are unconditional (clamped addresses) so that the waits the compiler places before
+// each MFMA are exact.  One activation fragment feeds NT MFMAs: the activation traffic
+// from L2 is 2 KiB per k-tile per wave against NT KiB of weights.
 //
 // The activations arrive in fragment layout, written by their producer: fp32 values
 // split into a bf16 high part and a bf16 remainder against bf16 weights (fp32 as is
@@ -18,8 +20,9 @@
 // accumulator.  It is formed from the producer's partial sums of squares, which are
 // loaded before the weights so that waiting for them never waits for the weights.
 //
-// The waves' accumulators are summed through LDS in wave order (no cross-workgroup
-// reduction, no device-scope fence, deterministic) and wave 0 applies the epilogue:
+// The waves' accumulators meet in LDS; wave w sums tile w (and w + NW, ...) over the
+// waves in wave order (deterministic, no cross-workgroup reduction, no device-scope
+// fence) and applies the epilogue:
 //   STORE  q/k/v (fp32, row-major),
 //   GELU   u = gelu_erf(y), written in fragment layout for the MLP down projection,
 //   RESID  x += y (fp32 residual stream), partial sums of squares of the new rows per
@@ -32,44 +35,44 @@ namespace td {
 namespace {
 
 // k-tiles in flight per wave: the VGPRs per k-tile (activation fragments of MT row
-// tiles + one weight fragment) into a budget that keeps two workgroups per CU
-// (1024-thread workgroups: one workgroup, 128 VGPRs).
-template <typename T, int MT, int NW> constexpr int wk_pass() {
-  constexpr int per = MT * 8 + (sizeof(T) == 2 ? 4 : 8);
-  constexpr int budget = NW == 16 ? 72 : 192;
+// tiles + NT weight fragments) into a budget that keeps two 256/512-thread workgroups
+// per CU (1024-thread workgroups: one workgroup, 128 VGPRs).
+template <typename T, int MT, int NT, int NW> constexpr int wk_pass() {
+  constexpr int per = MT * 8 + NT * (sizeof(T) == 2 ? 4 : 8);
+  constexpr int budget = NW == 16 ? 72 : 176;
   constexpr int p = budget / per;
   return p > 16 ? 16 : (p < 1 ? 1 : p);
 }
 
-template <typename T, int MT, int NW, int EPI, bool NORM>
+template <typename T, int MT, int NT, int NW, int EPI, bool NORM>
 __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
-  constexpr int PASS = wk_pass<T, MT, NW>();
+  constexpr int PASS = wk_pass<T, MT, NT, NW>();
   constexpr int ROWS = 16 * MT;
   constexpr int TPR = (64 * NW / ROWS) < 64 ? 64 * NW / ROWS : 64;   // threads per row (row scales)
   constexpr int SQB = 16;                                             // partial sums loaded per batch
-  if (a.done && *a.done) return;
   const int M = a.M;
   const int m0 = blockIdx.z * ROWS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int nt = blockIdx.x;
+  const int nt0 = blockIdx.x * NT;
   const int KT = a.K >> 5;
   const int kwt = (KT + NW - 1) / NW;            // k-tiles per wave
   const int kw0 = min(KT, wave * kwt), kw1 = min(KT, kw0 + kwt);
 
   __shared__ float s_rs[ROWS];
-  __shared__ f32x4_t s_red[NW - 1][MT][64];
+  __shared__ f32x4_t s_red[NW][MT * NT][64];
 
-  const T *Wl = reinterpret_cast<const T *>(a.Wp) + ((size_t)nt * KT) * 512 + (size_t)lane * 8;
+  const T *Wl = reinterpret_cast<const T *>(a.Wp) + ((size_t)nt0 * KT) * 512 + (size_t)lane * 8;
   const char *Al = reinterpret_cast<const char *>(a.A) + ((size_t)(m0 >> 4) * KT) * 2048 + (size_t)lane * 32;
   auto clampk = [&](int kt) { return max(0, min(kt, KT - 1)); };
   AFrag<T> xa[PASS][MT];
-  Frag<T> wb[PASS];
+  Frag<T> wb[PASS][NT];
   auto fill = [&](int i, int kt) __attribute__((always_inline)) {
     const int k = clampk(kt);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) xa[i][mt] = afl_get<T>(Al + ((size_t)mt * KT + k) * 2048);
-    wb[i].load(Wl + (size_t)k * 512);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) wb[i][j].load(Wl + ((size_t)j * KT + k) * 512);
   };
 
   // Partial sums of squares of this thread's row first (TPR threads per row).
@@ -84,6 +87,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
   // First PASS k-tiles of activations and weights.
 #pragma unroll
   for (int i = 0; i < PASS; ++i) fill(i, kw0 + i);
+  // The loop-exit flag is read only now, so that its latency overlaps the first loads
+  // (reading the operands is harmless when the block is already adopted).
+  if (a.done && *a.done) return;
   if constexpr (NORM) {
     float s = 0.f;
 #pragma unroll
@@ -94,17 +100,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
     if (sub == 0) s_rs[rr] = 1.0f / sqrtf(s / (float)a.K + a.norm_eps);
   }
 
-  f32x4_t acc[MT];
+  f32x4_t acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = zero4();
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[mt][j] = zero4();
   int p0 = kw0;
   for (; p0 + PASS < kw1; p0 += PASS) {
 #pragma unroll
     for (int i = 0; i < PASS; ++i) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = mma_a(xa[i][mt], wb[i], acc[mt]);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[mt][j] = mma_a(xa[i][mt], wb[i][j], acc[mt][j]);
       fill(i, p0 + PASS + i);
-      // Keep each refill right behind its MFMA: left alone, the scheduler sinks all
+      // Keep each refill right behind its MFMAs: left alone, the scheduler sinks all
       // refills below the pass's MFMAs and the stream stalls once per pass.
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -113,70 +123,64 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
   for (int i = 0; i < PASS; ++i) {
     if (p0 + i < kw1) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = mma_a(xa[i][mt], wb[i], acc[mt]);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[mt][j] = mma_a(xa[i][mt], wb[i][j], acc[mt][j]);
     }
   }
 
-  // Waves' partial sums, in wave order.
-  if (wave > 0) {
+  // Waves' partial sums meet in LDS; wave w finishes tiles w, w + NW, ... in wave order.
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) s_red[wave - 1][mt][lane] = acc[mt];
-  }
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) s_red[wave][mt * NT + j][lane] = acc[mt][j];
   __syncthreads();
-  if (wave > 0) return;
-#pragma unroll
-  for (int w = 0; w < NW - 1; ++w)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] += s_red[w][mt][lane];
-
-  const int col = nt * 16 + l16;
   const int KTo = a.N >> 5;   // k-tiles of a fragment-layout output (its K is this GEMM's N)
-  // Residual rows and the next gain, all loaded before any store (the outputs may alias
-  // nothing here, but the compiler cannot know that and would serialise the loads).
-  float xold[MT][4], gnext = 1.0f;
-  if constexpr (EPI == EPI_RESID) {
-    gnext = to_f32<T>(reinterpret_cast<const T *>(a.gain_next)[col]);
+  for (int q = wave; q < MT * NT; q += NW) {
+    const int mt = q / NT, j = q % NT;
+    f32x4_t y4 = s_red[0][q][lane];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int w = 1; w < NW; ++w) y4 += s_red[w][q][lane];
+    const int col = (nt0 + j) * 16 + l16;
+    // Residual rows and the next gain, loaded before any store (the compiler cannot
+    // tell that the outputs alias nothing and would otherwise serialise the loads).
+    float xold[4], gnext = 1.0f;
+    if constexpr (EPI == EPI_RESID) {
+      gnext = to_f32<T>(reinterpret_cast<const T *>(a.gain_next)[col]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = min(m0 + mt * 16 + 4 * g + r, M - 1);
-        xold[mt][r] = a.out[(size_t)row * a.ldo + col];
-      }
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+      for (int r = 0; r < 4; ++r) xold[r] = a.out[(size_t)min(m0 + mt * 16 + 4 * g + r, M - 1) * a.ldo + col];
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int ri = mt * 16 + 4 * g + r;
       const int row = m0 + ri;
       const bool ok = row < M;
-      float y = acc[mt][r];
+      float y = y4[r];
       if constexpr (NORM) y *= s_rs[ri];
       if constexpr (EPI == EPI_STORE) {
         if (ok) a.out[(size_t)row * a.ldo + col] = y;
       } else if constexpr (EPI == EPI_GELU) {
         if (ok) afl_put<T>(a.out_afl, KTo, row, col, gelu_erf(y));
       } else {
-        const float xv = ok ? xold[mt][r] + y : 0.f;
+        const float xv = ok ? xold[r] + y : 0.f;
         if (ok) {
           a.out[(size_t)row * a.ldo + col] = xv;
           afl_put<T>(a.out_afl, KTo, row, col, xv * gnext);
         }
         const float sq16 = sum16(xv * xv);
-        if (ok && l16 == 0) a.ssq_out[(size_t)nt * M + row] = sq16;
+        if (ok && l16 == 0) a.ssq_out[(size_t)(nt0 + j) * M + row] = sq16;
       }
     }
   }
 }
 
-template <typename T, int MT, int NW>
+template <typename T, int MT, int NT, int NW>
 hipError_t launch_nw(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
-  const dim3 grid(a.N / 16, 1, (a.M + 16 * MT - 1) / (16 * MT));
-#define TD_L(E, NRM)                                                                           \
-  if (epi == E && norm == NRM) {                                                           \
-    hipLaunchKernelGGL((gemm_wk_kernel<T, MT, NW, E, NRM>), grid, dim3(64 * NW), 0, s, a); \
-    return hipGetLastError();                                                              \
+  const dim3 grid(a.N / (16 * NT), 1, (a.M + 16 * MT - 1) / (16 * MT));
+#define TD_L(E, NRM)                                                                               \
+  if (epi == E && norm == NRM) {                                                               \
+    hipLaunchKernelGGL((gemm_wk_kernel<T, MT, NT, NW, E, NRM>), grid, dim3(64 * NW), 0, s, a); \
+    return hipGetLastError();                                                                  \
   }
   TD_L(EPI_STORE, true)
   TD_L(EPI_GELU, true)
@@ -185,19 +189,31 @@ hipError_t launch_nw(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <typename T, int MT, int NT>
+hipError_t launch_nt(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
+  if (a.nw == 4) return launch_nw<T, MT, NT, 4>(epi, norm, a, s);
+  if (a.nw == 8) return launch_nw<T, MT, NT, 8>(epi, norm, a, s);
+  // Four row tiles with 16 waves would spill (128 VGPRs per lane): 8 waves instead.
+  if (a.nw == 16) return MT == 4 ? launch_nw<T, MT, NT, 8>(epi, norm, a, s) : launch_nw<T, MT, NT, 16>(epi, norm, a, s);
+  return hipErrorInvalidValue;
+}
+
 template <typename T, int MT>
 hipError_t launch_mt(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
-  if (a.nw == 4) return launch_nw<T, MT, 4>(epi, norm, a, s);
-  if (a.nw == 8) return launch_nw<T, MT, 8>(epi, norm, a, s);
-  // Four row tiles with 16 waves would spill (128 VGPRs per lane): 8 waves instead.
-  if (a.nw == 16) return MT == 4 ? launch_nw<T, MT, 8>(epi, norm, a, s) : launch_nw<T, MT, 16>(epi, norm, a, s);
+  if (a.nt == 1) return launch_nt<T, MT, 1>(epi, norm, a, s);
+  if constexpr (sizeof(T) == 2) {   // several column tiles per workgroup: bf16 towers
+    if (a.nt == 2) return launch_nt<T, MT, 2>(epi, norm, a, s);
+    if constexpr (MT == 1) {
+      if (a.nt == 4) return launch_nt<T, MT, 4>(epi, norm, a, s);
+    }
+  }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_gemm_wk(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s) {
-  if (a.N % 32 || a.K % 32 || a.M <= 0) return hipErrorInvalidValue;
+  if (a.N % 32 || a.K % 32 || a.M <= 0 || a.nt < 1 || a.N % (16 * a.nt)) return hipErrorInvalidValue;
   if (norm && (a.ssq == nullptr || a.norm_nparts <= 0)) return hipErrorInvalidValue;
   if ((epi == EPI_GELU || epi == EPI_RESID) && a.out_afl == nullptr) return hipErrorInvalidValue;
   const bool small = a.M <= 16;

@@ -6,21 +6,117 @@
 // (max, sum exp(s - max), argmax) triple per row and column group, so the [rows x V]
 // logit matrix never reaches HBM.
 //
-// The merge kernel combines the groups of a row in a fixed tree order; the last
-// workgroup to finish (integer counter) applies the adoption rule of PredNext
-// "人工知能は拡散言語モデルの夢を見るか？", section 拡散言語モデルで推論するには
+// The groups of a row are combined in a fixed tree order; then the adoption rule of
+// PredNext "人工知能は拡散言語モデルの夢を見るか？", section 拡散言語モデルで推論するには
 // (adopt masked positions whose confidence clears the threshold, the others stay
-// [MASK]) with the fixed fallback of adopting the single most confident masked
-// position when none clears it, then rebuilds the list of still-masked rows for the
-// next step, so the block loop needs no host round-trip.
+// [MASK]) with the fixed fallback of adopting the single most confident masked position
+// when none clears it, and the list of still-masked rows is rebuilt for the next step,
+// so the block loop needs no host round-trip.  Two shapes:
+//   * few rows (the block sizes of one or a few sequences): ONE workgroup merges every
+//     row (a wave per row, eight groups per lane in flight) and commits: no
+//     cross-workgroup synchronisation at all;
+//   * many rows: one workgroup per row, and the last workgroup to finish (integer
+//     counter after a device-scope fence) commits for the whole batch.
 #include "td_device.h"
 #include "td_kernels.h"
-
-#include <type_traits>
 
 namespace td {
 
 namespace {
+
+constexpr int SMALL_ROWS = 128;   // largest row count of the single-workgroup shape
+
+// Adoption rule for every sequence, then the compacted list of still-masked rows.
+// Called by all threads of one workgroup after conf_row / arg_row are final.  One thread
+// per block position; a sequence's B positions are B consecutive lanes of one wave
+// (B divides 64 and every pass starts at a multiple of 64), so the rule's reductions --
+// is any position at or above gamma, which masked position is the most confident
+// (lowest position on ties), is any position still masked -- are lane shuffles.
+TD_DEV void commit_all(const CommitArgs &a, int *s_wave) {
+  const int t = *a.st.t;
+  const int M = a.n * a.B;
+  for (int r0 = 0; r0 < M; r0 += blockDim.x) {
+    const int r = r0 + threadIdx.x;
+    const bool in = r < M;
+    const int p = r % a.B;
+    const int pos = in ? a.st.rowpos[r] : -1;
+    const bool masked = in && !a.committed[r] && pos >= 0;   // pos < 0: row rejected by the state check
+    const float c = masked ? a.conf_row[pos] : -INFINITY;
+    const int arg = masked ? a.arg_row[pos] : 0;
+    int clear = (masked && c >= a.gamma) ? 1 : 0, any = masked ? 1 : 0;
+    float best = c;
+    int best_p = masked ? p : 0x7FFFFFFF;
+    for (int o = 1; o < a.B; o <<= 1) {
+      clear |= __shfl_xor(clear, o);
+      any |= __shfl_xor(any, o);
+      const float bo = __shfl_xor(best, o);
+      const int po = __shfl_xor(best_p, o);
+      if (bo > best || (bo == best && po < best_p)) {
+        best = bo;
+        best_p = po;
+      }
+    }
+    if (masked) {
+      if (a.conf_out) a.conf_out[r] = c;
+      if (a.argmax_out) a.argmax_out[r] = arg;
+    }
+    const bool adopt = masked && (clear ? (c >= a.gamma) : (p == best_p));
+    if (adopt) {
+      a.tokens[r] = arg;
+      a.committed[r] = 1;
+      if (a.commit_step) a.commit_step[r] = (int8_t)t;
+    }
+    if (in && a.newly) a.newly[r] = adopt ? 1 : 0;
+    if (in && p == 0 && a.steps && any) a.steps[r / a.B] += 1;
+  }
+  __syncthreads();
+  // Rows still masked, in row order, for the next step.
+  int base = 0;
+  for (int r0 = 0; r0 < M; r0 += blockDim.x) {
+    const int r = r0 + threadIdx.x;
+    const bool masked = r < M && !a.committed[r];
+    base = block_compact(masked, base, a.st.rowlist, a.st.rowpos, r < M ? r : -1, s_wave);
+  }
+  if (threadIdx.x == 0) {
+    *a.st.n_rows = base;
+    *a.st.done = base == 0 ? 1 : 0;
+    *a.st.t = t + 1;
+  }
+}
+
+TD_DEV VStat shfl_xor(const VStat &v, int o) {
+  return VStat{__shfl_xor(v.m, o), __shfl_xor(v.s, o), __shfl_xor(v.a, o)};
+}
+
+// Single workgroup (1024 threads): wave w merges rows w, w + 16, ...; lane l combines
+// groups l, l + 64, ... in order, then the wave combines its lanes in a fixed tree.
+__global__ __launch_bounds__(1024) void merge_commit_small_kernel(CommitArgs a) {
+  constexpr int PER = 8;
+  __shared__ int s_wave[16];
+  const int n_rows = *a.st.n_rows;   // loaded together with the loop-exit flag
+  if (*a.st.done) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int row = wave; row < n_rows; row += 16) {
+    const VStat *vp = a.vpart + (size_t)row * a.nslices;
+    VStat v{-INFINITY, 0.f, 0x7FFFFFFF};
+    for (int i0 = lane; i0 < a.nslices; i0 += 64 * PER) {
+      VStat u[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) u[j] = vp[min(i0 + 64 * j, a.nslices - 1)];
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (i0 + 64 * j < a.nslices) v = vstat_merge(v, u[j]);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = vstat_merge(v, shfl_xor(v, o));
+    if (lane == 0) {
+      a.conf_row[row] = 1.0f / v.s;
+      a.arg_row[row] = v.a;
+    }
+  }
+  __syncthreads();
+  commit_all(a, s_wave);
+}
 
 __global__ __launch_bounds__(256) void merge_commit_kernel(CommitArgs a) {
   if (*a.st.done) return;
@@ -51,58 +147,16 @@ __global__ __launch_bounds__(256) void merge_commit_kernel(CommitArgs a) {
   if (!s_last) return;
   __threadfence();
   if (threadIdx.x == 0) atomicExch(a.st.counter, 0u);
-  const int t = *a.st.t;
-  for (int i = threadIdx.x; i < a.n; i += blockDim.x) {
-    bool any_masked = false, any_clear = false;
-    float best = -INFINITY;
-    int best_p = -1;
-    for (int p = 0; p < a.B; ++p) {
-      const int r = i * a.B + p;
-      const int pos = a.st.rowpos[r];
-      if (a.committed[r] || pos < 0) continue;   // pos < 0: row rejected by the state check
-      const float c = a.conf_row[pos];
-      if (a.conf_out) a.conf_out[r] = c;
-      if (a.argmax_out) a.argmax_out[r] = a.arg_row[pos];
-      any_masked = true;
-      if (c >= a.gamma) any_clear = true;
-      if (c > best) { best = c; best_p = p; }
-    }
-    for (int p = 0; p < a.B; ++p) {
-      const int r = i * a.B + p;
-      bool adopt = false;
-      const int pos = a.st.rowpos[r];
-      if (!a.committed[r] && pos >= 0) {
-        adopt = any_clear ? (a.conf_row[pos] >= a.gamma) : (p == best_p);
-        if (adopt) {
-          a.tokens[r] = a.arg_row[pos];
-          a.committed[r] = 1;
-          if (a.commit_step) a.commit_step[r] = (int8_t)t;
-        }
-      }
-      if (a.newly) a.newly[r] = adopt ? 1 : 0;
-    }
-    if (a.steps && any_masked) a.steps[i] += 1;
-  }
-  __syncthreads();
-  // Rows still masked, in row order, for the next step.
-  const int M = a.n * a.B;
-  int base = 0;
-  for (int r0 = 0; r0 < M; r0 += blockDim.x) {
-    const int r = r0 + threadIdx.x;
-    const bool masked = r < M && !a.committed[r];
-    base = block_compact(masked, base, a.st.rowlist, a.st.rowpos, r < M ? r : -1, s_wave);
-  }
-  if (threadIdx.x == 0) {
-    *a.st.n_rows = base;
-    *a.st.done = base == 0 ? 1 : 0;
-    *a.st.t = t + 1;
-  }
+  commit_all(a, s_wave);
 }
 
 }  // namespace
 
 hipError_t launch_merge_commit(const CommitArgs &a, int max_rows, hipStream_t s) {
-  hipLaunchKernelGGL(merge_commit_kernel, dim3(max_rows), dim3(256), 0, s, a);
+  if (max_rows <= SMALL_ROWS)
+    hipLaunchKernelGGL(merge_commit_small_kernel, dim3(1), dim3(1024), 0, s, a);
+  else
+    hipLaunchKernelGGL(merge_commit_kernel, dim3(max_rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -72,9 +72,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int *tokens, const T *E, const T *Pos, const T *gain,
                                                     float *x, float *ssq, void *x_afl, int M, int B, int d, int V,
                                                     StepState st) {
-  if (*st.done) return;
   const int r = blockIdx.x;
-  int tok = tokens[r];
+  int tok = tokens[r];   // loaded together with the loop-exit flag
+  if (*st.done) return;
   if (tok < 0 || tok > V) {
     if (threadIdx.x == 0) atomicOr(st.err, 2);
     tok = V;

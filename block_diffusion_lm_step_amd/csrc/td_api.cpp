@@ -141,17 +141,25 @@ td_status validate_weights(const td_config &c, const td_weights *w) {
 }
 
 // The LM head (vocabulary statistics): 4 column tiles per wave, 256 columns per
-// workgroup.  Layer projections: one 16-column tile per workgroup.  At most 256 tiles
-// (one workgroup per CU): 16 waves along K (8 with four row tiles, for the register
-// file), so that one CU keeps many k-tiles in flight; more tiles: 4 waves, so that two
-// workgroups fit on a CU and 512 tiles run in one round.  Each wave keeps >= 2 k-tiles.
-GemmPlan plan_gemm(int M, int N, int K, bool vstat) {
+// workgroup.  Layer projections (bf16): each activation fragment a wave loads feeds NT
+// column tiles, and the L2 -> CU traffic of the activations (2 KiB per k-tile per wave)
+// is what bounds these kernels besides the weight stream, so outputs of more than 256
+// column tiles take two tiles per workgroup (4 waves along K); narrower outputs keep one
+// tile per workgroup (every CU busy) with 16 waves along K (8 with four row tiles, for
+// the register file).  Each wave keeps >= 2 k-tiles.
+GemmPlan plan_gemm(int M, int N, int K, bool vstat, int dtype) {
   GemmPlan p;
   if (vstat) {
     p.nt = N % 256 == 0 ? 4 : (N % 128 == 0 ? 2 : 1);
   } else {
     const int KT = K / 32, tiles = N / 16;
-    p.nw = tiles <= 256 ? (M <= 16 ? 16 : 8) : 4;
+    if (tiles > 256 && dtype == TD_BF16 && tiles % 2 == 0) {
+      p.nt = 2;
+      p.nw = 4;
+    } else {
+      p.nt = 1;
+      p.nw = tiles <= 256 ? (M <= 16 ? 16 : 8) : 4;
+    }
     while (p.nw > 4 && KT / p.nw < 2) p.nw /= 2;
   }
   return p;
@@ -492,11 +500,11 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
   {  // GEMM plans for this batch size
     const int M = n_seqs * g.block_size;
     const int d = g.d_model, F = g.d_ff, Hd = g.n_heads * g.head_dim;
-    c->p_qkv = plan_gemm(M, c->Nqkv, d, false);
-    c->p_wo = plan_gemm(M, d, Hd, false);
-    c->p_w1 = plan_gemm(M, F, d, false);
-    c->p_w2 = plan_gemm(M, d, F, false);
-    c->p_lm = plan_gemm(M, g.vocab, d, true);
+    c->p_qkv = plan_gemm(M, c->Nqkv, d, false, g.dtype);
+    c->p_wo = plan_gemm(M, d, Hd, false, g.dtype);
+    c->p_w1 = plan_gemm(M, F, d, false, g.dtype);
+    c->p_w2 = plan_gemm(M, d, F, false, g.dtype);
+    c->p_lm = plan_gemm(M, g.vocab, d, true, g.dtype);
   }
   c->offsets.assign(off, off + n_seqs + 1);
   c->kc.assign(k_cache_host, k_cache_host + g.n_layers);
