@@ -4,12 +4,12 @@
 //
 // The head matrix (V x d) is the largest weight of the step and is read once per step;
 // at block sizes (16 masked rows per sequence or fewer) the kernel is bound by that
-// stream.  Each wave owns NT consecutive 16-column tiles and the whole K range, and
-// keeps PASS k-tiles of its weights (pre-packed 16x32 MFMA tiles, one contiguous KiB per
+// stream.  Each of the NW waves of a workgroup owns NT consecutive 16-column tiles and
+// the whole K range, and keeps PASS k-tiles of its weights (pre-packed 16x32 MFMA tiles, one contiguous KiB per
 // load) and of the activation fragments in flight, refilling a slot right after its
 // MFMA; all loads are unconditional (clamped addresses) so the compiler's waits before
-// each MFMA are exact.  No LDS staging and no barrier inside the stream: the four waves
-// of a workgroup only meet to merge their statistics.
+// each MFMA are exact.  No LDS staging and no barrier inside the stream: the waves of a
+// workgroup only meet to merge their statistics.
 //
 // Rows are gathered through the row list (only positions still masked need logits).
 // Activations are the final RMSNorm's input in fragment layout, stored by the last
@@ -22,17 +22,17 @@ namespace td {
 
 namespace {
 
-template <typename T, int MT, int NT> constexpr int lm_pass() {
+template <typename T, int MT, int NT, int NW> constexpr int lm_pass() {
   constexpr int per = MT * 8 + NT * (sizeof(T) == 2 ? 4 : 8);   // VGPRs per k-tile in flight
-  constexpr int p = 160 / per;
+  constexpr int p = (NW == 8 ? 72 : 160) / per;   // two workgroups per CU
   return p > 8 ? 8 : (p < 1 ? 1 : p);
 }
 
-template <typename T, int MT, int NT>
-__global__ __launch_bounds__(256) void lmhead_kernel(GemmArgs a) {
-  constexpr int PASS = lm_pass<T, MT, NT>();
+template <typename T, int MT, int NT, int NW>
+__global__ __launch_bounds__(64 * NW) void lmhead_kernel(GemmArgs a) {
+  constexpr int PASS = lm_pass<T, MT, NT, NW>();
   constexpr int ROWS = 16 * MT;
-  constexpr int TPR = 256 / ROWS;   // threads per row for the row scales
+  constexpr int TPR = (64 * NW / ROWS) < 64 ? 64 * NW / ROWS : 64;   // threads per row (row scales)
   constexpr int SQB = 16;
   const int *done = a.done;
   const int nrows = a.n_rows ? *a.n_rows : a.M;
@@ -41,11 +41,11 @@ __global__ __launch_bounds__(256) void lmhead_kernel(GemmArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int KT = a.K >> 5;
-  const int ntw = (blockIdx.x * 4 + wave) * NT;   // this wave's first column tile
+  const int ntw = (blockIdx.x * NW + wave) * NT;   // this wave's first column tile
 
   __shared__ int s_row[ROWS];
   __shared__ float s_rs[ROWS];
-  __shared__ VStat s_stat[4][ROWS];
+  __shared__ VStat s_stat[NW][ROWS];
   if (threadIdx.x < ROWS) {
     const int i = m0 + threadIdx.x;
     s_row[threadIdx.x] = i < nrows ? (a.rowlist ? a.rowlist[i] : i) : -1;
@@ -153,27 +153,38 @@ __global__ __launch_bounds__(256) void lmhead_kernel(GemmArgs a) {
   if (threadIdx.x < ROWS && s_row[threadIdx.x] >= 0) {
     VStat v = s_stat[0][threadIdx.x];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) v = vstat_merge(v, s_stat[w][threadIdx.x]);
+    for (int w = 1; w < NW; ++w) v = vstat_merge(v, s_stat[w][threadIdx.x]);
     a.vpart[(size_t)(m0 + threadIdx.x) * gridDim.x + blockIdx.x] = v;
   }
 }
 
-template <typename T, int MT>
-hipError_t launch_t(const GemmArgs &a, dim3 grid, hipStream_t s) {
-  if (a.nt == 1) hipLaunchKernelGGL((lmhead_kernel<T, MT, 1>), grid, dim3(256), 0, s, a);
-  else if (a.nt == 2) hipLaunchKernelGGL((lmhead_kernel<T, MT, 2>), grid, dim3(256), 0, s, a);
-  else if (a.nt == 4) hipLaunchKernelGGL((lmhead_kernel<T, MT, 4>), grid, dim3(256), 0, s, a);
+template <typename T, int MT, int NW>
+hipError_t launch_nw(const GemmArgs &a, dim3 grid, hipStream_t s) {
+  if (a.nt == 1) hipLaunchKernelGGL((lmhead_kernel<T, MT, 1, NW>), grid, dim3(64 * NW), 0, s, a);
+  else if (a.nt == 2) hipLaunchKernelGGL((lmhead_kernel<T, MT, 2, NW>), grid, dim3(64 * NW), 0, s, a);
+  else if (a.nt == 4) hipLaunchKernelGGL((lmhead_kernel<T, MT, 4, NW>), grid, dim3(64 * NW), 0, s, a);
+  else if (MT == 1 && a.nt == 8) hipLaunchKernelGGL((lmhead_kernel<T, 1, 8, NW>), grid, dim3(64 * NW), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
+template <typename T, int MT>
+hipError_t launch_t(const GemmArgs &a, dim3 grid, hipStream_t s) {
+  if (a.nw == 4) return launch_nw<T, MT, 4>(a, grid, s);
+  if (a.nw == 8) return launch_nw<T, MT, 8>(a, grid, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+// Column groups (one vocabulary-statistics triple per row each) of the LM head.
+int lmhead_slices(int N, int nt, int nw) { return N / (16 * nt * nw); }
 
 hipError_t launch_gemm(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s) {
   if (epi != EPI_VSTAT || !norm || a.ssq == nullptr || a.norm_nparts <= 0) return hipErrorInvalidValue;
-  if (a.N % (64 * a.nt) || a.K % 32 || a.M <= 0) return hipErrorInvalidValue;
+  if (a.nt < 1 || a.nw < 1 || a.N % (16 * a.nt * a.nw) || a.K % 32 || a.M <= 0) return hipErrorInvalidValue;
   const int mt = a.M <= 16 ? 1 : 4;
-  const dim3 grid(a.N / (64 * a.nt), 1, (a.M + 16 * mt - 1) / (16 * mt));
+  const dim3 grid(lmhead_slices(a.N, a.nt, a.nw), 1, (a.M + 16 * mt - 1) / (16 * mt));
   if (dtype == DT_BF16) return mt == 1 ? launch_t<bf16_t, 1>(a, grid, s) : launch_t<bf16_t, 4>(a, grid, s);
   return mt == 1 ? launch_t<float, 1>(a, grid, s) : launch_t<float, 4>(a, grid, s);
 }

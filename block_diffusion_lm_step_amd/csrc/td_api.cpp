@@ -140,8 +140,7 @@ td_status validate_weights(const td_config &c, const td_weights *w) {
   return TD_OK;
 }
 
-// The LM head (vocabulary statistics): 4 column tiles per wave, 256 columns per
-// workgroup.  Layer projections (bf16): each activation fragment a wave loads feeds NT
+// Layer projections (bf16): each activation fragment a wave loads feeds NT
 // column tiles, and the L2 -> CU traffic of the activations (2 KiB per k-tile per wave)
 // is what bounds these kernels besides the weight stream, so outputs of more than 256
 // column tiles take two tiles per workgroup (4 waves along K); narrower outputs keep one
@@ -150,7 +149,10 @@ td_status validate_weights(const td_config &c, const td_weights *w) {
 GemmPlan plan_gemm(int M, int N, int K, bool vstat, int dtype) {
   GemmPlan p;
   if (vstat) {
-    p.nt = N % 256 == 0 ? 4 : (N % 128 == 0 ? 2 : 1);
+    // One row tile: 8 waves x 2 column tiles (measured best at V = 131072, d = 2048);
+    // four row tiles need more registers per k-tile: 4 waves x 4 column tiles.
+    p.nw = M <= 16 && N % 256 == 0 ? 8 : 4;
+    p.nt = M <= 16 ? (N % 256 == 0 ? 2 : 1) : (N % 256 == 0 ? 4 : (N % 128 == 0 ? 2 : 1));
   } else {
     const int KT = K / 32, tiles = N / 16;
     if (tiles > 256 && dtype == TD_BF16 && tiles % 2 == 0) {
@@ -295,7 +297,7 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   ca.V = g.vocab;
   ca.B = g.block_size;
   ca.n = c->n_seqs;
-  ca.nslices = g.vocab / (64 * c->p_lm.nt);
+  ca.nslices = lmhead_slices(g.vocab, c->p_lm.nt, c->p_lm.nw);
   ca.vpart = c->vpart;
   ca.conf_row = c->conf_row;
   ca.arg_row = c->arg_row;
@@ -390,7 +392,7 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   TD_HIP(c, hipMemsetAsync(c->au, 0, afl_bytes((int)M, (int)F), c->stream));
   TD_TRY(dmalloc(c, &c->conf_row, M * 4));
   TD_TRY(dmalloc(c, &c->arg_row, M * 4));
-  TD_TRY(dmalloc(c, &c->vpart, M * (V / 64) * sizeof(VStat)));
+  TD_TRY(dmalloc(c, &c->vpart, M * (V / 16) * sizeof(VStat)));   // up to one group per 16 columns
   TD_TRY(dmalloc(c, &c->state_ints, (2 * M + 8) * sizeof(int)));
   TD_HIP(c, hipMemsetAsync(c->state_ints, 0, (2 * M + 8) * sizeof(int), c->stream));
   int *si = c->state_ints;

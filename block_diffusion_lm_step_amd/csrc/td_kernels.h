@@ -40,8 +40,8 @@ struct GemmArgs {
   const int *rowlist;      // optional row gather: GEMM row r is activation row rowlist[r]
   const int *n_rows;       // optional live row count (device)
   const void *Wp;          // packed weight [N][K]
-  int nt;                  // launch_gemm: 16-column tiles per wave (1, 2, 4)
-  int nw;                  // launch_gemm_wk: waves per workgroup (4, 8, 16)
+  int nt;                  // 16-column tiles per wave (launch_gemm: 1, 2, 4, 8) or per workgroup (launch_gemm_wk: 1, 2, 4)
+  int nw;                  // waves per workgroup (launch_gemm: 4, 8; launch_gemm_wk: 4, 8, 16)
   float *out; int ldo;     // STORE: fp32 [M][ldo]; RESID: x [M][ldo], updated in place
   void *out_afl;           // GELU: gelu(y) [M][N] in fragment layout; RESID: x * gain_next, same layout
   const void *gain_next;   // RESID: [N] gain of the RMSNorm that consumes the updated x
@@ -51,9 +51,11 @@ struct GemmArgs {
   float *logits;           // VSTAT: optional capture [rows][N] of the raw logits
   const int *done;         // skip the launch when *done != 0 (nullable)
 };
-// Column-split layout with 4 waves x nt tiles per workgroup, activations staged in LDS;
-// used for the LM head (EPI_VSTAT).
+// The LM head (EPI_VSTAT): nw waves x nt column tiles per workgroup, each wave streaming
+// its own columns over the whole K range.
 hipError_t launch_gemm(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s);
+// Column groups of the LM head, i.e. vocabulary-statistics triples per row.
+int lmhead_slices(int N, int nt, int nw);
 // One 16-column tile per workgroup, its nw waves splitting K with all weights in flight;
 // used for the layer projections (STORE, GELU, RESID).
 hipError_t launch_gemm_wk(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s);
