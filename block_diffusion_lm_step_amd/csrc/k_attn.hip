@@ -27,8 +27,9 @@
 //     waves of a workgroup take alternate pages of the item with no LDS and no barrier
 //     in the key loop (the next page in flight while the current one is consumed), and
 //     merge their states in LDS at the end;
-//   * many rows (grouped-query heads): each page is copied once into LDS and the four
-//     waves, each owning RT 16-row tiles, read it from there.
+//   * many rows (grouped-query heads): each page is staged once into LDS through a
+//     three-page register ring and the eight waves, each owning RTW 16-row tiles, read
+//     it from there.
 // Queries are fp32 activations; against bf16 keys each query fragment enters the MFMA
 // as a bf16 high part plus a bf16 remainder, and the probabilities are split the same
 // way for P.V, so q and P keep ~16 significant bits.  Key slots past the end of a
@@ -155,14 +156,14 @@ template <int HD> constexpr int block_item_lds() { return 2 * BMAX * (HD + 1); }
 // The block's own keys of one (sequence, K/V head) pair, fp32 on the VALU: 16 threads
 // per query row (HD/16 dimensions each), 16 rows at a time.  sm: block_item_lds floats
 // of LDS.  Writes the pair's block partial (m, l, o) to the item's slot.
-template <int HD>
+template <int HD, int NT = 256>
 TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *sm) {
-  constexpr int EPT = HD / 16, KPT = BMAX * HD / 256;
+  constexpr int EPT = HD / 16, KPT = BMAX * HD / NT;
   float *s_k = sm, *s_v = sm + BMAX * (HD + 1);
   const float *base = a.qkv + (size_t)it.seq * a.B * a.Nqkv;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {   // all of the pair's block keys and values in flight at once
-    const int idx = threadIdx.x + 256 * i;
+    const int idx = threadIdx.x + NT * i;
     const int key = idx / HD, e = idx % HD;
     if (key < a.B) {
       s_k[key * (HD + 1) + e] = base[(size_t)key * a.Nqkv + (size_t)(a.H + it.kvh) * HD + e];
@@ -171,7 +172,7 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
   }
   __syncthreads();
   const int sub = threadIdx.x & 15, e0 = sub * EPT;
-  for (int rho0 = 0; rho0 < a.R; rho0 += 16) {
+  for (int rho0 = 0; rho0 < a.R; rho0 += NT / 16) {
     const int rho = rho0 + (threadIdx.x >> 4);
     if (rho >= a.R) break;   // whole 16-lane groups leave together
     const int j = rho / a.B, p = rho % a.B;
@@ -214,10 +215,12 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
   }
 }
 
-// Multi-head shape (R <= 32): waves take alternate pages, operands straight from HBM.
-template <typename T, int HD, int RT>
-__global__ __launch_bounds__(256) void attn_direct_kernel(AttnArgs a) {
-  constexpr int NW = 4, HC = HD / 32, OT = HD / 16;
+// Multi-head shape (R <= 32): the NW = 4 waves take pages w, w + 4, ..., operands
+// straight from HBM, each wave with two pages in flight.  (Eight waves, two per SIMD,
+// measured slower: their registers spill.)
+template <typename T, int HD, int RT, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
+  constexpr int HC = HD / 32, OT = HD / 16;
   constexpr int MERGE = NW * RT * 16 * (HD + 2);
   constexpr int LDS = MERGE > block_item_lds<HD>() ? MERGE : block_item_lds<HD>();
   __shared__ float smem[LDS];
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(256) void attn_direct_kernel(AttnArgs a) {
   const AttnItem it = a.items[blockIdx.x];   // loaded together with the loop-exit flag
   if (a.done && *a.done) return;
   if (it.is_block) {
-    block_item<HD>(a, it, blockIdx.x, smem);
+    block_item<HD, 64 * NW>(a, it, blockIdx.x, smem);
     return;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(256) void attn_direct_kernel(AttnArgs a) {
   __syncthreads();
   constexpr int EPT = HD / 16;
   const int e0 = (threadIdx.x & 15) * EPT;
-  for (int rr = threadIdx.x >> 4; rr < RT * 16 && rr < a.R; rr += 16) {
+  for (int rr = threadIdx.x >> 4; rr < RT * 16 && rr < a.R; rr += 4 * NW) {
     float Mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_ml[w][rr][0]);
@@ -333,27 +336,38 @@ __global__ __launch_bounds__(256) void attn_direct_kernel(AttnArgs a) {
   }
 }
 
-// Grouped-query shape (R > 32): each page is copied once into LDS (16-byte copies, K in
-// its page layout with padded 32-element rows, V^T rows padded) and the four waves, RT
-// 16-row tiles each, read it from there.
-template <typename T, int HD, int RT>
-__global__ __launch_bounds__(256) void attn_shared_kernel(AttnArgs a) {
-  constexpr int NW = 4, HC = HD / 32, OT = HD / 16;
+// Grouped-query shape (R > 32): eight waves (two per SIMD) share each page, wave w
+// owning RTW 16-row tiles of the pair's query rows (RTW = 1: 128 rows per workgroup;
+// more rows take several workgroups per item).  Pages reach LDS through a ring of
+// DEPTH pages held in registers (every thread loads its share of page p + DEPTH while
+// page p is multiplied), then one 16-byte store per chunk into the double-buffered,
+// padded LDS page (K in its page layout with 32-element rows, V^T rows); one barrier per
+// page.  Each wave reads a page's K fragments from LDS once and reuses them for all of
+// its row tiles; V fragments are read at their use.
+template <typename T, int HD, int RTW>
+__global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
+  constexpr int NW = 8, NT = 64 * NW, HC = HD / 32, OT = HD / 16;
+  constexpr int DEPTH = 3;                 // pages in flight in registers
   constexpr int KR = 32 + Pad<T>::K;       // K row stride in LDS (elements)
   constexpr int VP = SUB + Pad<T>::V;      // V^T row stride in LDS (elements)
   constexpr int KCH = SUB * HD / 8;        // 8-element chunks of a K page (= of a V page)
-  constexpr int PER_T = (KCH + 255) / 256;
-  constexpr int KBYTES = (HC * 2 * 16 * KR + HD * VP) * (int)sizeof(T);
-  constexpr int BBYTES = block_item_lds<HD>() * 4;
-  constexpr int BYTES = KBYTES > BBYTES ? KBYTES : BBYTES;
+  constexpr int CPT = (KCH + NT - 1) / NT; // chunks of each per thread
+  constexpr int KBUF = HC * 2 * 16 * KR, VBUF = HD * VP;   // elements of one LDS page
+  constexpr int BYTES_PAGES = 2 * (KBUF + VBUF) * (int)sizeof(T);
+  constexpr int BYTES_BLOCK = block_item_lds<HD>() * 4;
+  constexpr int BYTES = BYTES_PAGES > BYTES_BLOCK ? BYTES_PAGES : BYTES_BLOCK;
   __shared__ __attribute__((aligned(16))) char smem[BYTES];
-  T *s_k = reinterpret_cast<T *>(smem);
-  T *s_vt = s_k + HC * 2 * 16 * KR;
+  T *s_k = reinterpret_cast<T *>(smem);          // [2][KBUF]
+  T *s_vt = s_k + 2 * KBUF;                      // [2][VBUF]
 
-  const AttnItem it = a.items[blockIdx.x];   // loaded together with the loop-exit flag
+  // Workgroup b takes row group b % YS of item b / YS: the row groups of an item are
+  // neighbours in launch order, so its pages are read while still in the last-level cache.
+  const int YS = (a.R + NW * RTW * 16 - 1) / (NW * RTW * 16);
+  const int item = blockIdx.x / YS, ygrp = blockIdx.x % YS;
+  const AttnItem it = a.items[item];   // loaded together with the loop-exit flag
   if (a.done && *a.done) return;
   if (it.is_block) {
-    if (blockIdx.y == 0) block_item<HD>(a, it, blockIdx.x, reinterpret_cast<float *>(smem));
+    if (ygrp == 0) block_item<HD, NT>(a, it, item, reinterpret_cast<float *>(smem));
     return;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -363,64 +377,101 @@ __global__ __launch_bounds__(256) void attn_shared_kernel(AttnArgs a) {
   const size_t pstride = (size_t)a.Hkv * SUB * HD;
   const T *Kp = reinterpret_cast<const T *>(a.kc) + ((size_t)it.page0 * a.Hkv + it.kvh) * SUB * HD;
   const T *Vp = reinterpret_cast<const T *>(a.vc) + ((size_t)it.page0 * a.Hkv + it.kvh) * HD * SUB;
-  const int rt0 = (blockIdx.y * NW + wave) * RT;
+  const int rt0 = (ygrp * NW + wave) * RTW;
 
-  AFrag<T> qf[RT][HC];
-  load_q<T, HD, RT>(a, it, rt0, g, l16, qf);
-  float m_run[RT], l_run[RT];
-  f32x4_t o[RT][OT];
+  AFrag<T> qf[RTW][HC];
+  load_q<T, HD, RTW>(a, it, rt0, g, l16, qf);
+  float m_run[RTW], l_run[RTW];
+  f32x4_t o[RTW][OT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int rt = 0; rt < RTW; ++rt) {
     m_run[rt] = -INFINITY;
     l_run[rt] = 0.f;
 #pragma unroll
     for (int t = 0; t < OT; ++t) o[rt][t] = zero4();
   }
 
-  Frag<T> kreg[PER_T], vreg[PER_T];
-  auto fetch = [&](int pg) __attribute__((always_inline)) {
+  // Register ring: slot r holds this thread's chunks of one page.  Loads are
+  // unconditional (pages past the end reread the last page) so that the waits before
+  // each store are exact.
+  constexpr int W = frag_words<T>();
+  u32x4_t kreg[DEPTH][CPT][W], vreg[DEPTH][CPT][W];
+  auto fetch = [&](auto slotc, int pg) __attribute__((always_inline)) {
+    constexpr int r = decltype(slotc)::value;
+    const size_t base = (size_t)min(pg, npg - 1) * pstride;
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      if (c < KCH && pg < npg) {
-        kreg[i].load(Kp + (size_t)pg * pstride + (size_t)c * 8);
-        vreg[i].load(Vp + (size_t)pg * pstride + (size_t)c * 8);
+    for (int i = 0; i < CPT; ++i) {
+      const int c = min((int)threadIdx.x + NT * i, KCH - 1);
+      const u32x4_t *kp = reinterpret_cast<const u32x4_t *>(Kp + base + (size_t)c * 8);
+      const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(Vp + base + (size_t)c * 8);
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        kreg[r][i][w] = kp[w];
+        vreg[r][i][w] = vp[w];
       }
     }
   };
-  auto stash = [&](int kvalid) __attribute__((always_inline)) {
+  auto stash = [&](auto slotc, int buf, int kvalid) __attribute__((always_inline)) {
+    constexpr int r = decltype(slotc)::value;
+    T *sk = s_k + buf * KBUF;
+    T *sv = s_vt + buf * VBUF;
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int c = threadIdx.x + 256 * i;
+    for (int i = 0; i < CPT; ++i) {
+      const int c = threadIdx.x + NT * i;
       if (c < KCH) {
-        // K: 32-element rows in page order ((hd chunk, half, MFMA row)), 4 chunks per row.
-        *reinterpret_cast<Frag<T> *>(&s_k[(c >> 2) * KR + (c & 3) * 8]) = kreg[i];
+        *reinterpret_cast<Frag<T> *>(&sk[(c >> 2) * KR + (c & 3) * 8]) = frag_of(kreg[r][i], T{});
         const int vrow = c / (SUB / 8), vpart = c % (SUB / 8);
-        Frag<T> v = vreg[i];
+        Frag<T> v = frag_of(vreg[r][i], T{});
         mask_v<T>(v, vpart, kvalid);
-        *reinterpret_cast<Frag<T> *>(&s_vt[vrow * VP + vpart * 8]) = v;
+        *reinterpret_cast<Frag<T> *>(&sv[vrow * VP + vpart * 8]) = v;
       }
     }
   };
-
-  fetch(0);
-  for (int pg = 0; pg < npg; ++pg) {
-    const int kvalid = nkeys - pg * SUB;
-    __syncthreads();   // every wave is done reading the previous page
-    stash(kvalid);
-    __syncthreads();   // this page is in LDS
-    if (pg + 1 < npg) fetch(pg + 1);
+  auto compute = [&](int buf, int kvalid) __attribute__((always_inline)) {
+    const T *sk = s_k + buf * KBUF;
+    const T *sv = s_vt + buf * VBUF;
+    Frag<T> kf[2][HC];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-      PageMath<T, HD>::run(
-          [&](int h, int c) { return *reinterpret_cast<const Frag<T> *>(&s_k[((c * 2 + h) * 16 + l16) * KR + g * 8]); },
-          [&](int t) { return *reinterpret_cast<const Frag<T> *>(&s_vt[(16 * t + l16) * VP + g * 8]); }, qf[rt],
-          a.scale, kvalid, g, m_run[rt], l_run[rt], o[rt]);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < HC; ++c) kf[h][c] = *reinterpret_cast<const Frag<T> *>(&sk[((c * 2 + h) * 16 + l16) * KR + g * 8]);
+    // V fragments are read from LDS at their use (once per row tile): holding them too
+    // would exceed the 256 registers of a wave at two waves per SIMD.
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+      PageMath<T, HD>::run([&](int h, int c) -> const Frag<T> & { return kf[h][c]; },
+                           [&](int t) { return *reinterpret_cast<const Frag<T> *>(&sv[(16 * t + l16) * VP + g * 8]); },
+                           qf[rt], a.scale, kvalid, g, m_run[rt], l_run[rt], o[rt]);
+  };
+  // One page: prefetch page p + DEPTH into this page's (now free) slot, multiply page p,
+  // stage page p + 1 into the other LDS buffer, barrier.
+  auto step = [&](auto slotc, int p) __attribute__((always_inline)) {
+    constexpr int r = decltype(slotc)::value;
+    constexpr int rn = (r + 1) % DEPTH;
+    fetch(slotc, p + DEPTH);
+    compute(p & 1, nkeys - p * SUB);
+    if (p + 1 < npg) stash(std::integral_constant<int, rn>{}, (p + 1) & 1, nkeys - (p + 1) * SUB);
+    __syncthreads();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  fetch(S0{}, 0);
+  fetch(S1{}, 1);
+  fetch(S2{}, 2);
+  stash(S0{}, 0, nkeys);
+  __syncthreads();
+  for (int p = 0; p < npg; p += DEPTH) {
+    step(S0{}, p);
+    if (p + 1 >= npg) break;
+    step(S1{}, p + 1);
+    if (p + 2 >= npg) break;
+    step(S2{}, p + 2);
   }
-  float l_tot[RT];
+  float l_tot[RTW];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) l_tot[rt] = sum_groups(l_run[rt]);
-  store_partial<HD, RT>(a, blockIdx.x, rt0, g, l16, m_run, l_tot, o);
+  for (int rt = 0; rt < RTW; ++rt) l_tot[rt] = sum_groups(l_run[rt]);
+  store_partial<HD, RTW>(a, item, rt0, g, l16, m_run, l_tot, o);
 }
 
 // Merge of a pair's partials in item order (prefix runs, then the block), one thread
@@ -478,13 +529,11 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 template <typename T, int HD>
 hipError_t launch_hd(const AttnArgs &a, hipStream_t s) {
   if (a.R <= 16) {
-    hipLaunchKernelGGL((attn_direct_kernel<T, HD, 1>), dim3(a.n_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_direct_kernel<T, HD, 1, 4>), dim3(a.n_items), dim3(256), 0, s, a);
   } else if (a.R <= 32) {
-    hipLaunchKernelGGL((attn_direct_kernel<T, HD, 2>), dim3(a.n_items), dim3(256), 0, s, a);
-  } else if (a.R <= 64) {
-    hipLaunchKernelGGL((attn_shared_kernel<T, HD, 1>), dim3(a.n_items, (a.R + 63) / 64), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((attn_shared_kernel<T, HD, 4>), dim3(a.n_items, (a.R + 255) / 256), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_direct_kernel<T, HD, 2, 4>), dim3(a.n_items), dim3(256), 0, s, a);
+  } else {   // one 16-row tile per wave, 128 rows per workgroup (more would spill)
+    hipLaunchKernelGGL((attn_group_kernel<T, HD, 1>), dim3(a.n_items * ((a.R + 127) / 128)), dim3(512), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

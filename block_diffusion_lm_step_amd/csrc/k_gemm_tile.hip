@@ -1,0 +1,363 @@
+// Tiled MFMA GEMM for many rows (batches of sequences): Y[M][N] = A[M][K] * W[N][K]^T.
+//
+// At M >= 128 every weight element is used by many rows and the projections are bound
+// by the matrix cores, not by the weight stream.  A workgroup of 4 waves computes a
+// 128 x 128 output tile; wave (wm, wn) owns the 64 x 64 quarter (4 x 4 MFMA tiles of
+// 16 x 16).  K advances one 32-wide k-tile per stage through double-buffered LDS (48 KiB,
+// so two workgroups share a CU and one's LDS traffic overlaps the other's MFMAs), one
+// barrier per stage: the next stage is loaded from memory into registers while the
+// current one is multiplied, then written to the other buffer.
+// Both operands are already in MFMA fragment order in memory (weights packed at
+// creation, activations written in fragment layout by their producers), so staging is
+// a straight 16-byte copy; the activation fragments' bf16 high and low halves go to two
+// separate LDS planes so that a wave's 16-byte LDS reads are contiguous (no bank
+// conflicts).  Per k-tile and wave: 8 activation + 4 weight fragment reads from LDS,
+// 32 MFMAs (high and low parts of the activations against the bf16 weights).
+//
+// Epilogues as in the weight-streaming kernels (the RMSNorm row scale multiplies the
+// accumulator): STORE (q/k/v), GELU and RESID (fragment-layout outputs, partial sums of
+// squares per 16 columns), and VSTAT for the LM head (rows gathered through the row
+// list; per row one (max, sum of exp, argmax) triple per 128-column group).
+#include "td_device.h"
+#include "td_kernels.h"
+
+namespace td {
+
+namespace {
+
+constexpr int BM = 128, BN = 128;   // workgroup tile
+constexpr int KS = 1;               // k-tiles per stage
+constexpr int NF = (BM / 16) * KS * 64 / 256;   // fragments of each operand staged per thread
+constexpr int MTW = 4, NTW = 4;     // MFMA tiles per wave (rows, columns)
+
+// Small per-thread tables are vector values, not arrays: arrays indexed in loops are
+// turned into LDS or scratch copies before the loops are unrolled.
+typedef unsigned long long u64x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+struct alignas(16) StageLds {
+  u32x4_t a_hi[BM / 16][KS][64];   // activation fragments, bf16 high parts
+  u32x4_t a_lo[BM / 16][KS][64];   // ... bf16 remainders
+  u32x4_t w[BN / 16][KS][64];      // weight fragments
+};
+
+constexpr int EPI_PART = 100;   // split-K partial: store the raw accumulator tile
+
+template <int EPI, bool NORM>
+__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
+  __shared__ StageLds s_st[2];
+  __shared__ int s_row[BM];
+  __shared__ float s_rs[BM];
+  __shared__ float s_part[2][BM];
+  __shared__ VStat s_stat[2][BM];
+
+  const int nrows = a.n_rows ? *a.n_rows : a.M;   // live rows (LM head: masked rows)
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  if (m0 >= nrows) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  // K range of this workgroup: split blockIdx.z of a.splits (whole k-tiles).
+  const int KTall = a.K >> 5;
+  const int kt0 = (int)((int64_t)KTall * blockIdx.z / a.splits), kt1 = (int)((int64_t)KTall * (blockIdx.z + 1) / a.splits);
+  const int KT = KTall, nstage = (kt1 - kt0) / KS;
+
+  // Activation rows of this tile (gathered through the row list for the LM head);
+  // rows past the live count read a valid row and are never written.
+  if (threadIdx.x < BM) {
+    const int i = min(m0 + threadIdx.x, nrows - 1);
+    s_row[threadIdx.x] = a.rowlist ? a.rowlist[i] : i;
+  }
+  __syncthreads();
+
+  // Staging: each thread moves NF activation fragments (32 B) and NF weight fragments
+  // (16 B) per stage; fragment f = threadIdx.x + 256 i covers (tile f / (64 KS), k-tile
+  // (f / 64) % KS, lane f % 64).  Source offsets of stage 0; stage s adds s * KS k-tiles.
+  const char *Ab = reinterpret_cast<const char *>(a.A);
+  const bf16_t *Wb = reinterpret_cast<const bf16_t *>(a.Wp);
+  u64x4_t aoff, woff;
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int f = threadIdx.x + 256 * i;
+    const int fl = f & 63, kt = (f >> 6) % KS, t = f / (64 * KS);
+    const int row = s_row[t * 16 + (fl & 15)];
+    aoff[i] = (((size_t)(row >> 4) * KT + kt0 + kt) * 64 + (fl >> 4) * 16 + (row & 15)) * 32;
+    woff[i] = (((size_t)(n0 / 16 + t) * KT + kt0 + kt) * 64 + fl) * 8;
+  }
+  // (tile, k-tile) of fragment i = 0; fragment i is 4 / KS tiles further.
+  const int ft = threadIdx.x / (64 * KS), fkt = (threadIdx.x >> 6) % KS;
+  u32x4_t ra_hi[NF], ra_lo[NF], rw[NF];
+#define TD_LOAD_STAGE(S)                                                                        \
+  _Pragma("unroll") for (int i = 0; i < NF; ++i) {                                              \
+    const u32x4_t *p_ = reinterpret_cast<const u32x4_t *>(Ab + aoff[i] + (size_t)(S) * KS * 2048); \
+    ra_hi[i] = p_[0];                                                                           \
+    ra_lo[i] = p_[1];                                                                           \
+    rw[i] = *reinterpret_cast<const u32x4_t *>(Wb + woff[i] + (size_t)(S) * KS * 512);          \
+  }
+#define TD_STORE_STAGE(B)                                                                       \
+  _Pragma("unroll") for (int i = 0; i < NF; ++i) {                                              \
+    s_st[B].a_hi[ft + (4 / KS) * i][fkt][lane] = ra_hi[i];                                      \
+    s_st[B].a_lo[ft + (4 / KS) * i][fkt][lane] = ra_lo[i];                                      \
+    s_st[B].w[ft + (4 / KS) * i][fkt][lane] = rw[i];                                            \
+  }
+
+  TD_LOAD_STAGE(0)
+  // The loop-exit flag is read only now, so that its latency overlaps the first loads.
+  if (a.done && *a.done) return;
+  if constexpr (NORM && EPI != EPI_PART) {
+    // Row scales from the producer's partial sums of squares: thread t sums parts of
+    // parity t / 128 of row t % 128 (consecutive threads read consecutive rows).
+    const int r = threadIdx.x & (BM - 1), par = threadIdx.x >> 7;
+    const int row = s_row[r];
+    float sacc = 0.f;
+    for (int p0 = par; p0 < a.norm_nparts; p0 += 2 * 16) {
+      f32x16_t v;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = a.ssq[(size_t)min(p0 + 2 * j, a.norm_nparts - 1) * a.ld_ssq + row];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc += (p0 + 2 * j < a.norm_nparts) ? v[j] : 0.f;
+    }
+    s_part[par][r] = sacc;
+  }
+  TD_STORE_STAGE(0)
+  __syncthreads();
+  if constexpr (NORM && EPI != EPI_PART) {
+    if (threadIdx.x < BM) s_rs[threadIdx.x] = 1.0f / sqrtf((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) / (float)a.K + a.norm_eps);
+  }
+
+  f32x4_t acc[MTW][NTW];
+#pragma unroll
+  for (int i = 0; i < MTW; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = zero4();
+
+  for (int s = 0; s < nstage; ++s) {
+    const int b = s & 1;
+    if (s + 1 < nstage) {
+      TD_LOAD_STAGE(s + 1)
+    }
+#pragma unroll
+    for (int kt = 0; kt < KS; ++kt) {
+      AFrag<bf16_t> af[MTW];
+      Frag<bf16_t> wf[NTW];
+#pragma unroll
+      for (int i = 0; i < MTW; ++i) {
+        af[i].hi.raw = __builtin_bit_cast(uint4, s_st[b].a_hi[wm * MTW + i][kt][lane]);
+        af[i].lo.raw = __builtin_bit_cast(uint4, s_st[b].a_lo[wm * MTW + i][kt][lane]);
+      }
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) wf[j].raw = __builtin_bit_cast(uint4, s_st[b].w[wn * NTW + j][kt][lane]);
+#pragma unroll
+      for (int i = 0; i < MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[i][j] = mma_a(af[i], wf[j], acc[i][j]);
+    }
+    if (s + 1 < nstage) {   // the other buffer was last read in stage s - 1
+      if (b) {
+        TD_STORE_STAGE(0)
+      } else {
+        TD_STORE_STAGE(1)
+      }
+    }
+    __syncthreads();
+  }
+
+#undef TD_LOAD_STAGE
+#undef TD_STORE_STAGE
+
+  // ---------------------------------------------------------------- epilogues
+  if constexpr (EPI == EPI_PART) {
+    float *part = a.part + (size_t)blockIdx.z * a.M * a.N;
+#pragma unroll
+    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int col = n0 + (wn * NTW + j) * 16 + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + (wm * MTW + i) * 16 + 4 * g + r;
+          if (row < a.M) part[(size_t)row * a.N + col] = acc[i][j][r];
+        }
+      }
+  } else if constexpr (EPI == EPI_VSTAT) {
+#pragma unroll
+    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ri = (wm * MTW + i) * 16 + 4 * g + r;
+        const bool live = m0 + ri < nrows;
+        const int row = s_row[ri];
+        const float rs = s_rs[ri];
+        const float tau = (live && a.inv_temp) ? a.inv_temp[row] : 1.0f;
+        VStat v{-INFINITY, 0.f, 0x7FFFFFFF};
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const int col = n0 + (wn * NTW + j) * 16 + l16;
+          const float z = acc[i][j][r] * rs;
+          float sv = -INFINITY;
+          if (live) {
+            if (a.logits) a.logits[(size_t)row * a.N + col] = z;
+            sv = tau * z;
+          }
+          float mx = sv;
+          mx = fmaxf(mx, __shfl_xor(mx, 1)); mx = fmaxf(mx, __shfl_xor(mx, 2));
+          mx = fmaxf(mx, __shfl_xor(mx, 4)); mx = fmaxf(mx, __shfl_xor(mx, 8));
+          const float se = sum16(live ? __expf(sv - mx) : 0.f);
+          int am = (live && sv == mx) ? col : 0x7FFFFFFF;
+          am = min(am, __shfl_xor(am, 1)); am = min(am, __shfl_xor(am, 2));
+          am = min(am, __shfl_xor(am, 4)); am = min(am, __shfl_xor(am, 8));
+          v = vstat_merge(v, VStat{mx, se, am});
+        }
+        if (l16 == 0) s_stat[wn][ri] = v;
+      }
+    __syncthreads();
+    if (threadIdx.x < BM && m0 + threadIdx.x < nrows)
+      a.vpart[(size_t)(m0 + threadIdx.x) * gridDim.x + blockIdx.x] = vstat_merge(s_stat[0][threadIdx.x], s_stat[1][threadIdx.x]);
+  } else {
+    const int M = a.M;
+    const int KTo = a.N >> 5;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int col = n0 + (wn * NTW + j) * 16 + l16;
+      float gnext = 1.0f;
+      f32x16_t xold;   // [i * 4 + r]
+      if constexpr (EPI == EPI_RESID) {
+        gnext = to_f32<bf16_t>(reinterpret_cast<const bf16_t *>(a.gain_next)[col]);
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            xold[i * 4 + r] = a.out[(size_t)min(m0 + (wm * MTW + i) * 16 + 4 * g + r, M - 1) * a.ldo + col];
+      }
+#pragma unroll
+      for (int i = 0; i < MTW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ri = (wm * MTW + i) * 16 + 4 * g + r;
+          const int row = m0 + ri;
+          const bool ok = row < M;
+          float y = acc[i][j][r];
+          if constexpr (NORM) y *= s_rs[ri];
+          if constexpr (EPI == EPI_STORE) {
+            if (ok) a.out[(size_t)row * a.ldo + col] = y;
+          } else if constexpr (EPI == EPI_GELU) {
+            if (ok) afl_put<bf16_t>(a.out_afl, KTo, row, col, gelu_erf(y));
+          } else {
+            const float xv = ok ? xold[i * 4 + r] + y : 0.f;
+            if (ok) {
+              a.out[(size_t)row * a.ldo + col] = xv;
+              afl_put<bf16_t>(a.out_afl, KTo, row, col, xv * gnext);
+            }
+            const float sq16 = sum16(xv * xv);
+            if (ok && l16 == 0) a.ssq_out[(size_t)(col >> 4) * M + row] = sq16;
+          }
+        }
+    }
+  }
+}
+
+// Split-K reduction and epilogue: one workgroup per (row, 1024 columns); thread t holds
+// 4 consecutive columns, sums the partials in split order, applies the row scale and
+// the epilogue.  Four threads cover a 16-column group (partial sums of squares).
+template <int EPI, bool NORM>
+__global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a) {
+  __shared__ float s_red[4];
+  const int row = blockIdx.y;
+  const int col = blockIdx.x * 1024 + threadIdx.x * 4;
+  const bool in = col < a.N;
+  f32x4_t y = zero4();
+  if (in) {
+#pragma unroll 4
+    for (int sp = 0; sp < a.splits; ++sp)
+      y += *reinterpret_cast<const f32x4_t *>(a.part + ((size_t)sp * a.M + row) * a.N + col);
+  }
+  if (a.done && *a.done) return;
+  if constexpr (NORM) {
+    float s = 0.f;
+    for (int p = threadIdx.x; p < a.norm_nparts; p += 256) s += a.ssq[(size_t)p * a.ld_ssq + row];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    const float rs = 1.0f / sqrtf((s_red[0] + s_red[1] + s_red[2] + s_red[3]) / (float)a.K + a.norm_eps);
+    y *= rs;
+  }
+  if (!in) return;
+  const int KTo = a.N >> 5;
+  if constexpr (EPI == EPI_STORE) {
+    *reinterpret_cast<f32x4_t *>(a.out + (size_t)row * a.ldo + col) = y;
+  } else if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) afl_put<bf16_t>(a.out_afl, KTo, row, col + e, gelu_erf(y[e]));
+  } else {
+    f32x4_t *xp = reinterpret_cast<f32x4_t *>(a.out + (size_t)row * a.ldo + col);
+    const f32x4_t xv = *xp + y;
+    *xp = xv;
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      afl_put<bf16_t>(a.out_afl, KTo, row, col + e, xv[e] * to_f32<bf16_t>(reinterpret_cast<const bf16_t *>(a.gain_next)[col + e]));
+      sq += xv[e] * xv[e];
+    }
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    if ((threadIdx.x & 3) == 0) a.ssq_out[(size_t)(col >> 4) * a.M + row] = sq;
+  }
+}
+
+}  // namespace
+
+bool gemm_tile_supported(int dtype, int M, int N, int K) {
+  return dtype == DT_BF16 && M >= BM && N % BN == 0 && K % (32 * KS) == 0;
+}
+
+int gemm_tile_slices(int N) { return N / BN; }
+
+// Split only grids of less than one workgroup per CU (up to ~2 per CU, >= 8 k-tiles per
+// split): measured, a grid of 256 tiles runs faster whole than split in two.
+int gemm_tile_splits(int M, int N, int K) {
+  const int tiles = (N / BN) * ((M + BM - 1) / BM);
+  int s = 1;
+  if (tiles >= 256) return s;
+  while (tiles * s < 512 && (K / 32) / (2 * s) >= 8) s *= 2;
+  return s;
+}
+
+hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
+  if (a.N % BN || a.K % (32 * KS) || a.M <= 0 || a.splits < 1) return hipErrorInvalidValue;
+  if (norm && (a.ssq == nullptr || a.norm_nparts <= 0)) return hipErrorInvalidValue;
+  if ((epi == EPI_GELU || epi == EPI_RESID) && a.out_afl == nullptr) return hipErrorInvalidValue;
+  if (a.splits > 1) {
+    if (epi == EPI_VSTAT || a.part == nullptr || a.n_rows != nullptr) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_tile_kernel<EPI_PART, false>), dim3(a.N / BN, (a.M + BM - 1) / BM, a.splits), dim3(256),
+                       0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 rgrid((a.N + 1023) / 1024, a.M);
+#define TD_R(E, NRM)                                                                  \
+    if (epi == E && norm == NRM) {                                                \
+      hipLaunchKernelGGL((split_reduce_kernel<E, NRM>), rgrid, dim3(256), 0, s, a); \
+      return hipGetLastError();                                                   \
+    }
+    TD_R(EPI_STORE, true)
+    TD_R(EPI_GELU, true)
+    TD_R(EPI_RESID, false)
+#undef TD_R
+    return hipErrorInvalidValue;
+  }
+  const dim3 grid(a.N / BN, (a.M + BM - 1) / BM);
+#define TD_L(E, NRM)                                                                 \
+  if (epi == E && norm == NRM) {                                                 \
+    hipLaunchKernelGGL((gemm_tile_kernel<E, NRM>), grid, dim3(256), 0, s, a);    \
+    return hipGetLastError();                                                    \
+  }
+  TD_L(EPI_STORE, true)
+  TD_L(EPI_GELU, true)
+  TD_L(EPI_RESID, false)
+  TD_L(EPI_VSTAT, true)
+#undef TD_L
+  return hipErrorInvalidValue;
+}
+
+}  // namespace td

@@ -22,6 +22,8 @@ thread_local std::string g_create_error;
 
 struct GemmPlan {
   int nt = 1, nw = 4;
+  bool tile = false;   // many rows: the tiled MFMA kernel
+  int splits = 1;      // tiled kernel: K split (partials summed by a second kernel)
 };
 
 }  // namespace
@@ -59,6 +61,8 @@ struct td_ctx {
   int n_items = 0, n_pairs = 0;
   size_t items_cap = 0, pairs_cap = 0;
   float *att_o = nullptr, *att_ml = nullptr;
+  float *part = nullptr;     // split-K partial products of the tiled GEMMs
+  size_t part_cap = 0;       // floats
   size_t att_cap_rows = 0;   // capacity in partial rows (items * R)
 
   // profiling: event pairs around the launches of one kernel class
@@ -148,6 +152,11 @@ td_status validate_weights(const td_config &c, const td_weights *w) {
 // the register file).  Each wave keeps >= 2 k-tiles.
 GemmPlan plan_gemm(int M, int N, int K, bool vstat, int dtype) {
   GemmPlan p;
+  if (gemm_tile_supported(dtype == TD_BF16 ? DT_BF16 : DT_F32, M, N, K)) {
+    p.tile = true;
+    p.splits = vstat ? 1 : gemm_tile_splits(M, N, K);
+    return p;
+  }
   if (vstat) {
     // One row tile: 8 waves x 2 column tiles (measured best at V = 131072, d = 2048);
     // four row tiles need more registers per k-tile: 4 waves x 4 column tiles.
@@ -167,15 +176,19 @@ GemmPlan plan_gemm(int M, int N, int K, bool vstat, int dtype) {
   return p;
 }
 
-// Prefix keys per split-K item: a multiple of the page size chosen so that the whole
-// batch (total prefix keys summed over K/V heads) makes about one workgroup per CU, and
-// at least four pages (one per wave).  Long prefixes then take long items (each wave
-// streams many pages) instead of many partials for the merge.
-int chunk_keys(int64_t total_pair_keys) {
-  constexpr int64_t kTargetItems = 256;
-  int64_t tc = (total_pair_keys + kTargetItems - 1) / kTargetItems;
+// Prefix keys per split-K item: a multiple of the page size (at least eight pages)
+// chosen from the whole batch's prefix keys summed over K/V heads.  Multi-head items
+// (memory-bound) aim at about four workgroups per CU: that keeps the work balanced when
+// the prefix lengths of a batch differ (one item per pair would vary 16-fold) while long
+// prefixes still take long items and the merge sees few partials.  Grouped-query items
+// (matrix-core-bound pages, split into row groups of 128 query rows) aim at about one
+// workgroup per CU, counting the row groups (measured: more items were slower).
+int chunk_keys(int64_t total_pair_keys, int R) {
+  const int64_t row_groups = R <= 32 ? 1 : (R + 127) / 128;
+  const int64_t target = R <= 32 ? 1024 : std::max<int64_t>(1, 256 / row_groups);
+  int64_t tc = (total_pair_keys + target - 1) / target;
   tc = (tc + KV_PAGE - 1) / KV_PAGE * KV_PAGE;
-  return (int)std::min<int64_t>(std::max<int64_t>(tc, 4 * KV_PAGE), (int64_t)1 << 30);
+  return (int)std::min<int64_t>(std::max<int64_t>(tc, 8 * KV_PAGE), (int64_t)1 << 30);
 }
 
 constexpr size_t PROF_MAX = 65536;
@@ -257,7 +270,13 @@ td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const
   a.gain_next = gain_next;
   a.ssq_out = c->ssq;
   a.done = c->st.done;
-  if (epi == EPI_VSTAT) {
+  a.splits = p.tile ? p.splits : 1;
+  a.part = c->part;
+  if (p.tile) {
+    if (epi != EPI_VSTAT) TD_TRY(prof_mark(c, TD_PROF_GEMM, true));
+    TD_HIP(c, launch_gemm_tile(epi, norm, a, c->stream));
+    if (epi != EPI_VSTAT) TD_TRY(prof_mark(c, TD_PROF_GEMM, false));
+  } else if (epi == EPI_VSTAT) {
     TD_HIP(c, launch_gemm(c->cfg.dtype, epi, norm, a, c->stream));
   } else {
     TD_TRY(prof_mark(c, TD_PROF_GEMM, true));
@@ -297,7 +316,7 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   ca.V = g.vocab;
   ca.B = g.block_size;
   ca.n = c->n_seqs;
-  ca.nslices = lmhead_slices(g.vocab, c->p_lm.nt, c->p_lm.nw);
+  ca.nslices = c->p_lm.tile ? gemm_tile_slices(g.vocab) : lmhead_slices(g.vocab, c->p_lm.nt, c->p_lm.nw);
   ca.vpart = c->vpart;
   ca.conf_row = c->conf_row;
   ca.arg_row = c->arg_row;
@@ -335,7 +354,7 @@ void free_all(td_ctx *c) {
     for (void *p : *v) f(p);
   f(c->x); f(c->ssq); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->ah); f(c->ao); f(c->au);
   f(c->arg_row); f(c->state_ints); f(c->items_d); f(c->pair_first_d);
-  f(c->pair_count_d); f(c->att_o); f(c->att_ml);
+  f(c->pair_count_d); f(c->att_o); f(c->att_ml); f(c->part);
   for (hipEvent_t e : c->ev_start) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->ev_stop) (void)hipEventDestroy(e);
 }
@@ -458,7 +477,7 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
   for (int i = 0; i < n_seqs; ++i)
     if (off[i + 1] - off[i] > (int64_t)1 << 30) return fail(c, TD_EINVAL, "prefix of sequence %d too long", i);
   const int G = g.n_heads / g.n_kv_heads, R = G * g.block_size;
-  const int tc = chunk_keys(off[n_seqs] * g.n_kv_heads);
+  const int tc = chunk_keys(off[n_seqs] * g.n_kv_heads, R);
   std::vector<AttnItem> items;
   std::vector<int> pfirst, pcount;
   int64_t page_base = 0;   // first cache page of sequence i
@@ -507,6 +526,12 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
     c->p_w1 = plan_gemm(M, F, d, false, g.dtype);
     c->p_w2 = plan_gemm(M, d, F, false, g.dtype);
     c->p_lm = plan_gemm(M, g.vocab, d, true, g.dtype);
+    size_t need = 0;   // floats of split-K partials
+    const GemmPlan *plans[] = {&c->p_qkv, &c->p_wo, &c->p_w1, &c->p_w2};
+    const int widths[] = {c->Nqkv, d, F, d};
+    for (int i = 0; i < 4; ++i)
+      if (plans[i]->tile && plans[i]->splits > 1) need = std::max(need, (size_t)plans[i]->splits * M * widths[i]);
+    TD_TRY(grow(&c->part, c->part_cap, need, sizeof(float)));
   }
   c->offsets.assign(off, off + n_seqs + 1);
   c->kc.assign(k_cache_host, k_cache_host + g.n_layers);

@@ -36,6 +36,10 @@ template <typename T> TD_DEV T from_f32(float v);
 template <> TD_DEV float from_f32<float>(float v) { return v; }
 template <> TD_DEV bf16_t from_f32<bf16_t>(float v) { return f2bf(v); }
 
+// 16 bytes as a native vector: arrays of these stay in registers where arrays of the
+// uint4 struct can end up in scratch.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 // Eight consecutive contraction elements held by one lane.
 template <typename T> struct Frag;
 template <> struct Frag<bf16_t> {
@@ -67,6 +71,20 @@ template <> struct Frag<float> {
     hi = make_float4(v[4], v[5], v[6], v[7]);
   }
 };
+
+// A fragment from / to its 16-byte words (bf16: 1 word, fp32: 2).
+template <typename T> constexpr int frag_words() { return sizeof(T) / 2; }
+TD_DEV Frag<bf16_t> frag_of(const u32x4_t *w, bf16_t) {
+  Frag<bf16_t> f;
+  f.raw = __builtin_bit_cast(uint4, w[0]);
+  return f;
+}
+TD_DEV Frag<float> frag_of(const u32x4_t *w, float) {
+  Frag<float> f;
+  f.lo = __builtin_bit_cast(float4, w[0]);
+  f.hi = __builtin_bit_cast(float4, w[1]);
+  return f;
+}
 
 // acc += A(frag a) * B(frag b) over one 32-wide contraction step.
 TD_DEV f32x4_t mma(const Frag<bf16_t> &a, const Frag<bf16_t> &b, f32x4_t acc) {

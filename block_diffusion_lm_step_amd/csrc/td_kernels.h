@@ -50,12 +50,23 @@ struct GemmArgs {
   VStat *vpart;            // VSTAT: [row index][grid.x] statistics of each column group
   float *logits;           // VSTAT: optional capture [rows][N] of the raw logits
   const int *done;         // skip the launch when *done != 0 (nullable)
+  int splits;              // tiled kernel: K split over this many workgroups (1: none)
+  float *part;             // splits > 1: [splits][M][N] fp32 partial products (workspace)
 };
 // The LM head (EPI_VSTAT): nw waves x nt column tiles per workgroup, each wave streaming
 // its own columns over the whole K range.
 hipError_t launch_gemm(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s);
 // Column groups of the LM head, i.e. vocabulary-statistics triples per row.
 int lmhead_slices(int N, int nt, int nw);
+// Many rows (bf16, M >= 128, N % 128 == 0, K % 32 == 0): 128 x 128 tiles through
+// double-buffered LDS, every epilogue (VSTAT: one statistics triple per 128 columns).
+// With a.splits > 1 (not VSTAT) the K range is split over that many workgroups, which
+// store fp32 partials to a.part, and a second kernel sums them in split order and
+// applies the epilogue.
+bool gemm_tile_supported(int dtype, int M, int N, int K);
+int gemm_tile_slices(int N);
+int gemm_tile_splits(int M, int N, int K);   // splits that give the grid ~2 workgroups per CU
+hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a, hipStream_t s);
 // One 16-column tile per workgroup, its nw waves splitting K with all weights in flight;
 // used for the layer projections (STORE, GELU, RESID).
 hipError_t launch_gemm_wk(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s);
