@@ -112,6 +112,37 @@ struct PageMath {
   }
 };
 
+// Query values of rows (rt0 + rt) * 16 + l16, dimensions c * 32 + g * 8 .. + 7, as fp32:
+// loads only, no branch (rows past R read row 0 and are zeroed by q_frags), so that
+// the caller can issue further loads before the first wait.
+template <int HD, int RT>
+TD_DEV void load_q_raw(const AttnArgs &a, const AttnItem &it, int rt0, int g, int l16, float (&v)[RT][HD / 32][8]) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rho = (rt0 + rt) * 16 + l16;
+    const int rr = rho < a.R ? rho : 0;
+    const int j = rr / a.B, p = rr % a.B;
+#pragma unroll
+    for (int c = 0; c < HD / 32; ++c)
+      load8f(a.qkv + (size_t)(it.seq * a.B + p) * a.Nqkv + (size_t)(it.kvh * a.G + j) * HD + c * 32 + g * 8, v[rt][c]);
+  }
+}
+
+template <typename T, int HD, int RT>
+TD_DEV void q_frags(const AttnArgs &a, int rt0, int l16, const float (&v)[RT][HD / 32][8], AFrag<T> (&qf)[RT][HD / 32]) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const bool valid = (rt0 + rt) * 16 + l16 < a.R;
+#pragma unroll
+    for (int c = 0; c < HD / 32; ++c) {
+      float w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = valid ? v[rt][c][e] : 0.f;
+      qf[rt][c].set8(w);
+    }
+  }
+}
+
 template <typename T, int HD, int RT>
 TD_DEV void load_q(const AttnArgs &a, const AttnItem &it, int rt0, int g, int l16, AFrag<T> (&qf)[RT][HD / 32]) {
 #pragma unroll
@@ -215,22 +246,29 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
   }
 }
 
-// Multi-head shape (R <= 32): the NW = 4 waves take pages w, w + 4, ..., operands
-// straight from HBM, each wave with two pages in flight.  (Eight waves, two per SIMD,
-// measured slower: their registers spill.)
+// Few-row shape (R <= 32, multi-head attention): the NW = 4 waves take pages w, w + 4,
+// ..., operands straight from HBM, each wave with two pages in flight.  (Eight waves, two
+// per SIMD, measured slower: their registers spill.)  The pair's first item also attends
+// the block's own keys: their loads are issued before the first pages', so the fp32
+// block pass (block_item's arithmetic, into LDS) runs while the pages are in flight, and
+// its state is merged after the waves' in the fixed order waves 0..NW-1, block.
 template <typename T, int HD, int RT, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
-  constexpr int HC = HD / 32, OT = HD / 16;
-  constexpr int MERGE = NW * RT * 16 * (HD + 2);
-  constexpr int LDS = MERGE > block_item_lds<HD>() ? MERGE : block_item_lds<HD>();
+  constexpr int NT = 64 * NW, HC = HD / 32, OT = HD / 16, EPT = HD / 16, KPT = BMAX * HD / NT;
+  constexpr int MERGE = (NW + 1) * RT * 16 * (HD + 2);   // waves' and the block's states
+  constexpr int LDS = MERGE + block_item_lds<HD>();
   __shared__ float smem[LDS];
+  float(*s_o)[RT * 16][HD] = reinterpret_cast<float(*)[RT * 16][HD]>(smem);
+  float(*s_ml)[RT * 16][2] = reinterpret_cast<float(*)[RT * 16][2]>(smem + (NW + 1) * RT * 16 * HD);
+  float *s_bk = smem + MERGE, *s_bv = s_bk + BMAX * (HD + 1);
 
   const AttnItem it = a.items[blockIdx.x];   // loaded together with the loop-exit flag
   if (a.done && *a.done) return;
-  if (it.is_block) {
-    block_item<HD, 64 * NW>(a, it, blockIdx.x, smem);
+  if (it.is_block == 1) {
+    block_item<HD, NT>(a, it, blockIdx.x, smem);
     return;
   }
+  const bool with_block = it.is_block == 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int nkeys = it.k_end - it.k_begin;
@@ -239,8 +277,32 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
   const T *Kp = reinterpret_cast<const T *>(a.kc) + ((size_t)it.page0 * a.Hkv + it.kvh) * SUB * HD;
   const T *Vp = reinterpret_cast<const T *>(a.vc) + ((size_t)it.page0 * a.Hkv + it.kvh) * HD * SUB;
 
-  AFrag<T> qf[RT][HC];
-  load_q<T, HD, RT>(a, it, 0, g, l16, qf);
+  // Block keys/values (fp32, this thread's KPT elements) and the block pass's query
+  // values (16 threads per row, EPT dimensions each): issued first.
+  constexpr int BPASS = (RT * 16 + NT / 16 - 1) / (NT / 16);
+  const int sub = threadIdx.x & 15, e0 = sub * EPT;
+  const float *bbase = a.qkv + (size_t)it.seq * a.B * a.Nqkv;
+  float bk[KPT], bv[KPT], bq[BPASS][EPT];
+  if (with_block) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int idx = threadIdx.x + NT * i, key = idx / HD, e = idx % HD;
+      const int kk = key < a.B ? key : 0;
+      bk[i] = bbase[(size_t)kk * a.Nqkv + (size_t)(a.H + it.kvh) * HD + e];
+      bv[i] = bbase[(size_t)kk * a.Nqkv + (size_t)(a.H + a.Hkv + it.kvh) * HD + e];
+    }
+#pragma unroll
+    for (int ps = 0; ps < BPASS; ++ps) {
+      const int rho = ps * (NT / 16) + (threadIdx.x >> 4);
+      const int rr = rho < a.R ? rho : 0;
+      const float *q = bbase + (size_t)(rr % a.B) * a.Nqkv + (size_t)(it.kvh * a.G + rr / a.B) * HD + e0;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) bq[ps][e] = q[e];
+    }
+  }
+
+  float qraw[RT][HC][8];
+  load_q_raw<HD, RT>(a, it, 0, g, l16, qraw);
 
   float m_run[RT], l_run[RT];
   f32x4_t o[RT][OT];
@@ -252,6 +314,7 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
     for (int t = 0; t < OT; ++t) o[rt][t] = zero4();
   }
 
+  AFrag<T> qf[RT][HC];               // filled once the first pages are in flight
   Frag<T> kf[2][2][HC], vf[2][OT];   // [buffer] page operands
   auto fetch = [&](auto bufc, int pg) __attribute__((always_inline)) {
     constexpr int b = decltype(bufc)::value;
@@ -282,7 +345,58 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   int pg = wave;
+  __builtin_amdgcn_sched_barrier(0);   // the block and query loads stay ahead of the pages'
   fetch(B0{}, pg);
+  __builtin_amdgcn_sched_barrier(0);
+  q_frags<T, HD, RT>(a, 0, l16, qraw, qf);
+
+  if (with_block) {   // workgroup-uniform
+    // The block pass: scores over the B block keys in fp32, one softmax, into slot NW.
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int idx = threadIdx.x + NT * i, key = idx / HD, e = idx % HD;
+      s_bk[key * (HD + 1) + e] = bk[i];
+      s_bv[key * (HD + 1) + e] = bv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ps = 0; ps < BPASS; ++ps) {
+      const int rho = ps * (NT / 16) + (threadIdx.x >> 4);
+      float sc[BMAX];
+      float m = -INFINITY;
+#pragma unroll
+      for (int key = 0; key < BMAX; ++key) {
+        if (key < a.B) {
+          float dsum = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) dsum += bq[ps][e] * s_bk[key * (HD + 1) + e0 + e];
+          sc[key] = sum16(dsum) * a.scale;
+          m = fmaxf(m, sc[key]);
+        }
+      }
+      float l = 0.f, ov[EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) ov[e] = 0.f;
+#pragma unroll
+      for (int key = 0; key < BMAX; ++key) {
+        if (key < a.B) {
+          const float pk = __expf(sc[key] - m);
+          l += pk;
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) ov[e] += pk * s_bv[key * (HD + 1) + e0 + e];
+        }
+      }
+      if (rho < RT * 16) {
+        if (sub == 0) {
+          s_ml[NW][rho][0] = m;
+          s_ml[NW][rho][1] = l;
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) s_o[NW][rho][e0 + e] = ov[e];
+      }
+    }
+  }
+
   while (pg < npg) {
     fetch(B1{}, pg + NW);
     consume(B0{}, pg);
@@ -293,9 +407,7 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
     pg += NW;
   }
 
-  // Merge the four waves' states (wave order) through LDS.
-  float(*s_o)[RT * 16][HD] = reinterpret_cast<float(*)[RT * 16][HD]>(smem);
-  float(*s_ml)[RT * 16][2] = reinterpret_cast<float(*)[RT * 16][2]>(smem + NW * RT * 16 * HD);
+  // Merge the waves' states (wave order), then the block's, through LDS.
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float l_tot = sum_groups(l_run[rt]);
@@ -308,25 +420,27 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
     for (int t = 0; t < OT; ++t) *reinterpret_cast<f32x4_t *>(&s_o[wave][rr][16 * t + 4 * g]) = o[rt][t];
   }
   __syncthreads();
-  constexpr int EPT = HD / 16;
-  const int e0 = (threadIdx.x & 15) * EPT;
+  const int nst = with_block ? NW + 1 : NW;
   for (int rr = threadIdx.x >> 4; rr < RT * 16 && rr < a.R; rr += 4 * NW) {
     float Mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_ml[w][rr][0]);
+    for (int w = 0; w <= NW; ++w)
+      if (w < nst) Mx = fmaxf(Mx, s_ml[w][rr][0]);
     float L = 0.f, acc[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = s_ml[w][rr][0];
-      const float f = (mw == -INFINITY) ? 0.f : __expf(mw - Mx);
-      L += s_ml[w][rr][1] * f;
+    for (int w = 0; w <= NW; ++w) {
+      if (w < nst) {
+        const float mw = s_ml[w][rr][0];
+        const float f = (mw == -INFINITY) ? 0.f : __expf(mw - Mx);
+        L += s_ml[w][rr][1] * f;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) acc[e] += s_o[w][rr][e0 + e] * f;
+        for (int e = 0; e < EPT; ++e) acc[e] += s_o[w][rr][e0 + e] * f;
+      }
     }
     const size_t prow = (size_t)blockIdx.x * a.R + rr;
-    if ((threadIdx.x & 15) == 0) {
+    if (sub == 0) {
       a.part_ml[prow * 2 + 0] = Mx;
       a.part_ml[prow * 2 + 1] = L;
     }
@@ -480,7 +594,7 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
 // projection's input in fragment layout.
 template <typename T, int HD>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
-  constexpr int BATCH = 8;
+  constexpr int BATCH = 16;
   const int pair = blockIdx.x;
   const int first = a.pair_first[pair], cnt = a.pair_count[pair];   // loaded with the exit flag
   if (a.done && *a.done) return;
@@ -530,7 +644,7 @@ template <typename T, int HD>
 hipError_t launch_hd(const AttnArgs &a, hipStream_t s) {
   if (a.R <= 16) {
     hipLaunchKernelGGL((attn_direct_kernel<T, HD, 1, 4>), dim3(a.n_items), dim3(256), 0, s, a);
-  } else if (a.R <= 32) {
+  } else if (a.R <= ATTN_FEW_ROWS) {
     hipLaunchKernelGGL((attn_direct_kernel<T, HD, 2, 4>), dim3(a.n_items), dim3(256), 0, s, a);
   } else {   // one 16-row tile per wave, 128 rows per workgroup (more would spill)
     hipLaunchKernelGGL((attn_group_kernel<T, HD, 1>), dim3(a.n_items * ((a.R + 127) / 128)), dim3(512), 0, s, a);

@@ -86,8 +86,7 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < SQB; ++j) s += (sub + TPR * j < a.norm_nparts) ? sq[j] : 0.f;
     for (int p = sub + TPR * SQB; p < a.norm_nparts; p += TPR) s += a.ssq[(size_t)p * a.ld_ssq + srow];
-#pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o);
+    s = sum_lanes<TPR>(s);
     if (sub == 0) s_rs[rr] = 1.0f / sqrtf(s / (float)a.K + a.norm_eps);
   }
 
@@ -139,12 +138,10 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kernel(GemmArgs a) {
           sv = tau * z;
         }
         float mx = sv;
-        mx = fmaxf(mx, __shfl_xor(mx, 1)); mx = fmaxf(mx, __shfl_xor(mx, 2));
-        mx = fmaxf(mx, __shfl_xor(mx, 4)); mx = fmaxf(mx, __shfl_xor(mx, 8));
+        mx = max16(mx);
         const float se = sum16(row >= 0 ? __expf(sv - mx) : 0.f);
         int am = (row >= 0 && sv == mx) ? col : 0x7FFFFFFF;
-        am = min(am, __shfl_xor(am, 1)); am = min(am, __shfl_xor(am, 2));
-        am = min(am, __shfl_xor(am, 4)); am = min(am, __shfl_xor(am, 8));
+        am = min16(am);
         v = vstat_merge(v, VStat{mx, se, am});
       }
       if (l16 == 0) s_stat[wave][ri] = v;

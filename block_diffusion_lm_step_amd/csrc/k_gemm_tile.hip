@@ -201,12 +201,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
             sv = tau * z;
           }
           float mx = sv;
-          mx = fmaxf(mx, __shfl_xor(mx, 1)); mx = fmaxf(mx, __shfl_xor(mx, 2));
-          mx = fmaxf(mx, __shfl_xor(mx, 4)); mx = fmaxf(mx, __shfl_xor(mx, 8));
+          mx = max16(mx);
           const float se = sum16(live ? __expf(sv - mx) : 0.f);
           int am = (live && sv == mx) ? col : 0x7FFFFFFF;
-          am = min(am, __shfl_xor(am, 1)); am = min(am, __shfl_xor(am, 2));
-          am = min(am, __shfl_xor(am, 4)); am = min(am, __shfl_xor(am, 8));
+          am = min16(am);
           v = vstat_merge(v, VStat{mx, se, am});
         }
         if (l16 == 0) s_stat[wn][ri] = v;
@@ -276,8 +274,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a) {
   if constexpr (NORM) {
     float s = 0.f;
     for (int p = threadIdx.x; p < a.norm_nparts; p += 256) s += a.ssq[(size_t)p * a.ld_ssq + row];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+    s = sum_lanes<64>(s);
     if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = s;
     __syncthreads();
     const float rs = 1.0f / sqrtf((s_red[0] + s_red[1] + s_red[2] + s_red[3]) / (float)a.K + a.norm_eps);
@@ -300,8 +297,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a) {
       afl_put<bf16_t>(a.out_afl, KTo, row, col + e, xv[e] * to_f32<bf16_t>(reinterpret_cast<const bf16_t *>(a.gain_next)[col + e]));
       sq += xv[e] * xv[e];
     }
-    sq += __shfl_xor(sq, 1);
-    sq += __shfl_xor(sq, 2);
+    sq = sum_lanes<4>(sq);
     if ((threadIdx.x & 3) == 0) a.ssq_out[(size_t)(col >> 4) * a.M + row] = sq;
   }
 }

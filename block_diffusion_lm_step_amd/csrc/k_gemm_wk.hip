@@ -95,8 +95,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < SQB; ++j) s += (sub + TPR * j < a.norm_nparts) ? sq[j] : 0.f;
     for (int p = sub + TPR * SQB; p < a.norm_nparts; p += TPR) s += a.ssq[(size_t)p * a.ld_ssq + srow];
-#pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o);
+    s = sum_lanes<TPR>(s);
     if (sub == 0) s_rs[rr] = 1.0f / sqrtf(s / (float)a.K + a.norm_eps);
   }
 

@@ -184,8 +184,8 @@ GemmPlan plan_gemm(int M, int N, int K, bool vstat, int dtype) {
 // (matrix-core-bound pages, split into row groups of 128 query rows) aim at about one
 // workgroup per CU, counting the row groups (measured: more items were slower).
 int chunk_keys(int64_t total_pair_keys, int R) {
-  const int64_t row_groups = R <= 32 ? 1 : (R + 127) / 128;
-  const int64_t target = R <= 32 ? 1024 : std::max<int64_t>(1, 256 / row_groups);
+  const int64_t row_groups = R <= ATTN_FEW_ROWS ? 1 : (R + 127) / 128;
+  const int64_t target = R <= ATTN_FEW_ROWS ? 1024 : std::max<int64_t>(1, 256 / row_groups);
   int64_t tc = (total_pair_keys + target - 1) / target;
   tc = (tc + KV_PAGE - 1) / KV_PAGE * KV_PAGE;
   return (int)std::min<int64_t>(std::max<int64_t>(tc, 8 * KV_PAGE), (int64_t)1 << 30);
@@ -478,6 +478,9 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
     if (off[i + 1] - off[i] > (int64_t)1 << 30) return fail(c, TD_EINVAL, "prefix of sequence %d too long", i);
   const int G = g.n_heads / g.n_kv_heads, R = G * g.block_size;
   const int tc = chunk_keys(off[n_seqs] * g.n_kv_heads, R);
+  // Few-row path: the pair's first item also takes the block's keys (no item of its own,
+  // so the item count is the prefix pages' alone); grouped-query path: a block item last.
+  const bool few = R <= ATTN_FEW_ROWS;
   std::vector<AttnItem> items;
   std::vector<int> pfirst, pcount;
   int64_t page_base = 0;   // first cache page of sequence i
@@ -486,9 +489,11 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
     for (int h = 0; h < g.n_kv_heads; ++h) {
       const int pair = i * g.n_kv_heads + h;
       pfirst.push_back((int)items.size());
+      if (few && P == 0) items.push_back(AttnItem{i, h, 0, 0, 2, pair, page_base});
       for (int64_t k0 = 0; k0 < P; k0 += tc)
-        items.push_back(AttnItem{i, h, (int)k0, (int)std::min<int64_t>(P, k0 + tc), 0, pair, page_base + k0 / KV_PAGE});
-      items.push_back(AttnItem{i, h, 0, g.block_size, 1, pair, 0});
+        items.push_back(AttnItem{i, h, (int)k0, (int)std::min<int64_t>(P, k0 + tc), (few && k0 == 0) ? 2 : 0, pair,
+                                 page_base + k0 / KV_PAGE});
+      if (!few) items.push_back(AttnItem{i, h, 0, 0, 1, pair, 0});
       pcount.push_back((int)items.size() - pfirst.back());
     }
     page_base += (P + KV_PAGE - 1) / KV_PAGE;

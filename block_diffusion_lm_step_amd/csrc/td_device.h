@@ -191,19 +191,67 @@ TD_DEV void load8f(const float *p, float *v) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// Butterfly reductions over the 16 lanes that share l / 16 (offsets 1..8) or over the
-// four lane groups that share l % 16 (offsets 16, 32).
-TD_DEV float sum16(float v) {
-  v += __shfl_xor(v, 1); v += __shfl_xor(v, 2); v += __shfl_xor(v, 4); v += __shfl_xor(v, 8);
+// Cross-lane reductions in registers, no LDS round trip.  Inside a row of 16 lanes the
+// partner values come from DPP lane permutations: swap neighbours (quad_perm 1,0,3,2),
+// swap pairs (2,3,0,1), reverse each half row (lane i <-> 7 - i), reverse the row
+// (i <-> 15 - i); after the first k steps every lane holds the reduction over its aligned
+// block of 2^k lanes.  Across rows, the gfx950 lane swaps return, for source = old = v,
+// the even and the odd row of each 32-lane half (16-lane swap) or the lower and the
+// upper half (32-lane swap) to every lane, combined as (first op second).  Partner lanes
+// combine the same two operands in the same order, so every lane of a block ends with a
+// bit-identical result.
+template <int CTRL>
+TD_DEV float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+TD_DEV int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_SWAP1 = 0xB1, DPP_SWAP2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+// Sum over aligned blocks of N lanes (N a power of two up to 64).
+template <int N>
+TD_DEV float sum_lanes(float v) {
+  if constexpr (N >= 2) v += dpp_f<DPP_SWAP1>(v);
+  if constexpr (N >= 4) v += dpp_f<DPP_SWAP2>(v);
+  if constexpr (N >= 8) v += dpp_f<DPP_HALF_MIRROR>(v);
+  if constexpr (N >= 16) v += dpp_f<DPP_MIRROR>(v);
+  if constexpr (N >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (N >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   return v;
+}
+TD_DEV float sum16(float v) { return sum_lanes<16>(v); }
+TD_DEV float max16(float v) {
+  v = fmaxf(v, dpp_f<DPP_SWAP1>(v));
+  v = fmaxf(v, dpp_f<DPP_SWAP2>(v));
+  v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_f<DPP_MIRROR>(v));
+}
+TD_DEV int min16(int v) {
+  v = min(v, dpp_i<DPP_SWAP1>(v));
+  v = min(v, dpp_i<DPP_SWAP2>(v));
+  v = min(v, dpp_i<DPP_HALF_MIRROR>(v));
+  return min(v, dpp_i<DPP_MIRROR>(v));
+}
+// Over the four 16-lane rows, per lane position l % 16.
+TD_DEV float sum_groups(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 TD_DEV float max_groups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16)); v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
-}
-TD_DEV float sum_groups(float v) {
-  v += __shfl_xor(v, 16); v += __shfl_xor(v, 32);
-  return v;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Merge of two softmax-statistics triples: exact for (max, index), fixed-order for the sum.

@@ -83,13 +83,21 @@ hipError_t launch_gemm_wk(int dtype, int epi, bool norm, const GemmArgs &a, hipS
 // page_off[i] + t / 32, slot t % 32.
 constexpr int KV_PAGE = 32;
 
-// One split-K work item: prefix tokens [k_begin, k_end) (k_begin a multiple of the page
-// size, first page page0 of the cache), or the block's own keys.  The items of a
-// (seq, kv head) pair are consecutive; the block item is the pair's last.
+// Query rows per (seq, kv head) pair up to which attention takes the few-row path (four
+// waves per item straight from HBM); more rows take the grouped-query path.
+constexpr int ATTN_FEW_ROWS = 32;
+
+// One split-K work item of a (seq, kv head) pair: prefix tokens [k_begin, k_end)
+// (k_begin a multiple of the page size, first page page0 of the cache) and/or the
+// block's own keys.  The items of a pair are consecutive.  is_block:
+//   0  prefix keys only;
+//   1  the block's keys only (the pair's last item; grouped-query path);
+//   2  prefix keys and the block's keys (the pair's first item; few-row path; the
+//      prefix range is empty when the sequence has no prefix).
 struct AttnItem {
   int seq, kvh;            // sequence and key/value head
-  int k_begin, k_end;      // key range (prefix token index within the sequence; or 0..B)
-  int is_block;            // 1: keys/values are the block's own k/v from the projections
+  int k_begin, k_end;      // prefix key range (token index within the sequence)
+  int is_block;            // 0, 1 or 2 as above
   int pair;                // seq * Hkv + kvh
   int64_t page0;           // cache page holding token k_begin (prefix items)
 };
