@@ -18,6 +18,11 @@ LIB_PATH = os.path.join(_HERE, "libtd.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m block_diffusion_lm_step_amd.build` first")
 
+# torch first: its HIP runtime is then the one libtd binds to, the same instance that
+# owns the tensors and streams handed over (loading libtd first brings in a second
+# runtime, which finds no device).
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 
 TD_OK, TD_EINVAL, TD_ENOMEM, TD_EDEVICE, TD_EUNSUPPORTED = range(5)

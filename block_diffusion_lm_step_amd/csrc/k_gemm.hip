@@ -34,7 +34,11 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kernel(GemmArgs a) {
   constexpr int ROWS = 16 * MT;
   constexpr int TPR = (64 * NW / ROWS) < 64 ? 64 * NW / ROWS : 64;   // threads per row (row scales)
   constexpr int SQB = 16;
-  const int *done = a.done;
+  // The loop-exit flag is loaded before any operand: issued behind the operand stream it
+  // would queue with it and hold back the first MFMAs; it is tested once the first
+  // operand loads are in flight.
+  const int stop = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // a vector load
+  __builtin_amdgcn_sched_barrier(0);
   const int nrows = a.n_rows ? *a.n_rows : a.M;
   const int m0 = blockIdx.z * ROWS;
   if (m0 >= nrows) return;
@@ -79,8 +83,8 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kernel(GemmArgs a) {
   };
 #pragma unroll
   for (int i = 0; i < PASS; ++i) fill(i, i);
-  // The loop-exit flag is read only now, so that its latency overlaps the first loads.
-  if (done && *done) return;
+  asm volatile("" ::: "memory");   // the loads above are issued before the test below
+  if (stop) return;
   {
     float s = 0.f;
 #pragma unroll
@@ -179,6 +183,7 @@ int lmhead_slices(int N, int nt, int nw) { return N / (16 * nt * nw); }
 
 hipError_t launch_gemm(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s) {
   if (epi != EPI_VSTAT || !norm || a.ssq == nullptr || a.norm_nparts <= 0) return hipErrorInvalidValue;
+  if (a.done == nullptr) return hipErrorInvalidValue;
   if (a.nt < 1 || a.nw < 1 || a.N % (16 * a.nt * a.nw) || a.K % 32 || a.M <= 0) return hipErrorInvalidValue;
   const int mt = a.M <= 16 ? 1 : 4;
   const dim3 grid(lmhead_slices(a.N, a.nt, a.nw), 1, (a.M + 16 * mt - 1) / (16 * mt));

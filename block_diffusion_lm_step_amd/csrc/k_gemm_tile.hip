@@ -52,6 +52,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   __shared__ float s_part[2][BM];
   __shared__ VStat s_stat[2][BM];
 
+  // The loop-exit flag is loaded before any operand: issued behind the operand stream it
+  // would queue with it and hold back the first MFMAs; it is tested once the first
+  // operand loads are in flight.
+  const int stop = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // a vector load
+  __builtin_amdgcn_sched_barrier(0);
   const int nrows = a.n_rows ? *a.n_rows : a.M;   // live rows (LM head: masked rows)
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   if (m0 >= nrows) return;
@@ -103,8 +108,8 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   }
 
   TD_LOAD_STAGE(0)
-  // The loop-exit flag is read only now, so that its latency overlaps the first loads.
-  if (a.done && *a.done) return;
+  asm volatile("" ::: "memory");   // the loads above are issued before the test below
+  if (stop) return;
   if constexpr (NORM && EPI != EPI_PART) {
     // Row scales from the producer's partial sums of squares: thread t sums parts of
     // parity t / 128 of row t % 128 (consecutive threads read consecutive rows).
@@ -320,8 +325,24 @@ int gemm_tile_splits(int M, int N, int K) {
   return s;
 }
 
+hipError_t launch_split_reduce(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
+  if (a.splits < 2 || a.part == nullptr || a.N % 16 || a.M <= 0) return hipErrorInvalidValue;
+  const dim3 rgrid((a.N + 1023) / 1024, a.M);
+#define TD_R(E, NRM)                                                                \
+  if (epi == E && norm == NRM) {                                                \
+    hipLaunchKernelGGL((split_reduce_kernel<E, NRM>), rgrid, dim3(256), 0, s, a); \
+    return hipGetLastError();                                                   \
+  }
+  TD_R(EPI_STORE, true)
+  TD_R(EPI_GELU, true)
+  TD_R(EPI_RESID, false)
+#undef TD_R
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
   if (a.N % BN || a.K % (32 * KS) || a.M <= 0 || a.splits < 1) return hipErrorInvalidValue;
+  if (a.done == nullptr) return hipErrorInvalidValue;
   if (norm && (a.ssq == nullptr || a.norm_nparts <= 0)) return hipErrorInvalidValue;
   if ((epi == EPI_GELU || epi == EPI_RESID) && a.out_afl == nullptr) return hipErrorInvalidValue;
   if (a.splits > 1) {
@@ -330,17 +351,7 @@ hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a, hipStream_t s
                        0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 rgrid((a.N + 1023) / 1024, a.M);
-#define TD_R(E, NRM)                                                                  \
-    if (epi == E && norm == NRM) {                                                \
-      hipLaunchKernelGGL((split_reduce_kernel<E, NRM>), rgrid, dim3(256), 0, s, a); \
-      return hipGetLastError();                                                   \
-    }
-    TD_R(EPI_STORE, true)
-    TD_R(EPI_GELU, true)
-    TD_R(EPI_RESID, false)
-#undef TD_R
-    return hipErrorInvalidValue;
+    return launch_split_reduce(epi, norm, a, s);
   }
   const dim3 grid(a.N / BN, (a.M + BM - 1) / BM);
 #define TD_L(E, NRM)                                                                 \

@@ -20,9 +20,15 @@
 // accumulator.  It is formed from the producer's partial sums of squares, which are
 // loaded before the weights so that waiting for them never waits for the weights.
 //
+// With a.splits > 1 the K range is also split over workgroups (blockIdx.y: a contiguous
+// run of whole k-tiles each) so that few column tiles still fill the chip and each CU
+// re-reads less of the activations: the workgroups store fp32 partials
+// part[split][M][N] and launch_split_reduce sums them in split order (deterministic)
+// and applies the row scale and the epilogue.  (An in-kernel reduction by the last
+// workgroup to arrive needs device-scope release/acquire fences, which measured ~10 us.)
+//
 // The waves' accumulators meet in LDS; wave w sums tile w (and w + NW, ...) over the
-// waves in wave order (deterministic, no cross-workgroup reduction, no device-scope
-// fence) and applies the epilogue:
+// waves in wave order (deterministic, no device-scope fence) and applies the epilogue:
 //   STORE  q/k/v (fp32, row-major),
 //   GELU   u = gelu_erf(y), written in fragment layout for the MLP down projection,
 //   RESID  x += y (fp32 residual stream), partial sums of squares of the new rows per
@@ -36,7 +42,8 @@ namespace {
 
 // k-tiles in flight per wave: the VGPRs per k-tile (activation fragments of MT row
 // tiles + NT weight fragments) into a budget that keeps two 256/512-thread workgroups
-// per CU (1024-thread workgroups: one workgroup, 128 VGPRs).
+// per CU (1024-thread workgroups: one workgroup, 128 VGPRs).  (Every k-tile of a
+// 2048-deep wave range in flight at once, one workgroup per CU, measured slower.)
 template <typename T, int MT, int NT, int NW> constexpr int wk_pass() {
   constexpr int per = MT * 8 + NT * (sizeof(T) == 2 ? 4 : 8);
   constexpr int budget = NW == 16 ? 72 : 176;
@@ -50,21 +57,29 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
   constexpr int ROWS = 16 * MT;
   constexpr int TPR = (64 * NW / ROWS) < 64 ? 64 * NW / ROWS : 64;   // threads per row (row scales)
   constexpr int SQB = 16;                                             // partial sums loaded per batch
+  // The loop-exit flag is loaded before any operand: issued behind the operand stream it
+  // would queue with it and hold back the first MFMAs; it is tested once the first
+  // operand loads are in flight.
+  const int stop = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // a vector load
+  __builtin_amdgcn_sched_barrier(0);
   const int M = a.M;
   const int m0 = blockIdx.z * ROWS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int nt0 = blockIdx.x * NT;
   const int KT = a.K >> 5;
-  const int kwt = (KT + NW - 1) / NW;            // k-tiles per wave
-  const int kw0 = min(KT, wave * kwt), kw1 = min(KT, kw0 + kwt);
+  const int ks0 = (int)((int64_t)KT * blockIdx.y / a.splits), ks1 = (int)((int64_t)KT * (blockIdx.y + 1) / a.splits);
+  const int kwt = (ks1 - ks0 + NW - 1) / NW;     // k-tiles per wave
+  const int kw0 = min(ks1, ks0 + wave * kwt), kw1 = min(ks1, kw0 + kwt);
 
   __shared__ float s_rs[ROWS];
   __shared__ f32x4_t s_red[NW][MT * NT][64];
 
   const T *Wl = reinterpret_cast<const T *>(a.Wp) + ((size_t)nt0 * KT) * 512 + (size_t)lane * 8;
   const char *Al = reinterpret_cast<const char *>(a.A) + ((size_t)(m0 >> 4) * KT) * 2048 + (size_t)lane * 32;
-  auto clampk = [&](int kt) { return max(0, min(kt, KT - 1)); };
+  // Loads past the wave's range re-read its last k-tile (unconditional loads keep the
+  // compiler's waits exact; they are never multiplied).
+  auto clampk = [&](int kt) { return max(0, min(min(kt, kw1 - 1), KT - 1)); };
   AFrag<T> xa[PASS][MT];
   Frag<T> wb[PASS][NT];
   auto fill = [&](int i, int kt) __attribute__((always_inline)) {
@@ -87,9 +102,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
   // First PASS k-tiles of activations and weights.
 #pragma unroll
   for (int i = 0; i < PASS; ++i) fill(i, kw0 + i);
-  // The loop-exit flag is read only now, so that its latency overlaps the first loads
-  // (reading the operands is harmless when the block is already adopted).
-  if (a.done && *a.done) return;
+  // (Reading the operands is harmless when the block is already adopted.)
+  asm volatile("" ::: "memory");   // the loads above are issued before the test below
+  if (stop) return;
   if constexpr (NORM) {
     float s = 0.f;
 #pragma unroll
@@ -134,12 +149,40 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) s_red[wave][mt * NT + j][lane] = acc[mt][j];
   __syncthreads();
-  const int KTo = a.N >> 5;   // k-tiles of a fragment-layout output (its K is this GEMM's N)
-  for (int q = wave; q < MT * NT; q += NW) {
-    const int mt = q / NT, j = q % NT;
-    f32x4_t y4 = s_red[0][q][lane];
+  constexpr int QW = (MT * NT + NW - 1) / NW;   // tiles finished per wave
+  f32x4_t yq[QW];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) y4 += s_red[w][q][lane];
+  for (int i = 0; i < QW; ++i) {
+    const int q = wave + NW * i;
+    if (q < MT * NT) {
+      yq[i] = s_red[0][q][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) yq[i] += s_red[w][q][lane];
+    }
+  }
+  if (a.splits > 1) {   // this split's partial; launch_split_reduce finishes
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+      const int q = wave + NW * i;
+      if (q < MT * NT) {
+        const int col = (nt0 + q % NT) * 16 + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + (q / NT) * 16 + 4 * g + r;
+          if (row < M) a.part[((size_t)blockIdx.y * M + row) * a.N + col] = yq[i][r];
+        }
+      }
+    }
+    return;
+  }
+
+  const int KTo = a.N >> 5;   // k-tiles of a fragment-layout output (its K is this GEMM's N)
+#pragma unroll
+  for (int i = 0; i < QW; ++i) {
+    const int q = wave + NW * i;
+    if (q >= MT * NT) break;
+    const int mt = q / NT, j = q % NT;
+    const f32x4_t y4 = yq[i];
     const int col = (nt0 + j) * 16 + l16;
     // Residual rows and the next gain, loaded before any store (the compiler cannot
     // tell that the outputs alias nothing and would otherwise serialise the loads).
@@ -175,7 +218,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
 
 template <typename T, int MT, int NT, int NW>
 hipError_t launch_nw(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
-  const dim3 grid(a.N / (16 * NT), 1, (a.M + 16 * MT - 1) / (16 * MT));
+  const dim3 grid(a.N / (16 * NT), a.splits, (a.M + 16 * MT - 1) / (16 * MT));
 #define TD_L(E, NRM)                                                                               \
   if (epi == E && norm == NRM) {                                                               \
     hipLaunchKernelGGL((gemm_wk_kernel<T, MT, NT, NW, E, NRM>), grid, dim3(64 * NW), 0, s, a); \
@@ -213,11 +256,18 @@ hipError_t launch_mt(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
 
 hipError_t launch_gemm_wk(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s) {
   if (a.N % 32 || a.K % 32 || a.M <= 0 || a.nt < 1 || a.N % (16 * a.nt)) return hipErrorInvalidValue;
+  if (a.done == nullptr) return hipErrorInvalidValue;
   if (norm && (a.ssq == nullptr || a.norm_nparts <= 0)) return hipErrorInvalidValue;
   if ((epi == EPI_GELU || epi == EPI_RESID) && a.out_afl == nullptr) return hipErrorInvalidValue;
+  // Split K only for bf16 towers (the reduction writes bf16 fragment layout).
+  if (a.splits < 1 || a.splits > a.K / 32 || (a.splits > 1 && (a.part == nullptr || dtype != DT_BF16)))
+    return hipErrorInvalidValue;
   const bool small = a.M <= 16;
-  if (dtype == DT_BF16) return small ? launch_mt<bf16_t, 1>(epi, norm, a, s) : launch_mt<bf16_t, 4>(epi, norm, a, s);
-  return small ? launch_mt<float, 1>(epi, norm, a, s) : launch_mt<float, 4>(epi, norm, a, s);
+  hipError_t e;
+  if (dtype == DT_BF16) e = small ? launch_mt<bf16_t, 1>(epi, norm, a, s) : launch_mt<bf16_t, 4>(epi, norm, a, s);
+  else e = small ? launch_mt<float, 1>(epi, norm, a, s) : launch_mt<float, 4>(epi, norm, a, s);
+  if (e != hipSuccess || a.splits == 1) return e;
+  return launch_split_reduce(epi, norm, a, s);
 }
 
 }  // namespace td

@@ -61,7 +61,7 @@ struct td_ctx {
   int n_items = 0, n_pairs = 0;
   size_t items_cap = 0, pairs_cap = 0;
   float *att_o = nullptr, *att_ml = nullptr;
-  float *part = nullptr;     // split-K partial products of the tiled GEMMs
+  float *part = nullptr;     // split-K partial products
   size_t part_cap = 0;       // floats
   size_t att_cap_rows = 0;   // capacity in partial rows (items * R)
 
@@ -164,9 +164,17 @@ GemmPlan plan_gemm(int M, int N, int K, bool vstat, int dtype) {
     p.nt = M <= 16 ? (N % 256 == 0 ? 2 : 1) : (N % 256 == 0 ? 4 : (N % 128 == 0 ? 2 : 1));
   } else {
     const int KT = K / 32, tiles = N / 16;
-    if (tiles > 256 && dtype == TD_BF16 && tiles % 2 == 0) {
+    const int pairs = tiles / 2;
+    if (dtype == TD_BF16 && tiles % 2 == 0 && (pairs > 128 || KT >= 2 * 64)) {
+      // Two column tiles per wave, four waves.  Few column pairs over a deep K (the MLP
+      // down projection) split K over up to 256 workgroups, at least 64 k-tiles each:
+      // each CU then streams a short run of K and re-reads that much of the
+      // activations instead of all of it, and a second kernel sums the partials.
+      // (Measured: the extra launch costs more than it saves for shallower K.)
       p.nt = 2;
       p.nw = 4;
+      if (pairs <= 128)
+        while (pairs * p.splits < 256 && KT / (2 * p.splits) >= 64) p.splits *= 2;
     } else {
       p.nt = 1;
       p.nw = tiles <= 256 ? (M <= 16 ? 16 : 8) : 4;
@@ -270,7 +278,7 @@ td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const
   a.gain_next = gain_next;
   a.ssq_out = c->ssq;
   a.done = c->st.done;
-  a.splits = p.tile ? p.splits : 1;
+  a.splits = epi == EPI_VSTAT ? 1 : p.splits;
   a.part = c->part;
   if (p.tile) {
     if (epi != EPI_VSTAT) TD_TRY(prof_mark(c, TD_PROF_GEMM, true));
@@ -535,7 +543,7 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
     const GemmPlan *plans[] = {&c->p_qkv, &c->p_wo, &c->p_w1, &c->p_w2};
     const int widths[] = {c->Nqkv, d, F, d};
     for (int i = 0; i < 4; ++i)
-      if (plans[i]->tile && plans[i]->splits > 1) need = std::max(need, (size_t)plans[i]->splits * M * widths[i]);
+      if (plans[i]->splits > 1) need = std::max(need, (size_t)plans[i]->splits * M * widths[i]);
     TD_TRY(grow(&c->part, c->part_cap, need, sizeof(float)));
   }
   c->offsets.assign(off, off + n_seqs + 1);

@@ -49,8 +49,8 @@ struct GemmArgs {
   const float *inv_temp;   // VSTAT: [rows] inverse temperature, or nullptr (1)
   VStat *vpart;            // VSTAT: [row index][grid.x] statistics of each column group
   float *logits;           // VSTAT: optional capture [rows][N] of the raw logits
-  const int *done;         // skip the launch when *done != 0 (nullable)
-  int splits;              // tiled kernel: K split over this many workgroups (1: none)
+  const int *done;         // skip the launch when *done != 0 (required: read before the operands)
+  int splits;              // K split over this many workgroups (1: none; not VSTAT)
   float *part;             // splits > 1: [splits][M][N] fp32 partial products (workspace)
 };
 // The LM head (EPI_VSTAT): nw waves x nt column tiles per workgroup, each wave streaming
@@ -67,6 +67,9 @@ bool gemm_tile_supported(int dtype, int M, int N, int K);
 int gemm_tile_slices(int N);
 int gemm_tile_splits(int M, int N, int K);   // splits that give the grid ~2 workgroups per CU
 hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a, hipStream_t s);
+// Sum of a.splits fp32 partials part[split][M][N] in split order, then the row scale and
+// the epilogue (STORE, GELU or RESID) of the projection.
+hipError_t launch_split_reduce(int epi, bool norm, const GemmArgs &a, hipStream_t s);
 // One 16-column tile per workgroup, its nw waves splitting K with all weights in flight;
 // used for the layer projections (STORE, GELU, RESID).
 hipError_t launch_gemm_wk(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s);

@@ -1,8 +1,9 @@
 """GPU parity on batched towers: many sequences per call, ragged prefixes, GQA, B = 8/16/32.
 
 Small towers (oracle on every sequence) exercise the multi-tile GEMM and LM-head paths
-(M = n*B > 16, and the tiled kernel at M >= 128), ragged split-K attention with empty
-and one-token prefixes, grouped-query heads and every block size.  The full-size batched workloads (ragged 32 x U{512..8192};
+(M = n*B > 16, K split over workgroups, and the tiled kernel at M >= 128), ragged split-K
+attention with empty and one-token prefixes, grouped-query heads and every block size.
+The full-size batched workloads (ragged 32 x U{512..8192};
 4 x 65536 GQA on the d 4096 tower; 64 x U{1024..4096} at B 8/16/32 and gamma 0.5/0.8/0.95)
 run the whole batch on the GPU and check a fixed sample of sequences against the oracle:
 sequences never interact (each has its own prefix, block and loop), so the oracle of a
@@ -105,6 +106,11 @@ SMALL = {
     # M = 72, head dim 128, block 8.
     "bf16_n9_b8": dict(n=9, plen=("uniform", 0, 100), B=8, d=256, H=4, Hkv=4, hd=128, L=2, F=512, V=4096,
                        dtype="bf16"),
+    # M = 80, MLP down projection 512 x 4096: K split over two workgroups per column
+    # group (fp32 partials summed in split order by a second kernel), two row tiles, the
+    # second partial.
+    "bf16_n5_b16_split": dict(n=5, plen=("uniform", 0, 300), B=16, d=512, H=4, Hkv=2, hd=128, L=2, F=4096,
+                              V=4096, dtype="bf16"),
     # M = 144: the tiled many-row GEMM (128-row tiles, the second one partial) for every
     # projection and the LM head.
     "bf16_n9_b16_tiled": dict(n=9, plen=("uniform", 0, 200), B=16, d=256, H=4, Hkv=2, hd=64, L=2, F=1024,
