@@ -59,7 +59,21 @@ def source_hash(*names) -> str:
 
 
 LMHEAD_SOURCES = ("k_gemm.hip", "td_device.h", "td_kernels.h")
-LMHEAD_KERNEL = "lmhead_kernel"
+# Names of the LM-head kernels: activations staged in LDS (at most 16 rows, d <= 2048,
+# the bench workload) and the row-list variant.
+LMHEAD_KERNELS = ("lmhead_lds_kernel", "lmhead_kernel")
+
+
+def lmhead_kernel_name(w) -> str:
+    """The LM-head kernel the library plans for this workload's first step (all rows masked)."""
+    M = w.n * w.B
+    if w.dtype == "bf16" and M <= 16 and w.d <= 2048 and w.V % 512 == 0:
+        k = "lmhead_lds_kernel (activations staged in LDS)"
+    elif w.dtype == "bf16" and M >= 128 and w.V % 128 == 0 and w.d % 32 == 0:
+        k = "gemm_tile_kernel<VSTAT> (128x128 MFMA tiles)"
+    else:
+        k = "lmhead_kernel (row-list gather)"
+    return k + ": LM head GEMM + fused tau-scaled vocab max/sumexp/argmax"
 
 
 def traffic_path(workload: str) -> str:
@@ -96,7 +110,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, calib_mb: int) 
                     continue
                 v = float(row["Counter_Value"]) * 1024.0
                 k = row["Kernel_Name"]
-                if LMHEAD_KERNEL in k:
+                if any(n in k for n in LMHEAD_KERNELS):
                     lm.append(v)
                 elif "copyBuffer" in k:
                     blit.append(v)
@@ -109,7 +123,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, calib_mb: int) 
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         lm, blit, elem = per_dispatch(path, counter)
         if not lm or not elem:
-            raise SystemExit(f"{path}: no {LMHEAD_KERNEL} or calibration dispatches with {counter}")
+            raise SystemExit(f"{path}: no LM-head or calibration dispatches with {counter}")
         factor = calib / max(elem)
         work = sorted(v for v in lm if v > 0.5 * max(lm)) if name == "fetch" else sorted(lm)
         if name == "fetch":
@@ -118,7 +132,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, calib_mb: int) 
         out[name] = dict(counter=counter, raw_bytes_per_launch=raw, calibration_kernel="elementwise (16 B per lane)",
                          calibration_raw_bytes=max(elem), factor=factor, bytes_per_launch=raw * factor,
                          dispatches=len(work), blit_copy_raw_bytes=max(blit) if blit else None)
-    rec = dict(kernel=LMHEAD_KERNEL, workload=workload, source_sha256_16=source_hash(*LMHEAD_SOURCES),
+    rec = dict(kernel="/".join(LMHEAD_KERNELS), workload=workload, source_sha256_16=source_hash(*LMHEAD_SOURCES),
                calibration_copy_bytes=calib, fetch=out["fetch"], write=out["write"],
                hbm_bytes_per_launch=out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"],
                working_launches=fetch_work)
@@ -300,7 +314,7 @@ def main():
                    "vocab": w.V},
         "denoise_steps_per_s": round(steps_per_s, 3),
         "denoise_steps_per_block": S,
-        "roofline": {"kernel": "lmhead_kernel (LM head GEMM + fused tau-scaled vocab max/sumexp/argmax)",
+        "roofline": {"kernel": lmhead_kernel_name(w),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": lm_bytes, "avg_launch_ms": round(lm_avg_ms, 5),

@@ -159,6 +159,139 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- few rows, activations in LDS
+// At most 16 rows and a contraction of at most 2048 (bf16 towers): the activation block
+// (rows 0..15 in fragment layout: K / 32 slots of 2 KiB, one contiguous run) fits in
+// LDS.  Each workgroup copies it there once, with loads issued before its first weights,
+// and its 16 waves then stream only weights -- PASS k-tiles of two column tiles each in
+// flight -- taking the activation fragments from LDS instead of re-reading them from L2
+// per wave.  Every row is multiplied (the MFMA is 16 rows wide either way); statistics
+// are written only for rows still masked, at their position in the row list.  The
+// arithmetic of each row and column is that of lmhead_kernel.
+constexpr int LDS_NW = 16, LDS_NT = 2, LDS_KMAX = 2048;
+
+__global__ __launch_bounds__(64 * LDS_NW) void lmhead_lds_kernel(GemmArgs a) {
+  constexpr int NW = LDS_NW, NT = LDS_NT, KTMAX = LDS_KMAX / 32;
+  constexpr int PASS = 10;                        // weight k-tiles in flight per wave (measured: 8 and 6 slower)
+  constexpr int APT = KTMAX * 128 / (64 * NW);    // 16-byte words of the block per thread
+  __shared__ u32x4_t s_a[KTMAX * 128];            // [k-tile][lane][hi, lo]
+  __shared__ float s_rs[16], s_tau[16];
+  __shared__ int s_pos[16];
+  __shared__ VStat s_stat[NW][16];
+
+  // The loop-exit flag first (see lmhead_kernel), then the small per-row values, the
+  // activation block and the first weights.
+  const int stop = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_sched_barrier(0);
+  const int M = a.M, KT = a.K >> 5;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int ntw = (blockIdx.x * NW + wave) * NT;   // this wave's first column tile
+
+  const int r16 = min((int)(threadIdx.x & 15), M - 1);
+  const int pos = a.rowpos[r16];
+  const float tau = a.inv_temp ? a.inv_temp[r16] : 1.0f;
+  const int srow = min(wave, M - 1);   // wave w sums the partial squares of row w
+  const float sq0 = a.ssq[(size_t)min(lane, a.norm_nparts - 1) * a.ld_ssq + srow];
+  const float sq1 = a.ssq[(size_t)min(lane + 64, a.norm_nparts - 1) * a.ld_ssq + srow];
+
+  const u32x4_t *ga = reinterpret_cast<const u32x4_t *>(a.A);
+  const int nwords = KT * 128;
+  u32x4_t ra[APT];
+#pragma unroll
+  for (int i = 0; i < APT; ++i) ra[i] = ga[min((int)threadIdx.x + 64 * NW * i, nwords - 1)];
+
+  const bf16_t *Wl = reinterpret_cast<const bf16_t *>(a.Wp) + ((size_t)ntw * KT) * 512 + (size_t)lane * 8;
+  Frag<bf16_t> wb[PASS][NT];
+  auto fill = [&](int i, int kt) __attribute__((always_inline)) {
+    const int k = min(kt, KT - 1);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) wb[i][j].load(Wl + ((size_t)j * KT + k) * 512);
+  };
+#pragma unroll
+  for (int i = 0; i < PASS; ++i) fill(i, i);
+  asm volatile("" ::: "memory");   // the loads above are issued before the test below
+  if (stop) return;
+
+  // Waiting for the block waits for nothing issued after it: the weights stay in flight.
+#pragma unroll
+  for (int i = 0; i < APT; ++i) s_a[threadIdx.x + 64 * NW * i] = ra[i];
+  if (threadIdx.x < 16) {
+    s_pos[threadIdx.x] = threadIdx.x < (unsigned)M ? pos : -1;
+    s_tau[threadIdx.x] = tau;
+  }
+  {
+    float sq = (lane < a.norm_nparts ? sq0 : 0.f) + (lane + 64 < a.norm_nparts ? sq1 : 0.f);
+    sq = sum_lanes<64>(sq);
+    if (lane == 0) s_rs[wave] = 1.0f / sqrtf(sq / (float)a.K + a.norm_eps);
+  }
+  __syncthreads();
+
+  auto afrag = [&](int kt) __attribute__((always_inline)) {
+    const u32x4_t *p = s_a + ((size_t)min(kt, KT - 1) * 64 + lane) * 2;
+    AFrag<bf16_t> f;
+    f.hi.raw = __builtin_bit_cast(uint4, p[0]);
+    f.lo.raw = __builtin_bit_cast(uint4, p[1]);
+    return f;
+  };
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = zero4();
+  AFrag<bf16_t> xa = afrag(0);   // one k-tile ahead of its MFMAs
+  int p0 = 0;
+  for (; p0 + PASS < KT; p0 += PASS) {
+#pragma unroll
+    for (int i = 0; i < PASS; ++i) {
+      const AFrag<bf16_t> cur = xa;
+      xa = afrag(p0 + i + 1);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = mma_a(cur, wb[i][j], acc[j]);
+      fill(i, p0 + PASS + i);
+      __builtin_amdgcn_sched_barrier(0);   // keep the refill right behind its MFMAs
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PASS; ++i) {
+    if (p0 + i < KT) {
+      const AFrag<bf16_t> cur = xa;
+      xa = afrag(p0 + i + 1);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = mma_a(cur, wb[i][j], acc[j]);
+    }
+  }
+
+  // Statistics of this wave's 16 NT columns per row, then of the workgroup's columns.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * g + r;
+    const bool live = s_pos[row] >= 0;
+    const float rs = s_rs[row], tr = s_tau[row];
+    VStat v{-INFINITY, 0.f, 0x7FFFFFFF};
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int col = (ntw + j) * 16 + l16;
+      const float z = acc[j][r] * rs;
+      float sv = -INFINITY;
+      if (live) {
+        if (a.logits) a.logits[(size_t)row * a.N + col] = z;
+        sv = tr * z;
+      }
+      const float mx = max16(sv);
+      const float se = sum16(live ? __expf(sv - mx) : 0.f);
+      const int am = min16((live && sv == mx) ? col : 0x7FFFFFFF);
+      v = vstat_merge(v, VStat{mx, se, am});
+    }
+    if (l16 == 0) s_stat[wave][row] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 16 && s_pos[threadIdx.x] >= 0) {
+    VStat v = s_stat[0][threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v = vstat_merge(v, s_stat[w][threadIdx.x]);
+    a.vpart[(size_t)s_pos[threadIdx.x] * gridDim.x + blockIdx.x] = v;
+  }
+}
+
 template <typename T, int MT, int NW>
 hipError_t launch_nw(const GemmArgs &a, dim3 grid, hipStream_t s) {
   if (a.nt == 1) hipLaunchKernelGGL((lmhead_kernel<T, MT, 1, NW>), grid, dim3(64 * NW), 0, s, a);
@@ -185,6 +318,12 @@ hipError_t launch_gemm(int dtype, int epi, bool norm, const GemmArgs &a, hipStre
   if (epi != EPI_VSTAT || !norm || a.ssq == nullptr || a.norm_nparts <= 0) return hipErrorInvalidValue;
   if (a.done == nullptr) return hipErrorInvalidValue;
   if (a.nt < 1 || a.nw < 1 || a.N % (16 * a.nt * a.nw) || a.K % 32 || a.M <= 0) return hipErrorInvalidValue;
+  if (a.nt == LDS_NT && a.nw == LDS_NW) {   // few rows, activations staged in LDS
+    if (dtype != DT_BF16 || a.M > 16 || a.K > LDS_KMAX || a.rowpos == nullptr || a.norm_nparts > 128)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lmhead_lds_kernel, dim3(lmhead_slices(a.N, a.nt, a.nw)), dim3(64 * LDS_NW), 0, s, a);
+    return hipGetLastError();
+  }
   const int mt = a.M <= 16 ? 1 : 4;
   const dim3 grid(lmhead_slices(a.N, a.nt, a.nw), 1, (a.M + 16 * mt - 1) / (16 * mt));
   if (dtype == DT_BF16) return mt == 1 ? launch_t<bf16_t, 1>(a, grid, s) : launch_t<bf16_t, 4>(a, grid, s);

@@ -158,8 +158,14 @@ GemmPlan plan_gemm(int M, int N, int K, bool vstat, int dtype) {
     return p;
   }
   if (vstat) {
-    // One row tile: 8 waves x 2 column tiles (measured best at V = 131072, d = 2048);
-    // four row tiles need more registers per k-tile: 4 waves x 4 column tiles.
+    // At most 16 rows of a bf16 tower with d <= 2048: the activations staged in LDS, 16
+    // waves x 2 column tiles per workgroup.  Otherwise one row tile: 8 waves x 2 column
+    // tiles; four row tiles need more registers per k-tile: 4 waves x 4 column tiles.
+    if (M <= 16 && K <= 2048 && N % 512 == 0 && dtype == TD_BF16) {
+      p.nw = 16;
+      p.nt = 2;
+      return p;
+    }
     p.nw = M <= 16 && N % 256 == 0 ? 8 : 4;
     p.nt = M <= 16 ? (N % 256 == 0 ? 2 : 1) : (N % 256 == 0 ? 4 : (N % 128 == 0 ? 2 : 1));
   } else {
@@ -313,6 +319,7 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   }
   GemmArgs lm{};
   lm.rowlist = c->st.rowlist;
+  lm.rowpos = c->st.rowpos;
   lm.n_rows = c->st.n_rows;
   lm.inv_temp = inv_temp;
   lm.vpart = c->vpart;

@@ -38,6 +38,7 @@ struct GemmArgs {
   int norm_nparts, ld_ssq;
   float norm_eps;
   const int *rowlist;      // optional row gather: GEMM row r is activation row rowlist[r]
+  const int *rowpos;       // VSTAT, few-row kernel: position of each row in the row list, or -1
   const int *n_rows;       // optional live row count (device)
   const void *Wp;          // packed weight [N][K]
   int nt;                  // 16-column tiles per wave (launch_gemm: 1, 2, 4, 8) or per workgroup (launch_gemm_wk: 1, 2, 4)

@@ -111,6 +111,13 @@ SMALL = {
     # second partial.
     "bf16_n5_b16_split": dict(n=5, plen=("uniform", 0, 300), B=16, d=512, H=4, Hkv=2, hd=128, L=2, F=4096,
                               V=4096, dtype="bf16"),
+    # At most 16 rows: the LM head with the activations staged in LDS, all rows multiplied
+    # and statistics written for the masked ones at their row-list position; M = 8 (rows
+    # 8..15 padding) and two sequences in M = 16.
+    "bf16_n1_b8_lds": dict(n=1, plen=("uniform", 1, 300), B=8, d=256, H=4, Hkv=4, hd=64, L=2, F=1024, V=4096,
+                           dtype="bf16"),
+    "bf16_n2_b8_lds": dict(n=2, plen=("uniform", 0, 300), B=8, d=512, H=4, Hkv=2, hd=128, L=2, F=2048, V=4096,
+                           dtype="bf16"),
     # M = 144: the tiled many-row GEMM (128-row tiles, the second one partial) for every
     # projection and the LM head.
     "bf16_n9_b16_tiled": dict(n=9, plen=("uniform", 0, 200), B=16, d=256, H=4, Hkv=2, hd=64, L=2, F=1024,
