@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the path runs in the HIP kernels behind the C
 ABI.  torch tensors provide device memory and the HIP stream.  Importing this package
-raises if libtd.so has not been built (build with `python -m block_diffusion_lm_step_amd.build`
+raises if libtd.so has not been built (build with `python block_diffusion_lm_step_amd/build.py`
 or `__graft_entry__.build()`); there is no fallback implementation.
 """
 from __future__ import annotations
@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtd.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m block_diffusion_lm_step_amd.build` first")
+    raise ImportError(f"{LIB_PATH} is not built; run `python block_diffusion_lm_step_amd/build.py` first")
 
 # torch first: its HIP runtime is then the one libtd binds to, the same instance that
 # owns the tensors and streams handed over (loading libtd first brings in a second
@@ -44,30 +44,37 @@ class TdWeights(ctypes.Structure):
 
 
 _CTX = c_void_p
-lib.td_create.argtypes = [POINTER(TdConfig), POINTER(TdWeights), c_void_p, POINTER(_CTX)]
-lib.td_set_prefix.argtypes = [_CTX, c_int32, POINTER(c_int64), POINTER(c_void_p), POINTER(c_void_p)]
-lib.td_denoise_step.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_void_p]
-lib.td_generate_block.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
-lib.td_debug_attention.argtypes = [_CTX, c_int32, c_void_p, c_void_p]
-lib.td_sync.argtypes = [_CTX]
-lib.td_profile_begin.argtypes = [_CTX, c_int32]
-lib.td_profile_begin.restype = c_int
-lib.td_profile_end.argtypes = [_CTX, POINTER(c_float), c_int32]
-lib.td_profile_end.restype = c_int32
-lib.td_kernels_per_step.argtypes = [_CTX]
-lib.td_kernels_per_step.restype = c_int32
-lib.td_destroy.argtypes = [_CTX]
-lib.td_destroy.restype = None
-lib.td_last_error.argtypes = [_CTX]
-lib.td_last_error.restype = c_char_p
-lib.td_version.restype = c_char_p
-for _f in ("td_create", "td_set_prefix", "td_denoise_step", "td_generate_block", "td_debug_attention", "td_sync"):
-    getattr(lib, _f).restype = c_int
+try:
+    lib.td_create.argtypes = [POINTER(TdConfig), POINTER(TdWeights), c_void_p, POINTER(_CTX)]
+    lib.td_set_prefix.argtypes = [_CTX, c_int32, POINTER(c_int64), POINTER(c_void_p), POINTER(c_void_p)]
+    lib.td_denoise_step.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.td_generate_block.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
+    lib.td_set_commit_rule.argtypes = [_CTX, c_int32, c_int32]
+    lib.td_debug_attention.argtypes = [_CTX, c_int32, c_void_p, c_void_p]
+    lib.td_sync.argtypes = [_CTX]
+    lib.td_profile_begin.argtypes = [_CTX, c_int32]
+    lib.td_profile_begin.restype = c_int
+    lib.td_profile_end.argtypes = [_CTX, POINTER(c_float), c_int32]
+    lib.td_profile_end.restype = c_int32
+    lib.td_kernels_per_step.argtypes = [_CTX]
+    lib.td_kernels_per_step.restype = c_int32
+    lib.td_destroy.argtypes = [_CTX]
+    lib.td_destroy.restype = None
+    lib.td_last_error.argtypes = [_CTX]
+    lib.td_last_error.restype = c_char_p
+    lib.td_version.restype = c_char_p
+    for _f in ("td_create", "td_set_prefix", "td_denoise_step", "td_generate_block", "td_set_commit_rule",
+               "td_debug_attention", "td_sync"):
+        getattr(lib, _f).restype = c_int
+except AttributeError as e:   # a library built from older sources
+    raise ImportError(f"{LIB_PATH} is stale ({e}); rebuild with `python block_diffusion_lm_step_amd/build.py`") from e
 
 # Every symbol the C header declares.
-EXPORTED = ("td_create", "td_set_prefix", "td_denoise_step", "td_generate_block", "td_debug_attention", "td_sync",
-            "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_destroy", "td_last_error", "td_version")
+EXPORTED = ("td_create", "td_set_prefix", "td_denoise_step", "td_generate_block", "td_set_commit_rule",
+            "td_debug_attention", "td_sync", "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_destroy",
+            "td_last_error", "td_version")
 TD_PROF_OFF, TD_PROF_LMHEAD, TD_PROF_GEMM, TD_PROF_ATTENTION, TD_PROF_STEP = range(5)
+TD_RULE_THRESHOLD, TD_RULE_LEFT_TO_RIGHT = range(2)
 
 
 class TdError(RuntimeError):
@@ -138,6 +145,9 @@ class Denoiser:
     def generate_block(self, tokens, committed, inv_temp, gamma: float, steps=None, commit_step=None) -> None:
         self._check(lib.td_generate_block(self._ctx, _ptr(tokens), _ptr(committed), _ptr(inv_temp), float(gamma),
                                           _ptr(steps), _ptr(commit_step)))
+
+    def set_commit_rule(self, rule: int, min_adopt: int = 1) -> None:
+        self._check(lib.td_set_commit_rule(self._ctx, int(rule), int(min_adopt)))
 
     def debug_attention(self, layer: int, qkv, o) -> None:
         self._check(lib.td_debug_attention(self._ctx, int(layer), _ptr(qkv), _ptr(o)))

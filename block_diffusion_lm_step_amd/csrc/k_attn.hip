@@ -47,6 +47,9 @@ namespace td {
 namespace {
 
 constexpr int SUB = KV_PAGE;   // keys per page
+// Pages in flight per wave in the few-row kernel (measured: three were slower at every
+// shape, batch 1 to 64 x 4096).
+constexpr int DIRECT_DEPTH = 2;
 constexpr int BMAX = 32;       // largest block size
 
 // Element offset, within a K page block, of MFMA row i of S^T half h, hd chunk c (32
@@ -247,12 +250,20 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
 }
 
 // Few-row shape (R <= 32, multi-head attention): the NW = 4 waves take pages w, w + 4,
-// ..., operands straight from HBM, each wave with two pages in flight.  (Eight waves, two
+// ..., operands straight from HBM, each wave with DEPTH pages in flight (a ring).  (Eight waves, two
 // per SIMD, measured slower: their registers spill.)  The pair's first item also attends
 // the block's own keys: their loads are issued before the first pages', so the fp32
 // block pass (block_item's arithmetic, into LDS) runs while the pages are in flight, and
 // its state is merged after the waves' in the fixed order waves 0..NW-1, block.
-template <typename T, int HD, int RT, int NW>
+template <int N, typename F>
+TD_DEV void static_for(F &&f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+template <typename T, int HD, int RT, int NW, int DEPTH>
 __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
   constexpr int NT = 64 * NW, HC = HD / 32, OT = HD / 16, EPT = HD / 16, KPT = BMAX * HD / NT;
   constexpr int MERGE = (NW + 1) * RT * 16 * (HD + 2);   // waves' and the block's states
@@ -314,8 +325,8 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
     for (int t = 0; t < OT; ++t) o[rt][t] = zero4();
   }
 
-  AFrag<T> qf[RT][HC];               // filled once the first pages are in flight
-  Frag<T> kf[2][2][HC], vf[2][OT];   // [buffer] page operands
+  AFrag<T> qf[RT][HC];                       // filled once the first pages are in flight
+  Frag<T> kf[DEPTH][2][HC], vf[DEPTH][OT];   // [buffer] page operands
   auto fetch = [&](auto bufc, int pg) __attribute__((always_inline)) {
     constexpr int b = decltype(bufc)::value;
     if (pg < npg) {
@@ -342,11 +353,9 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
                            [&](int t) -> const Frag<T> & { return vf[b][t]; }, qf[rt], a.scale, kvalid, g,
                            m_run[rt], l_run[rt], o[rt]);
   };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  int pg = wave;
+  const int pg0 = wave;
   __builtin_amdgcn_sched_barrier(0);   // the block and query loads stay ahead of the pages'
-  fetch(B0{}, pg);
+  static_for<DEPTH - 1>([&](auto sc) { fetch(sc, pg0 + decltype(sc)::value * NW); });
   __builtin_amdgcn_sched_barrier(0);
   q_frags<T, HD, RT>(a, 0, l16, qraw, qf);
 
@@ -397,14 +406,15 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
     }
   }
 
-  while (pg < npg) {
-    fetch(B1{}, pg + NW);
-    consume(B0{}, pg);
-    pg += NW;
-    if (pg >= npg) break;
-    fetch(B0{}, pg + NW);
-    consume(B1{}, pg);
-    pg += NW;
+  // Ring of DEPTH pages per wave: page pg + s * NW sits in buffer s; the page DEPTH - 1
+  // steps ahead is requested before each page is consumed.
+  for (int pg = pg0; pg < npg; pg += DEPTH * NW) {
+    static_for<DEPTH>([&](auto sc) {
+      constexpr int st = decltype(sc)::value;
+      using Ahead = std::integral_constant<int, (st + DEPTH - 1) % DEPTH>;
+      fetch(Ahead{}, pg + (st + DEPTH - 1) * NW);
+      if (pg + st * NW < npg) consume(sc, pg + st * NW);
+    });
   }
 
   // Merge the waves' states (wave order), then the block's, through LDS.
@@ -643,9 +653,9 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 template <typename T, int HD>
 hipError_t launch_hd(const AttnArgs &a, hipStream_t s) {
   if (a.R <= 16) {
-    hipLaunchKernelGGL((attn_direct_kernel<T, HD, 1, 4>), dim3(a.n_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_direct_kernel<T, HD, 1, 4, DIRECT_DEPTH>), dim3(a.n_items), dim3(256), 0, s, a);
   } else if (a.R <= ATTN_FEW_ROWS) {
-    hipLaunchKernelGGL((attn_direct_kernel<T, HD, 2, 4>), dim3(a.n_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_direct_kernel<T, HD, 2, 4, DIRECT_DEPTH>), dim3(a.n_items), dim3(256), 0, s, a);
   } else {   // one 16-row tile per wave, 128 rows per workgroup (more would spill)
     hipLaunchKernelGGL((attn_group_kernel<T, HD, 1>), dim3(a.n_items * ((a.R + 127) / 128)), dim3(512), 0, s, a);
   }

@@ -10,8 +10,10 @@
 // PredNext "人工知能は拡散言語モデルの夢を見るか？", section 拡散言語モデルで推論するには
 // (adopt masked positions whose confidence clears the threshold, the others stay
 // [MASK]) with the fixed fallback of adopting the single most confident masked position
-// when none clears it, and the list of still-masked rows is rebuilt for the next step,
-// so the block loop needs no host round-trip.  Two shapes:
+// when none clears it -- or one of the variants chosen by td_set_commit_rule: the
+// min_adopt most confident forced (the same step names forcing the top few), or the
+// lowest masked position only (the mock-AR mode) -- and the list of still-masked rows
+// is rebuilt for the next step, so the block loop needs no host round-trip.  Two shapes:
 //   * few rows (the block sizes of one or a few sequences): ONE workgroup merges every
 //     row (a wave per row, eight groups per lane in flight) and commits: no
 //     cross-workgroup synchronisation at all;
@@ -43,11 +45,12 @@ TD_DEV void commit_all(const CommitArgs &a, int *s_wave) {
     const bool masked = in && !a.committed[r] && pos >= 0;   // pos < 0: row rejected by the state check
     const float c = masked ? a.conf_row[pos] : -INFINITY;
     const int arg = masked ? a.arg_row[pos] : 0;
-    int clear = (masked && c >= a.gamma) ? 1 : 0, any = masked ? 1 : 0;
+    // Butterfly over the sequence's B lanes: any position masked, the most confident
+    // masked position (lowest on ties), the lowest masked position.
+    int any = masked ? 1 : 0;
     float best = c;
-    int best_p = masked ? p : 0x7FFFFFFF;
+    int best_p = masked ? p : 0x7FFFFFFF, first_p = best_p;
     for (int o = 1; o < a.B; o <<= 1) {
-      clear |= __shfl_xor(clear, o);
       any |= __shfl_xor(any, o);
       const float bo = __shfl_xor(best, o);
       const int po = __shfl_xor(best_p, o);
@@ -55,12 +58,28 @@ TD_DEV void commit_all(const CommitArgs &a, int *s_wave) {
         best = bo;
         best_p = po;
       }
+      first_p = min(first_p, __shfl_xor(first_p, o));
     }
     if (masked) {
       if (a.conf_out) a.conf_out[r] = c;
       if (a.argmax_out) a.argmax_out[r] = arg;
     }
-    const bool adopt = masked && (clear ? (c >= a.gamma) : (p == best_p));
+    bool adopt;
+    if (a.rule == RULE_LEFT_TO_RIGHT) {
+      adopt = masked && p == first_p;
+    } else if (a.min_adopt <= 1) {   // the most confident one is forced; it clears gamma if any does
+      adopt = masked && (c >= a.gamma || p == best_p);
+    } else {
+      // Rank among the sequence's masked positions by (confidence descending, position
+      // ascending); unmasked lanes hold -inf and never outrank a masked one.
+      const int lane0 = (int)(threadIdx.x & 63) - p;   // lane of the sequence's position 0
+      int rank = 0;
+      for (int j = 0; j < a.B; ++j) {
+        const float cj = __shfl(c, lane0 + j);
+        rank += (cj > c || (cj == c && j < p)) ? 1 : 0;
+      }
+      adopt = masked && (c >= a.gamma || rank < a.min_adopt);
+    }
     if (adopt) {
       a.tokens[r] = arg;
       a.committed[r] = 1;

@@ -39,6 +39,9 @@ struct td_ctx {
   void *tok_emb = nullptr, *pos_emb = nullptr, *final_norm = nullptr, *lm_head = nullptr;
   std::vector<void *> attn_norm, mlp_norm, wqkv, wo, w1, w2;
 
+  // adoption rule (td_set_commit_rule)
+  int rule = RULE_THRESHOLD, min_adopt = 1;
+
   // workspace
   int Mmax = 0, Nqkv = 0;
   float *x = nullptr, *ssq = nullptr, *conf_row = nullptr;
@@ -338,6 +341,8 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   ca.tokens = tokens;
   ca.committed = committed;
   ca.gamma = gamma;
+  ca.rule = c->rule;
+  ca.min_adopt = c->min_adopt;
   ca.newly = newly;
   ca.conf_out = conf_out;
   ca.argmax_out = argmax_out;
@@ -586,6 +591,21 @@ td_status td_generate_block(td_ctx *c, int32_t *tokens, uint8_t *committed, cons
   for (int s = 0; s < g.block_size; ++s)
     TD_TRY(enqueue_step(c, tokens, committed, inv_temp, gamma, nullptr, nullptr, nullptr, nullptr, steps,
                         commit_step));
+  return TD_OK;
+}
+
+td_status td_set_commit_rule(td_ctx *c, int32_t rule, int32_t min_adopt) {
+  TD_TRY(check_ctx(c));
+  if (rule == TD_RULE_LEFT_TO_RIGHT) {
+    c->rule = RULE_LEFT_TO_RIGHT;
+    c->min_adopt = 1;
+    return TD_OK;
+  }
+  if (rule != TD_RULE_THRESHOLD) return fail(c, TD_EINVAL, "unknown commit rule %d", rule);
+  if (min_adopt < 1 || min_adopt > c->cfg.block_size)
+    return fail(c, TD_EINVAL, "min_adopt must be in [1, block_size=%d]", c->cfg.block_size);
+  c->rule = RULE_THRESHOLD;
+  c->min_adopt = min_adopt;
   return TD_OK;
 }
 

@@ -140,8 +140,10 @@ hipError_t launch_embed(int dtype, const int *tokens, const void *E, const void 
                         float *ssq, void *x_afl, int M, int B, int d, int V, StepState st, hipStream_t s);
 
 // ---------------------------------------------------------------- vocab merge + commit
+enum { RULE_THRESHOLD = 0, RULE_LEFT_TO_RIGHT = 1 };   // = td_commit_rule
 struct CommitArgs {
   int V, B, n, nslices;
+  int rule, min_adopt;             // adoption rule (td_set_commit_rule)
   const VStat *vpart;              // [row index][nslices]
   float *conf_row; int *arg_row;   // [M] per-row results (indexed by position in rowlist)
   int *tokens; uint8_t *committed;

@@ -137,6 +137,28 @@ td_status td_denoise_step(td_ctx *ctx, int32_t *tokens, uint8_t *committed, cons
 td_status td_generate_block(td_ctx *ctx, int32_t *tokens, uint8_t *committed, const float *inv_temp,
                             float gamma, int32_t *steps, int8_t *commit_step);
 
+/* Adoption rules for td_set_commit_rule. */
+typedef enum {
+  TD_RULE_THRESHOLD = 0,     /* conf >= gamma, plus the min_adopt most confident */
+  TD_RULE_LEFT_TO_RIGHT = 1  /* the lowest masked position, one per step */
+} td_commit_rule;
+
+/* Choose the adoption rule of every later td_denoise_step / td_generate_block on this
+ * ctx (the default is TD_RULE_THRESHOLD with min_adopt 1, the rule described at the top).
+ *  TD_RULE_THRESHOLD: adopt the masked positions whose confidence is at least gamma,
+ *    together with the min_adopt most confident masked positions (lowest position on
+ *    ties; every masked position if fewer remain).  PredNext, section
+ *    拡散言語モデルで推論するには, step 3 names forcing the top few positions as an
+ *    alternative to the threshold; min_adopt = 1 is the single-position fallback, and
+ *    gamma > 1 with min_adopt = k adopts exactly k per step.
+ *  TD_RULE_LEFT_TO_RIGHT: adopt only the lowest masked position of each sequence (its
+ *    prediction), one per step, B steps per block: the mock-AR mode of dzen.guru, section
+ *    "Что нового" (one token per step through the diffusion tower), read as
+ *    autoregressive order.  gamma and min_adopt are ignored.
+ *  min_adopt: 1 .. block_size (TD_RULE_THRESHOLD); any value for TD_RULE_LEFT_TO_RIGHT.
+ * Errors: TD_EINVAL for an unknown rule or min_adopt outside 1 .. block_size. */
+td_status td_set_commit_rule(td_ctx *ctx, int32_t rule, int32_t min_adopt);
+
 /* Debug hook: run the layer-`layer` attention (prefix split-K + in-block keys + merge)
  * on caller-provided projections qkv [n*B][(n_heads + 2*n_kv_heads)*head_dim] (q, then
  * k, then v of the block; fp32, the precision the step carries activations in) and

@@ -20,6 +20,8 @@ from .denoise import (  # noqa: F401
     OracleTower,
     vocab_reduce,
     commit_rule,
+    RULE_THRESHOLD,
+    RULE_LEFT_TO_RIGHT,
     StepResult,
     oracle_step,
     oracle_generate,

@@ -31,7 +31,11 @@ What is computed, and where it comes from:
   least gamma; if none is, adopt the single most confident masked position
   (lowest position on ties); the rest stay [MASK]; repeat until no [MASK] is left.
   Adopted tokens never change.  Every step adopts at least one position, so a
-  block of B ends in at most B steps.
+  block of B ends in at most B steps.  Variants (commit_rule): the same step 3 names
+  forcing the top few positions as another way (adopt the min_adopt most confident
+  together with those clearing gamma; min_adopt = 1 is the rule above), and the
+  pages' mock-AR mode (dzen, section "Что нового": one token per step through the
+  diffusion tower) is read as left-to-right order.
 
 Precision.  Everything is float64.  Mode "bf16" additionally rounds to the nearest
 bfloat16 (ties to even) exactly at the points where the GPU stores bfloat16: the
@@ -189,18 +193,38 @@ def vocab_reduce(z: np.ndarray, tau: np.ndarray):
     return conf, arg.astype(np.int64), conf - p2
 
 
-def commit_rule(conf: np.ndarray, masked: np.ndarray, gamma: float) -> np.ndarray:
-    """Positions adopted this step: masked with conf >= gamma, else the single most confident.
+RULE_THRESHOLD, RULE_LEFT_TO_RIGHT = 0, 1
 
-    Decided in float32.  Ties in the fallback go to the lowest position.  A block with
-    no masked position adopts nothing.
+
+def commit_rule(conf: np.ndarray, masked: np.ndarray, gamma: float, rule: int = RULE_THRESHOLD,
+                min_adopt: int = 1) -> np.ndarray:
+    """Positions adopted this step.
+
+    RULE_THRESHOLD (PredNext, section 拡散言語モデルで推論するには, step 3: adopt the
+    positions whose output clears the threshold; the same step names forcing the top few
+    as another way): masked positions with conf >= gamma, together with the min_adopt
+    most confident masked positions (ties to the lowest position).  min_adopt = 1 is the
+    fixed fallback: the single most confident position when none clears gamma.
+
+    RULE_LEFT_TO_RIGHT (dzen, section Что нового: the mock-AR mode, one token per step
+    through the diffusion tower, read as autoregressive order): the lowest masked
+    position; gamma and min_adopt play no part.
+
+    Decided in float32.  A block with no masked position adopts nothing.
     """
+    masked = np.asarray(masked, bool)
+    U = np.zeros_like(masked)
+    if not masked.any():
+        return U
+    if rule == RULE_LEFT_TO_RIGHT:
+        U[int(np.argmax(masked))] = True
+        return U
+    if rule != RULE_THRESHOLD or min_adopt < 1:
+        raise ValueError("unknown commit rule")
     c32 = np.asarray(conf, np.float64).astype(np.float32)
     U = masked & (c32 >= np.float32(gamma))
-    if not U.any() and masked.any():
-        cand = np.where(masked, c32, np.float32(-np.inf))
-        U = np.zeros_like(masked)
-        U[int(np.argmax(cand))] = True
+    ranked = sorted(np.nonzero(masked)[0].tolist(), key=lambda p: (-float(c32[p]), p))
+    U[ranked[:min_adopt]] = True
     return U
 
 
@@ -217,7 +241,7 @@ class StepResult:
 
 def oracle_step(tower: OracleTower, tok: np.ndarray, committed: np.ndarray, tau: np.ndarray,
                 gamma: float, kv: KVProvider, seqs: Optional[Sequence[int]] = None,
-                keep_logits: bool = False) -> StepResult:
+                keep_logits: bool = False, rule: int = RULE_THRESHOLD, min_adopt: int = 1) -> StepResult:
     """One denoising step for S independent sequences from state (tok, committed)."""
     S, B = tok.shape
     seqs = list(range(S)) if seqs is None else list(seqs)
@@ -240,14 +264,15 @@ def oracle_step(tower: OracleTower, tok: np.ndarray, committed: np.ndarray, tau:
     conf, arg, gap = conf.reshape(S, B), arg.reshape(S, B), gap.reshape(S, B)
     U = np.zeros((S, B), dtype=bool)
     for s in range(S):
-        U[s] = commit_rule(conf[s], masked[s], gamma)
+        U[s] = commit_rule(conf[s], masked[s], gamma, rule, min_adopt)
     new_tok = np.where(U, arg, tok)
     new_c = committed.astype(bool) | U
     return StepResult(conf, arg, gap, U, new_tok, new_c, z_all)
 
 
 def oracle_generate(tower: OracleTower, S: int, B: int, tau: np.ndarray, gamma: float, kv: KVProvider,
-                    seqs: Optional[Sequence[int]] = None, keep_trace: bool = True):
+                    seqs: Optional[Sequence[int]] = None, keep_trace: bool = True, rule: int = RULE_THRESHOLD,
+                    min_adopt: int = 1):
     """Run the block loop from an all-[MASK] block until every position is adopted.
 
     Returns (tok [S][B], commit_step [S][B], steps [S], trace: list of StepResult).
@@ -261,7 +286,7 @@ def oracle_generate(tower: OracleTower, S: int, B: int, tau: np.ndarray, gamma: 
     t = 0
     while not committed.all():
         active = ~committed.all(axis=1)
-        r = oracle_step(tower, tok, committed, tau, gamma, kv, seqs)
+        r = oracle_step(tower, tok, committed, tau, gamma, kv, seqs, rule=rule, min_adopt=min_adopt)
         assert (r.U.sum(axis=1)[active] >= 1).all(), "an active sequence must adopt at least one position"
         commit_step[r.U] = t
         steps += active

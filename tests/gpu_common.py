@@ -90,8 +90,14 @@ def logits_rel_err(z_gpu: np.ndarray, z_orc: np.ndarray) -> np.ndarray:
     return np.abs(z_gpu.astype(np.float64) - z_orc).max(axis=-1) / np.abs(z_orc).max(axis=-1)
 
 
-def decision_mismatches(g: dict, r, committed_in: np.ndarray, gamma: float) -> List[str]:
-    """Non-exempt differences between the GPU step `g` and the oracle StepResult `r`."""
+def decision_mismatches(g: dict, r, committed_in: np.ndarray, gamma: float, rule: int = 0,
+                        min_adopt: int = 1) -> List[str]:
+    """Non-exempt differences between the GPU step `g` and the oracle StepResult `r`.
+
+    Exempt: predictions whose top-2 probability gap is under EXEMPT; adoptions within
+    EXEMPT of gamma; the forced choice (most confident, or the min_adopt-th most
+    confident) when the candidates on both sides of it are within EXEMPT.  The
+    left-to-right rule involves no floating-point decision and must match exactly."""
     bad = []
     masked = ~committed_in.astype(bool)
     S, B = masked.shape
@@ -100,7 +106,10 @@ def decision_mismatches(g: dict, r, committed_in: np.ndarray, gamma: float) -> L
         gap_o = r.gap[s]
         mc = np.where(masked[s], conf_o, -np.inf)
         top = np.sort(mc)[::-1]
+        topm = np.sort(conf_o[masked[s]])[::-1]
         fallback_possible = not (mc >= gamma + EXEMPT).any()
+        k = min_adopt
+        k_tie = (len(topm) > k and topm[k - 1] - topm[k] < EXEMPT and topm[k] < gamma + EXEMPT)
         for p in range(B):
             if not masked[s, p]:
                 continue
@@ -109,11 +118,15 @@ def decision_mismatches(g: dict, r, committed_in: np.ndarray, gamma: float) -> L
                 bad.append(f"seq {s} pos {p}: arg gpu {g['arg'][s, p]} oracle {r.arg[s, p]} "
                            f"(conf {conf_o[p]:.6f}, gap {gap_o[p]:.2e})")
             if g["U"][s, p] != r.U[s, p]:
-                fb_tie = fallback_possible and conf_o[p] >= top[0] - EXEMPT and (top[0] - top[1] < EXEMPT
-                                                                               if B > 1 else False)
-                if not (near_gamma or fb_tie):
+                if rule == 1:
+                    bad.append(f"seq {s} pos {p}: left-to-right commit gpu {g['U'][s, p]} oracle {r.U[s, p]}")
+                    continue
+                fb_tie = k == 1 and fallback_possible and conf_o[p] >= top[0] - EXEMPT and (
+                    top[0] - top[1] < EXEMPT if B > 1 else False)
+                rank_tie = k > 1 and k_tie and topm[k] - EXEMPT <= conf_o[p] <= topm[k - 1] + EXEMPT
+                if not (near_gamma or fb_tie or rank_tie):
                     bad.append(f"seq {s} pos {p}: commit gpu {g['U'][s, p]} oracle {r.U[s, p]} "
-                               f"(conf {conf_o[p]:.6f}, gamma {gamma}, top2 {top[:2]})")
+                               f"(conf {conf_o[p]:.6f}, gamma {gamma}, min_adopt {k}, top {topm[:k + 1]})")
     return bad
 
 

@@ -51,48 +51,57 @@ def _check_step0(case, sample):
     assert bad == [], bad
 
 
-def _check_generate(case, sample, gamma):
+def _check_generate(case, sample, gamma, rule=0, min_adopt=1):
     """td_generate_block on the whole batch; the sample's tokens, commit steps, step counts."""
     from oracle import oracle_generate
     w = case.w
     torch = case.torch
     tok_o, cs_o, steps_o, _ = oracle_generate(case.orc, len(sample), w.B, case.tau[sample], gamma, case.kv,
-                                              seqs=sample, keep_trace=False)
+                                              seqs=sample, keep_trace=False, rule=rule, min_adopt=min_adopt)
     tok = torch.zeros((w.n, w.B), dtype=torch.int32, device="cuda")
     com = torch.zeros((w.n, w.B), dtype=torch.uint8, device="cuda")
     steps = torch.zeros(w.n, dtype=torch.int32, device="cuda")
     cstep = torch.zeros((w.n, w.B), dtype=torch.int8, device="cuda")
-    case.dev.generate_block(tok, com, case.tau_d, gamma, steps=steps, commit_step=cstep)
-    case.dev.sync()
+    case.dev.set_commit_rule(rule, min_adopt)
+    try:
+        case.dev.generate_block(tok, com, case.tau_d, gamma, steps=steps, commit_step=cstep)
+        case.dev.sync()
+    finally:
+        case.dev.set_commit_rule(0, 1)
     tg, cg, sg = tok.cpu().numpy(), cstep.cpu().numpy(), steps.cpu().numpy()
-    log(f"[{w.name}] generate gamma {gamma}: steps gpu {sg[sample]} oracle {steps_o}; batch steps "
-        f"min {sg.min()} max {sg.max()}")
+    log(f"[{w.name}] generate gamma {gamma} rule {rule} min_adopt {min_adopt}: steps gpu {sg[sample]} oracle "
+        f"{steps_o}; batch steps min {sg.min()} max {sg.max()}")
     assert com.cpu().numpy().all() and (sg >= 1).all() and (sg <= w.B).all()
     assert np.array_equal(tg[sample], tok_o)
     assert np.array_equal(cg[sample], cs_o)
     assert np.array_equal(sg[sample], steps_o)
 
 
-def _check_trace(case, sample):
+def _check_trace(case, sample, rule=0, min_adopt=1):
     """Teacher-forced steps: the sample follows the oracle's states; the other sequences of
     the batch are fully committed (they still run through the layers, never the LM head)."""
     from oracle import oracle_generate
     w = case.w
-    _, _, _, trace = oracle_generate(case.orc, len(sample), w.B, case.tau[sample], w.gamma, case.kv, seqs=sample)
+    _, _, _, trace = oracle_generate(case.orc, len(sample), w.B, case.tau[sample], w.gamma, case.kv, seqs=sample,
+                                     rule=rule, min_adopt=min_adopt)
     tok = np.zeros((w.n, w.B), dtype=np.int64)
     c = np.ones((w.n, w.B), bool)
     tok[sample] = w.V
     c[sample] = False
-    for t, r in enumerate(trace):
-        g = gpu_step(case, tok, c, w.gamma)
-        gs = {k: v[sample] for k, v in g.items()}
-        bad = decision_mismatches(gs, r, c[sample], w.gamma)
-        log(f"[{w.name}] step {t}: commits oracle {int(r.U.sum())} gpu {int(gs['U'].sum())}, "
-            f"conf err {conf_abs_err(gs, r, c[sample]):.2e}")
-        assert bad == [], f"step {t}: {bad}"
-        others = np.setdiff1d(np.arange(w.n), sample)
-        assert not g["U"][others].any(), "a committed sequence adopted a position"
-        tok[sample], c[sample] = r.tok, r.committed
+    case.dev.set_commit_rule(rule, min_adopt)
+    try:
+        for t, r in enumerate(trace):
+            g = gpu_step(case, tok, c, w.gamma)
+            gs = {k: v[sample] for k, v in g.items()}
+            bad = decision_mismatches(gs, r, c[sample], w.gamma, rule, min_adopt)
+            log(f"[{w.name}] step {t} (rule {rule}, min_adopt {min_adopt}): commits oracle {int(r.U.sum())} gpu "
+                f"{int(gs['U'].sum())}, conf err {conf_abs_err(gs, r, c[sample]):.2e}")
+            assert bad == [], f"step {t}: {bad}"
+            others = np.setdiff1d(np.arange(w.n), sample)
+            assert not g["U"][others].any(), "a committed sequence adopted a position"
+            tok[sample], c[sample] = r.tok, r.committed
+    finally:
+        case.dev.set_commit_rule(0, 1)
 
 
 # ---------------------------------------------------------------- small towers, every sequence checked
@@ -145,6 +154,17 @@ def test_small_trace(small):
 
 def test_small_generate(small):
     _check_generate(small, list(range(small.w.n)), small.w.gamma)
+
+
+# Commit-rule variants: the top k forced together with the threshold (k = 3 at the tower's
+# gamma and at gamma > 1, exactly k per step) and the left-to-right mock-AR rule.
+@pytest.mark.parametrize("rule,k,gamma", [(0, 3, None), (0, 3, 1.5), (1, 1, None)])
+def test_small_generate_commit_rules(small, rule, k, gamma):
+    _check_generate(small, list(range(small.w.n)), small.w.gamma if gamma is None else gamma, rule, k)
+
+
+def test_small_trace_top3(small):
+    _check_trace(small, list(range(small.w.n)), rule=0, min_adopt=3)
 
 
 # ---------------------------------------------------------------- full-size batched workloads

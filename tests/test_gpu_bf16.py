@@ -73,3 +73,11 @@ def test_generate_block(b1, b1_trace):
         f"commit order equal {np.array_equal(cg, cs_o)}")
     assert com.cpu().numpy().all() and (sg <= w.B).all()
     assert np.array_equal(tg, tok_o) and np.array_equal(cg, cs_o) and np.array_equal(sg, steps_o)
+
+
+@pytest.mark.parametrize("rule,k", [(0, 4), (1, 1)])
+def test_generate_block_commit_rules(b1, rule, k):
+    """The commit-rule variants at full size: the top 4 forced with the threshold, and the
+    left-to-right mock-AR rule (16 steps, position p adopted at step p)."""
+    from tests.test_gpu_batched import _check_generate
+    _check_generate(b1, [0], b1.w.gamma, rule, k)

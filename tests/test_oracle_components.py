@@ -200,5 +200,29 @@ def test_commit_rule_golden():
     for c in cases:
         conf = np.array(c["conf"], dtype=np.float64)
         masked = np.array(c["masked"], dtype=bool)
-        U = commit_rule(conf, masked, c["gamma"])
+        U = commit_rule(conf, masked, c["gamma"], c.get("rule", 0), c.get("min_adopt", 1))
         assert U.tolist() == c["adopt"], c
+
+
+def test_commit_rule_min_adopt_one_is_the_fallback_rule():
+    """Forced adoption of the top 1 together with the threshold is the threshold rule with
+    its single-most-confident fallback, on random states (brute force)."""
+    rng = np.random.default_rng(3)
+    for _ in range(500):
+        B = int(rng.integers(1, 9))
+        conf = rng.choice([0.2, 0.5, 0.8, 0.9], size=B).astype(np.float64)
+        masked = rng.random(B) < 0.7
+        gamma = float(rng.choice([0.0, 0.5, 0.8, 0.95, 1.5]))
+        c32 = conf.astype(np.float32)
+        want = masked & (c32 >= np.float32(gamma))
+        if masked.any() and not want.any():
+            best = max((p for p in range(B) if masked[p]), key=lambda p: (c32[p], -p))
+            want[best] = True
+        assert commit_rule(conf, masked, gamma, 0, 1).tolist() == want.tolist()
+
+
+def test_commit_rule_rejects_unknown_rules():
+    with pytest.raises(ValueError):
+        commit_rule(np.ones(2), np.ones(2, bool), 0.5, 7, 1)
+    with pytest.raises(ValueError):
+        commit_rule(np.ones(2), np.ones(2, bool), 0.5, 0, 0)

@@ -57,6 +57,47 @@ def test_gamma_above_one_takes_exactly_B_steps(mini):
             assert conf[p] == conf.max() and p == int(np.argmax(conf))
 
 
+@pytest.mark.parametrize("k", [2, 3, 16])
+def test_forced_top_k_above_gamma_one_adopts_k_per_step(mini, k):
+    """gamma > 1 with the top k forced: exactly min(k, masked) positions per step, the k
+    most confident in fp32 (lowest position on ties), ceil(B / k) steps."""
+    w, orc, W, plens, tau, kv = mini
+    tok, cstep, steps, trace = oracle_generate(orc, w.n, w.B, tau, 1.5, kv, min_adopt=k)
+    assert (steps == -(-w.B // k)).all() and len(trace) == -(-w.B // k)
+    for r in trace:
+        for s in range(w.n):
+            masked = ~np.isnan(r.conf[s])
+            assert r.U[s].sum() == min(k, masked.sum())
+            c32 = np.where(masked, r.conf[s], -1).astype(np.float32)
+            order = sorted(np.nonzero(masked)[0].tolist(), key=lambda p: (-float(c32[p]), p))
+            assert sorted(np.nonzero(r.U[s])[0].tolist()) == sorted(order[:k])
+
+
+def test_left_to_right_commits_position_p_at_step_p(mini):
+    """The mock-AR rule: one position per step, in position order, B steps; each adopted
+    token is the argmax of that step's forward at that position."""
+    w, orc, W, plens, tau, kv = mini
+    tok, cstep, steps, trace = oracle_generate(orc, w.n, w.B, tau, 0.8, kv, rule=od.RULE_LEFT_TO_RIGHT)
+    assert (steps == w.B).all() and len(trace) == w.B
+    assert (cstep == np.arange(w.B)[None, :]).all()
+    for t, r in enumerate(trace):
+        assert (r.U.sum(axis=1) == 1).all() and r.U[:, t].all()
+        assert np.array_equal(tok[:, t], r.arg[:, t])
+
+
+def test_forced_top_k_with_threshold_is_a_superset_of_the_threshold_rule(mini):
+    """From the same state, top-k forcing adopts everything the plain rule adopts, and more
+    only where the plain rule adopted fewer than k."""
+    w, orc, W, plens, tau, kv = mini
+    tok = np.full((w.n, w.B), w.V)
+    c = np.zeros((w.n, w.B), bool)
+    r1 = oracle_step(orc, tok, c, tau, 0.8, kv)
+    r3 = oracle_step(orc, tok, c, tau, 0.8, kv, min_adopt=3)
+    assert (r3.U | ~r1.U).all()
+    for s in range(w.n):
+        assert r3.U[s].sum() == max(r1.U[s].sum(), 3)
+
+
 @pytest.mark.parametrize("gamma", [0.3, 0.8, 0.95])
 def test_loop_invariants(mini, gamma):
     w, orc, W, plens, tau, kv = mini
