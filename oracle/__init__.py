@@ -25,4 +25,6 @@ from .denoise import (  # noqa: F401
     StepResult,
     oracle_step,
     oracle_generate,
+    OracleContextTower,
+    oracle_generate_blocks,
 )

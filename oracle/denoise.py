@@ -83,14 +83,17 @@ def gelu(x: np.ndarray) -> np.ndarray:
 
 
 def joint_attention(q: np.ndarray, k_pre: np.ndarray, v_pre: np.ndarray, k_blk: np.ndarray,
-                    v_blk: np.ndarray) -> np.ndarray:
-    """Block queries against [prefix keys ; block keys], one softmax per query row, no mask.
+                    v_blk: np.ndarray, causal: bool = False) -> np.ndarray:
+    """Block queries against [prefix keys ; block keys], one softmax per query row.
 
     q [B][H][hd]; k_pre, v_pre [P][Hkv][hd] (P may be 0); k_blk, v_blk [B][Hkv][hd].
-    Returns o [B][H][hd].  Query head j reads K/V head j // (H // Hkv).
+    Returns o [B][H][hd].  Query head j reads K/V head j // (H // Hkv).  No mask for the
+    denoiser; causal=True (the context tower) shows block query p the whole prefix and the
+    block keys 0..p only.
     """
     Bq, H, hd = q.shape
     Hkv = k_blk.shape[1]
+    P = k_pre.shape[0]
     G = H // Hkv
     o = np.empty((Bq, H, hd), dtype=np.float64)
     for j in range(H):
@@ -98,6 +101,9 @@ def joint_attention(q: np.ndarray, k_pre: np.ndarray, v_pre: np.ndarray, k_blk: 
         K = np.concatenate([k_pre[:, g, :], k_blk[:, g, :]], axis=0)
         Vv = np.concatenate([v_pre[:, g, :], v_blk[:, g, :]], axis=0)
         s = (q[:, j, :] @ K.T) / np.sqrt(hd)
+        if causal:
+            later = np.arange(k_blk.shape[0])[None, :] > np.arange(Bq)[:, None]
+            s[:, P:][later] = -np.inf
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
         p = p / p.sum(axis=1, keepdims=True)
@@ -173,6 +179,52 @@ class OracleTower:
     def logits(self, hf_rows: np.ndarray) -> np.ndarray:
         """z = hf Wlm^T for rows hf_rows [R][d] (float64, never rounded)."""
         return hf_rows @ self._w("lm_head").T
+
+
+class OracleContextTower:
+    """The frozen context tower over a committed block, float64.
+
+    The pages describe it as the causal tower whose cached K/V the denoiser reads
+    (poko, section 技術/ビジネス面; dzen, section Что нового: frozen).  Readings: the
+    denoiser's shapes with weights of its own (tok_emb [V+1][d]; per layer wq, wk, wv,
+    wo, w1, w2, attn_norm, mlp_norm), no position table (the causal mask orders its
+    tokens), each block query attending causally inside the block and to the whole
+    cached prefix.  block_kv returns, per layer, the k and v of the block's tokens: what
+    is appended to the cache that layer l of the denoiser reads.
+    """
+
+    def __init__(self, weights: Dict[str, object], *, H: int, Hkv: int, hd: int, eps: float = 1e-6):
+        self.W = weights
+        self.H, self.Hkv, self.hd, self.eps = H, Hkv, hd, eps
+        self.L = len(weights["wq"])
+        self.d = weights["tok_emb"].shape[1]
+
+    def _w(self, name: str, layer: int) -> np.ndarray:
+        return np.asarray(self.W[name][layer], dtype=np.float64)
+
+    def block_kv(self, tok: np.ndarray, kv: KVProvider, seqs: Sequence[int]):
+        """[(k [S][B][Hkv][hd], v [S][B][Hkv][hd]) for each layer] of token blocks tok [S][B]."""
+        S, B = tok.shape
+        H, Hkv, hd = self.H, self.Hkv, self.hd
+        x = np.asarray(self.W["tok_emb"][tok.reshape(-1)], dtype=np.float64).reshape(S, B, self.d)
+        out = []
+        for l in range(self.L):
+            h = rmsnorm(x, self._w("attn_norm", l), self.eps)
+            q = (h @ self._w("wq", l).T).reshape(S, B, H, hd)
+            k = (h @ self._w("wk", l).T).reshape(S, B, Hkv, hd)
+            v = (h @ self._w("wv", l).T).reshape(S, B, Hkv, hd)
+            out.append((k, v))
+            if l == self.L - 1:
+                break          # nothing above the last layer's K/V is read
+            o = np.empty((S, B, H, hd))
+            for s in range(S):
+                kp, vp = kv(l, seqs[s])
+                o[s] = joint_attention(q[s], np.asarray(kp, np.float64), np.asarray(vp, np.float64), k[s], v[s],
+                                       causal=True)
+            x = x + o.reshape(S, B, H * hd) @ self._w("wo", l).T
+            h2 = rmsnorm(x, self._w("mlp_norm", l), self.eps)
+            x = x + gelu(h2 @ self._w("w1", l).T) @ self._w("w2", l).T
+        return out
 
 
 # ----------------------------------------------------------------------------- reduction + commit
@@ -268,6 +320,42 @@ def oracle_step(tower: OracleTower, tok: np.ndarray, committed: np.ndarray, tau:
     new_tok = np.where(U, arg, tok)
     new_c = committed.astype(bool) | U
     return StepResult(conf, arg, gap, U, new_tok, new_c, z_all)
+
+
+def oracle_generate_blocks(tower: OracleTower, context: OracleContextTower, n_blocks: int, S: int, B: int,
+                           tau: np.ndarray, gamma: float, kv: KVProvider, seqs: Optional[Sequence[int]] = None,
+                           cache_bf16: bool = True, rule: int = RULE_THRESHOLD, min_adopt: int = 1):
+    """Generation of n_blocks consecutive blocks: each block is refined to completion by
+    the block loop; the context tower then runs over its tokens and their K/V (rounded
+    to bf16 when the cache holds bf16) are appended to every layer's cache, so the next
+    block sees them as prefix.  The same inverse temperatures serve every block.
+
+    Returns (tok [n_blocks][S][B], commit_step [n_blocks][S][B], steps [n_blocks][S]).
+    """
+    seqs = list(range(S)) if seqs is None else list(seqs)
+    added: Dict[Tuple[int, int], List[Tuple[np.ndarray, np.ndarray]]] = {}
+
+    def kv_now(l: int, s: int):
+        K, V = kv(l, s)
+        extra = added.get((l, s), [])
+        if not extra:
+            return K, V
+        return (np.concatenate([np.asarray(K, np.float64)] + [e[0] for e in extra], axis=0),
+                np.concatenate([np.asarray(V, np.float64)] + [e[1] for e in extra], axis=0))
+
+    toks, csteps, steps = [], [], []
+    for _ in range(n_blocks):
+        tok, cs, st, _ = oracle_generate(tower, S, B, tau, gamma, kv_now, seqs, keep_trace=False, rule=rule,
+                                         min_adopt=min_adopt)
+        toks.append(tok)
+        csteps.append(cs)
+        steps.append(st)
+        kvs = context.block_kv(tok, kv_now, seqs)
+        for l, (k, v) in enumerate(kvs):
+            for i, s in enumerate(seqs):
+                kk, vv = (round_bf16(k[i]), round_bf16(v[i])) if cache_bf16 else (k[i], v[i])
+                added.setdefault((l, s), []).append((kk, vv))
+    return np.stack(toks), np.stack(csteps), np.stack(steps)
 
 
 def oracle_generate(tower: OracleTower, S: int, B: int, tau: np.ndarray, gamma: float, kv: KVProvider,

@@ -29,7 +29,8 @@ def host_to_device(a: np.ndarray, bf16: bool, device="cuda"):
 def tower_to_device(tw: TowerInputs, device="cuda") -> Dict:
     bf = tw.is_bf16
     up = lambda a: host_to_device(a, bf, device)  # noqa: E731
-    return dict(tok_emb=up(tw.tok_emb), pos_emb=up(tw.pos_emb), final_norm=up(tw.final_norm), lm_head=up(tw.lm_head),
+    upn = lambda a: None if a is None else up(a)  # noqa: E731  (context tower: no pos/final/head)
+    return dict(tok_emb=up(tw.tok_emb), pos_emb=upn(tw.pos_emb), final_norm=upn(tw.final_norm), lm_head=upn(tw.lm_head),
                 attn_norm=[up(a) for a in tw.attn_norm], mlp_norm=[up(a) for a in tw.mlp_norm],
                 wq=[up(a) for a in tw.wq], wk=[up(a) for a in tw.wk], wv=[up(a) for a in tw.wv],
                 wo=[up(a) for a in tw.wo], w1=[up(a) for a in tw.w1], w2=[up(a) for a in tw.w2])
