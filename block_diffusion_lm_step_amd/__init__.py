@@ -50,6 +50,10 @@ try:
     lib.td_denoise_step.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.td_generate_block.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
     lib.td_set_commit_rule.argtypes = [_CTX, c_int32, c_int32]
+    lib.td_bind_cache.argtypes = [_CTX, c_int32, POINTER(c_int64), POINTER(c_int64), POINTER(c_void_p),
+                                  POINTER(c_void_p)]
+    lib.td_set_context_tower.argtypes = [_CTX, POINTER(TdWeights)]
+    lib.td_append_block.argtypes = [_CTX, c_void_p]
     lib.td_debug_attention.argtypes = [_CTX, c_int32, c_void_p, c_void_p]
     lib.td_sync.argtypes = [_CTX]
     lib.td_profile_begin.argtypes = [_CTX, c_int32]
@@ -63,16 +67,16 @@ try:
     lib.td_last_error.argtypes = [_CTX]
     lib.td_last_error.restype = c_char_p
     lib.td_version.restype = c_char_p
-    for _f in ("td_create", "td_set_prefix", "td_denoise_step", "td_generate_block", "td_set_commit_rule",
-               "td_debug_attention", "td_sync"):
+    for _f in ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_generate_block",
+               "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_debug_attention", "td_sync"):
         getattr(lib, _f).restype = c_int
 except AttributeError as e:   # a library built from older sources
     raise ImportError(f"{LIB_PATH} is stale ({e}); rebuild with `python block_diffusion_lm_step_amd/build.py`") from e
 
 # Every symbol the C header declares.
-EXPORTED = ("td_create", "td_set_prefix", "td_denoise_step", "td_generate_block", "td_set_commit_rule",
-            "td_debug_attention", "td_sync", "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_destroy",
-            "td_last_error", "td_version")
+EXPORTED = ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_generate_block",
+            "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_debug_attention", "td_sync",
+            "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_destroy", "td_last_error", "td_version")
 TD_PROF_OFF, TD_PROF_LMHEAD, TD_PROF_GEMM, TD_PROF_ATTENTION, TD_PROF_STEP = range(5)
 TD_RULE_THRESHOLD, TD_RULE_LEFT_TO_RIGHT = range(2)
 
@@ -136,6 +140,25 @@ class Denoiser:
         ka, va = _ptr_array(k_caches), _ptr_array(v_caches)
         self._check(lib.td_set_prefix(self._ctx, n, off, ka, va))
         self._prefix_refs = (list(k_caches), list(v_caches))   # borrowed by the ctx
+
+    def bind_cache(self, lengths: Sequence[int], page_capacity: Sequence[int], k_caches: Sequence,
+                   v_caches: Sequence) -> None:
+        n = len(lengths)
+        ln = (c_int64 * n)(*[int(v) for v in lengths])
+        cp = (c_int64 * n)(*[int(v) for v in page_capacity])
+        ka, va = _ptr_array(k_caches), _ptr_array(v_caches)
+        self._check(lib.td_bind_cache(self._ctx, n, ln, cp, ka, va))
+        self._prefix_refs = (list(k_caches), list(v_caches))   # borrowed by the ctx
+
+    def set_context_tower(self, weights: Dict) -> None:
+        """weights: tok_emb and the per-layer lists, as for the denoiser (no pos/final/head)."""
+        keep = {k: _ptr_array(weights[k]) for k in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w1", "w2")}
+        w = TdWeights(weights["tok_emb"].data_ptr(), None, keep["attn_norm"], keep["wq"], keep["wk"], keep["wv"],
+                      keep["wo"], keep["mlp_norm"], keep["w1"], keep["w2"], None, None)
+        self._check(lib.td_set_context_tower(self._ctx, ctypes.byref(w)))
+
+    def append_block(self, tokens) -> None:
+        self._check(lib.td_append_block(self._ctx, _ptr(tokens)))
 
     def denoise_step(self, tokens, committed, inv_temp, gamma: float, newly=None, conf=None, argmax=None,
                      logits=None) -> None:

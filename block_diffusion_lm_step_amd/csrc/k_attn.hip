@@ -36,7 +36,9 @@
 // sequence's last page are masked (scores to -inf, values to 0).
 //
 // Block items: the B block keys/values are fp32 activations from the QKV projection and
-// few, so they are attended in fp32 on the VALU (16 threads per query row).
+// few, so they are attended in fp32 on the VALU (16 threads per query row).  For the
+// frozen context tower's pass (causal) block query p sees block keys 0..p only; the
+// prefix is always seen whole.
 #include "td_device.h"
 #include "td_kernels.h"
 
@@ -214,6 +216,7 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
     float qv[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) qv[e] = q[e];
+    const int kmax = a.causal ? min(a.B, p + 1) : a.B;   // causal: block keys 0..p
     float sc[BMAX];
     float m = -INFINITY;
 #pragma unroll
@@ -222,7 +225,7 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
         float dsum = 0.f;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) dsum += qv[e] * s_k[key * (HD + 1) + e0 + e];
-        sc[key] = sum16(dsum) * a.scale;
+        sc[key] = key < kmax ? sum16(dsum) * a.scale : -INFINITY;
         m = fmaxf(m, sc[key]);
       }
     }
@@ -231,7 +234,7 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
     for (int e = 0; e < EPT; ++e) ov[e] = 0.f;
 #pragma unroll
     for (int key = 0; key < BMAX; ++key) {
-      if (key < a.B) {
+      if (key < kmax) {
         const float pk = __expf(sc[key] - m);
         l += pk;
 #pragma unroll
@@ -373,13 +376,14 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
       const int rho = ps * (NT / 16) + (threadIdx.x >> 4);
       float sc[BMAX];
       float m = -INFINITY;
+      const int kmax = a.causal ? min(a.B, rho % a.B + 1) : a.B;   // causal: block keys 0..p
 #pragma unroll
       for (int key = 0; key < BMAX; ++key) {
         if (key < a.B) {
           float dsum = 0.f;
 #pragma unroll
           for (int e = 0; e < EPT; ++e) dsum += bq[ps][e] * s_bk[key * (HD + 1) + e0 + e];
-          sc[key] = sum16(dsum) * a.scale;
+          sc[key] = key < kmax ? sum16(dsum) * a.scale : -INFINITY;
           m = fmaxf(m, sc[key]);
         }
       }
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
       for (int e = 0; e < EPT; ++e) ov[e] = 0.f;
 #pragma unroll
       for (int key = 0; key < BMAX; ++key) {
-        if (key < a.B) {
+        if (key < kmax) {
           const float pk = __expf(sc[key] - m);
           l += pk;
 #pragma unroll

@@ -80,13 +80,13 @@ __global__ __launch_bounds__(256) void embed_kernel(const int *tokens, const T *
     tok = V;
   }
   const T *e = E + (size_t)tok * d;
-  const T *p = Pos + (size_t)(r % B) * d;
+  const T *p = Pos ? Pos + (size_t)(r % B) * d : nullptr;   // no table: the context tower
   for (int grp = threadIdx.x; grp < d / 16; grp += blockDim.x) {
     float s = 0.f, v[16], vg[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       const int k = grp * 16 + c;
-      v[c] = to_f32<T>(e[k]) + to_f32<T>(p[k]);
+      v[c] = to_f32<T>(e[k]) + (p ? to_f32<T>(p[k]) : 0.f);
       vg[c] = v[c] * to_f32<T>(gain[k]);
       x[(size_t)r * d + k] = v[c];
       s += v[c] * v[c];
@@ -97,7 +97,39 @@ __global__ __launch_bounds__(256) void embed_kernel(const int *tokens, const T *
   }
 }
 
+// One thread per (block row, K/V head, element): the k and v of the row go to slot
+// t % 32 of page seq_page[seq] + t / 32, t = seq_len[seq] + p.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_append_kernel(const float *qkv, int Nqkv, int H, int Hkv, int hd, T *kc,
+                                                        T *vc, const int *seq_len, const int *seq_page, int B) {
+  const int r = blockIdx.x, seq = r / B, p = r % B;
+  const int idx = blockIdx.y * blockDim.x + threadIdx.x;
+  if (idx >= Hkv * hd) return;
+  const int h = idx / hd, e = idx % hd;
+  const int t = seq_len[seq] + p;
+  const size_t page = (size_t)seq_page[seq] + t / KV_PAGE;
+  const int slot = t % KV_PAGE;
+  const float kv = qkv[(size_t)r * Nqkv + (size_t)(H + h) * hd + e];
+  const float vv = qkv[(size_t)r * Nqkv + (size_t)(H + Hkv + h) * hd + e];
+  const int half = (slot / 4) % 2, row = (slot / 8) * 4 + slot % 4;
+  kc[(page * Hkv + h) * KV_PAGE * hd + ((e / 32) * 2 + half) * 512 + row * 32 + e % 32] = from_f32<T>(kv);
+  vc[((page * Hkv + h) * hd + e) * KV_PAGE + slot] = from_f32<T>(vv);
+}
+
 }  // namespace
+
+hipError_t launch_kv_append(int dtype, const float *qkv, int Nqkv, int H, int Hkv, int hd, void *kc, void *vc,
+                            const int *seq_len, const int *seq_page, int n, int B, hipStream_t s) {
+  if (n <= 0 || B <= 0 || hd % 32 || !kc || !vc) return hipErrorInvalidValue;
+  const dim3 grid(n * B, (Hkv * hd + 255) / 256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(kv_append_kernel<bf16_t>, grid, dim3(256), 0, s, qkv, Nqkv, H, Hkv, hd, (bf16_t *)kc,
+                       (bf16_t *)vc, seq_len, seq_page, B);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(256), 0, s, qkv, Nqkv, H, Hkv, hd, (float *)kc,
+                       (float *)vc, seq_len, seq_page, B);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_weight(int dtype, const void *W, void *Wp, int N, int K, hipStream_t s) {
   if (N % 16 || K % 32) return hipErrorInvalidValue;

@@ -28,6 +28,11 @@ struct GemmPlan {
 
 }  // namespace
 
+// Per-layer weights of one tower (packed).
+struct Layers {
+  std::vector<void *> attn_norm, mlp_norm, wqkv, wo, w1, w2;
+};
+
 struct td_ctx {
   td_config cfg{};
   int dev = 0;
@@ -37,7 +42,12 @@ struct td_ctx {
 
   // weights (ctx-owned, packed)
   void *tok_emb = nullptr, *pos_emb = nullptr, *final_norm = nullptr, *lm_head = nullptr;
-  std::vector<void *> attn_norm, mlp_norm, wqkv, wo, w1, w2;
+  Layers layers;
+  // frozen context tower (td_set_context_tower)
+  void *ctx_tok_emb = nullptr;
+  Layers context;
+  int *zero_flag = nullptr;          // a loop-exit flag that stays 0 (the context pass)
+  const int *gemm_done = nullptr;    // flag the layer GEMMs test; nullptr: the step's
 
   // adoption rule (td_set_commit_rule)
   int rule = RULE_THRESHOLD, min_adopt = 1;
@@ -57,7 +67,8 @@ struct td_ctx {
 
   // prefix binding
   int n_seqs = 0;
-  std::vector<int64_t> offsets;
+  std::vector<int64_t> lengths, caps;   // tokens and reserved pages of each bound sequence
+  int *seq_lp_d = nullptr;              // device [2][max_batch]: lengths, first pages
   std::vector<const void *> kc, vc;
   AttnItem *items_d = nullptr;
   int *pair_first_d = nullptr, *pair_count_d = nullptr;
@@ -134,9 +145,9 @@ td_status validate_config(const td_config *cfg) {
   return TD_OK;
 }
 
-td_status validate_weights(const td_config &c, const td_weights *w) {
+td_status validate_weights(const td_config &c, const td_weights *w, bool context = false) {
   if (!w) return fail(nullptr, TD_EINVAL, "weights is NULL");
-  if (!w->tok_emb || !w->pos_emb || !w->final_norm || !w->lm_head)
+  if (!w->tok_emb || (!context && (!w->pos_emb || !w->final_norm || !w->lm_head)))
     return fail(nullptr, TD_EINVAL, "a global weight pointer is NULL");
   const void *const *lists[] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w1, w->w2};
   for (auto *l : lists) {
@@ -230,7 +241,8 @@ td_status prof_mark(td_ctx *c, int kind, bool start) {
   return TD_OK;
 }
 
-td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, void *o_afl, const int *done) {
+td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, void *o_afl, const int *done,
+                            bool causal = false) {
   const td_config &g = c->cfg;
   AttnArgs a{};
   a.B = g.block_size;
@@ -255,6 +267,7 @@ td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, vo
   a.o_afl = o_afl;
   a.scale = 1.0f / std::sqrt((float)g.head_dim);
   a.done = done;
+  a.causal = causal ? 1 : 0;
   TD_TRY(prof_mark(c, TD_PROF_ATTENTION, true));
   TD_HIP(c, launch_attention(g.dtype, a, c->stream));
   TD_TRY(prof_mark(c, TD_PROF_ATTENTION, false));
@@ -286,7 +299,7 @@ td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const
   a.out_afl = out_afl;
   a.gain_next = gain_next;
   a.ssq_out = c->ssq;
-  a.done = c->st.done;
+  a.done = c->gemm_done ? c->gemm_done : c->st.done;
   a.splits = epi == EPI_VSTAT ? 1 : p.splits;
   a.part = c->part;
   if (p.tile) {
@@ -310,15 +323,15 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   const int M = c->n_seqs * g.block_size;
   const int d = g.d_model, Hd = g.n_heads * g.head_dim;
   TD_TRY(prof_mark(c, TD_PROF_STEP, true));
-  TD_HIP(c, launch_embed(g.dtype, tokens, c->tok_emb, c->pos_emb, c->attn_norm[0], c->x, c->ssq, c->ah, M,
+  TD_HIP(c, launch_embed(g.dtype, tokens, c->tok_emb, c->pos_emb, c->layers.attn_norm[0], c->x, c->ssq, c->ah, M,
                          g.block_size, d, g.vocab, c->st, c->stream));
   for (int l = 0; l < g.n_layers; ++l) {
-    const void *gain_after = l + 1 < g.n_layers ? c->attn_norm[l + 1] : c->final_norm;
-    TD_TRY(enqueue_gemm(c, EPI_STORE, true, M, c->Nqkv, d, c->ah, c->wqkv[l], c->p_qkv, c->qkv, nullptr, nullptr));
+    const void *gain_after = l + 1 < g.n_layers ? c->layers.attn_norm[l + 1] : c->final_norm;
+    TD_TRY(enqueue_gemm(c, EPI_STORE, true, M, c->Nqkv, d, c->ah, c->layers.wqkv[l], c->p_qkv, c->qkv, nullptr, nullptr));
     TD_TRY(enqueue_attention(c, l, c->qkv, nullptr, c->ao, c->st.done));
-    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, Hd, c->ao, c->wo[l], c->p_wo, c->x, c->ah, c->mlp_norm[l]));
-    TD_TRY(enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, c->ah, c->w1[l], c->p_w1, nullptr, c->au, nullptr));
-    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->au, c->w2[l], c->p_w2, c->x, c->ah, gain_after));
+    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, Hd, c->ao, c->layers.wo[l], c->p_wo, c->x, c->ah, c->layers.mlp_norm[l]));
+    TD_TRY(enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, c->ah, c->layers.w1[l], c->p_w1, nullptr, c->au, nullptr));
+    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->au, c->layers.w2[l], c->p_w2, c->x, c->ah, gain_after));
   }
   GemmArgs lm{};
   lm.rowlist = c->st.rowlist;
@@ -354,6 +367,47 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   return TD_OK;
 }
 
+// The frozen context tower over the bound batch's block tokens (committed ids): embedding
+// without a position table, then per layer the fused QKV projection, attention that is
+// causal inside the block and sees the whole cached prefix, the append of this layer's
+// K/V to its cache at each sequence's current length, and the residual MLP.  The last
+// layer stops after its K/V.  The layer GEMMs test a flag that stays 0 (the step's flag
+// says the block is done).
+td_status enqueue_context_pass(td_ctx *c, const int32_t *tokens) {
+  const td_config &g = c->cfg;
+  const int M = c->n_seqs * g.block_size;
+  const int d = g.d_model, Hd = g.n_heads * g.head_dim;
+  StepState st = c->st;
+  st.done = c->zero_flag;
+  TD_HIP(c, launch_embed(g.dtype, tokens, c->ctx_tok_emb, nullptr, c->context.attn_norm[0], c->x, c->ssq, c->ah, M,
+                         g.block_size, d, g.vocab, st, c->stream));
+  c->gemm_done = c->zero_flag;
+  td_status s = TD_OK;
+  for (int l = 0; l < g.n_layers && s == TD_OK; ++l) {
+    s = enqueue_gemm(c, EPI_STORE, true, M, c->Nqkv, d, c->ah, c->context.wqkv[l], c->p_qkv, c->qkv, nullptr,
+                     nullptr);
+    const bool last = l + 1 == g.n_layers;
+    if (s == TD_OK && !last) s = enqueue_attention(c, l, c->qkv, nullptr, c->ao, nullptr, true);
+    if (s == TD_OK) {
+      const hipError_t e = launch_kv_append(g.dtype, c->qkv, c->Nqkv, g.n_heads, g.n_kv_heads, g.head_dim,
+                                            const_cast<void *>(c->kc[l]), const_cast<void *>(c->vc[l]), c->seq_lp_d,
+                                            c->seq_lp_d + c->n_seqs, c->n_seqs, g.block_size, c->stream);
+      if (e != hipSuccess) s = fail(c, TD_EDEVICE, "K/V append launch failed: %s", hipGetErrorString(e));
+    }
+    if (s == TD_OK && !last) {
+      s = enqueue_gemm(c, EPI_RESID, false, M, d, Hd, c->ao, c->context.wo[l], c->p_wo, c->x, c->ah,
+                       c->context.mlp_norm[l]);
+      if (s == TD_OK)
+        s = enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, c->ah, c->context.w1[l], c->p_w1, nullptr, c->au, nullptr);
+      if (s == TD_OK)
+        s = enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->au, c->context.w2[l], c->p_w2, c->x, c->ah,
+                         c->context.attn_norm[l + 1]);
+    }
+  }
+  c->gemm_done = nullptr;
+  return s;
+}
+
 td_status check_ctx(td_ctx *c) {
   if (!c) return fail(nullptr, TD_EINVAL, "ctx is NULL");
   return TD_OK;
@@ -370,13 +424,42 @@ void free_all(td_ctx *c) {
     if (p) (void)hipFree(p);
   };
   f(c->tok_emb); f(c->pos_emb); f(c->final_norm); f(c->lm_head);
-  for (auto *v : {&c->attn_norm, &c->mlp_norm, &c->wqkv, &c->wo, &c->w1, &c->w2})
-    for (void *p : *v) f(p);
+  for (Layers *t : {&c->layers, &c->context})
+    for (auto *v : {&t->attn_norm, &t->mlp_norm, &t->wqkv, &t->wo, &t->w1, &t->w2})
+      for (void *p : *v) f(p);
+  f(c->ctx_tok_emb); f(c->zero_flag); f(c->seq_lp_d);
   f(c->x); f(c->ssq); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->ah); f(c->ao); f(c->au);
   f(c->arg_row); f(c->state_ints); f(c->items_d); f(c->pair_first_d);
   f(c->pair_count_d); f(c->att_o); f(c->att_ml); f(c->part);
   for (hipEvent_t e : c->ev_start) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->ev_stop) (void)hipEventDestroy(e);
+}
+
+// Per-layer weights of a tower, packed into MFMA tiles (W_q, W_k, W_v fused).
+td_status pack_layers(td_ctx *c, const td_weights &w, Layers &t) {
+  const td_config &g = c->cfg;
+  const size_t e = c->elt, d = g.d_model, F = g.d_ff, L = g.n_layers;
+  const size_t Hd = (size_t)g.n_heads * g.head_dim, KVd = (size_t)g.n_kv_heads * g.head_dim;
+  t.attn_norm.assign(L, nullptr); t.mlp_norm.assign(L, nullptr); t.wqkv.assign(L, nullptr);
+  t.wo.assign(L, nullptr); t.w1.assign(L, nullptr); t.w2.assign(L, nullptr);
+  for (size_t l = 0; l < L; ++l) {
+    TD_TRY(dmalloc(c, &t.attn_norm[l], d * e));
+    TD_TRY(dmalloc(c, &t.mlp_norm[l], d * e));
+    TD_TRY(dmalloc(c, &t.wqkv[l], (size_t)c->Nqkv * d * e));
+    TD_TRY(dmalloc(c, &t.wo[l], d * Hd * e));
+    TD_TRY(dmalloc(c, &t.w1[l], F * d * e));
+    TD_TRY(dmalloc(c, &t.w2[l], d * F * e));
+    TD_HIP(c, hipMemcpyAsync(t.attn_norm[l], w.attn_norm[l], d * e, hipMemcpyDeviceToDevice, c->stream));
+    TD_HIP(c, hipMemcpyAsync(t.mlp_norm[l], w.mlp_norm[l], d * e, hipMemcpyDeviceToDevice, c->stream));
+    char *qkv = (char *)t.wqkv[l];
+    TD_HIP(c, launch_pack_weight(g.dtype, w.wq[l], qkv, (int)Hd, (int)d, c->stream));
+    TD_HIP(c, launch_pack_weight(g.dtype, w.wk[l], qkv + Hd * d * e, (int)KVd, (int)d, c->stream));
+    TD_HIP(c, launch_pack_weight(g.dtype, w.wv[l], qkv + (Hd + KVd) * d * e, (int)KVd, (int)d, c->stream));
+    TD_HIP(c, launch_pack_weight(g.dtype, w.wo[l], t.wo[l], (int)d, (int)Hd, c->stream));
+    TD_HIP(c, launch_pack_weight(g.dtype, w.w1[l], t.w1[l], (int)F, (int)d, c->stream));
+    TD_HIP(c, launch_pack_weight(g.dtype, w.w2[l], t.w2[l], (int)d, (int)F, c->stream));
+  }
+  return TD_OK;
 }
 
 td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
@@ -398,25 +481,7 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   TD_HIP(c, hipMemcpyAsync(c->pos_emb, w.pos_emb, (size_t)g.block_size * d * e, hipMemcpyDeviceToDevice, c->stream));
   TD_HIP(c, hipMemcpyAsync(c->final_norm, w.final_norm, d * e, hipMemcpyDeviceToDevice, c->stream));
   TD_HIP(c, launch_pack_weight(g.dtype, w.lm_head, c->lm_head, (int)V, (int)d, c->stream));
-  c->attn_norm.assign(L, nullptr); c->mlp_norm.assign(L, nullptr); c->wqkv.assign(L, nullptr);
-  c->wo.assign(L, nullptr); c->w1.assign(L, nullptr); c->w2.assign(L, nullptr);
-  for (size_t l = 0; l < L; ++l) {
-    TD_TRY(dmalloc(c, &c->attn_norm[l], d * e));
-    TD_TRY(dmalloc(c, &c->mlp_norm[l], d * e));
-    TD_TRY(dmalloc(c, &c->wqkv[l], (size_t)c->Nqkv * d * e));
-    TD_TRY(dmalloc(c, &c->wo[l], d * Hd * e));
-    TD_TRY(dmalloc(c, &c->w1[l], F * d * e));
-    TD_TRY(dmalloc(c, &c->w2[l], d * F * e));
-    TD_HIP(c, hipMemcpyAsync(c->attn_norm[l], w.attn_norm[l], d * e, hipMemcpyDeviceToDevice, c->stream));
-    TD_HIP(c, hipMemcpyAsync(c->mlp_norm[l], w.mlp_norm[l], d * e, hipMemcpyDeviceToDevice, c->stream));
-    char *qkv = (char *)c->wqkv[l];
-    TD_HIP(c, launch_pack_weight(g.dtype, w.wq[l], qkv, (int)Hd, (int)d, c->stream));
-    TD_HIP(c, launch_pack_weight(g.dtype, w.wk[l], qkv + Hd * d * e, (int)KVd, (int)d, c->stream));
-    TD_HIP(c, launch_pack_weight(g.dtype, w.wv[l], qkv + (Hd + KVd) * d * e, (int)KVd, (int)d, c->stream));
-    TD_HIP(c, launch_pack_weight(g.dtype, w.wo[l], c->wo[l], (int)d, (int)Hd, c->stream));
-    TD_HIP(c, launch_pack_weight(g.dtype, w.w1[l], c->w1[l], (int)F, (int)d, c->stream));
-    TD_HIP(c, launch_pack_weight(g.dtype, w.w2[l], c->w2[l], (int)d, (int)F, c->stream));
-  }
+  TD_TRY(pack_layers(c, w, c->layers));
 
   // Workspace sized for max_batch.
   TD_TRY(dmalloc(c, &c->x, M * d * 4));
@@ -432,6 +497,9 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   TD_TRY(dmalloc(c, &c->conf_row, M * 4));
   TD_TRY(dmalloc(c, &c->arg_row, M * 4));
   TD_TRY(dmalloc(c, &c->vpart, M * (V / 16) * sizeof(VStat)));   // up to one group per 16 columns
+  TD_TRY(dmalloc(c, &c->seq_lp_d, 2 * (size_t)g.max_batch * sizeof(int)));
+  TD_TRY(dmalloc(c, &c->zero_flag, sizeof(int)));
+  TD_HIP(c, hipMemsetAsync(c->zero_flag, 0, sizeof(int), c->stream));
   TD_TRY(dmalloc(c, &c->state_ints, (2 * M + 8) * sizeof(int)));
   TD_HIP(c, hipMemsetAsync(c->state_ints, 0, (2 * M + 8) * sizeof(int), c->stream));
   int *si = c->state_ints;
@@ -476,26 +544,32 @@ td_status td_create(const td_config *cfg, const td_weights *w, void *stream, td_
   return TD_OK;
 }
 
-td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const void *const *k_cache_host,
-                        const void *const *v_cache_host) {
-  TD_TRY(check_ctx(c));
+// Binds caches whose sequence i holds len[i] tokens in cap[i] reserved pages, the pages
+// of sequence i starting after those of sequences 0..i-1.
+td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const int64_t *cap,
+                    const void *const *k_cache_host, const void *const *v_cache_host) {
   const td_config &g = c->cfg;
-  if (n_seqs < 1 || n_seqs > g.max_batch) return fail(c, TD_EINVAL, "n_seqs must be in [1, max_batch=%d]", g.max_batch);
-  if (!off || !k_cache_host || !v_cache_host) return fail(c, TD_EINVAL, "NULL offsets or cache array");
-  if (off[0] != 0) return fail(c, TD_EINVAL, "prefix_offsets[0] must be 0");
-  for (int i = 0; i < n_seqs; ++i)
-    if (off[i + 1] < off[i]) return fail(c, TD_EINVAL, "prefix_offsets must be non-decreasing");
-  if (off[n_seqs] > g.max_prefix_tokens)
-    return fail(c, TD_ENOMEM, "sum of prefix lengths %lld exceeds max_prefix_tokens %lld", (long long)off[n_seqs],
+  int64_t total = 0, pages = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    if (len[i] < 0 || len[i] > (int64_t)1 << 30) return fail(c, TD_EINVAL, "length of sequence %d out of range", i);
+    if (cap[i] < (len[i] + KV_PAGE - 1) / KV_PAGE)
+      return fail(c, TD_EINVAL, "sequence %d: %lld tokens do not fit %lld pages", i, (long long)len[i],
+                  (long long)cap[i]);
+    total += len[i];
+    pages += cap[i];
+  }
+  if (total > g.max_prefix_tokens)
+    return fail(c, TD_ENOMEM, "sum of prefix lengths %lld exceeds max_prefix_tokens %lld", (long long)total,
                 (long long)g.max_prefix_tokens);
+  if (pages > ((int64_t)1 << 31) - 1) return fail(c, TD_EINVAL, "too many cache pages");
   for (int l = 0; l < g.n_layers; ++l)
-    if (off[n_seqs] > 0 && (!k_cache_host[l] || !v_cache_host[l]))
+    if (pages > 0 && (!k_cache_host[l] || !v_cache_host[l]))
       return fail(c, TD_EINVAL, "cache pointer of layer %d is NULL", l);
   TD_HIP(c, hipSetDevice(c->dev));
   TD_HIP(c, hipStreamSynchronize(c->stream));   // previous work may still read the old binding
 
-  for (int i = 0; i < n_seqs; ++i)
-    if (off[i + 1] - off[i] > (int64_t)1 << 30) return fail(c, TD_EINVAL, "prefix of sequence %d too long", i);
+  std::vector<int64_t> off(n_seqs + 1, 0);
+  for (int i = 0; i < n_seqs; ++i) off[i + 1] = off[i] + len[i];
   const int G = g.n_heads / g.n_kv_heads, R = G * g.block_size;
   const int tc = chunk_keys(off[n_seqs] * g.n_kv_heads, R);
   // Few-row path: the pair's first item also takes the block's keys (no item of its own,
@@ -516,7 +590,7 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
       if (!few) items.push_back(AttnItem{i, h, 0, 0, 1, pair, 0});
       pcount.push_back((int)items.size() - pfirst.back());
     }
-    page_base += (P + KV_PAGE - 1) / KV_PAGE;
+    page_base += cap[i];
   }
   if (items.size() > ((size_t)1 << 28)) return fail(c, TD_EINVAL, "too many attention work items");
   auto grow = [&](auto **p, size_t &cap, size_t need, size_t elt) -> td_status {
@@ -558,13 +632,50 @@ td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const voi
       if (plans[i]->splits > 1) need = std::max(need, (size_t)plans[i]->splits * M * widths[i]);
     TD_TRY(grow(&c->part, c->part_cap, need, sizeof(float)));
   }
-  c->offsets.assign(off, off + n_seqs + 1);
+  {  // per-sequence length and first page for the K/V append
+    std::vector<int> lp(2 * n_seqs);
+    int64_t pb = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+      lp[i] = (int)len[i];
+      lp[n_seqs + i] = (int)pb;
+      pb += cap[i];
+    }
+    TD_HIP(c, hipMemcpy(c->seq_lp_d, lp.data(), lp.size() * sizeof(int), hipMemcpyHostToDevice));
+  }
+  c->lengths.assign(len, len + n_seqs);
+  c->caps.assign(cap, cap + n_seqs);
   c->kc.assign(k_cache_host, k_cache_host + g.n_layers);
   c->vc.assign(v_cache_host, v_cache_host + g.n_layers);
   c->n_items = (int)items.size();
   c->n_pairs = (int)pfirst.size();
   c->n_seqs = n_seqs;
   return TD_OK;
+}
+
+td_status td_set_prefix(td_ctx *c, int32_t n_seqs, const int64_t *off, const void *const *k_cache_host,
+                        const void *const *v_cache_host) {
+  TD_TRY(check_ctx(c));
+  const td_config &g = c->cfg;
+  if (n_seqs < 1 || n_seqs > g.max_batch) return fail(c, TD_EINVAL, "n_seqs must be in [1, max_batch=%d]", g.max_batch);
+  if (!off || !k_cache_host || !v_cache_host) return fail(c, TD_EINVAL, "NULL offsets or cache array");
+  if (off[0] != 0) return fail(c, TD_EINVAL, "prefix_offsets[0] must be 0");
+  std::vector<int64_t> len(n_seqs), cap(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    if (off[i + 1] < off[i]) return fail(c, TD_EINVAL, "prefix_offsets must be non-decreasing");
+    len[i] = off[i + 1] - off[i];
+    cap[i] = (len[i] + KV_PAGE - 1) / KV_PAGE;
+  }
+  return bind_impl(c, n_seqs, len.data(), cap.data(), k_cache_host, v_cache_host);
+}
+
+td_status td_bind_cache(td_ctx *c, int32_t n_seqs, const int64_t *lengths_host, const int64_t *page_capacity_host,
+                        const void *const *k_cache_host, const void *const *v_cache_host) {
+  TD_TRY(check_ctx(c));
+  const td_config &g = c->cfg;
+  if (n_seqs < 1 || n_seqs > g.max_batch) return fail(c, TD_EINVAL, "n_seqs must be in [1, max_batch=%d]", g.max_batch);
+  if (!lengths_host || !page_capacity_host || !k_cache_host || !v_cache_host)
+    return fail(c, TD_EINVAL, "NULL lengths, capacities or cache array");
+  return bind_impl(c, n_seqs, lengths_host, page_capacity_host, k_cache_host, v_cache_host);
 }
 
 td_status td_denoise_step(td_ctx *c, int32_t *tokens, uint8_t *committed, const float *inv_temp, float gamma,
@@ -607,6 +718,48 @@ td_status td_set_commit_rule(td_ctx *c, int32_t rule, int32_t min_adopt) {
   c->rule = RULE_THRESHOLD;
   c->min_adopt = min_adopt;
   return TD_OK;
+}
+
+td_status td_set_context_tower(td_ctx *c, const td_weights *w) {
+  TD_TRY(check_ctx(c));
+  if (validate_weights(c->cfg, w, true) != TD_OK) return fail(c, TD_EINVAL, "%s", g_create_error.c_str());
+  TD_HIP(c, hipSetDevice(c->dev));
+  TD_HIP(c, hipStreamSynchronize(c->stream));   // a previous context tower may still be in use
+  auto f = [](void *p) {
+    if (p) (void)hipFree(p);
+  };
+  for (auto *v : {&c->context.attn_norm, &c->context.mlp_norm, &c->context.wqkv, &c->context.wo, &c->context.w1,
+                  &c->context.w2}) {
+    for (void *p : *v) f(p);
+    v->clear();
+  }
+  f(c->ctx_tok_emb);
+  c->ctx_tok_emb = nullptr;
+  const size_t e = c->elt, d = c->cfg.d_model, V = c->cfg.vocab;
+  TD_TRY(dmalloc(c, &c->ctx_tok_emb, (V + 1) * d * e));
+  TD_HIP(c, hipMemcpyAsync(c->ctx_tok_emb, w->tok_emb, (V + 1) * d * e, hipMemcpyDeviceToDevice, c->stream));
+  TD_TRY(pack_layers(c, *w, c->context));
+  TD_HIP(c, hipStreamSynchronize(c->stream));
+  return TD_OK;
+}
+
+td_status td_append_block(td_ctx *c, const int32_t *tokens) {
+  TD_TRY(check_ctx(c));
+  if (!tokens) return fail(c, TD_EINVAL, "tokens must not be NULL");
+  if (!c->ctx_tok_emb) return fail(c, TD_EINVAL, "no context tower: call td_set_context_tower first");
+  TD_TRY(check_bound(c));
+  const int B = c->cfg.block_size;
+  std::vector<int64_t> len = c->lengths;
+  for (int i = 0; i < c->n_seqs; ++i) {
+    if (len[i] + B > c->caps[i] * KV_PAGE)
+      return fail(c, TD_EINVAL, "sequence %d: no room for %d more tokens (%lld tokens, %lld pages)", i, B,
+                  (long long)len[i], (long long)c->caps[i]);
+    len[i] += B;
+  }
+  TD_TRY(enqueue_context_pass(c, tokens));
+  const std::vector<int64_t> cap = c->caps;
+  const std::vector<const void *> kc = c->kc, vc = c->vc;
+  return bind_impl(c, c->n_seqs, len.data(), cap.data(), kc.data(), vc.data());
 }
 
 td_status td_debug_attention(td_ctx *c, int32_t layer, const void *qkv, void *o) {

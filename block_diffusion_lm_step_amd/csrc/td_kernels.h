@@ -107,6 +107,7 @@ struct AttnItem {
 };
 struct AttnArgs {
   int B, H, Hkv, hd, Nqkv, G, R;   // R = G * B query rows per (seq, kv head)
+  int causal;                      // 1: block query p sees block keys 0..p only (context tower)
   const float *qkv;                // [n*B][Nqkv]: q | k_block | v_block (fp32)
   const void *kc, *vc;             // prefix cache pages (layout above)
   const AttnItem *items; int n_items;
@@ -154,5 +155,10 @@ struct CommitArgs {
   StepState st;
 };
 hipError_t launch_merge_commit(const CommitArgs &a, int max_rows, hipStream_t s);
+// K/V of the block rows of qkv ([n*B][Nqkv] fp32: q | k | v) appended to one layer's cache
+// (layout above; bf16 caches round to nearest even): row seq*B + p is token
+// seq_len[seq] + p of sequence seq, whose pages start at seq_page[seq].
+hipError_t launch_kv_append(int dtype, const float *qkv, int Nqkv, int H, int Hkv, int hd, void *kc, void *vc,
+                            const int *seq_len, const int *seq_page, int n, int B, hipStream_t s);
 
 }  // namespace td

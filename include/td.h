@@ -112,6 +112,37 @@ td_status td_create(const td_config *cfg, const td_weights *w, void *stream, td_
 td_status td_set_prefix(td_ctx *ctx, int32_t n_seqs, const int64_t *prefix_offsets_host,
                         const void *const *k_cache_host, const void *const *v_cache_host);
 
+/* Bind caches with room to grow (multi-block generation): sequence i holds
+ * lengths_host[i] tokens in page_capacity_host[i] reserved pages (32 tokens each,
+ * lengths_host[i] <= 32 * page_capacity_host[i]); its pages start after the reserved
+ * pages of sequences 0..i-1, in the layout above.  td_set_prefix is this call with no
+ * room (page_capacity = ceil(length / 32)).  Same ownership, errors and workspace
+ * growth as td_set_prefix. */
+td_status td_bind_cache(td_ctx *ctx, int32_t n_seqs, const int64_t *lengths_host, const int64_t *page_capacity_host,
+                        const void *const *k_cache_host, const void *const *v_cache_host);
+
+/* The frozen context tower that writes the cache: the causal tower whose cached K/V the
+ * denoiser reads (poko-everyday.com Nemotron-TwoTower news item, section 技術/ビジネス面;
+ * dzen.guru, section "Что нового": frozen).  Same shapes and storage dtype as the
+ * denoiser; tok_emb [vocab+1][d] and every per-layer pointer are read, pos_emb,
+ * final_norm and lm_head are ignored (may be NULL).  The tower has no position table:
+ * its causal mask orders the tokens.  Device pointers, copied and packed into the ctx
+ * (the caller may free them afterwards); a later call replaces the tower.
+ * Errors: TD_EINVAL for a NULL pointer, TD_ENOMEM. */
+td_status td_set_context_tower(td_ctx *ctx, const td_weights *w);
+
+/* Append a committed block to the prefix (the loop of multi-block generation): run the
+ * context tower over tokens [n][B] (committed vocabulary ids, e.g. the output of
+ * td_generate_block) -- every block query attends to its sequence's whole cached prefix
+ * and causally to the block's earlier positions -- and write each layer's K/V of the B
+ * tokens into that layer's cache at positions length .. length+B-1 (bf16 towers round
+ * to nearest even), then advance every bound length by B and rebuild the work lists.
+ * The next td_generate_block then continues after the appended block.  Needs
+ * td_set_context_tower and a binding with room for B more tokens per sequence
+ * (td_bind_cache); otherwise TD_EINVAL and nothing is enqueued.  Waits for the ctx's
+ * stream before returning (the work lists are rebuilt on the host). */
+td_status td_append_block(td_ctx *ctx, const int32_t *tokens);
+
 /* One denoising step over the bound batch.
  *  tokens     int32 [n][B] in/out: a token id, or vocab ([MASK]) exactly where
  *             committed == 0.

@@ -324,13 +324,15 @@ def oracle_step(tower: OracleTower, tok: np.ndarray, committed: np.ndarray, tau:
 
 def oracle_generate_blocks(tower: OracleTower, context: OracleContextTower, n_blocks: int, S: int, B: int,
                            tau: np.ndarray, gamma: float, kv: KVProvider, seqs: Optional[Sequence[int]] = None,
-                           cache_bf16: bool = True, rule: int = RULE_THRESHOLD, min_adopt: int = 1):
+                           cache_bf16: bool = True, rule: int = RULE_THRESHOLD, min_adopt: int = 1,
+                           return_kv: bool = False):
     """Generation of n_blocks consecutive blocks: each block is refined to completion by
     the block loop; the context tower then runs over its tokens and their K/V (rounded
     to bf16 when the cache holds bf16) are appended to every layer's cache, so the next
     block sees them as prefix.  The same inverse temperatures serve every block.
 
-    Returns (tok [n_blocks][S][B], commit_step [n_blocks][S][B], steps [n_blocks][S]).
+    Returns (tok [n_blocks][S][B], commit_step [n_blocks][S][B], steps [n_blocks][S]) and,
+    with return_kv, the appended {(layer, seq): [(k, v) [B][Hkv][hd] per block]} as stored.
     """
     seqs = list(range(S)) if seqs is None else list(seqs)
     added: Dict[Tuple[int, int], List[Tuple[np.ndarray, np.ndarray]]] = {}
@@ -355,6 +357,8 @@ def oracle_generate_blocks(tower: OracleTower, context: OracleContextTower, n_bl
             for i, s in enumerate(seqs):
                 kk, vv = (round_bf16(k[i]), round_bf16(v[i])) if cache_bf16 else (k[i], v[i])
                 added.setdefault((l, s), []).append((kk, vv))
+    if return_kv:
+        return np.stack(toks), np.stack(csteps), np.stack(steps), added
     return np.stack(toks), np.stack(csteps), np.stack(steps)
 
 

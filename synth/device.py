@@ -64,20 +64,26 @@ def page_prefix(k: np.ndarray, v: np.ndarray, page: int = KV_PAGE):
     return np.ascontiguousarray(kp), np.ascontiguousarray(vp)
 
 
-def prefix_to_device(w: Workload, plens: Sequence[int], device="cuda", layers: int = None
+def cache_pages(plens: Sequence[int], room: int = 0) -> List[int]:
+    """Pages reserved per sequence: its prefix plus `room` more tokens."""
+    return [(int(p) + int(room) + KV_PAGE - 1) // KV_PAGE for p in plens]
+
+
+def prefix_to_device(w: Workload, plens: Sequence[int], device="cuda", layers: int = None, room: int = 0
                      ) -> Tuple[List[int], List, List]:
     """Per-layer paged prefix caches for a batch with prefix lengths plens.
 
-    Returns (token offsets [n+1], K caches, V caches); sequence s owns ceil(P_s / 32)
-    consecutive pages starting after the pages of sequences 0..s-1.
+    Returns (token offsets [n+1], K caches, V caches); sequence s owns cache_pages(plens,
+    room)[s] consecutive pages (its prefix, then room for `room` appended tokens) starting
+    after the pages of sequences 0..s-1.
     """
     torch = _torch()
     offsets = [0]
     for p in plens:
         offsets.append(offsets[-1] + int(p))
     page_off = [0]
-    for p in plens:
-        page_off.append(page_off[-1] + (int(p) + KV_PAGE - 1) // KV_PAGE)
+    for c in cache_pages(plens, room):
+        page_off.append(page_off[-1] + c)
     npages = max(page_off[-1], 1)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     bf = w.dtype == "bf16"
@@ -93,8 +99,9 @@ def prefix_to_device(w: Workload, plens: Sequence[int], device="cuda", layers: i
                 k = draw_prefix_kv(w, l, s, int(P), "k", pool=pool)
                 v = draw_prefix_kv(w, l, s, int(P), "v", pool=pool)
                 kp, vp = page_prefix(k, v)
-                kt[page_off[s]:page_off[s + 1]] = host_to_device(kp, bf, device)
-                vt[page_off[s]:page_off[s + 1]] = host_to_device(vp, bf, device)
+                n_pg = kp.shape[0]
+                kt[page_off[s]:page_off[s] + n_pg] = host_to_device(kp, bf, device)
+                vt[page_off[s]:page_off[s] + n_pg] = host_to_device(vp, bf, device)
             ks.append(kt)
             vs.append(vt)
     return offsets, ks, vs

@@ -14,7 +14,7 @@ def mini_workload(**kw) -> Workload:
 
 def oracle_weights(tw) -> dict:
     """Stored tower values widened exactly to float32, keyed as the oracle expects."""
-    f = tw.as_f32
+    f = lambda a: None if a is None else tw.as_f32(a)  # noqa: E731  (the context tower has no pos/final/head)
     return dict(tok_emb=f(tw.tok_emb), pos_emb=f(tw.pos_emb), final_norm=f(tw.final_norm), lm_head=f(tw.lm_head),
                 wq=[f(a) for a in tw.wq], wk=[f(a) for a in tw.wk], wv=[f(a) for a in tw.wv],
                 wo=[f(a) for a in tw.wo], w1=[f(a) for a in tw.w1], w2=[f(a) for a in tw.w2],
