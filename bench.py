@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--breakdown", action="store_true", help="also time each kernel class (extra blocks)")
+    p.add_argument("--blocks", type=int, default=0,
+                   help="also time K consecutive blocks of multi-block generation (each block generated, then "
+                        "appended to the prefix by the context tower): reported under 'multiblock'")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="before the timed region, one device-to-device copy of this many MiB (a plain copy "
                         "kernel of known size, the scale of the HBM byte counters)")
@@ -199,6 +202,51 @@ def cpu_baseline(w, budget_s: float):
                 denoise_steps_per_s=steps / dt, seconds=dt)
 
 
+def time_multiblock(args, w, plens, tau, dev, tok, com, steps) -> dict:
+    """K consecutive blocks of multi-block generation on caches bound with room for them:
+    each block is generated, then the context tower appends its K/V to the prefix.  The
+    binding is reset to the original prefix before each timed repetition."""
+    import torch
+
+    from synth import draw_tower
+    from synth.device import cache_pages, prefix_to_device, tower_to_device
+
+    K = args.blocks
+    room = K * w.B
+    _, ks, vs = prefix_to_device(w, plens, room=room)
+    caps = cache_pages(plens, room)
+    dev.set_context_tower(tower_to_device(draw_tower(w, context=True)))
+    lengths = [int(p) for p in plens]
+
+    def run():
+        dev.bind_cache(lengths, caps, ks, vs)
+        t_gen = t_app = 0.0
+        for _ in range(K):
+            a = time.perf_counter()
+            dev.generate_block(tok, com, tau, w.gamma, steps=steps)
+            dev.sync()
+            b = time.perf_counter()
+            dev.append_block(tok)
+            dev.sync()
+            t_gen += b - a
+            t_app += time.perf_counter() - b
+        return t_gen, t_app
+
+    run()
+    reps = 3
+    tg = ta = 0.0
+    for _ in range(reps):
+        g, a = run()
+        tg += g
+        ta += a
+    tg, ta = tg / reps, ta / reps
+    log(f"[bench] multi-block: {K} blocks, generate {tg * 1e3:.2f} ms, append {ta * 1e3:.2f} ms")
+    return dict(blocks=K, value=round(K * w.n * w.B / (tg + ta), 3), unit="committed tokens/s",
+                ms_per_block_generate=round(tg * 1e3 / K, 4), ms_per_block_append=round(ta * 1e3 / K, 4),
+                timing="host clock around each call with a stream sync after it (the append rebuilds the "
+                       "work lists on the host)")
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -228,7 +276,8 @@ def main():
     plens = draw_prefix_lengths(w)
     offsets, ks, vs = prefix_to_device(w, plens)
     tau = torch.from_numpy(draw_inv_temp(w)).cuda()
-    dev = Denoiser(tower_config(w, max_batch=w.n, max_prefix_tokens=max(1, offsets[-1])), dW)
+    room = args.blocks * w.B * w.n   # tokens appended by --blocks
+    dev = Denoiser(tower_config(w, max_batch=w.n, max_prefix_tokens=max(1, offsets[-1] + room)), dW)
     dev.set_prefix(offsets, ks, vs)
     del dW
     torch.cuda.synchronize()
@@ -296,6 +345,10 @@ def main():
         breakdown["step_alg_bytes"] = step_bytes
         breakdown["step_hbm_frac"] = step_bytes / (breakdown["step"]["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS
 
+    multiblock = None
+    if args.blocks > 0:
+        multiblock = time_multiblock(args, w, plens, tau, dev, tok, com, steps)
+
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 3),
@@ -322,6 +375,8 @@ def main():
     }
     if breakdown:
         out["breakdown"] = breakdown
+    if multiblock:
+        out["multiblock"] = multiblock
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -1,6 +1,6 @@
 """GPU parity of multi-block generation: td_generate_block, then td_append_block (the
 frozen context tower's causal pass over the block and the K/V append into caches bound
-with room), repeated for three blocks.
+with room), repeated for three blocks on small towers and two at full size (batch 1, prefix 4096).
 
 Every block of every sequence is compared with the oracle's multi-block loop: tokens,
 commit steps and step counts exactly.  The appended cache entries are compared with the
@@ -31,7 +31,7 @@ class MB:
     pass
 
 
-@pytest.fixture(scope="module", params=sorted(CASES))
+@pytest.fixture(scope="module", params=sorted(CASES) + ["b1_p4096"])
 def mb(request):
     import torch
 
@@ -41,14 +41,20 @@ def mb(request):
     from synth.device import cache_pages, prefix_to_device, tower_config, tower_to_device
     from tests.helpers import kv_provider, oracle_weights
 
+    from synth import get_workload
     m = MB()
-    m.w = w = Workload(name=request.param, tower="mb_" + request.param, weight_std=0.02, **CASES[request.param])
+    if request.param in CASES:
+        m.w = w = Workload(name=request.param, tower="mb_" + request.param, weight_std=0.02, **CASES[request.param])
+        m.blocks = N_BLOCKS
+    else:   # full size: the single-sequence 4096-prefix workload, two blocks
+        m.w = w = get_workload(request.param)
+        m.blocks = 2
     log(f"[mb] building {w.name}")
     tw, tc = draw_tower(w), draw_tower(w, context=True)
     m.plens = draw_prefix_lengths(w)
     m.tau = draw_inv_temp(w)
     m.kv = kv_provider(w, m.plens)
-    room = N_BLOCKS * w.B
+    room = m.blocks * w.B
     m.caps = cache_pages(m.plens, room)
     m.page_off = np.concatenate([[0], np.cumsum(m.caps)]).astype(int)
     _, m.ks, m.vs = prefix_to_device(w, m.plens, room=room)
@@ -82,10 +88,11 @@ def test_generate_and_append_blocks(mb):
     from oracle import oracle_generate_blocks
     w, torch = mb.w, mb.torch
     bf = w.dtype == "bf16"
-    toks_o, cs_o, st_o, added = oracle_generate_blocks(mb.orc, mb.ctx, N_BLOCKS, w.n, w.B, mb.tau, w.gamma, mb.kv,
+    nb = mb.blocks
+    toks_o, cs_o, st_o, added = oracle_generate_blocks(mb.orc, mb.ctx, nb, w.n, w.B, mb.tau, w.gamma, mb.kv,
                                                       cache_bf16=bf, return_kv=True)
     before = [(k.float().cpu().numpy().copy(), v.float().cpu().numpy().copy()) for k, v in zip(mb.ks, mb.vs)]
-    for b in range(N_BLOCKS):
+    for b in range(nb):
         tok = torch.zeros((w.n, w.B), dtype=torch.int32, device="cuda")
         com = torch.zeros((w.n, w.B), dtype=torch.uint8, device="cuda")
         steps = torch.zeros(w.n, dtype=torch.int32, device="cuda")
@@ -103,7 +110,7 @@ def test_generate_and_append_blocks(mb):
         kt, vt = mb.ks[l].float().cpu().numpy(), mb.vs[l].float().cpu().numpy()
         for s in range(w.n):
             P = int(mb.plens[s])
-            kg, vg = _unpage(w, kt, vt, mb.page_off[s], P, P + N_BLOCKS * w.B)
+            kg, vg = _unpage(w, kt, vt, mb.page_off[s], P, P + nb * w.B)
             ko = np.concatenate([e[0] for e in added[(l, s)]])
             vo = np.concatenate([e[1] for e in added[(l, s)]])
             for g, o in ((kg, ko), (vg, vo)):
@@ -118,7 +125,7 @@ def test_generate_and_append_blocks(mb):
             assert np.array_equal(ka, kb) and np.array_equal(va, vb), "prefix entries changed"
         # pages of no sequence's tokens (the slack after each sequence's tokens) untouched
         for s in range(w.n):
-            end_tok = int(mb.plens[s]) + N_BLOCKS * w.B
+            end_tok = int(mb.plens[s]) + nb * w.B
             first_free = mb.page_off[s] + (end_tok + 31) // 32
             assert np.array_equal(kt[first_free:mb.page_off[s + 1]], before[l][0][first_free:mb.page_off[s + 1]])
     log(f"[{w.name}] appended K/V: worst relative error {worst:.2e}, identical {same}/{total}")
