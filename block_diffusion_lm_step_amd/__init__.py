@@ -54,6 +54,7 @@ try:
                                   POINTER(c_void_p)]
     lib.td_set_context_tower.argtypes = [_CTX, POINTER(TdWeights)]
     lib.td_append_block.argtypes = [_CTX, c_void_p]
+    lib.td_ar_step.argtypes = [_CTX, c_void_p]
     lib.td_debug_attention.argtypes = [_CTX, c_int32, c_void_p, c_void_p]
     lib.td_sync.argtypes = [_CTX]
     lib.td_profile_begin.argtypes = [_CTX, c_int32]
@@ -68,14 +69,15 @@ try:
     lib.td_last_error.restype = c_char_p
     lib.td_version.restype = c_char_p
     for _f in ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_generate_block",
-               "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_debug_attention", "td_sync"):
+               "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_ar_step", "td_debug_attention",
+               "td_sync"):
         getattr(lib, _f).restype = c_int
 except AttributeError as e:   # a library built from older sources
     raise ImportError(f"{LIB_PATH} is stale ({e}); rebuild with `python block_diffusion_lm_step_amd/build.py`") from e
 
 # Every symbol the C header declares.
 EXPORTED = ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_generate_block",
-            "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_debug_attention", "td_sync",
+            "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_ar_step", "td_debug_attention", "td_sync",
             "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_destroy", "td_last_error", "td_version")
 TD_PROF_OFF, TD_PROF_LMHEAD, TD_PROF_GEMM, TD_PROF_ATTENTION, TD_PROF_STEP = range(5)
 TD_RULE_THRESHOLD, TD_RULE_LEFT_TO_RIGHT = range(2)
@@ -151,14 +153,19 @@ class Denoiser:
         self._prefix_refs = (list(k_caches), list(v_caches))   # borrowed by the ctx
 
     def set_context_tower(self, weights: Dict) -> None:
-        """weights: tok_emb and the per-layer lists, as for the denoiser (no pos/final/head)."""
+        """weights: tok_emb and the per-layer lists, as for the denoiser; final_norm and lm_head
+        optional (AR decoding)."""
         keep = {k: _ptr_array(weights[k]) for k in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w1", "w2")}
+        head = [weights[k].data_ptr() if weights.get(k) is not None else None for k in ("final_norm", "lm_head")]
         w = TdWeights(weights["tok_emb"].data_ptr(), None, keep["attn_norm"], keep["wq"], keep["wk"], keep["wv"],
-                      keep["wo"], keep["mlp_norm"], keep["w1"], keep["w2"], None, None)
+                      keep["wo"], keep["mlp_norm"], keep["w1"], keep["w2"], head[0], head[1])
         self._check(lib.td_set_context_tower(self._ctx, ctypes.byref(w)))
 
     def append_block(self, tokens) -> None:
         self._check(lib.td_append_block(self._ctx, _ptr(tokens)))
+
+    def ar_step(self, tokens) -> None:
+        self._check(lib.td_ar_step(self._ctx, _ptr(tokens)))
 
     def denoise_step(self, tokens, committed, inv_temp, gamma: float, newly=None, conf=None, argmax=None,
                      logits=None) -> None:

@@ -44,8 +44,9 @@ struct td_ctx {
   void *tok_emb = nullptr, *pos_emb = nullptr, *final_norm = nullptr, *lm_head = nullptr;
   Layers layers;
   // frozen context tower (td_set_context_tower)
-  void *ctx_tok_emb = nullptr;
+  void *ctx_tok_emb = nullptr, *ctx_final_norm = nullptr, *ctx_lm_head = nullptr;
   Layers context;
+  uint8_t *ar_committed = nullptr;   // [max_batch] adoption flags of an AR step
   int *zero_flag = nullptr;          // a loop-exit flag that stays 0 (the context pass)
   const int *gemm_done = nullptr;    // flag the layer GEMMs test; nullptr: the step's
 
@@ -134,8 +135,8 @@ td_status validate_config(const td_config *cfg) {
   if (c.head_dim != 64 && c.head_dim != 128) return fail(nullptr, TD_EINVAL, "head_dim must be 64 or 128");
   if (c.n_heads < 1 || c.n_kv_heads < 1 || c.n_heads % c.n_kv_heads)
     return fail(nullptr, TD_EINVAL, "n_heads must be a positive multiple of n_kv_heads");
-  if (c.block_size != 8 && c.block_size != 16 && c.block_size != 32)
-    return fail(nullptr, TD_EINVAL, "block_size must be 8, 16 or 32");
+  if (c.block_size != 1 && c.block_size != 8 && c.block_size != 16 && c.block_size != 32)
+    return fail(nullptr, TD_EINVAL, "block_size must be 1, 8, 16 or 32");
   if (c.max_batch < 1 || (int64_t)c.max_batch * c.block_size > (1 << 20))
     return fail(nullptr, TD_EINVAL, "max_batch must be in [1, 2^20 / block_size]");
   if (c.max_prefix_tokens < 0 || c.max_prefix_tokens > ((int64_t)1 << 40))
@@ -316,6 +317,10 @@ td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const
   return TD_OK;
 }
 
+td_status enqueue_head_commit(td_ctx *c, const void *head, int *tokens, uint8_t *committed, const float *inv_temp,
+                              float gamma, int rule, int min_adopt, uint8_t *newly, float *conf_out, int *argmax_out,
+                              float *logits, int *steps, int8_t *commit_step);
+
 td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *inv_temp, float gamma,
                        uint8_t *newly, float *conf_out, int *argmax_out, float *logits, int *steps,
                        int8_t *commit_step) {
@@ -333,6 +338,21 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
     TD_TRY(enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, c->ah, c->layers.w1[l], c->p_w1, nullptr, c->au, nullptr));
     TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->au, c->layers.w2[l], c->p_w2, c->x, c->ah, gain_after));
   }
+  TD_TRY(enqueue_head_commit(c, c->lm_head, tokens, committed, inv_temp, gamma, c->rule, c->min_adopt, newly, conf_out,
+                             argmax_out, logits, steps, commit_step));
+  TD_TRY(prof_mark(c, TD_PROF_STEP, false));
+  return TD_OK;
+}
+
+// The LM head (head: packed [vocab][d]) with the fused vocabulary statistics over the rows
+// still masked, then the merge and the adoption rule.  The head's input is c->ah, the
+// last residual update's x * final gain, with its sums of squares in c->ssq.
+td_status enqueue_head_commit(td_ctx *c, const void *head, int *tokens, uint8_t *committed, const float *inv_temp,
+                              float gamma, int rule, int min_adopt, uint8_t *newly, float *conf_out, int *argmax_out,
+                              float *logits, int *steps, int8_t *commit_step) {
+  const td_config &g = c->cfg;
+  const int M = c->n_seqs * g.block_size;
+  const int d = g.d_model;
   GemmArgs lm{};
   lm.rowlist = c->st.rowlist;
   lm.rowpos = c->st.rowpos;
@@ -341,7 +361,7 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   lm.vpart = c->vpart;
   lm.logits = logits;
   TD_TRY(prof_mark(c, TD_PROF_LMHEAD, true));
-  TD_TRY(enqueue_gemm(c, EPI_VSTAT, true, M, g.vocab, d, c->ah, c->lm_head, c->p_lm, nullptr, nullptr, nullptr, &lm));
+  TD_TRY(enqueue_gemm(c, EPI_VSTAT, true, M, g.vocab, d, c->ah, head, c->p_lm, nullptr, nullptr, nullptr, &lm));
   TD_TRY(prof_mark(c, TD_PROF_LMHEAD, false));
   CommitArgs ca{};
   ca.V = g.vocab;
@@ -354,8 +374,8 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   ca.tokens = tokens;
   ca.committed = committed;
   ca.gamma = gamma;
-  ca.rule = c->rule;
-  ca.min_adopt = c->min_adopt;
+  ca.rule = rule;
+  ca.min_adopt = min_adopt;
   ca.newly = newly;
   ca.conf_out = conf_out;
   ca.argmax_out = argmax_out;
@@ -363,7 +383,6 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   ca.commit_step = commit_step;
   ca.st = c->st;
   TD_HIP(c, launch_merge_commit(ca, M, c->stream));
-  TD_TRY(prof_mark(c, TD_PROF_STEP, false));
   return TD_OK;
 }
 
@@ -371,9 +390,10 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
 // without a position table, then per layer the fused QKV projection, attention that is
 // causal inside the block and sees the whole cached prefix, the append of this layer's
 // K/V to its cache at each sequence's current length, and the residual MLP.  The last
-// layer stops after its K/V.  The layer GEMMs test a flag that stays 0 (the step's flag
-// says the block is done).
-td_status enqueue_context_pass(td_ctx *c, const int32_t *tokens) {
+// layer stops after its K/V, unless `full` (AR decoding): then it completes and leaves
+// x * final gain in c->ah for the head.  The layer GEMMs test a flag that stays 0 (the
+// step's flag says the block is done).
+td_status enqueue_context_pass(td_ctx *c, const int32_t *tokens, bool full = false) {
   const td_config &g = c->cfg;
   const int M = c->n_seqs * g.block_size;
   const int d = g.d_model, Hd = g.n_heads * g.head_dim;
@@ -386,7 +406,7 @@ td_status enqueue_context_pass(td_ctx *c, const int32_t *tokens) {
   for (int l = 0; l < g.n_layers && s == TD_OK; ++l) {
     s = enqueue_gemm(c, EPI_STORE, true, M, c->Nqkv, d, c->ah, c->context.wqkv[l], c->p_qkv, c->qkv, nullptr,
                      nullptr);
-    const bool last = l + 1 == g.n_layers;
+    const bool last = l + 1 == g.n_layers && !full;   // full: through the last layer (AR decoding)
     if (s == TD_OK && !last) s = enqueue_attention(c, l, c->qkv, nullptr, c->ao, nullptr, true);
     if (s == TD_OK) {
       const hipError_t e = launch_kv_append(g.dtype, c->qkv, c->Nqkv, g.n_heads, g.n_kv_heads, g.head_dim,
@@ -401,7 +421,7 @@ td_status enqueue_context_pass(td_ctx *c, const int32_t *tokens) {
         s = enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, c->ah, c->context.w1[l], c->p_w1, nullptr, c->au, nullptr);
       if (s == TD_OK)
         s = enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->au, c->context.w2[l], c->p_w2, c->x, c->ah,
-                         c->context.attn_norm[l + 1]);
+                         l + 1 < g.n_layers ? c->context.attn_norm[l + 1] : c->ctx_final_norm);
     }
   }
   c->gemm_done = nullptr;
@@ -427,7 +447,7 @@ void free_all(td_ctx *c) {
   for (Layers *t : {&c->layers, &c->context})
     for (auto *v : {&t->attn_norm, &t->mlp_norm, &t->wqkv, &t->wo, &t->w1, &t->w2})
       for (void *p : *v) f(p);
-  f(c->ctx_tok_emb); f(c->zero_flag); f(c->seq_lp_d);
+  f(c->ctx_tok_emb); f(c->ctx_final_norm); f(c->ctx_lm_head); f(c->ar_committed); f(c->zero_flag); f(c->seq_lp_d);
   f(c->x); f(c->ssq); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->ah); f(c->ao); f(c->au);
   f(c->arg_row); f(c->state_ints); f(c->items_d); f(c->pair_first_d);
   f(c->pair_count_d); f(c->att_o); f(c->att_ml); f(c->part);
@@ -498,6 +518,7 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   TD_TRY(dmalloc(c, &c->arg_row, M * 4));
   TD_TRY(dmalloc(c, &c->vpart, M * (V / 16) * sizeof(VStat)));   // up to one group per 16 columns
   TD_TRY(dmalloc(c, &c->seq_lp_d, 2 * (size_t)g.max_batch * sizeof(int)));
+  TD_TRY(dmalloc(c, &c->ar_committed, M));
   TD_TRY(dmalloc(c, &c->zero_flag, sizeof(int)));
   TD_HIP(c, hipMemsetAsync(c->zero_flag, 0, sizeof(int), c->stream));
   TD_TRY(dmalloc(c, &c->state_ints, (2 * M + 8) * sizeof(int)));
@@ -733,11 +754,17 @@ td_status td_set_context_tower(td_ctx *c, const td_weights *w) {
     for (void *p : *v) f(p);
     v->clear();
   }
-  f(c->ctx_tok_emb);
-  c->ctx_tok_emb = nullptr;
+  f(c->ctx_tok_emb); f(c->ctx_final_norm); f(c->ctx_lm_head);
+  c->ctx_tok_emb = c->ctx_final_norm = c->ctx_lm_head = nullptr;
   const size_t e = c->elt, d = c->cfg.d_model, V = c->cfg.vocab;
   TD_TRY(dmalloc(c, &c->ctx_tok_emb, (V + 1) * d * e));
   TD_HIP(c, hipMemcpyAsync(c->ctx_tok_emb, w->tok_emb, (V + 1) * d * e, hipMemcpyDeviceToDevice, c->stream));
+  if (w->final_norm && w->lm_head) {   // a head of its own: AR decoding (td_ar_step)
+    TD_TRY(dmalloc(c, &c->ctx_final_norm, d * e));
+    TD_TRY(dmalloc(c, &c->ctx_lm_head, V * d * e));
+    TD_HIP(c, hipMemcpyAsync(c->ctx_final_norm, w->final_norm, d * e, hipMemcpyDeviceToDevice, c->stream));
+    TD_HIP(c, launch_pack_weight(c->cfg.dtype, w->lm_head, c->ctx_lm_head, (int)V, (int)d, c->stream));
+  }
   TD_TRY(pack_layers(c, *w, c->context));
   TD_HIP(c, hipStreamSynchronize(c->stream));
   return TD_OK;
@@ -757,6 +784,31 @@ td_status td_append_block(td_ctx *c, const int32_t *tokens) {
     len[i] += B;
   }
   TD_TRY(enqueue_context_pass(c, tokens));
+  const std::vector<int64_t> cap = c->caps;
+  const std::vector<const void *> kc = c->kc, vc = c->vc;
+  return bind_impl(c, c->n_seqs, len.data(), cap.data(), kc.data(), vc.data());
+}
+
+td_status td_ar_step(td_ctx *c, int32_t *tokens) {
+  TD_TRY(check_ctx(c));
+  if (!tokens) return fail(c, TD_EINVAL, "tokens must not be NULL");
+  if (c->cfg.block_size != 1) return fail(c, TD_EINVAL, "AR decoding needs a ctx created with block_size 1");
+  if (!c->ctx_lm_head) return fail(c, TD_EINVAL, "no context tower with an LM head: call td_set_context_tower");
+  TD_TRY(check_bound(c));
+  std::vector<int64_t> len = c->lengths;
+  for (int i = 0; i < c->n_seqs; ++i) {
+    if (len[i] + 1 > c->caps[i] * KV_PAGE)
+      return fail(c, TD_EINVAL, "sequence %d: no room for another token (%lld tokens, %lld pages)", i,
+                  (long long)len[i], (long long)c->caps[i]);
+    len[i] += 1;
+  }
+  const td_config &g = c->cfg;
+  TD_TRY(enqueue_context_pass(c, tokens, true));
+  // Every row masked, then the head and the adoption rule at gamma 0: each row adopts its
+  // prediction, the lowest id of its largest logit.
+  TD_HIP(c, launch_init_block(tokens, c->ar_committed, nullptr, nullptr, c->n_seqs, 1, g.vocab, c->st, c->stream));
+  TD_TRY(enqueue_head_commit(c, c->ctx_lm_head, tokens, c->ar_committed, nullptr, 0.f, RULE_THRESHOLD, 1, nullptr,
+                             nullptr, nullptr, nullptr, nullptr, nullptr));
   const std::vector<int64_t> cap = c->caps;
   const std::vector<const void *> kc = c->kc, vc = c->vc;
   return bind_impl(c, c->n_seqs, len.data(), cap.data(), kc.data(), vc.data());

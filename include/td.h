@@ -47,7 +47,8 @@ typedef enum {
 
 typedef enum { TD_F32 = 0, TD_BF16 = 1 } td_dtype;
 
-/* Tower shape and capacity.  Supported: head_dim in {64, 128}; block_size in {8, 16, 32};
+/* Tower shape and capacity.  Supported: head_dim in {64, 128}; block_size in {8, 16, 32}
+ * (and 1, one row per sequence: the ctx for AR decoding, td_ar_step);
  * n_heads % n_kv_heads == 0; d_model, d_ff, vocab multiples of 64; n_heads*head_dim a
  * multiple of 64.  dtype is the storage type of weights and prefix K/V.  Activations
  * (the residual stream, normed inputs, q/k/v, attention output, MLP activation) and all
@@ -124,12 +125,25 @@ td_status td_bind_cache(td_ctx *ctx, int32_t n_seqs, const int64_t *lengths_host
 /* The frozen context tower that writes the cache: the causal tower whose cached K/V the
  * denoiser reads (poko-everyday.com Nemotron-TwoTower news item, section 技術/ビジネス面;
  * dzen.guru, section "Что нового": frozen).  Same shapes and storage dtype as the
- * denoiser; tok_emb [vocab+1][d] and every per-layer pointer are read, pos_emb,
- * final_norm and lm_head are ignored (may be NULL).  The tower has no position table:
+ * denoiser; tok_emb [vocab+1][d] and every per-layer pointer are read, pos_emb is
+ * ignored (may be NULL), final_norm [d] and lm_head [vocab][d] are optional (both or
+ * neither; needed by td_ar_step).  The tower has no position table:
  * its causal mask orders the tokens.  Device pointers, copied and packed into the ctx
  * (the caller may free them afterwards); a later call replaces the tower.
  * Errors: TD_EINVAL for a NULL pointer, TD_ENOMEM. */
 td_status td_set_context_tower(td_ctx *ctx, const td_weights *w);
+
+/* One step of AR decoding with the context tower (dzen.guru, section "Что нового": the
+ * classic autoregressive mode of the same model; read as the context tower used as an AR
+ * model with a final norm and LM head of its own, given to td_set_context_tower):
+ * tokens [n] in/out.  In: each sequence's current token (a vocabulary id).  The full
+ * tower runs over it, attending to the sequence's cached prefix and itself; its K/V of
+ * every layer are appended to the caches (as td_append_block does for a block of one),
+ * the bound lengths advance by 1, and tokens receives the prediction: the lowest id of
+ * the largest logit (greedy).  Needs a ctx created with block_size 1, a context tower
+ * with final_norm and lm_head, and a binding with room for one more token per sequence;
+ * otherwise TD_EINVAL and nothing is enqueued.  Waits for the ctx's stream. */
+td_status td_ar_step(td_ctx *ctx, int32_t *tokens);
 
 /* Append a committed block to the prefix (the loop of multi-block generation): run the
  * context tower over tokens [n][B] (committed vocabulary ids, e.g. the output of

@@ -27,4 +27,5 @@ from .denoise import (  # noqa: F401
     oracle_generate,
     OracleContextTower,
     oracle_generate_blocks,
+    oracle_ar_decode,
 )

@@ -202,6 +202,35 @@ class OracleContextTower:
     def _w(self, name: str, layer: int) -> np.ndarray:
         return np.asarray(self.W[name][layer], dtype=np.float64)
 
+    def ar_step(self, tok: np.ndarray, kv: KVProvider, seqs: Sequence[int]):
+        """One autoregressive decode step (dzen, section Что нового: the classic AR mode;
+        read as the context tower used as an AR model with a final norm and LM head of
+        its own, final_norm [d] and lm_head [V][d]): the full tower over one token per
+        sequence, tok [S], attending to its cached prefix and itself.
+
+        Returns ([(k [S][1][Hkv][hd], v ...) per layer], logits z [S][V] float64); the
+        next token is the lowest id of the largest fp32 logit."""
+        S = tok.shape[0]
+        H, Hkv, hd = self.H, self.Hkv, self.hd
+        x = np.asarray(self.W["tok_emb"][tok.reshape(-1)], dtype=np.float64).reshape(S, 1, self.d)
+        out = []
+        for l in range(self.L):
+            h = rmsnorm(x, self._w("attn_norm", l), self.eps)
+            q = (h @ self._w("wq", l).T).reshape(S, 1, H, hd)
+            k = (h @ self._w("wk", l).T).reshape(S, 1, Hkv, hd)
+            v = (h @ self._w("wv", l).T).reshape(S, 1, Hkv, hd)
+            out.append((k, v))
+            o = np.empty((S, 1, H, hd))
+            for s in range(S):
+                kp, vp = kv(l, seqs[s])
+                o[s] = joint_attention(q[s], np.asarray(kp, np.float64), np.asarray(vp, np.float64), k[s], v[s],
+                                       causal=True)
+            x = x + o.reshape(S, 1, H * hd) @ self._w("wo", l).T
+            h2 = rmsnorm(x, self._w("mlp_norm", l), self.eps)
+            x = x + gelu(h2 @ self._w("w1", l).T) @ self._w("w2", l).T
+        hf = rmsnorm(x.reshape(S, self.d), np.asarray(self.W["final_norm"], np.float64), self.eps)
+        return out, hf @ np.asarray(self.W["lm_head"], np.float64).T
+
     def block_kv(self, tok: np.ndarray, kv: KVProvider, seqs: Sequence[int]):
         """[(k [S][B][Hkv][hd], v [S][B][Hkv][hd]) for each layer] of token blocks tok [S][B]."""
         S, B = tok.shape
@@ -360,6 +389,38 @@ def oracle_generate_blocks(tower: OracleTower, context: OracleContextTower, n_bl
     if return_kv:
         return np.stack(toks), np.stack(csteps), np.stack(steps), added
     return np.stack(toks), np.stack(csteps), np.stack(steps)
+
+
+def oracle_ar_decode(context: OracleContextTower, first: np.ndarray, n_steps: int, kv: KVProvider,
+                     seqs: Optional[Sequence[int]] = None, cache_bf16: bool = True):
+    """Greedy AR decoding with the context tower: n_steps steps from tokens first [S];
+    each step appends the input token's K/V (rounded to bf16 when the cache holds bf16)
+    and predicts the next token (argmax of the fp32 logits, lowest id on ties).
+
+    Returns tokens [S][n_steps] (the prediction of every step)."""
+    S = first.shape[0]
+    seqs = list(range(S)) if seqs is None else list(seqs)
+    added: Dict[Tuple[int, int], List[Tuple[np.ndarray, np.ndarray]]] = {}
+
+    def kv_now(l: int, s: int):
+        K, V = kv(l, s)
+        extra = added.get((l, s), [])
+        if not extra:
+            return K, V
+        return (np.concatenate([np.asarray(K, np.float64)] + [e[0] for e in extra], axis=0),
+                np.concatenate([np.asarray(V, np.float64)] + [e[1] for e in extra], axis=0))
+
+    tok = np.asarray(first, np.int64)
+    outs = []
+    for _ in range(n_steps):
+        kvs, z = context.ar_step(tok, kv_now, seqs)
+        for l, (k, v) in enumerate(kvs):
+            for i, s in enumerate(seqs):
+                kk, vv = (round_bf16(k[i]), round_bf16(v[i])) if cache_bf16 else (k[i], v[i])
+                added.setdefault((l, s), []).append((kk, vv))
+        tok = np.argmax(z.astype(np.float32), axis=1).astype(np.int64)
+        outs.append(tok)
+    return np.stack(outs, axis=1)
 
 
 def oracle_generate(tower: OracleTower, S: int, B: int, tau: np.ndarray, gamma: float, kv: KVProvider,

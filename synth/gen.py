@@ -128,12 +128,13 @@ class TowerInputs:
                     w2=self.w2[l], attn_norm=self.attn_norm[l], mlp_norm=self.mlp_norm[l])
 
 
-def draw_tower(w: Workload, *, layers: Optional[int] = None, context: bool = False) -> TowerInputs:
+def draw_tower(w: Workload, *, layers: Optional[int] = None, context: bool = False,
+               ar_head: bool = False) -> TowerInputs:
     """Draw the tower weights of workload `w` (optionally only its first `layers` layers).
 
     context=True draws the frozen context tower that writes the prefix cache: the same
     shapes from streams of its own (owner "<tower>/context"); it has no position table,
-    final norm or LM head (those fields are None).
+    and no final norm or LM head unless ar_head=True (the AR decoding mode).
     """
     bf = w.dtype == "bf16"
     own = _owner(w.tower + "/context" if context else w.tower)
@@ -151,11 +152,11 @@ def draw_tower(w: Workload, *, layers: Optional[int] = None, context: bool = Fal
         wo = [nrm((w.d, w.H * w.hd), T_WO, l) for l in range(L)]
         w1 = [nrm((w.F, w.d), T_W1, l) for l in range(L)]
         w2 = [nrm((w.d, w.F), T_W2, l) for l in range(L)]
-        lm_head = None if context else nrm((w.V, w.d), T_LM_HEAD)
+        lm_head = None if context and not ar_head else nrm((w.V, w.d), T_LM_HEAD)
     one = bf16_bits_from_f32(np.ones(w.d, np.float32)) if bf else np.ones(w.d, np.float32)
     return TowerInputs(w=w, tok_emb=tok_emb, pos_emb=pos_emb, wq=wq, wk=wk, wv=wv, wo=wo, w1=w1, w2=w2,
                        attn_norm=[one.copy() for _ in range(L)], mlp_norm=[one.copy() for _ in range(L)],
-                       final_norm=None if context else one.copy(), lm_head=lm_head)
+                       final_norm=None if context and not ar_head else one.copy(), lm_head=lm_head)
 
 
 def draw_prefix_lengths(w: Workload) -> np.ndarray:

@@ -106,3 +106,61 @@ def test_multi_block_reduces_to_the_one_block_loop():
     t2, c2, s2, _ = oracle_generate(orc, w.n, w.B, tau, 0.8, kv2, keep_trace=False)
     assert np.array_equal(toks[1], t2) and np.array_equal(cst[1], c2) and np.array_equal(steps[1], s2)
     assert not np.array_equal(toks[0], toks[1])
+
+
+def _ctx_ar(w):
+    tw = draw_tower(w, context=True, ar_head=True)
+    W = oracle_weights(tw)
+    return OracleContextTower(W, H=w.H, Hkv=w.Hkv, hd=w.hd, eps=w.rms_eps), W
+
+
+def test_ar_step_without_prefix_attends_only_to_itself():
+    """P = 0: one key, softmax weight 1, so every layer's attention output is the token's
+    own value vector; the whole step is then a closed form of the MLP tower."""
+    from oracle.denoise import gelu
+    w = mini_workload(L=1)
+    ctx, W = _ctx_ar(w)
+    f64 = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    empty = lambda l, s: (np.zeros((0, w.Hkv, w.hd)), np.zeros((0, w.Hkv, w.hd)))  # noqa: E731
+    tok = np.array([3, 7])
+    kvs, z = ctx.ar_step(tok, empty, [0, 1])
+    x = f64(W["tok_emb"][tok])
+    h = rmsnorm(x, f64(W["attn_norm"][0]), w.rms_eps)
+    v = (h @ f64(W["wv"][0]).T).reshape(2, w.Hkv, w.hd)
+    o = np.repeat(v, w.H // w.Hkv, axis=1).reshape(2, -1)
+    x = x + o @ f64(W["wo"][0]).T
+    x = x + gelu(rmsnorm(x, f64(W["mlp_norm"][0]), w.rms_eps) @ f64(W["w1"][0]).T) @ f64(W["w2"][0]).T
+    zc = rmsnorm(x, f64(W["final_norm"]), w.rms_eps) @ f64(W["lm_head"]).T
+    np.testing.assert_allclose(z, zc, rtol=1e-12, atol=1e-12)
+
+
+def test_ar_step_kv_equals_one_token_block_kv():
+    """The K/V an AR step appends are the context tower's K/V of a one-token block."""
+    w = mini_workload()
+    ctx, _ = _ctx_ar(w)
+    plens, tau, kv = inputs(w)
+    tok = np.array([5, 11])
+    kvs, _ = ctx.ar_step(tok, kv, range(w.n))
+    ref = ctx.block_kv(tok[:, None], kv, range(w.n))
+    for (k, v), (kr, vr) in zip(kvs, ref):
+        np.testing.assert_array_equal(k, kr)
+        np.testing.assert_array_equal(v, vr)
+
+
+def test_ar_decode_is_greedy_and_appends():
+    """Each decoded token is the argmax of the step's logits given all earlier appends."""
+    from oracle import oracle_ar_decode
+    w = mini_workload()
+    ctx, _ = _ctx_ar(w)
+    plens, tau, kv = inputs(w)
+    first = np.array([1, 2])
+    toks = oracle_ar_decode(ctx, first, 3, kv, cache_bf16=False)
+    kvs0, z0 = ctx.ar_step(first, kv, range(w.n))
+    assert np.array_equal(toks[:, 0], np.argmax(z0.astype(np.float32), axis=1))
+
+    def kv1(l, s):
+        K, V = kv(l, s)
+        return np.concatenate([K, kvs0[l][0][s]]), np.concatenate([V, kvs0[l][1][s]])
+
+    _, z1 = ctx.ar_step(toks[:, 0], kv1, range(w.n))
+    assert np.array_equal(toks[:, 1], np.argmax(z1.astype(np.float32), axis=1))
