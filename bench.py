@@ -41,6 +41,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--breakdown", action="store_true", help="also time each kernel class (extra blocks)")
+    p.add_argument("--ar", type=int, default=0,
+                   help="also time K steps of AR decoding (td_ar_step: the context tower with its own head, one "
+                        "token per sequence per step) on a block-size-1 ctx: reported under 'ar', with the ratio "
+                        "of the block rate to it")
     p.add_argument("--blocks", type=int, default=0,
                    help="also time K consecutive blocks of multi-block generation (each block generated, then "
                         "appended to the prefix by the context tower): reported under 'multiblock'")
@@ -202,6 +206,46 @@ def cpu_baseline(w, budget_s: float):
                 denoise_steps_per_s=steps / dt, seconds=dt)
 
 
+def time_ar(args, w, plens) -> dict:
+    """K greedy AR decoding steps of the context tower (with its own final norm and LM
+    head) on a ctx of block size 1 over the same prefix: one token per sequence per step,
+    each step appending the token's K/V.  The binding is reset before each repetition."""
+    import torch
+
+    from block_diffusion_lm_step_amd import Denoiser
+    from synth import draw_tower
+    from synth.device import cache_pages, prefix_to_device, tower_config, tower_to_device
+
+    K = args.ar
+    w1 = w.with_(B=1)
+    _, ks, vs = prefix_to_device(w1, plens, room=K)
+    caps = cache_pages(plens, K)
+    dev = Denoiser(tower_config(w1, max_batch=w.n, max_prefix_tokens=int(plens.sum()) + K * w.n),
+                   tower_to_device(draw_tower(w1)))
+    dev.set_context_tower(tower_to_device(draw_tower(w1, context=True, ar_head=True)))
+    lengths = [int(p) for p in plens]
+    tok = torch.zeros(w.n, dtype=torch.int32, device="cuda")
+
+    def run():
+        dev.bind_cache(lengths, caps, ks, vs)
+        tok.fill_(1)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(K):
+            dev.ar_step(tok)
+        dev.sync()
+        return time.perf_counter() - t
+
+    run()
+    reps = 3
+    el = sum(run() for _ in range(reps)) / reps
+    dev.close()
+    log(f"[bench] AR: {K} steps in {el * 1e3:.2f} ms")
+    return dict(steps=K, value=round(K * w.n / el, 3), unit="tokens/s", ms_per_token_step=round(el * 1e3 / K, 4),
+                timing="host clock around K td_ar_step calls (each waits for the stream: the work lists are rebuilt "
+                       "on the host)")
+
+
 def time_multiblock(args, w, plens, tau, dev, tok, com, steps) -> dict:
     """K consecutive blocks of multi-block generation on caches bound with room for them:
     each block is generated, then the context tower appends its K/V to the prefix.  The
@@ -348,6 +392,10 @@ def main():
     multiblock = None
     if args.blocks > 0:
         multiblock = time_multiblock(args, w, plens, tau, dev, tok, com, steps)
+    ar = None
+    if args.ar > 0:
+        ar = time_ar(args, w, plens)
+        ar["diffusion_to_ar"] = round((multiblock["value"] if multiblock else tokens_per_s) / ar["value"], 4)
 
     out = {
         "metric": METRIC,
@@ -377,6 +425,8 @@ def main():
         out["breakdown"] = breakdown
     if multiblock:
         out["multiblock"] = multiblock
+    if ar:
+        out["ar"] = ar
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
