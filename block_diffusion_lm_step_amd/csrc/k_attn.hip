@@ -278,7 +278,12 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
 
   const AttnItem it = a.items[blockIdx.x];   // loaded together with the loop-exit flag
   if (a.done && *a.done) return;
+  // A sequence whose block is fully adopted needs no attention.  Its flag is read with a
+  // scalar load (nothing in the kernel writes it, and the kernel's start invalidates the
+  // scalar cache), whose wait does not hold the vector loads back; the pages' items test
+  // it once their first pages are requested.
   if (it.is_block == 1) {
+    if (a.seq_done[it.seq]) return;
     block_item<HD, NT>(a, it, blockIdx.x, smem);
     return;
   }
@@ -360,6 +365,7 @@ __global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
   __builtin_amdgcn_sched_barrier(0);   // the block and query loads stay ahead of the pages'
   static_for<DEPTH - 1>([&](auto sc) { fetch(sc, pg0 + decltype(sc)::value * NW); });
   __builtin_amdgcn_sched_barrier(0);
+  if (a.seq_done[it.seq]) return;
   q_frags<T, HD, RT>(a, 0, l16, qraw, qf);
 
   if (with_block) {   // workgroup-uniform
@@ -494,6 +500,7 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
   const int item = blockIdx.x / YS, ygrp = blockIdx.x % YS;
   const AttnItem it = a.items[item];   // loaded together with the loop-exit flag
   if (a.done && *a.done) return;
+  if (a.seq_done[it.seq]) return;   // block fully adopted: no attention needed
   if (it.is_block) {
     if (ygrp == 0) block_item<HD, NT>(a, it, item, reinterpret_cast<float *>(smem));
     return;
@@ -612,6 +619,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   const int pair = blockIdx.x;
   const int first = a.pair_first[pair], cnt = a.pair_count[pair];   // loaded with the exit flag
   if (a.done && *a.done) return;
+  if (a.seq_done[pair / a.Hkv]) return;   // block fully adopted: rows not read again
   const int rho = blockIdx.y * 16 + (threadIdx.x >> 2);
   const int e0 = blockIdx.z * 32 + (threadIdx.x & 3) * 8;
   if (rho >= a.R) return;
@@ -672,7 +680,7 @@ hipError_t launch_hd(const AttnArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(int dtype, const AttnArgs &a, hipStream_t s) {
-  if (a.n_items <= 0 || a.n_pairs <= 0 || a.B > BMAX) return hipErrorInvalidValue;
+  if (a.n_items <= 0 || a.n_pairs <= 0 || a.B > BMAX || a.seq_done == nullptr) return hipErrorInvalidValue;
   if (dtype == DT_BF16) {
     if (a.hd == 128) return launch_hd<bf16_t, 128>(a, s);
     if (a.hd == 64) return launch_hd<bf16_t, 64>(a, s);

@@ -188,12 +188,18 @@ __global__ __launch_bounds__(64 * LDS_NW) void lmhead_lds_kernel(GemmArgs a) {
   const int g = lane >> 4, l16 = lane & 15;
   const int ntw = (blockIdx.x * NW + wave) * NT;   // this wave's first column tile
 
+  static_assert(16 % NW == 0 || NW % 16 == 0, "rows per wave");
+  constexpr int RPW = NW >= 16 ? 1 : 16 / NW;    // rows whose scale each wave forms
   const int r16 = min((int)(threadIdx.x & 15), M - 1);
   const int pos = a.rowpos[r16];
   const float tau = a.inv_temp ? a.inv_temp[r16] : 1.0f;
-  const int srow = min(wave, M - 1);   // wave w sums the partial squares of row w
-  const float sq0 = a.ssq[(size_t)min(lane, a.norm_nparts - 1) * a.ld_ssq + srow];
-  const float sq1 = a.ssq[(size_t)min(lane + 64, a.norm_nparts - 1) * a.ld_ssq + srow];
+  float sq0[RPW], sq1[RPW];   // wave w sums the partial squares of rows w, w + NW, ...
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int srow = min(wave + NW * i, M - 1);
+    sq0[i] = a.ssq[(size_t)min(lane, a.norm_nparts - 1) * a.ld_ssq + srow];
+    sq1[i] = a.ssq[(size_t)min(lane + 64, a.norm_nparts - 1) * a.ld_ssq + srow];
+  }
 
   const u32x4_t *ga = reinterpret_cast<const u32x4_t *>(a.A);
   const int nwords = KT * 128;
@@ -220,10 +226,11 @@ __global__ __launch_bounds__(64 * LDS_NW) void lmhead_lds_kernel(GemmArgs a) {
     s_pos[threadIdx.x] = threadIdx.x < (unsigned)M ? pos : -1;
     s_tau[threadIdx.x] = tau;
   }
-  {
-    float sq = (lane < a.norm_nparts ? sq0 : 0.f) + (lane + 64 < a.norm_nparts ? sq1 : 0.f);
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    float sq = (lane < a.norm_nparts ? sq0[i] : 0.f) + (lane + 64 < a.norm_nparts ? sq1[i] : 0.f);
     sq = sum_lanes<64>(sq);
-    if (lane == 0) s_rs[wave] = 1.0f / sqrtf(sq / (float)a.K + a.norm_eps);
+    if (lane == 0 && wave + NW * i < 16) s_rs[wave + NW * i] = 1.0f / sqrtf(sq / (float)a.K + a.norm_eps);
   }
   __syncthreads();
 

@@ -87,6 +87,10 @@ TD_DEV void commit_all(const CommitArgs &a, int *s_wave) {
     }
     if (in && a.newly) a.newly[r] = adopt ? 1 : 0;
     if (in && p == 0 && a.steps && any) a.steps[r / a.B] += 1;
+    // Finished after this step: no position left masked (attention then skips it).
+    int rem = (masked && !adopt) ? 1 : 0;
+    for (int o = 1; o < a.B; o <<= 1) rem |= __shfl_xor(rem, o);
+    if (in && p == 0) a.st.seq_done[r / a.B] = rem ? 0 : 1;
   }
   __syncthreads();
   // Rows still masked, in row order, for the next step.

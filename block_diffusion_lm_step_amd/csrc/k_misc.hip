@@ -22,8 +22,8 @@ __global__ void pack_weight_kernel(const T *__restrict__ W, T *__restrict__ Wp, 
   for (int e = 0; e < 8; ++e) dst[e] = src[e];
 }
 
-__global__ __launch_bounds__(1024) void prep_kernel(const int *tokens, const uint8_t *committed, int M, int V,
-                                                    StepState st) {
+__global__ __launch_bounds__(1024) void prep_kernel(const int *tokens, const uint8_t *committed, int M, int B,
+                                                    int V, StepState st) {
   __shared__ int s_wave[16];
   int base = 0, err = 0;
   for (int r0 = 0; r0 < M; r0 += 1024) {
@@ -38,6 +38,10 @@ __global__ __launch_bounds__(1024) void prep_kernel(const int *tokens, const uin
         masked = false;    // an invalid row is left untouched
       }
     }
+    // A sequence is finished when none of its B rows (B consecutive lanes) is masked.
+    int any = masked ? 1 : 0;
+    for (int o = 1; o < B; o <<= 1) any |= __shfl_xor(any, o);
+    if (r < M && r % B == 0) st.seq_done[r / B] = any ? 0 : 1;
     base = block_compact(masked, base, st.rowlist, st.rowpos, r < M ? r : -1, s_wave);
   }
   if (err) atomicOr(st.err, 1);
@@ -57,8 +61,10 @@ __global__ __launch_bounds__(1024) void init_block_kernel(int *tokens, uint8_t *
     st.rowlist[r] = r;
     st.rowpos[r] = r;
   }
-  if (steps)
-    for (int i = threadIdx.x; i < n; i += blockDim.x) steps[i] = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    if (steps) steps[i] = 0;
+    st.seq_done[i] = 0;
+  }
   if (threadIdx.x == 0) {
     *st.n_rows = M;
     *st.done = M == 0 ? 1 : 0;
@@ -142,8 +148,9 @@ hipError_t launch_pack_weight(int dtype, const void *W, void *Wp, int N, int K, 
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const int *tokens, const uint8_t *committed, int M, int V, StepState st, hipStream_t s) {
-  hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, s, tokens, committed, M, V, st);
+hipError_t launch_prep(const int *tokens, const uint8_t *committed, int M, int B, int V, StepState st, hipStream_t s) {
+  if (B < 1 || 64 % B) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, s, tokens, committed, M, B, V, st);
   return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ struct td_ctx {
   Layers context;
   uint8_t *ar_committed = nullptr;   // [max_batch] adoption flags of an AR step
   int *zero_flag = nullptr;          // a loop-exit flag that stays 0 (the context pass)
+  int *zero_seq = nullptr;           // [max_batch] finished-sequence flags that stay 0
   const int *gemm_done = nullptr;    // flag the layer GEMMs test; nullptr: the step's
 
   // adoption rule (td_set_commit_rule)
@@ -269,6 +270,9 @@ td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, vo
   a.scale = 1.0f / std::sqrt((float)g.head_dim);
   a.done = done;
   a.causal = causal ? 1 : 0;
+  // The denoiser's step skips finished sequences (one sequence: the step's own flag does);
+  // other passes skip nothing (flags that stay 0).
+  a.seq_done = done && c->n_seqs > 1 ? c->st.seq_done : c->zero_seq;
   TD_TRY(prof_mark(c, TD_PROF_ATTENTION, true));
   TD_HIP(c, launch_attention(g.dtype, a, c->stream));
   TD_TRY(prof_mark(c, TD_PROF_ATTENTION, false));
@@ -447,7 +451,7 @@ void free_all(td_ctx *c) {
   for (Layers *t : {&c->layers, &c->context})
     for (auto *v : {&t->attn_norm, &t->mlp_norm, &t->wqkv, &t->wo, &t->w1, &t->w2})
       for (void *p : *v) f(p);
-  f(c->ctx_tok_emb); f(c->ctx_final_norm); f(c->ctx_lm_head); f(c->ar_committed); f(c->zero_flag); f(c->seq_lp_d);
+  f(c->ctx_tok_emb); f(c->ctx_final_norm); f(c->ctx_lm_head); f(c->ar_committed); f(c->st.seq_done); f(c->zero_seq); f(c->zero_flag); f(c->seq_lp_d);
   f(c->x); f(c->ssq); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->ah); f(c->ao); f(c->au);
   f(c->arg_row); f(c->state_ints); f(c->items_d); f(c->pair_first_d);
   f(c->pair_count_d); f(c->att_o); f(c->att_ml); f(c->part);
@@ -519,6 +523,10 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   TD_TRY(dmalloc(c, &c->vpart, M * (V / 16) * sizeof(VStat)));   // up to one group per 16 columns
   TD_TRY(dmalloc(c, &c->seq_lp_d, 2 * (size_t)g.max_batch * sizeof(int)));
   TD_TRY(dmalloc(c, &c->ar_committed, M));
+  TD_TRY(dmalloc(c, &c->st.seq_done, g.max_batch * sizeof(int)));
+  TD_HIP(c, hipMemsetAsync(c->st.seq_done, 0, g.max_batch * sizeof(int), c->stream));
+  TD_TRY(dmalloc(c, &c->zero_seq, g.max_batch * sizeof(int)));
+  TD_HIP(c, hipMemsetAsync(c->zero_seq, 0, g.max_batch * sizeof(int), c->stream));
   TD_TRY(dmalloc(c, &c->zero_flag, sizeof(int)));
   TD_HIP(c, hipMemsetAsync(c->zero_flag, 0, sizeof(int), c->stream));
   TD_TRY(dmalloc(c, &c->state_ints, (2 * M + 8) * sizeof(int)));
@@ -706,7 +714,7 @@ td_status td_denoise_step(td_ctx *c, int32_t *tokens, uint8_t *committed, const 
   if (!finite(gamma)) return fail(c, TD_EINVAL, "gamma must be finite");
   TD_TRY(check_bound(c));
   const int M = c->n_seqs * c->cfg.block_size;
-  TD_HIP(c, launch_prep(tokens, committed, M, c->cfg.vocab, c->st, c->stream));
+  TD_HIP(c, launch_prep(tokens, committed, M, c->cfg.block_size, c->cfg.vocab, c->st, c->stream));
   return enqueue_step(c, tokens, committed, inv_temp, gamma, newly, conf_out, argmax_out, logits_out, nullptr,
                       nullptr);
 }

@@ -108,6 +108,7 @@ struct AttnItem {
 struct AttnArgs {
   int B, H, Hkv, hd, Nqkv, G, R;   // R = G * B query rows per (seq, kv head)
   int causal;                      // 1: block query p sees block keys 0..p only (context tower)
+  const int *seq_done;             // [n] 1: the sequence's block is fully adopted, skip it (never null)
   const float *qkv;                // [n*B][Nqkv]: q | k_block | v_block (fp32)
   const void *kc, *vc;             // prefix cache pages (layout above)
   const AttnItem *items; int n_items;
@@ -131,8 +132,9 @@ struct StepState {                 // device-resident loop state owned by the ct
   int *t;                          // step counter of td_generate_block
   int *err;                        // device-side input error flags
   unsigned *counter;               // last-workgroup counter of the vocab merge
+  int *seq_done;                   // [n] 1 when the sequence has no masked position left
 };
-hipError_t launch_prep(const int *tokens, const uint8_t *committed, int M, int V, StepState st, hipStream_t s);
+hipError_t launch_prep(const int *tokens, const uint8_t *committed, int M, int B, int V, StepState st, hipStream_t s);
 hipError_t launch_init_block(int *tokens, uint8_t *committed, int8_t *commit_step, int *steps, int n, int B,
                              int V, StepState st, hipStream_t s);
 // x = E[token] + Pos[position] (fp32), partial sums of squares per 16 columns, and
