@@ -16,6 +16,8 @@ from .denoise import (  # noqa: F401
     round_bf16,
     rmsnorm,
     gelu,
+    moe_route,
+    moe_ffn,
     joint_attention,
     OracleTower,
     vocab_reduce,

@@ -37,12 +37,21 @@ What is computed, and where it comes from:
   pages' mock-AR mode (dzen, section "Что нового": one token per step through the
   diffusion tower) is read as left-to-right order.
 
+* Mixture-of-experts MLP (optional; dzen, section "Что нового": the tower's layers
+  are MoE layers in which 6 of 128 experts plus 2 shared ones are active per token).
+  Readings: a router row per expert scores the normed MLP input; each token takes its
+  top_k experts by score (lowest expert id on ties) with gates given by a softmax over
+  the chosen scores; every expert, routed or shared, is the same ungated GELU MLP of
+  width d_expert; shared experts always apply with weight 1; the MoE replaces the
+  denoiser's dense MLP in every layer.  See moe_ffn.
+
 Precision.  Everything is float64.  Mode "bf16" additionally rounds to the nearest
 bfloat16 (ties to even) exactly at the points where the GPU stores bfloat16: the
 normed GEMM inputs (h, h2, hf), q/k/v, the attention output o and the MLP
 activation u.  Logits are never rounded.  Decisions that turn floats into
-integers (argmax, conf >= gamma, the fallback choice) are taken on float32
-roundings of the float64 values, the precision the kernels decide in.
+integers (argmax, conf >= gamma, the fallback choice, the experts a token is routed
+to) are taken on float32 roundings of the float64 values, the precision the kernels
+decide in.
 """
 from __future__ import annotations
 
@@ -77,6 +86,58 @@ def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
 def gelu(x: np.ndarray) -> np.ndarray:
     """Exact GELU: 0.5 * x * (1 + erf(x / sqrt(2)))."""
     return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+# ----------------------------------------------------------------------------- mixture of experts
+
+
+def moe_route(scores: np.ndarray, top_k: int):
+    """Experts and gates of each row from router scores [R][E] (float64).
+
+    The top_k experts of a row are those with the largest float32-rounded scores, the
+    lowest expert id first among equal scores, listed by rank; the gates are a softmax
+    over the chosen float64 scores (they sum to 1).  Returns (experts [R][top_k] int64,
+    gates [R][top_k] float64).
+    """
+    R, E = scores.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("top_k must be in [1, E]")
+    s32 = scores.astype(np.float32)
+    experts = np.empty((R, top_k), dtype=np.int64)
+    gates = np.empty((R, top_k))
+    for r in range(R):
+        ranked = sorted(range(E), key=lambda e: (-float(s32[r, e]), e))[:top_k]
+        experts[r] = ranked
+        sel = scores[r, ranked]
+        w = np.exp(sel - sel.max())
+        gates[r] = w / w.sum()
+    return experts, gates
+
+
+def moe_ffn(h2: np.ndarray, router, w1, w2, sw1, sw2, top_k: int, rnd=lambda a: a):
+    """Mixture-of-experts MLP output for normed inputs h2 [R][d] (float64).
+
+    router [E][d]; w1[e] [d_expert][d] and w2[e] [d][d_expert] for the routed experts;
+    sw1[s], sw2[s] likewise for the shared experts (empty sequences for none).  Expert
+    weights are read one expert at a time (any indexable container).  With expert(h) =
+    gelu(h W1^T) W2^T (its GELU output passed through rnd, the storage rounding):
+
+        y_r = sum over the row's chosen experts e of gate_{r,e} * expert_e(h2_r)
+              + sum over shared experts s of shared_s(h2_r)
+
+    Returns (y [R][d], experts [R][top_k], gates [R][top_k], scores [R][E]).
+    """
+    scores = h2 @ np.asarray(router, np.float64).T
+    experts, gates = moe_route(scores, top_k)
+    y = np.zeros_like(h2)
+    for e in np.unique(experts):
+        rows, slot = np.nonzero(experts == e)
+        u = rnd(gelu(h2[rows] @ np.asarray(w1[e], np.float64).T))
+        y[rows] += gates[rows, slot][:, None] * (u @ np.asarray(w2[e], np.float64).T)
+    for s in range(len(sw1)):
+        u = rnd(gelu(h2 @ np.asarray(sw1[s], np.float64).T))
+        y += u @ np.asarray(sw2[s], np.float64).T
+    return y, experts, gates, scores
 
 
 # ----------------------------------------------------------------------------- attention
@@ -123,6 +184,11 @@ class OracleTower:
     bfloat16 widened to float32): tok_emb [V+1][d], pos_emb [B][d], final_norm [d],
     lm_head [V][d], and per-layer lists wq [H*hd][d], wk/wv [Hkv*hd][d],
     wo [d][H*hd], w1 [F][d], w2 [d][F], attn_norm [d], mlp_norm [d].
+
+    An optional "moe" entry replaces every layer's dense MLP with a mixture of experts
+    (moe_ffn): a dict with top_k and per-layer lists router [E][d], w1 [E][d_expert][d],
+    w2 [E][d][d_expert], sw1 [n_shared][d_expert][d], sw2 [n_shared][d][d_expert] (the
+    per-layer entries index by expert; w1/w2 of the dense MLP are then unused).
     """
 
     def __init__(self, weights: Dict[str, object], *, H: int, Hkv: int, hd: int, eps: float = 1e-6,
@@ -132,6 +198,7 @@ class OracleTower:
         self.W = weights
         self.H, self.Hkv, self.hd, self.eps, self.mode = H, Hkv, hd, eps, mode
         self.L = len(weights["wq"])
+        self.moe = weights.get("moe")
         self.V = weights["lm_head"].shape[0]
         self.d = weights["lm_head"].shape[1]
         self._f64: Dict[Tuple[str, int], np.ndarray] = {}
@@ -170,8 +237,18 @@ class OracleTower:
             o = self._rnd(o.reshape(S, B, H * hd))
             x = x + o @ self._w("wo", l).T
             h2 = self._rnd(rmsnorm(x, self._w("mlp_norm", l), self.eps))
-            u = self._rnd(gelu(h2 @ self._w("w1", l).T))
-            x = x + u @ self._w("w2", l).T
+            if self.moe is not None:
+                m = self.moe
+                y, ex, gt, sc = moe_ffn(h2.reshape(S * B, self.d), m["router"][l], m["w1"][l], m["w2"][l],
+                                        m["sw1"][l], m["sw2"][l], m["top_k"], self._rnd)
+                x = x + y.reshape(S, B, self.d)
+                if capture is not None:
+                    capture.setdefault("experts", []).append(ex.reshape(S, B, -1))
+                    capture.setdefault("gates", []).append(gt.reshape(S, B, -1))
+                    capture.setdefault("scores", []).append(sc.reshape(S, B, -1))
+            else:
+                u = self._rnd(gelu(h2 @ self._w("w1", l).T))
+                x = x + u @ self._w("w2", l).T
             if capture is not None:
                 capture.setdefault("x", []).append(x.copy())
         return self._rnd(rmsnorm(x, self._w("final_norm"), self.eps))

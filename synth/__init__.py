@@ -16,7 +16,9 @@ section "Что нового": blocks of 16, confidence threshold gamma).
 from .workloads import WORKLOADS, Workload, get_workload  # noqa: F401
 from .gen import (  # noqa: F401
     TowerInputs,
+    MoeInputs,
     draw_tower,
+    draw_moe,
     draw_prefix_lengths,
     draw_inv_temp,
     draw_prefix_kv,

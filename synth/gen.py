@@ -26,6 +26,7 @@ CHUNK = 1 << 22
 T_TOK_EMB, T_POS_EMB = 1, 2
 T_WQ, T_WK, T_WV, T_WO, T_W1, T_W2 = 10, 11, 12, 13, 14, 15
 T_LM_HEAD = 20
+T_MOE_ROUTER, T_MOE_W1, T_MOE_W2, T_MOE_SW1, T_MOE_SW2 = 16, 17, 18, 19, 21
 T_PREFIX_K, T_PREFIX_V = 30, 31
 T_INV_TEMP, T_PREFIX_LEN = 40, 41
 
@@ -150,13 +151,47 @@ def draw_tower(w: Workload, *, layers: Optional[int] = None, context: bool = Fal
         wk = [nrm((w.Hkv * w.hd, w.d), T_WK, l) for l in range(L)]
         wv = [nrm((w.Hkv * w.hd, w.d), T_WV, l) for l in range(L)]
         wo = [nrm((w.d, w.H * w.hd), T_WO, l) for l in range(L)]
-        w1 = [nrm((w.F, w.d), T_W1, l) for l in range(L)]
-        w2 = [nrm((w.d, w.F), T_W2, l) for l in range(L)]
+        dense = not (w.moe and not context)   # a mixture-of-experts denoiser has no dense MLP
+        w1 = [nrm((w.F, w.d), T_W1, l) for l in range(L)] if dense else []
+        w2 = [nrm((w.d, w.F), T_W2, l) for l in range(L)] if dense else []
         lm_head = None if context and not ar_head else nrm((w.V, w.d), T_LM_HEAD)
     one = bf16_bits_from_f32(np.ones(w.d, np.float32)) if bf else np.ones(w.d, np.float32)
     return TowerInputs(w=w, tok_emb=tok_emb, pos_emb=pos_emb, wq=wq, wk=wk, wv=wv, wo=wo, w1=w1, w2=w2,
                        attn_norm=[one.copy() for _ in range(L)], mlp_norm=[one.copy() for _ in range(L)],
                        final_norm=None if context and not ar_head else one.copy(), lm_head=lm_head)
+
+
+@dataclasses.dataclass
+class MoeInputs:
+    """Mixture-of-experts weights of a denoiser, per layer, in the storage dtype:
+    router [E][d], w1 [E][d_expert][d], w2 [E][d][d_expert], sw1 [n_shared][d_expert][d],
+    sw2 [n_shared][d][d_expert]."""
+    w: Workload
+    router: List[np.ndarray]
+    w1: List[np.ndarray]
+    w2: List[np.ndarray]
+    sw1: List[np.ndarray]
+    sw2: List[np.ndarray]
+
+
+def draw_moe(w: Workload, *, layers: Optional[int] = None) -> MoeInputs:
+    """Draw the expert weights of workload `w` (N(0, weight_std^2), like the other weights)."""
+    if not w.moe:
+        raise ValueError(f"workload {w.name} has no mixture of experts")
+    E, _, S, de = w.moe
+    bf = w.dtype == "bf16"
+    own = _owner(w.tower)
+    L = w.L if layers is None else layers
+    with cf.ThreadPoolExecutor(_workers()) as ex:
+        def nrm(shape, tid, layer):
+            return draw_normal(shape, [w.seed, own, tid, layer, 0], w.weight_std, bf, pool=ex)
+
+        router = [nrm((E, w.d), T_MOE_ROUTER, l) for l in range(L)]
+        w1 = [nrm((E, de, w.d), T_MOE_W1, l) for l in range(L)]
+        w2 = [nrm((E, w.d, de), T_MOE_W2, l) for l in range(L)]
+        sw1 = [nrm((S, de, w.d), T_MOE_SW1, l) for l in range(L)]
+        sw2 = [nrm((S, w.d, de), T_MOE_SW2, l) for l in range(L)]
+    return MoeInputs(w=w, router=router, w1=w1, w2=w2, sw1=sw1, sw2=sw2)
 
 
 def draw_prefix_lengths(w: Workload) -> np.ndarray:

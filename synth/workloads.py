@@ -37,6 +37,9 @@ class Workload:
     seed: int = 0
     rms_eps: float = 1e-6
     batch_key: str = ""   # key of the prefix-length / prefix-K/V streams ("" = the workload name)
+    # Mixture-of-experts MLP in every denoiser layer: (experts, top_k, shared experts,
+    # expert width); () = the dense MLP of width F.
+    moe: Tuple = ()
 
     @property
     def batch(self) -> str:
@@ -57,9 +60,16 @@ class Workload:
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
 
-    def weight_params(self) -> int:
-        """Parameters streamed once per step (layer GEMMs + LM head; the embedding is a gather)."""
-        per_layer = self.qkv_dim * self.d + self.d * self.H * self.hd + 2 * self.F * self.d
+    def weight_params(self, active_experts: float = 0.0) -> int:
+        """Parameters streamed once per step (layer GEMMs + LM head; the embedding is a gather).
+
+        With a mixture of experts: the router plus `active_experts` experts (routed and
+        shared) per layer, the experts that hold at least one row."""
+        mlp = 2 * self.F * self.d
+        if self.moe:
+            E, _, _, de = self.moe
+            mlp = E * self.d + int(round(active_experts * 2 * de * self.d))
+        per_layer = self.qkv_dim * self.d + self.d * self.H * self.hd + mlp
         return self.L * per_layer + self.V * self.d
 
 
@@ -83,6 +93,11 @@ WORKLOADS = {
                             **_D2048),
     "sweep64_b32": Workload(name="sweep64_b32", batch_key="sweep64", n=64, plen=("uniform", 1024, 4096), B=32,
                             **_D2048),
+    # The batch-1 tower with each MLP a mixture of 128 experts, 6 routed + 2 shared per token
+    # (the counts of the pages' MoE layers), expert width 1024: the eight active experts
+    # together are as wide as the dense MLP (F = 8192).
+    "moe_b1_p4096": Workload(name="moe_b1_p4096", batch_key="b1_p4096", n=1, plen=("fixed", 4096), B=16,
+                             moe=(128, 6, 2, 1024), **_D2048),
 }
 
 SWEEP_GAMMAS = (0.5, 0.8, 0.95)

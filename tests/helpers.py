@@ -12,13 +12,32 @@ def mini_workload(**kw) -> Workload:
     return Workload(**base)
 
 
-def oracle_weights(tw) -> dict:
-    """Stored tower values widened exactly to float32, keyed as the oracle expects."""
+class _Widened:
+    """Experts of one layer, widened to float32 one at a time when the oracle reads them."""
+
+    def __init__(self, a, tw):
+        self.a, self.tw = a, tw
+
+    def __getitem__(self, e):
+        return self.tw.as_f32(self.a[e])
+
+    def __len__(self):
+        return self.a.shape[0]
+
+
+def oracle_weights(tw, moe=None) -> dict:
+    """Stored tower values widened exactly to float32, keyed as the oracle expects;
+    `moe` (synth.MoeInputs) adds the mixture of experts."""
     f = lambda a: None if a is None else tw.as_f32(a)  # noqa: E731  (the context tower has no pos/final/head)
-    return dict(tok_emb=f(tw.tok_emb), pos_emb=f(tw.pos_emb), final_norm=f(tw.final_norm), lm_head=f(tw.lm_head),
-                wq=[f(a) for a in tw.wq], wk=[f(a) for a in tw.wk], wv=[f(a) for a in tw.wv],
-                wo=[f(a) for a in tw.wo], w1=[f(a) for a in tw.w1], w2=[f(a) for a in tw.w2],
-                attn_norm=[f(a) for a in tw.attn_norm], mlp_norm=[f(a) for a in tw.mlp_norm])
+    W = dict(tok_emb=f(tw.tok_emb), pos_emb=f(tw.pos_emb), final_norm=f(tw.final_norm), lm_head=f(tw.lm_head),
+             wq=[f(a) for a in tw.wq], wk=[f(a) for a in tw.wk], wv=[f(a) for a in tw.wv],
+             wo=[f(a) for a in tw.wo], w1=[f(a) for a in tw.w1], w2=[f(a) for a in tw.w2],
+             attn_norm=[f(a) for a in tw.attn_norm], mlp_norm=[f(a) for a in tw.mlp_norm])
+    if moe is not None:
+        W["moe"] = dict(top_k=moe.w.moe[1], router=[f(a) for a in moe.router],
+                        w1=[_Widened(a, tw) for a in moe.w1], w2=[_Widened(a, tw) for a in moe.w2],
+                        sw1=[_Widened(a, tw) for a in moe.sw1], sw2=[_Widened(a, tw) for a in moe.sw2])
+    return W
 
 
 def kv_provider(w: Workload, plens):
