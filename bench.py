@@ -167,6 +167,12 @@ def cpu_baseline(w, budget_s: float):
              w1=[f(a) for a in tw.w1], w2=[f(a) for a in tw.w2], attn_norm=[f(a) for a in tw.attn_norm],
              mlp_norm=[f(a) for a in tw.mlp_norm])
     del tw
+    if w.moe:   # the mixture of experts, widened to float32 (the oracle reads it expert by expert)
+        from synth import draw_moe
+        mi = draw_moe(w)
+        W["moe"] = dict(top_k=w.moe[1], router=[f(a) for a in mi.router], w1=[f(a) for a in mi.w1],
+                        w2=[f(a) for a in mi.w2], sw1=[f(a) for a in mi.sw1], sw2=[f(a) for a in mi.sw2])
+        del mi
     orc = OracleTower(W, H=w.H, Hkv=w.Hkv, hd=w.hd, eps=w.rms_eps, mode="plain")
     plens = draw_prefix_lengths(w)
     tau = draw_inv_temp(w)
@@ -185,7 +191,7 @@ def cpu_baseline(w, budget_s: float):
     for l in range(w.L):   # inputs staged and weights widened before timing, as td_create is untimed
         for s in range(n_s):
             kv(l, s)
-        for name in ("wq", "wk", "wv", "wo", "w1", "w2", "attn_norm", "mlp_norm"):
+        for name in ("wq", "wk", "wv", "wo", "attn_norm", "mlp_norm") + (() if w.moe else ("w1", "w2")):
             orc._w(name, l)
     for name in ("lm_head", "pos_emb", "final_norm"):
         orc._w(name)
@@ -304,7 +310,8 @@ def main():
         sys.exit(2)
     import torch
 
-    from block_diffusion_lm_step_amd import TD_PROF_ATTENTION, TD_PROF_GEMM, TD_PROF_LMHEAD, TD_PROF_STEP, Denoiser
+    from block_diffusion_lm_step_amd import (TD_PROF_ATTENTION, TD_PROF_GEMM, TD_PROF_LMHEAD, TD_PROF_MOE,
+                                             TD_PROF_STEP, Denoiser)
     from synth import draw_inv_temp, draw_prefix_lengths, draw_tower, get_workload
     from synth.device import prefix_to_device, tower_config, tower_to_device
 
@@ -322,8 +329,14 @@ def main():
     tau = torch.from_numpy(draw_inv_temp(w)).cuda()
     room = args.blocks * w.B * w.n   # tokens appended by --blocks
     dev = Denoiser(tower_config(w, max_batch=w.n, max_prefix_tokens=max(1, offsets[-1] + room)), dW)
-    dev.set_prefix(offsets, ks, vs)
     del dW
+    if w.moe:   # every layer's MLP a mixture of experts
+        from synth import draw_moe
+        from synth.device import moe_config, moe_to_device
+        dM = moe_to_device(draw_moe(w))
+        dev.set_moe(moe_config(w), dM)
+        del dM
+    dev.set_prefix(offsets, ks, vs)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM ({time.time() - t:.1f} s)")
 
@@ -350,7 +363,11 @@ def main():
         del src, dst
     log("[bench] warmup done")
 
-    dev.profile_begin(TD_PROF_LMHEAD)
+    # The dominant kernel's launches are timed inside the timed region: the LM head, or
+    # with a mixture of experts the expert projections.
+    dev.profile_begin(TD_PROF_MOE if w.moe else TD_PROF_LMHEAD)
+    if w.moe:
+        dev.moe_stats()   # reset the expert counters
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -358,6 +375,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     lm_ms = dev.profile_end()
+    moe_launches, moe_active = dev.moe_stats() if w.moe else (0, 0)
     dev.sync()
     elapsed = t1 - t0
     st = steps.cpu().numpy()
@@ -367,17 +385,33 @@ def main():
 
     tokens_per_s = args.steps * w.n * w.B / elapsed
     steps_per_s = args.steps * S / elapsed
-    # LM-head launches that did work: the first S of every block's B launches.
-    lm = np.array(lm_ms).reshape(args.steps, w.B)[:, :S]
-    lm_avg_ms = float(lm.mean())
     elt = 2 if w.dtype == "bf16" else 4
-    lm_bytes = w.V * w.d * elt
+    if w.moe:
+        # Expert launches that did work: per working step, L layers x (up, down).  Each
+        # reads the W1 (or W2) of every expert that holds a row, once: the counters give
+        # the experts per layer-step.
+        lm = np.array(lm_ms).reshape(args.steps, w.B, w.L, 2)[:, :S]
+        assert moe_launches == args.steps * S * w.L, (moe_launches, args.steps, S)
+        active_per_layer = moe_active / moe_launches
+        lm_bytes = int(round(active_per_layer * w.moe[3] * w.d * elt))
+        kernel = ("moe_gemm_kernel: expert up (gathered rows, GELU) and down projections, weights of the "
+                  f"{active_per_layer:.1f} experts (routed + shared) holding a row per layer")
+        traffic = None
+    else:
+        # LM-head launches that did work: the first S of every block's B launches.
+        lm = np.array(lm_ms).reshape(args.steps, w.B)[:, :S]
+        lm_bytes = w.V * w.d * elt
+        kernel = lmhead_kernel_name(w)
+        traffic = traffic_record(w.name)
+    lm_avg_ms = float(lm.mean())
     achieved = lm_bytes / (lm_avg_ms * 1e-3) / 1e9
-    traffic = traffic_record(w.name)
 
     breakdown = {}
     if args.breakdown:
-        for name, kind in (("gemm", TD_PROF_GEMM), ("attention", TD_PROF_ATTENTION), ("step", TD_PROF_STEP)):
+        kinds = (("gemm", TD_PROF_GEMM), ("attention", TD_PROF_ATTENTION), ("step", TD_PROF_STEP))
+        if w.moe:
+            kinds += (("moe_experts", TD_PROF_MOE),)
+        for name, kind in kinds:
             dev.profile_begin(kind)
             for _ in range(3):
                 block()
@@ -385,7 +419,8 @@ def main():
             per = len(ms) // (3 * w.B)
             ms = ms.reshape(3, w.B, per)[:, :S, :]
             breakdown[name] = dict(ms_per_step=float(ms.sum(axis=2).mean()), launches_per_step=per)
-        step_bytes = w.weight_params() * elt + int(plens.sum()) * w.L * 2 * w.Hkv * w.hd * elt
+        step_bytes = (w.weight_params(moe_active / max(1, moe_launches)) * elt
+                      + int(plens.sum()) * w.L * 2 * w.Hkv * w.hd * elt)
         breakdown["step_alg_bytes"] = step_bytes
         breakdown["step_hbm_frac"] = step_bytes / (breakdown["step"]["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS
 
@@ -412,10 +447,11 @@ def main():
         "data": "synthetic (seeded; random-init tower weights N(0,0.02), prefix K/V N(0,1))",
         "config": {"workload": w.name, "batch": w.n, "prefix_tokens": int(plens.sum()), "block": w.B, "gamma": w.gamma,
                    "d_model": w.d, "heads": w.H, "kv_heads": w.Hkv, "head_dim": w.hd, "layers": w.L, "d_ff": w.F,
-                   "vocab": w.V},
+                   "vocab": w.V, **({"moe": {"experts": w.moe[0], "top_k": w.moe[1], "shared": w.moe[2],
+                                              "d_expert": w.moe[3]}} if w.moe else {})},
         "denoise_steps_per_s": round(steps_per_s, 3),
         "denoise_steps_per_block": S,
-        "roofline": {"kernel": lmhead_kernel_name(w),
+        "roofline": {"kernel": kernel,
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": lm_bytes, "avg_launch_ms": round(lm_avg_ms, 5),

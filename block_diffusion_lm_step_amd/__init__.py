@@ -43,6 +43,15 @@ class TdWeights(ctypes.Structure):
                 ("w2", POINTER(c_void_p)), ("final_norm", c_void_p), ("lm_head", c_void_p)]
 
 
+class TdMoeConfig(ctypes.Structure):
+    _fields_ = [("n_experts", c_int32), ("top_k", c_int32), ("n_shared", c_int32), ("d_expert", c_int32)]
+
+
+class TdMoeWeights(ctypes.Structure):
+    _fields_ = [("router", POINTER(c_void_p)), ("w1", POINTER(c_void_p)), ("w2", POINTER(c_void_p)),
+                ("shared_w1", POINTER(c_void_p)), ("shared_w2", POINTER(c_void_p))]
+
+
 _CTX = c_void_p
 try:
     lib.td_create.argtypes = [POINTER(TdConfig), POINTER(TdWeights), c_void_p, POINTER(_CTX)]
@@ -55,6 +64,8 @@ try:
     lib.td_set_context_tower.argtypes = [_CTX, POINTER(TdWeights)]
     lib.td_append_block.argtypes = [_CTX, c_void_p]
     lib.td_ar_step.argtypes = [_CTX, c_void_p]
+    lib.td_set_moe.argtypes = [_CTX, POINTER(TdMoeConfig), POINTER(TdMoeWeights)]
+    lib.td_moe_stats.argtypes = [_CTX, POINTER(c_int64), POINTER(c_int64)]
     lib.td_debug_attention.argtypes = [_CTX, c_int32, c_void_p, c_void_p]
     lib.td_sync.argtypes = [_CTX]
     lib.td_profile_begin.argtypes = [_CTX, c_int32]
@@ -69,17 +80,18 @@ try:
     lib.td_last_error.restype = c_char_p
     lib.td_version.restype = c_char_p
     for _f in ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_generate_block",
-               "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_ar_step", "td_debug_attention",
-               "td_sync"):
+               "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_ar_step", "td_set_moe",
+               "td_moe_stats", "td_debug_attention", "td_sync"):
         getattr(lib, _f).restype = c_int
 except AttributeError as e:   # a library built from older sources
     raise ImportError(f"{LIB_PATH} is stale ({e}); rebuild with `python block_diffusion_lm_step_amd/build.py`") from e
 
 # Every symbol the C header declares.
 EXPORTED = ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_generate_block",
-            "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_ar_step", "td_debug_attention", "td_sync",
+            "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_ar_step", "td_set_moe", "td_moe_stats",
+            "td_debug_attention", "td_sync",
             "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_destroy", "td_last_error", "td_version")
-TD_PROF_OFF, TD_PROF_LMHEAD, TD_PROF_GEMM, TD_PROF_ATTENTION, TD_PROF_STEP = range(5)
+TD_PROF_OFF, TD_PROF_LMHEAD, TD_PROF_GEMM, TD_PROF_ATTENTION, TD_PROF_STEP, TD_PROF_MOE = range(6)
 TD_RULE_THRESHOLD, TD_RULE_LEFT_TO_RIGHT = range(2)
 
 
@@ -93,7 +105,10 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _ptr_array(ts: Sequence) -> ctypes.Array:
+def _ptr_array(ts: Optional[Sequence]):
+    """Device pointers of a list of tensors as a C array; None (or empty) -> NULL."""
+    if not ts:
+        return None
     return (c_void_p * len(ts))(*[t.data_ptr() for t in ts])
 
 
@@ -103,7 +118,8 @@ class Denoiser:
     cfg keys: n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ff, vocab, block_size,
     max_batch, max_prefix_tokens, dtype ("f32"/"bf16"), rms_eps.
     weights: torch tensors on the GPU in the config's dtype (bf16 as torch.bfloat16),
-    keys as in td_weights; per-layer entries are lists.
+    keys as in td_weights; per-layer entries are lists.  w1 and w2 may be None when the
+    MLP is a mixture of experts (set_moe before the first step).
     """
 
     def __init__(self, cfg: Dict, weights: Dict, stream=None):
@@ -114,7 +130,7 @@ class Denoiser:
         c = TdConfig(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"],
                      cfg["d_ff"], cfg["vocab"], cfg["block_size"], cfg["max_batch"], cfg["max_prefix_tokens"],
                      TD_BF16 if cfg["dtype"] == "bf16" else TD_F32, cfg.get("rms_eps", 1e-6))
-        self._keep = {k: _ptr_array(weights[k]) for k in
+        self._keep = {k: _ptr_array(weights.get(k)) for k in
                       ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w1", "w2")}
         w = TdWeights(weights["tok_emb"].data_ptr(), weights["pos_emb"].data_ptr(), self._keep["attn_norm"],
                       self._keep["wq"], self._keep["wk"], self._keep["wv"], self._keep["wo"],
@@ -160,6 +176,21 @@ class Denoiser:
         w = TdWeights(weights["tok_emb"].data_ptr(), None, keep["attn_norm"], keep["wq"], keep["wk"], keep["wv"],
                       keep["wo"], keep["mlp_norm"], keep["w1"], keep["w2"], head[0], head[1])
         self._check(lib.td_set_context_tower(self._ctx, ctypes.byref(w)))
+
+    def set_moe(self, cfg: Dict, weights: Dict) -> None:
+        """cfg: n_experts, top_k, n_shared, d_expert.  weights: per-layer lists router
+        [E][d], w1 [E][d_expert][d], w2 [E][d][d_expert], shared_w1, shared_w2 (None when
+        n_shared is 0); copied and packed by the library."""
+        c = TdMoeConfig(cfg["n_experts"], cfg["top_k"], cfg["n_shared"], cfg["d_expert"])
+        keep = {k: _ptr_array(weights.get(k)) for k in ("router", "w1", "w2", "shared_w1", "shared_w2")}
+        w = TdMoeWeights(keep["router"], keep["w1"], keep["w2"], keep["shared_w1"], keep["shared_w2"])
+        self._check(lib.td_set_moe(self._ctx, ctypes.byref(c), ctypes.byref(w)))
+
+    def moe_stats(self):
+        """(expert-layer launches, sum of their active experts) since the previous call."""
+        n, a = c_int64(0), c_int64(0)
+        self._check(lib.td_moe_stats(self._ctx, ctypes.byref(n), ctypes.byref(a)))
+        return n.value, a.value
 
     def append_block(self, tokens) -> None:
         self._check(lib.td_append_block(self._ctx, _ptr(tokens)))

@@ -54,6 +54,18 @@ struct td_ctx {
   // adoption rule (td_set_commit_rule)
   int rule = RULE_THRESHOLD, min_adopt = 1;
 
+  // mixture-of-experts MLP of the denoiser (td_set_moe)
+  bool moe = false;
+  td_moe_config moe_cfg{};
+  int moe_Epad = 0, moe_max_tiles = 0, moe_cap_rows = 0;
+  std::vector<void *> moe_router, moe_w1, moe_w2;   // packed per layer; w1/w2: routed then shared experts
+  float *moe_scores = nullptr, *moe_gates = nullptr, *moe_rs = nullptr, *moe_y = nullptr;
+  int *moe_experts = nullptr, *moe_slot_pos = nullptr, *moe_src_row = nullptr, *moe_n_tiles = nullptr;
+  int4 *moe_tiles = nullptr;
+  void *moe_u = nullptr;             // GELU outputs of the sorted rows, fragment layout
+  long long *moe_stats = nullptr;    // launches, active experts
+  GemmPlan p_router;
+
   // workspace
   int Mmax = 0, Nqkv = 0;
   float *x = nullptr, *ssq = nullptr, *conf_row = nullptr;
@@ -151,8 +163,13 @@ td_status validate_weights(const td_config &c, const td_weights *w, bool context
   if (!w) return fail(nullptr, TD_EINVAL, "weights is NULL");
   if (!w->tok_emb || (!context && (!w->pos_emb || !w->final_norm || !w->lm_head)))
     return fail(nullptr, TD_EINVAL, "a global weight pointer is NULL");
+  // The denoiser may leave both MLP arrays NULL: its MLP is then a mixture of experts
+  // (td_set_moe); the context tower always has a dense MLP.
+  const bool no_mlp = !context && !w->w1 && !w->w2;
   const void *const *lists[] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w1, w->w2};
-  for (auto *l : lists) {
+  for (int k = 0; k < 8; ++k) {
+    const void *const *l = lists[k];
+    if (k >= 6 && no_mlp) continue;
     if (!l) return fail(nullptr, TD_EINVAL, "a per-layer weight array is NULL");
     for (int i = 0; i < c.n_layers; ++i)
       if (!l[i]) return fail(nullptr, TD_EINVAL, "per-layer weight pointer %d is NULL", i);
@@ -204,6 +221,14 @@ GemmPlan plan_gemm(int M, int N, int K, bool vstat, int dtype) {
     while (p.nw > 4 && KT / p.nw < 2) p.nw /= 2;
   }
   return p;
+}
+
+// Upper bound on the 16-row tiles of the expert-sorted rows of M token rows: the routed
+// experts' rows, each nonempty expert padded by at most 15, plus every shared expert's M.
+int moe_max_tiles(int M, const td_moe_config &mc) {
+  const int64_t mk = (int64_t)M * mc.top_k;
+  const int64_t routed = (mk + 15 * std::min<int64_t>(mc.n_experts, mk) + 15) / 16;
+  return (int)(routed + (int64_t)mc.n_shared * ((M + 15) / 16));
 }
 
 // Prefix keys per split-K item: a multiple of the page size (at least eight pages)
@@ -325,6 +350,90 @@ td_status enqueue_head_commit(td_ctx *c, const void *head, int *tokens, uint8_t 
                               float gamma, int rule, int min_adopt, uint8_t *newly, float *conf_out, int *argmax_out,
                               float *logits, int *steps, int8_t *commit_step);
 
+// The mixture-of-experts MLP of layer l over M rows: router scores (a weight-streaming
+// GEMM over the normed input c->ah with its row scale), routing and the expert-sorted
+// tile table, the expert up and down projections, then the gated sum into the residual
+// stream, which leaves x, its partial sums of squares and x * gain_after in fragment
+// layout exactly as the dense MLP's down projection does.
+td_status enqueue_moe(td_ctx *c, int l, int M, const void *gain_after) {
+  const td_config &g = c->cfg;
+  const td_moe_config &mc = c->moe_cfg;
+  const int d = g.d_model;
+  TD_TRY(enqueue_gemm(c, EPI_STORE, true, M, c->moe_Epad, d, c->ah, c->moe_router[l], c->p_router, c->moe_scores,
+                      nullptr, nullptr));
+  MoeRoute r{};
+  r.M = M;
+  r.E = mc.n_experts;
+  r.Epad = c->moe_Epad;
+  r.top_k = mc.top_k;
+  r.n_shared = mc.n_shared;
+  r.d = d;
+  r.scores = c->moe_scores;
+  r.ssq = c->ssq;
+  r.eps = g.rms_eps;
+  r.experts = c->moe_experts;
+  r.gates = c->moe_gates;
+  r.rs = c->moe_rs;
+  r.slot_pos = c->moe_slot_pos;
+  r.src_row = c->moe_src_row;
+  r.tiles = c->moe_tiles;
+  r.n_tiles = c->moe_n_tiles;
+  r.stats = c->moe_stats;
+  // Rows of finished sequences are skipped with more than one sequence bound (one
+  // sequence: the step's own flag ends the loop).
+  r.seq_done = c->n_seqs > 1 ? c->st.seq_done : c->zero_seq;
+  r.B = g.block_size;
+  r.done = c->st.done;
+  TD_HIP(c, launch_moe_route(r, c->stream));
+  const int NE = mc.n_experts + mc.n_shared;
+  const int tiles = moe_max_tiles(M, mc);
+  MoeGemm up{};
+  up.N = mc.d_expert;
+  up.K = d;
+  up.A = c->ah;
+  up.src_row = c->moe_src_row;
+  up.rs = c->moe_rs;
+  up.Wp = c->moe_w1[l];
+  up.tiles = c->moe_tiles;
+  up.n_tiles = c->moe_n_tiles;
+  up.max_tiles = tiles;
+  up.out_afl = c->moe_u;
+  up.done = c->st.done;
+  MoeGemm dn = up;
+  dn.N = d;
+  dn.K = mc.d_expert;
+  dn.A = c->moe_u;
+  dn.src_row = nullptr;
+  dn.rs = nullptr;
+  dn.Wp = c->moe_w2[l];
+  dn.out_afl = nullptr;
+  dn.out = c->moe_y;
+  (void)NE;
+  TD_TRY(prof_mark(c, TD_PROF_MOE, true));
+  TD_HIP(c, launch_moe_gemm(g.dtype, true, up, c->stream));
+  TD_TRY(prof_mark(c, TD_PROF_MOE, false));
+  TD_TRY(prof_mark(c, TD_PROF_MOE, true));
+  TD_HIP(c, launch_moe_gemm(g.dtype, false, dn, c->stream));
+  TD_TRY(prof_mark(c, TD_PROF_MOE, false));
+  MoeCombine cb{};
+  cb.M = M;
+  cb.d = d;
+  cb.top_k = mc.top_k;
+  cb.n_shared = mc.n_shared;
+  cb.slot_pos = c->moe_slot_pos;
+  cb.gates = c->moe_gates;
+  cb.y = c->moe_y;
+  cb.x = c->x;
+  cb.out_afl = c->ah;
+  cb.gain_next = gain_after;
+  cb.ssq_out = c->ssq;
+  cb.seq_done = r.seq_done;
+  cb.B = g.block_size;
+  cb.done = c->st.done;
+  TD_HIP(c, launch_moe_combine(g.dtype, cb, c->stream));
+  return TD_OK;
+}
+
 td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *inv_temp, float gamma,
                        uint8_t *newly, float *conf_out, int *argmax_out, float *logits, int *steps,
                        int8_t *commit_step) {
@@ -339,8 +448,12 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
     TD_TRY(enqueue_gemm(c, EPI_STORE, true, M, c->Nqkv, d, c->ah, c->layers.wqkv[l], c->p_qkv, c->qkv, nullptr, nullptr));
     TD_TRY(enqueue_attention(c, l, c->qkv, nullptr, c->ao, c->st.done));
     TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, Hd, c->ao, c->layers.wo[l], c->p_wo, c->x, c->ah, c->layers.mlp_norm[l]));
-    TD_TRY(enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, c->ah, c->layers.w1[l], c->p_w1, nullptr, c->au, nullptr));
-    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->au, c->layers.w2[l], c->p_w2, c->x, c->ah, gain_after));
+    if (c->moe) {
+      TD_TRY(enqueue_moe(c, l, M, gain_after));
+    } else {
+      TD_TRY(enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, c->ah, c->layers.w1[l], c->p_w1, nullptr, c->au, nullptr));
+      TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->au, c->layers.w2[l], c->p_w2, c->x, c->ah, gain_after));
+    }
   }
   TD_TRY(enqueue_head_commit(c, c->lm_head, tokens, committed, inv_temp, gamma, c->rule, c->min_adopt, newly, conf_out,
                              argmax_out, logits, steps, commit_step));
@@ -443,6 +556,24 @@ td_status check_bound(td_ctx *c) {
   return TD_OK;
 }
 
+void free_moe(td_ctx *c) {
+  auto f = [](void *p) {
+    if (p) (void)hipFree(p);
+  };
+  for (auto *v : {&c->moe_router, &c->moe_w1, &c->moe_w2}) {
+    for (void *p : *v) f(p);
+    v->clear();
+  }
+  f(c->moe_scores); f(c->moe_gates); f(c->moe_rs); f(c->moe_y); f(c->moe_experts); f(c->moe_slot_pos);
+  f(c->moe_src_row); f(c->moe_n_tiles); f(c->moe_tiles); f(c->moe_u); f(c->moe_stats);
+  c->moe_scores = c->moe_gates = c->moe_rs = c->moe_y = nullptr;
+  c->moe_experts = c->moe_slot_pos = c->moe_src_row = c->moe_n_tiles = nullptr;
+  c->moe_tiles = nullptr;
+  c->moe_u = nullptr;
+  c->moe_stats = nullptr;
+  c->moe = false;
+}
+
 void free_all(td_ctx *c) {
   auto f = [](void *p) {
     if (p) (void)hipFree(p);
@@ -455,6 +586,7 @@ void free_all(td_ctx *c) {
   f(c->x); f(c->ssq); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->ah); f(c->ao); f(c->au);
   f(c->arg_row); f(c->state_ints); f(c->items_d); f(c->pair_first_d);
   f(c->pair_count_d); f(c->att_o); f(c->att_ml); f(c->part);
+  free_moe(c);
   for (hipEvent_t e : c->ev_start) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->ev_stop) (void)hipEventDestroy(e);
 }
@@ -471,8 +603,10 @@ td_status pack_layers(td_ctx *c, const td_weights &w, Layers &t) {
     TD_TRY(dmalloc(c, &t.mlp_norm[l], d * e));
     TD_TRY(dmalloc(c, &t.wqkv[l], (size_t)c->Nqkv * d * e));
     TD_TRY(dmalloc(c, &t.wo[l], d * Hd * e));
-    TD_TRY(dmalloc(c, &t.w1[l], F * d * e));
-    TD_TRY(dmalloc(c, &t.w2[l], d * F * e));
+    if (w.w1) {
+      TD_TRY(dmalloc(c, &t.w1[l], F * d * e));
+      TD_TRY(dmalloc(c, &t.w2[l], d * F * e));
+    }
     TD_HIP(c, hipMemcpyAsync(t.attn_norm[l], w.attn_norm[l], d * e, hipMemcpyDeviceToDevice, c->stream));
     TD_HIP(c, hipMemcpyAsync(t.mlp_norm[l], w.mlp_norm[l], d * e, hipMemcpyDeviceToDevice, c->stream));
     char *qkv = (char *)t.wqkv[l];
@@ -480,8 +614,10 @@ td_status pack_layers(td_ctx *c, const td_weights &w, Layers &t) {
     TD_HIP(c, launch_pack_weight(g.dtype, w.wk[l], qkv + Hd * d * e, (int)KVd, (int)d, c->stream));
     TD_HIP(c, launch_pack_weight(g.dtype, w.wv[l], qkv + (Hd + KVd) * d * e, (int)KVd, (int)d, c->stream));
     TD_HIP(c, launch_pack_weight(g.dtype, w.wo[l], t.wo[l], (int)d, (int)Hd, c->stream));
-    TD_HIP(c, launch_pack_weight(g.dtype, w.w1[l], t.w1[l], (int)F, (int)d, c->stream));
-    TD_HIP(c, launch_pack_weight(g.dtype, w.w2[l], t.w2[l], (int)d, (int)F, c->stream));
+    if (w.w1) {
+      TD_HIP(c, launch_pack_weight(g.dtype, w.w1[l], t.w1[l], (int)F, (int)d, c->stream));
+      TD_HIP(c, launch_pack_weight(g.dtype, w.w2[l], t.w2[l], (int)d, (int)F, c->stream));
+    }
   }
   return TD_OK;
 }
@@ -655,9 +791,10 @@ td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const int64_t
     c->p_w2 = plan_gemm(M, d, F, false, g.dtype);
     c->p_lm = plan_gemm(M, g.vocab, d, true, g.dtype);
     size_t need = 0;   // floats of split-K partials
-    const GemmPlan *plans[] = {&c->p_qkv, &c->p_wo, &c->p_w1, &c->p_w2};
-    const int widths[] = {c->Nqkv, d, F, d};
-    for (int i = 0; i < 4; ++i)
+    c->p_router = plan_gemm(M, std::max(c->moe_Epad, 32), d, false, g.dtype);
+    const GemmPlan *plans[] = {&c->p_qkv, &c->p_wo, &c->p_w1, &c->p_w2, &c->p_router};
+    const int widths[] = {c->Nqkv, d, F, d, c->moe_Epad};
+    for (int i = 0; i < 5; ++i)
       if (plans[i]->splits > 1) need = std::max(need, (size_t)plans[i]->splits * M * widths[i]);
     TD_TRY(grow(&c->part, c->part_cap, need, sizeof(float)));
   }
@@ -707,9 +844,16 @@ td_status td_bind_cache(td_ctx *c, int32_t n_seqs, const int64_t *lengths_host, 
   return bind_impl(c, n_seqs, lengths_host, page_capacity_host, k_cache_host, v_cache_host);
 }
 
+td_status check_mlp(td_ctx *c) {
+  if (!c->moe && (c->layers.w1.empty() || !c->layers.w1[0]))
+    return fail(c, TD_EINVAL, "the denoiser has no MLP weights: pass w1/w2 to td_create or call td_set_moe");
+  return TD_OK;
+}
+
 td_status td_denoise_step(td_ctx *c, int32_t *tokens, uint8_t *committed, const float *inv_temp, float gamma,
                           uint8_t *newly, float *conf_out, int32_t *argmax_out, float *logits_out) {
   TD_TRY(check_ctx(c));
+  TD_TRY(check_mlp(c));
   if (!tokens || !committed) return fail(c, TD_EINVAL, "tokens and committed must not be NULL");
   if (!finite(gamma)) return fail(c, TD_EINVAL, "gamma must be finite");
   TD_TRY(check_bound(c));
@@ -722,6 +866,7 @@ td_status td_denoise_step(td_ctx *c, int32_t *tokens, uint8_t *committed, const 
 td_status td_generate_block(td_ctx *c, int32_t *tokens, uint8_t *committed, const float *inv_temp, float gamma,
                             int32_t *steps, int8_t *commit_step) {
   TD_TRY(check_ctx(c));
+  TD_TRY(check_mlp(c));
   if (!tokens || !committed) return fail(c, TD_EINVAL, "tokens and committed must not be NULL");
   if (!finite(gamma)) return fail(c, TD_EINVAL, "gamma must be finite");
   TD_TRY(check_bound(c));
@@ -822,6 +967,124 @@ td_status td_ar_step(td_ctx *c, int32_t *tokens) {
   return bind_impl(c, c->n_seqs, len.data(), cap.data(), kc.data(), vc.data());
 }
 
+td_status set_moe_impl(td_ctx *c, const td_moe_config &m, const td_moe_weights &w) {
+  const td_config &g = c->cfg;
+  const size_t e = c->elt, d = g.d_model, de = m.d_expert, L = g.n_layers;
+  const size_t E = m.n_experts, S = m.n_shared, NE = E + S;
+  c->moe_cfg = m;
+  c->moe_Epad = (m.n_experts + 31) / 32 * 32;
+  c->moe_max_tiles = moe_max_tiles(c->Mmax, m);
+  c->moe_cap_rows = 16 * c->moe_max_tiles;
+  const size_t Ep = c->moe_Epad, M = c->Mmax, cap = c->moe_cap_rows;
+  c->moe_router.assign(L, nullptr);
+  c->moe_w1.assign(L, nullptr);
+  c->moe_w2.assign(L, nullptr);
+  void *tmp = nullptr;   // the router padded to Epad rows of zeros
+  TD_TRY(dmalloc(c, &tmp, Ep * d * e));
+  td_status st = TD_OK;
+  for (size_t l = 0; l < L && st == TD_OK; ++l) {
+    st = [&]() -> td_status {
+      TD_TRY(dmalloc(c, &c->moe_router[l], Ep * d * e));
+      TD_TRY(dmalloc(c, &c->moe_w1[l], NE * de * d * e));
+      TD_TRY(dmalloc(c, &c->moe_w2[l], NE * d * de * e));
+      TD_HIP(c, hipMemsetAsync(tmp, 0, Ep * d * e, c->stream));
+      TD_HIP(c, hipMemcpyAsync(tmp, w.router[l], E * d * e, hipMemcpyDeviceToDevice, c->stream));
+      TD_HIP(c, launch_pack_weight(g.dtype, tmp, c->moe_router[l], (int)Ep, (int)d, c->stream));
+      // Expert e's rows of a per-layer [E * rows][cols] matrix pack to one contiguous block.
+      TD_HIP(c, launch_pack_weight(g.dtype, w.w1[l], c->moe_w1[l], (int)(E * de), (int)d, c->stream));
+      TD_HIP(c, launch_pack_weight(g.dtype, w.w2[l], c->moe_w2[l], (int)(E * d), (int)de, c->stream));
+      if (S) {
+        TD_HIP(c, launch_pack_weight(g.dtype, w.shared_w1[l], (char *)c->moe_w1[l] + E * de * d * e, (int)(S * de),
+                                     (int)d, c->stream));
+        TD_HIP(c, launch_pack_weight(g.dtype, w.shared_w2[l], (char *)c->moe_w2[l] + E * d * de * e, (int)(S * d),
+                                     (int)de, c->stream));
+      }
+      TD_HIP(c, hipStreamSynchronize(c->stream));   // tmp is reused by the next layer
+      return TD_OK;
+    }();
+  }
+  (void)hipFree(tmp);
+  TD_TRY(st);
+  TD_TRY(dmalloc(c, &c->moe_scores, M * Ep * 4));
+  TD_TRY(dmalloc(c, &c->moe_experts, M * m.top_k * 4));
+  TD_TRY(dmalloc(c, &c->moe_gates, M * m.top_k * 4));
+  TD_TRY(dmalloc(c, &c->moe_rs, M * 4));
+  TD_TRY(dmalloc(c, &c->moe_slot_pos, M * (m.top_k + S) * 4));
+  TD_TRY(dmalloc(c, &c->moe_src_row, cap * 4));
+  TD_TRY(dmalloc(c, &c->moe_tiles, (size_t)c->moe_max_tiles * sizeof(int4)));
+  TD_TRY(dmalloc(c, &c->moe_n_tiles, 4));
+  TD_TRY(dmalloc(c, &c->moe_u, afl_bytes((int)cap, (int)de)));
+  TD_TRY(dmalloc(c, &c->moe_y, cap * d * 4));
+  TD_TRY(dmalloc(c, &c->moe_stats, 2 * sizeof(long long)));
+  // The grouped GEMMs read tile entries and sorted rows beyond the live ones before they
+  // test the live count: zeroed entries (expert 0, row 0) keep those reads in bounds.
+  TD_HIP(c, hipMemsetAsync(c->moe_src_row, 0, cap * 4, c->stream));
+  TD_HIP(c, hipMemsetAsync(c->moe_tiles, 0, (size_t)c->moe_max_tiles * sizeof(int4), c->stream));
+  TD_HIP(c, hipMemsetAsync(c->moe_n_tiles, 0, 4, c->stream));
+  TD_HIP(c, hipMemsetAsync(c->moe_u, 0, afl_bytes((int)cap, (int)de), c->stream));
+  TD_HIP(c, hipMemsetAsync(c->moe_stats, 0, 2 * sizeof(long long), c->stream));
+  TD_HIP(c, hipStreamSynchronize(c->stream));
+  return TD_OK;
+}
+
+td_status td_set_moe(td_ctx *c, const td_moe_config *mc, const td_moe_weights *w) {
+  TD_TRY(check_ctx(c));
+  if (!mc || !w) return fail(c, TD_EINVAL, "MoE config and weights must not be NULL");
+  const td_moe_config m = *mc;
+  if (m.n_experts < 1 || m.n_experts > MOE_MAX_EXPERTS)
+    return fail(c, TD_EINVAL, "n_experts must be in [1, %d]", MOE_MAX_EXPERTS);
+  if (m.top_k < 1 || m.top_k > MOE_MAX_TOP_K || m.top_k > m.n_experts)
+    return fail(c, TD_EINVAL, "top_k must be in [1, min(%d, n_experts)]", MOE_MAX_TOP_K);
+  if (m.n_shared < 0 || m.n_shared > MOE_MAX_SHARED)
+    return fail(c, TD_EINVAL, "n_shared must be in [0, %d]", MOE_MAX_SHARED);
+  if (m.d_expert < 64 || m.d_expert % 64 || m.d_expert > (1 << 20))
+    return fail(c, TD_EINVAL, "d_expert must be a positive multiple of 64");
+  const void *const *lists[] = {w->router, w->w1, w->w2, w->shared_w1, w->shared_w2};
+  for (int k = 0; k < 5; ++k) {
+    if (k >= 3 && m.n_shared == 0) continue;
+    if (!lists[k]) return fail(c, TD_EINVAL, "a per-layer MoE weight array is NULL");
+    for (int l = 0; l < c->cfg.n_layers; ++l)
+      if (!lists[k][l]) return fail(c, TD_EINVAL, "MoE weight pointer of layer %d is NULL", l);
+  }
+  TD_HIP(c, hipSetDevice(c->dev));
+  TD_HIP(c, hipStreamSynchronize(c->stream));   // earlier steps may still read the old experts
+  free_moe(c);
+  td_status s = set_moe_impl(c, m, *w);
+  if (s == TD_OK && c->n_seqs > 0) {   // the router's GEMM plan for the bound batch
+    const int M = c->n_seqs * c->cfg.block_size;
+    c->p_router = plan_gemm(M, c->moe_Epad, c->cfg.d_model, false, c->cfg.dtype);
+    const size_t need = c->p_router.splits > 1 ? (size_t)c->p_router.splits * M * c->moe_Epad : 0;
+    if (need > c->part_cap) {
+      if (c->part) (void)hipFree(c->part);
+      c->part = nullptr;
+      c->part_cap = 0;
+      s = dmalloc(c, &c->part, need * sizeof(float));
+      if (s == TD_OK) c->part_cap = need;
+    }
+  }
+  if (s != TD_OK) {
+    (void)hipStreamSynchronize(c->stream);
+    free_moe(c);
+    return s;
+  }
+  c->moe = true;
+  return TD_OK;
+}
+
+td_status td_moe_stats(td_ctx *c, int64_t *launches, int64_t *active) {
+  TD_TRY(check_ctx(c));
+  if (!c->moe) return fail(c, TD_EINVAL, "no mixture of experts set: call td_set_moe first");
+  if (!launches || !active) return fail(c, TD_EINVAL, "output pointers must not be NULL");
+  TD_HIP(c, hipSetDevice(c->dev));
+  TD_HIP(c, hipStreamSynchronize(c->stream));
+  long long v[2] = {0, 0};
+  TD_HIP(c, hipMemcpy(v, c->moe_stats, sizeof v, hipMemcpyDeviceToHost));
+  TD_HIP(c, hipMemset(c->moe_stats, 0, sizeof v));
+  *launches = v[0];
+  *active = v[1];
+  return TD_OK;
+}
+
 td_status td_debug_attention(td_ctx *c, int32_t layer, const void *qkv, void *o) {
   TD_TRY(check_ctx(c));
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, TD_EINVAL, "layer out of range");
@@ -849,7 +1112,7 @@ td_status td_sync(td_ctx *c) {
 
 td_status td_profile_begin(td_ctx *c, int32_t kind) {
   TD_TRY(check_ctx(c));
-  if (kind < TD_PROF_OFF || kind > TD_PROF_STEP) return fail(c, TD_EINVAL, "unknown profiling kind %d", kind);
+  if (kind < TD_PROF_OFF || kind > TD_PROF_MOE) return fail(c, TD_EINVAL, "unknown profiling kind %d", kind);
   c->prof_kind = kind;
   return TD_OK;
 }
@@ -870,7 +1133,8 @@ int32_t td_profile_end(td_ctx *c, float *ms_out, int32_t max) {
 
 int32_t td_kernels_per_step(const td_ctx *c) {
   if (!c) return -1;
-  return 1 + 1 + 6 * c->cfg.n_layers + 2;   // prep/init, embed, per layer 6, LM head, merge+commit
+  // prep/init, embed, per layer 6 (10 with a mixture of experts), LM head, merge+commit
+  return 1 + 1 + (c->moe ? 10 : 6) * c->cfg.n_layers + 2;
 }
 
 void td_destroy(td_ctx *c) {

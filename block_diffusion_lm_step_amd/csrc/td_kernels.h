@@ -163,4 +163,53 @@ hipError_t launch_merge_commit(const CommitArgs &a, int max_rows, hipStream_t s)
 hipError_t launch_kv_append(int dtype, const float *qkv, int Nqkv, int H, int Hkv, int hd, void *kc, void *vc,
                             const int *seq_len, const int *seq_page, int n, int B, hipStream_t s);
 
+// ---------------------------------------------------------------- mixture of experts
+// Routing, expert-grouped weight streaming and the gated sum of a mixture-of-experts MLP
+// (see k_moe.hip).  Experts 0 .. E-1 are routed, E .. E+n_shared-1 shared.  Expert-sorted
+// rows: every expert's rows form a segment padded to a multiple of 16, so each 16-row
+// tile belongs to one expert.
+constexpr int MOE_MAX_EXPERTS = 256, MOE_MAX_TOP_K = 8, MOE_MAX_SHARED = 4;
+struct MoeRoute {
+  int M, E, Epad, top_k, n_shared, d;
+  const float *scores;        // [M][Epad] router scores (fp32, row scale applied)
+  const float *ssq;           // [d/16][M] partial sums of squares of the MLP input rows
+  float eps;                  // RMSNorm epsilon
+  int *experts;               // [M][top_k] chosen experts by rank
+  float *gates;               // [M][top_k]
+  float *rs;                  // [M] RMSNorm row scale of each row
+  int *slot_pos;              // [M][top_k + n_shared] sorted row of each (row, slot)
+  int *src_row;               // [cap_rows] token row of each sorted row (padding: row 0)
+  int4 *tiles;                // [max_tiles] (expert, first sorted row, live rows, 0)
+  int *n_tiles;               // tiles in use
+  long long *stats;           // [2] launches, sum of active experts
+  const int *seq_done;        // [M / B] 1: the sequence's block is adopted, its rows are not routed
+  int B;                      // rows per sequence
+  const int *done;
+};
+hipError_t launch_moe_route(const MoeRoute &a, hipStream_t s);   // route + bucket (two kernels)
+struct MoeGemm {
+  int N, K;                   // per expert: Y[rows][N] = A[rows][K] * W_e[N][K]^T
+  const void *A;              // W1: the MLP input x * gain in fragment layout, gathered by
+                              // src_row; W2: the sorted GELU output in fragment layout
+  const int *src_row;         // W1 only
+  const float *rs;            // W1 only: row scales, indexed by token row
+  const void *Wp;             // packed experts, expert e at e * N * K elements
+  const int4 *tiles; const int *n_tiles; int max_tiles;
+  void *out_afl;              // W1: gelu(y) of the sorted rows in fragment layout (all 16 rows of a tile)
+  float *out;                 // W2: y of the sorted rows, fp32 [cap_rows][N] (live rows)
+  const int *done;
+};
+hipError_t launch_moe_gemm(int dtype, bool up, const MoeGemm &a, hipStream_t s);
+struct MoeCombine {
+  int M, d, top_k, n_shared;
+  const int *slot_pos; const float *gates; const float *y;
+  float *x;                   // [M][d] residual stream, updated in place
+  void *out_afl;              // x * gain_next in fragment layout
+  const void *gain_next;      // [d]
+  float *ssq_out;             // [d/16][M]
+  const int *seq_done; int B; // rows of adopted sequences are left as they are
+  const int *done;
+};
+hipError_t launch_moe_combine(int dtype, const MoeCombine &a, hipStream_t s);
+
 }  // namespace td

@@ -77,7 +77,10 @@ typedef struct {
   const void *const *wo;               /* L x [d][n_heads*head_dim] */
   const void *const *mlp_norm;         /* L x [d] RMSNorm gains before the MLP */
   const void *const *w1;               /* L x [d_ff][d]   (u = gelu_erf(h W1^T)) */
-  const void *const *w2;               /* L x [d][d_ff]   (x += u W2^T) */
+  const void *const *w2;               /* L x [d][d_ff]   (x += u W2^T)
+                                        * w1 and w2 may both be NULL in td_create for a
+                                        * denoiser whose MLP is a mixture of experts
+                                        * (td_set_moe before the first step). */
   const void *final_norm;              /* [d] */
   const void *lm_head;                 /* [vocab][d], untied; never predicts [MASK] */
 } td_weights;
@@ -157,6 +160,47 @@ td_status td_ar_step(td_ctx *ctx, int32_t *tokens);
  * stream before returning (the work lists are rebuilt on the host). */
 td_status td_append_block(td_ctx *ctx, const int32_t *tokens);
 
+/* Mixture-of-experts MLP of the denoiser (dzen.guru, section "Что нового": the tower's
+ * MoE layers activate 6 of 128 experts plus 2 shared ones per token).  Readings: a
+ * router row per expert scores the normed MLP input h2 (the same RMSNorm as the dense
+ * MLP); each token takes the top_k experts of largest fp32 score (lowest expert id on
+ * ties) with gates = softmax over the chosen scores; every expert, routed or shared, is
+ * an ungated GELU MLP of width d_expert; shared experts apply to every token with weight
+ * 1:  x += sum_j gate_j * gelu(h2 W1_{e_j}^T) W2_{e_j}^T + sum_s gelu(h2 S1_s^T) S2_s^T.
+ * Supported: 1 <= n_experts <= 256, 1 <= top_k <= min(8, n_experts), 0 <= n_shared <= 4,
+ * d_expert a positive multiple of 64. */
+typedef struct {
+  int32_t n_experts, top_k, n_shared, d_expert;
+} td_moe_config;
+
+/* Expert weights, DEVICE pointers in the config's dtype; every entry is a HOST array of
+ * n_layers device pointers.  Experts of one layer are contiguous: expert e of w1 starts
+ * at element e * d_expert * d, of w2 at e * d * d_expert. */
+typedef struct {
+  const void *const *router;      /* L x [n_experts][d] */
+  const void *const *w1;          /* L x [n_experts][d_expert][d] */
+  const void *const *w2;          /* L x [n_experts][d][d_expert] */
+  const void *const *shared_w1;   /* L x [n_shared][d_expert][d]; NULL when n_shared == 0 */
+  const void *const *shared_w2;   /* L x [n_shared][d][d_expert]; NULL when n_shared == 0 */
+} td_moe_weights;
+
+/* Replace the MLP of every denoiser layer with the mixture of experts above (a later
+ * call replaces it again).  The weights are copied and packed into the ctx (the caller
+ * may free them once the stream has synchronised); the workspace for max_batch rows is
+ * allocated here.  The context tower keeps its dense MLP.  Routing, the expert
+ * products and their gated sum all run on the device inside every later step.
+ * Errors: TD_EINVAL (NULL pointer, unsupported shape), TD_ENOMEM. */
+td_status td_set_moe(td_ctx *ctx, const td_moe_config *cfg, const td_moe_weights *w);
+
+/* Expert counters of the MoE layers since the previous call (then reset): the number of
+ * expert-layer launches that ran (a layer of a step whose block was not yet adopted) and
+ * the sum over them of the distinct experts, routed plus shared, that held at least one
+ * token: the expert weights read per launch are active / launches experts' W1 and W2.
+ * With more than one sequence bound, the rows of a sequence whose block is already
+ * adopted are not routed (they are not read again) and count for no expert.
+ * Waits for the stream.  Errors: TD_EINVAL (no MoE set, NULL pointer). */
+td_status td_moe_stats(td_ctx *ctx, int64_t *launches_host, int64_t *active_experts_host);
+
 /* One denoising step over the bound batch.
  *  tokens     int32 [n][B] in/out: a token id, or vocab ([MASK]) exactly where
  *             committed == 0.
@@ -220,7 +264,8 @@ typedef enum {
   TD_PROF_LMHEAD = 1,     /* LM head + fused vocab statistics (one launch per step) */
   TD_PROF_GEMM = 2,       /* the 4 L layer projections of a step */
   TD_PROF_ATTENTION = 3,  /* split-K attention + merge, L per step */
-  TD_PROF_STEP = 4        /* one whole step, embedding to commit */
+  TD_PROF_STEP = 4,       /* one whole step, embedding to commit */
+  TD_PROF_MOE = 5         /* the expert up and down projections, 2 L per step (td_set_moe) */
 } td_prof_kind;
 
 /* Profiling: from now on bracket every launch of kernel class `kind` with a pair of HIP

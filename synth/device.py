@@ -30,10 +30,26 @@ def tower_to_device(tw: TowerInputs, device="cuda") -> Dict:
     bf = tw.is_bf16
     up = lambda a: host_to_device(a, bf, device)  # noqa: E731
     upn = lambda a: None if a is None else up(a)  # noqa: E731  (context tower: no pos/final/head)
+    # A mixture-of-experts denoiser has no dense MLP: w1/w2 None.
     return dict(tok_emb=up(tw.tok_emb), pos_emb=upn(tw.pos_emb), final_norm=upn(tw.final_norm), lm_head=upn(tw.lm_head),
                 attn_norm=[up(a) for a in tw.attn_norm], mlp_norm=[up(a) for a in tw.mlp_norm],
                 wq=[up(a) for a in tw.wq], wk=[up(a) for a in tw.wk], wv=[up(a) for a in tw.wv],
-                wo=[up(a) for a in tw.wo], w1=[up(a) for a in tw.w1], w2=[up(a) for a in tw.w2])
+                wo=[up(a) for a in tw.wo], w1=[up(a) for a in tw.w1] if tw.w1 else None,
+                w2=[up(a) for a in tw.w2] if tw.w2 else None)
+
+
+def moe_to_device(mi, device="cuda") -> Dict:
+    """Expert weights as the binding's set_moe expects them (per-layer lists)."""
+    bf = mi.w.dtype == "bf16"
+    up = lambda a: host_to_device(a, bf, device)  # noqa: E731
+    S = mi.w.moe[2]
+    return dict(router=[up(a) for a in mi.router], w1=[up(a) for a in mi.w1], w2=[up(a) for a in mi.w2],
+                shared_w1=[up(a) for a in mi.sw1] if S else None, shared_w2=[up(a) for a in mi.sw2] if S else None)
+
+
+def moe_config(w: Workload) -> Dict:
+    E, k, S, de = w.moe
+    return dict(n_experts=E, top_k=k, n_shared=S, d_expert=de)
 
 
 def tower_config(w: Workload, max_batch: int = None, max_prefix_tokens: int = 0) -> Dict:

@@ -47,18 +47,27 @@ def build_case(w, plens=None, mode=None, device="cuda") -> Case:
     from tests.helpers import kv_provider, oracle_weights
     from oracle import OracleTower
 
-    log(f"[case] building {w.name}: n={w.n} B={w.B} d={w.d} L={w.L} V={w.V} dtype={w.dtype}")
+    log(f"[case] building {w.name}: n={w.n} B={w.B} d={w.d} L={w.L} V={w.V} dtype={w.dtype} moe={w.moe}")
     tw = draw_tower(w)
+    mi = None
+    if w.moe:
+        from synth import draw_moe
+        mi = draw_moe(w)
     plens = draw_prefix_lengths(w) if plens is None else np.asarray(plens, dtype=np.int64)
     tau = draw_inv_temp(w)
     # The GPU carries activations at fp32 precision (no bf16 rounding of activations), so
     # the reference is the plain float64 oracle for every workload.
     mode = mode or "plain"
-    orc = OracleTower(oracle_weights(tw), H=w.H, Hkv=w.Hkv, hd=w.hd, eps=w.rms_eps, mode=mode)
+    orc = OracleTower(oracle_weights(tw, mi), H=w.H, Hkv=w.Hkv, hd=w.hd, eps=w.rms_eps, mode=mode)
     kv = kv_provider(w, plens)
     dW = tower_to_device(tw, device)
     offsets, ks, vs = prefix_to_device(w, plens, device)
     dev = Denoiser(tower_config(w, max_batch=w.n, max_prefix_tokens=max(1, offsets[-1])), dW)
+    if mi is not None:
+        from synth.device import moe_config, moe_to_device
+        dM = moe_to_device(mi, device)
+        dev.set_moe(moe_config(w), dM)
+        del dM
     dev.set_prefix(offsets, ks, vs)
     del dW
     torch.cuda.synchronize()
