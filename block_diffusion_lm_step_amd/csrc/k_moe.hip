@@ -206,15 +206,17 @@ __global__ __launch_bounds__(1024) void moe_bucket_kernel(MoeRoute a) {
 // k-tile in a budget that keeps two workgroups of NW = 4 waves per CU.
 template <typename T, int NT> constexpr int moe_pass() {
   constexpr int per = 8 + NT * (sizeof(T) == 2 ? 4 : 8);
-  constexpr int p = 144 / per;
+  constexpr int p = 128 / per;
   return p > 16 ? 16 : (p < 1 ? 1 : p);
 }
 
 // Work items: (16-row tile of one expert, NT 16-column tiles), tile-major.  A grid of at
 // most two workgroups per CU walks the live items (the tile count is known on the device
-// only): item blockIdx.x, then every gridDim.x-th.  NW waves split K.  UP: the gathered
-// up projection with the row scale and GELU (W1); else the down projection of the
-// sorted rows (W2).
+// only): item blockIdx.x, then every gridDim.x-th.  NW waves split K.  The next item's
+// first PASS k-tiles are requested as soon as the current item's last MFMAs have read
+// their registers, so the wave reduction and the epilogue overlap those loads.  UP: the
+// gathered up projection with the row scale and GELU (W1); else the down projection of
+// the sorted rows (W2).
 template <typename T, int NT, int NW, bool UP>
 __global__ __launch_bounds__(64 * NW) void moe_gemm_kernel(MoeGemm a) {
   constexpr int PASS = moe_pass<T, NT>();
@@ -230,34 +232,41 @@ __global__ __launch_bounds__(64 * NW) void moe_gemm_kernel(MoeGemm a) {
 
   __shared__ f32x4_t s_red[NW][NT][64];
 
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int t = item / ncg, nt0 = (item - t * ncg) * NT;
+  Frag<T> wb[PASS][NT];
+  AFrag<T> xa[PASS];
+  const T *Wl;
+  const char *Al;
+  int row0 = 0, nrows = 0, nt0 = 0;
+  float rsv[4] = {1.f, 1.f, 1.f, 1.f};   // row scales of the 4 output rows a lane finishes (W1)
+  // Requests the first PASS k-tiles of `item` and sets its addresses.
+  auto issue = [&](int item) __attribute__((always_inline)) {
+    const int t = item / ncg;
+    nt0 = (item - t * ncg) * NT;
     const int4 tile = a.tiles[t];
-    const int expert = tile.x, row0 = tile.y, nrows = tile.z;
+    row0 = tile.y;
+    nrows = tile.z;
     // Gathered row of this lane (W1) or the tile's own rows (W2).
     int srow = row0 + l16;
     if constexpr (UP) srow = a.src_row[row0 + l16];
-    const T *Wl = reinterpret_cast<const T *>(a.Wp) + (size_t)expert * a.N * a.K + ((size_t)nt0 * KT) * 512 +
-                  (size_t)lane * 8;
-    Frag<T> wb[PASS][NT];
-    AFrag<T> xa[PASS];
+    Wl = reinterpret_cast<const T *>(a.Wp) + (size_t)tile.x * a.N * a.K + ((size_t)nt0 * KT) * 512 + (size_t)lane * 8;
 #pragma unroll
     for (int i = 0; i < PASS; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j) wb[i][j].load(Wl + ((size_t)j * KT + clampk(kw0 + i)) * 512);
-    // Fragment (row, k-tile kt) of lane (g, l16) in fragment layout: ((row/16 * KT + kt) * 64
-    // + 16 g + row % 16) * 32 bytes.
-    const char *Al = reinterpret_cast<const char *>(a.A) +
-                     ((size_t)(srow >> 4) * KT * 64 + 16 * g + (srow & 15)) * 32;
+    // Fragment (row, k-tile kt) of lane (g, l16) in fragment layout: ((row/16 * KT + kt)
+    // * 64 + 16 g + row % 16) * 32 bytes.
+    Al = reinterpret_cast<const char *>(a.A) + ((size_t)(srow >> 4) * KT * 64 + 16 * g + (srow & 15)) * 32;
 #pragma unroll
     for (int i = 0; i < PASS; ++i) xa[i] = afl_get<T>(Al + (size_t)clampk(kw0 + i) * 2048);
-    // Row scales of the 4 output rows this lane finishes (W1).
-    float rsv[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (UP) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) rsv[r] = a.rs[__shfl(srow, 4 * g + r)];
     }
+  };
 
+  int item = blockIdx.x;
+  if (item < items) issue(item);
+  for (; item < items; item += gridDim.x) {
     f32x4_t acc[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = zero4();
@@ -281,6 +290,14 @@ __global__ __launch_bounds__(64 * NW) void moe_gemm_kernel(MoeGemm a) {
         for (int j = 0; j < NT; ++j) acc[j] = mma_a(xa[i], wb[i][j], acc[j]);
       }
     }
+    // This item's epilogue needs its rows, column tiles and row scales; then the next
+    // item's loads go out.
+    const int row0c = row0, nrowsc = nrows, nt0c = nt0;
+    float rsc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rsc[r] = rsv[r];
+    __builtin_amdgcn_sched_barrier(0);
+    if (item + (int)gridDim.x < items) issue(item + gridDim.x);
 
 #pragma unroll
     for (int j = 0; j < NT; ++j) s_red[wave][j][lane] = acc[j];
@@ -290,14 +307,14 @@ __global__ __launch_bounds__(64 * NW) void moe_gemm_kernel(MoeGemm a) {
       f32x4_t y4 = s_red[0][j][lane];
 #pragma unroll
       for (int w = 1; w < NW; ++w) y4 += s_red[w][j][lane];
-      const int col = (nt0 + j) * 16 + l16;
+      const int col = (nt0c + j) * 16 + l16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ri = 4 * g + r;
         if constexpr (UP) {
-          afl_put<T>(a.out_afl, a.N >> 5, row0 + ri, col, gelu_erf(y4[r] * rsv[r]));
+          afl_put<T>(a.out_afl, a.N >> 5, row0c + ri, col, gelu_erf(y4[r] * rsc[r]));
         } else {
-          if (ri < nrows) a.out[(size_t)(row0 + ri) * a.N + col] = y4[r];
+          if (ri < nrowsc) a.out[(size_t)(row0c + ri) * a.N + col] = y4[r];
         }
       }
     }
