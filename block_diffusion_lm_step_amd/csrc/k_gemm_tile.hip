@@ -2,8 +2,10 @@
 //
 // At M >= 128 every weight element is used by many rows and the projections are bound
 // by the matrix cores, not by the weight stream.  A workgroup of 4 waves computes a
-// 128 x 128 output tile; wave (wm, wn) owns the 64 x 64 quarter (4 x 4 MFMA tiles of
-// 16 x 16).  K advances one 32-wide k-tile per stage through double-buffered LDS (48 KiB,
+// BM x 128 output tile; wave (wm, wn) owns a (BM/2) x 64 quarter ((BM/32) x 4 MFMA tiles
+// of 16 x 16).  BM = 128, or 64 for layer projections whose 128-row tiles would give
+// about one workgroup per CU: that leaves each SIMD a single wave, whose LDS and barrier
+// latencies nothing overlaps (measured: the MFMA pipes were busy 22% of such a launch).  K advances one 32-wide k-tile per stage through double-buffered LDS (48 KiB,
 // so two workgroups share a CU and one's LDS traffic overlaps the other's MFMAs), one
 // barrier per stage: the next stage is loaded from memory into registers while the
 // current one is multiplied, then written to the other buffer.
@@ -25,10 +27,10 @@ namespace td {
 
 namespace {
 
-constexpr int BM = 128, BN = 128;   // workgroup tile
+constexpr int BN = 128;             // workgroup tile columns
 constexpr int KS = 1;               // k-tiles per stage
-constexpr int NF = (BM / 16) * KS * 64 / 256;   // fragments of each operand staged per thread
-constexpr int MTW = 4, NTW = 4;     // MFMA tiles per wave (rows, columns)
+constexpr int NTW = 4;              // MFMA column tiles per wave
+constexpr int NFW = (BN / 16) * KS * 64 / 256;   // weight fragments staged per thread
 
 // Small per-thread tables are vector values, not arrays: arrays indexed in loops are
 // turned into LDS or scratch copies before the loops are unrolled.
@@ -36,6 +38,7 @@ typedef unsigned long long u64x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+template <int BM>
 struct alignas(16) StageLds {
   u32x4_t a_hi[BM / 16][KS][64];   // activation fragments, bf16 high parts
   u32x4_t a_lo[BM / 16][KS][64];   // ... bf16 remainders
@@ -44,12 +47,15 @@ struct alignas(16) StageLds {
 
 constexpr int EPI_PART = 100;   // split-K partial: store the raw accumulator tile
 
-template <int EPI, bool NORM>
+template <int EPI, bool NORM, int BM>
 __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
-  __shared__ StageLds s_st[2];
+  constexpr int MTW = BM / 32;                     // MFMA row tiles per wave
+  constexpr int NFA = (BM / 16) * KS * 64 / 256;   // activation fragments staged per thread
+  constexpr int NPAR = 256 / BM;                   // threads per row summing squares
+  __shared__ StageLds<BM> s_st[2];
   __shared__ int s_row[BM];
   __shared__ float s_rs[BM];
-  __shared__ float s_part[2][BM];
+  __shared__ float s_part[NPAR][BM];
   __shared__ VStat s_stat[2][BM];
 
   // The loop-exit flag is loaded before any operand: issued behind the operand stream it
@@ -76,59 +82,70 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   }
   __syncthreads();
 
-  // Staging: each thread moves NF activation fragments (32 B) and NF weight fragments
+  // Staging: each thread moves NFA activation fragments (32 B) and NFW weight fragments
   // (16 B) per stage; fragment f = threadIdx.x + 256 i covers (tile f / (64 KS), k-tile
   // (f / 64) % KS, lane f % 64).  Source offsets of stage 0; stage s adds s * KS k-tiles.
   const char *Ab = reinterpret_cast<const char *>(a.A);
   const bf16_t *Wb = reinterpret_cast<const bf16_t *>(a.Wp);
   u64x4_t aoff, woff;
 #pragma unroll
-  for (int i = 0; i < NF; ++i) {
+  for (int i = 0; i < NFA; ++i) {
     const int f = threadIdx.x + 256 * i;
     const int fl = f & 63, kt = (f >> 6) % KS, t = f / (64 * KS);
     const int row = s_row[t * 16 + (fl & 15)];
     aoff[i] = (((size_t)(row >> 4) * KT + kt0 + kt) * 64 + (fl >> 4) * 16 + (row & 15)) * 32;
+  }
+#pragma unroll
+  for (int i = 0; i < NFW; ++i) {
+    const int f = threadIdx.x + 256 * i;
+    const int fl = f & 63, kt = (f >> 6) % KS, t = f / (64 * KS);
     woff[i] = (((size_t)(n0 / 16 + t) * KT + kt0 + kt) * 64 + fl) * 8;
   }
   // (tile, k-tile) of fragment i = 0; fragment i is 4 / KS tiles further.
   const int ft = threadIdx.x / (64 * KS), fkt = (threadIdx.x >> 6) % KS;
-  u32x4_t ra_hi[NF], ra_lo[NF], rw[NF];
+  u32x4_t ra_hi[NFA], ra_lo[NFA], rw[NFW];
 #define TD_LOAD_STAGE(S)                                                                        \
-  _Pragma("unroll") for (int i = 0; i < NF; ++i) {                                              \
+  _Pragma("unroll") for (int i = 0; i < NFA; ++i) {                                             \
     const u32x4_t *p_ = reinterpret_cast<const u32x4_t *>(Ab + aoff[i] + (size_t)(S) * KS * 2048); \
     ra_hi[i] = p_[0];                                                                           \
     ra_lo[i] = p_[1];                                                                           \
-    rw[i] = *reinterpret_cast<const u32x4_t *>(Wb + woff[i] + (size_t)(S) * KS * 512);          \
-  }
+  }                                                                                             \
+  _Pragma("unroll") for (int i = 0; i < NFW; ++i)                                               \
+    rw[i] = *reinterpret_cast<const u32x4_t *>(Wb + woff[i] + (size_t)(S) * KS * 512);
 #define TD_STORE_STAGE(B)                                                                       \
-  _Pragma("unroll") for (int i = 0; i < NF; ++i) {                                              \
+  _Pragma("unroll") for (int i = 0; i < NFA; ++i) {                                             \
     s_st[B].a_hi[ft + (4 / KS) * i][fkt][lane] = ra_hi[i];                                      \
     s_st[B].a_lo[ft + (4 / KS) * i][fkt][lane] = ra_lo[i];                                      \
-    s_st[B].w[ft + (4 / KS) * i][fkt][lane] = rw[i];                                            \
-  }
+  }                                                                                             \
+  _Pragma("unroll") for (int i = 0; i < NFW; ++i) s_st[B].w[ft + (4 / KS) * i][fkt][lane] = rw[i];
 
   TD_LOAD_STAGE(0)
   asm volatile("" ::: "memory");   // the loads above are issued before the test below
   if (stop) return;
   if constexpr (NORM && EPI != EPI_PART) {
-    // Row scales from the producer's partial sums of squares: thread t sums parts of
-    // parity t / 128 of row t % 128 (consecutive threads read consecutive rows).
-    const int r = threadIdx.x & (BM - 1), par = threadIdx.x >> 7;
+    // Row scales from the producer's partial sums of squares: thread t sums the parts
+    // p = t / BM (mod NPAR) of row t % BM (consecutive threads read consecutive rows).
+    const int r = threadIdx.x & (BM - 1), par = threadIdx.x / BM;
     const int row = s_row[r];
     float sacc = 0.f;
-    for (int p0 = par; p0 < a.norm_nparts; p0 += 2 * 16) {
+    for (int p0 = par; p0 < a.norm_nparts; p0 += NPAR * 16) {
       f32x16_t v;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = a.ssq[(size_t)min(p0 + 2 * j, a.norm_nparts - 1) * a.ld_ssq + row];
+      for (int j = 0; j < 16; ++j) v[j] = a.ssq[(size_t)min(p0 + NPAR * j, a.norm_nparts - 1) * a.ld_ssq + row];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sacc += (p0 + 2 * j < a.norm_nparts) ? v[j] : 0.f;
+      for (int j = 0; j < 16; ++j) sacc += (p0 + NPAR * j < a.norm_nparts) ? v[j] : 0.f;
     }
     s_part[par][r] = sacc;
   }
   TD_STORE_STAGE(0)
   __syncthreads();
   if constexpr (NORM && EPI != EPI_PART) {
-    if (threadIdx.x < BM) s_rs[threadIdx.x] = 1.0f / sqrtf((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) / (float)a.K + a.norm_eps);
+    if (threadIdx.x < BM) {
+      float q = 0.f;
+#pragma unroll
+      for (int p = 0; p < NPAR; ++p) q += s_part[p][threadIdx.x];
+      s_rs[threadIdx.x] = 1.0f / sqrtf(q / (float)a.K + a.norm_eps);
+    }
   }
 
   f32x4_t acc[MTW][NTW];
@@ -309,16 +326,29 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a) {
 
 }  // namespace
 
+// Rows per workgroup tile: 64 for a layer projection with between a half and one
+// 128-row tile per CU (the 64-row tiles then fill the chip without a K split), else 128,
+// and always 128 for the LM head (its statistics come in 128-column groups of 128-row
+// tiles).  Measured: with 1.5-2 tiles of 128 rows per CU the 64-row tiles were slower,
+// bound by LDS bandwidth at their lower reuse, and fewer tiles are better split in K.
+static int tile_bm(int epi, int M, int N) {
+  if (epi == EPI_VSTAT) return 128;
+  const int t128 = (N / BN) * ((M + 127) / 128);
+  return t128 > 128 && t128 <= 256 ? 64 : 128;
+}
+
 bool gemm_tile_supported(int dtype, int M, int N, int K) {
-  return dtype == DT_BF16 && M >= BM && N % BN == 0 && K % (32 * KS) == 0;
+  return dtype == DT_BF16 && M >= 128 && N % BN == 0 && K % (32 * KS) == 0;
 }
 
 int gemm_tile_slices(int N) { return N / BN; }
 
 // Split only grids of less than one workgroup per CU (up to ~2 per CU, >= 8 k-tiles per
-// split): measured, a grid of 256 tiles runs faster whole than split in two.
+// split): measured, a grid of 256 tiles runs faster whole than split in two.  (For the
+// layer projections, the only ones split.)
 int gemm_tile_splits(int M, int N, int K) {
-  const int tiles = (N / BN) * ((M + BM - 1) / BM);
+  const int bm = tile_bm(EPI_STORE, M, N);
+  const int tiles = (N / BN) * ((M + bm - 1) / bm);
   int s = 1;
   if (tiles >= 256) return s;
   while (tiles * s < 512 && (K / 32) / (2 * s) >= 8) s *= 2;
@@ -345,25 +375,31 @@ hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a, hipStream_t s
   if (a.done == nullptr) return hipErrorInvalidValue;
   if (norm && (a.ssq == nullptr || a.norm_nparts <= 0)) return hipErrorInvalidValue;
   if ((epi == EPI_GELU || epi == EPI_RESID) && a.out_afl == nullptr) return hipErrorInvalidValue;
+  const int bm = tile_bm(epi, a.M, a.N);
   if (a.splits > 1) {
     if (epi == EPI_VSTAT || a.part == nullptr || a.n_rows != nullptr) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_tile_kernel<EPI_PART, false>), dim3(a.N / BN, (a.M + BM - 1) / BM, a.splits), dim3(256),
-                       0, s, a);
+    const dim3 pgrid(a.N / BN, (a.M + bm - 1) / bm, a.splits);
+    if (bm == 64) hipLaunchKernelGGL((gemm_tile_kernel<EPI_PART, false, 64>), pgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_tile_kernel<EPI_PART, false, 128>), pgrid, dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_reduce(epi, norm, a, s);
   }
-  const dim3 grid(a.N / BN, (a.M + BM - 1) / BM);
-#define TD_L(E, NRM)                                                                 \
-  if (epi == E && norm == NRM) {                                                 \
-    hipLaunchKernelGGL((gemm_tile_kernel<E, NRM>), grid, dim3(256), 0, s, a);    \
-    return hipGetLastError();                                                    \
+  const dim3 grid(a.N / BN, (a.M + bm - 1) / bm);
+#define TD_L(E, NRM)                                                                        \
+  if (epi == E && norm == NRM) {                                                        \
+    if (bm == 64) hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 64>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 128>), grid, dim3(256), 0, s, a);         \
+    return hipGetLastError();                                                           \
   }
   TD_L(EPI_STORE, true)
   TD_L(EPI_GELU, true)
   TD_L(EPI_RESID, false)
-  TD_L(EPI_VSTAT, true)
 #undef TD_L
+  if (epi == EPI_VSTAT && norm) {
+    hipLaunchKernelGGL((gemm_tile_kernel<EPI_VSTAT, true, 128>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   return hipErrorInvalidValue;
 }
 
