@@ -64,11 +64,8 @@ TD_DEV void argmax_wave(float &v, int &i) {
 
 constexpr int SPL = MOE_MAX_EXPERTS / 64;   // router scores per lane
 
-__global__ __launch_bounds__(256) void moe_route_kernel(MoeRoute a) {
-  if (*a.done) return;
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= a.M) return;
+// Routing of token row m by one wave.
+TD_DEV void route_row(const MoeRoute &a, int m, int lane) {
   if (a.seq_done[m / a.B]) {   // no routed expert for this row
     if (lane < a.top_k) a.experts[(size_t)m * a.top_k + lane] = -1;
     return;
@@ -121,11 +118,17 @@ __global__ __launch_bounds__(256) void moe_route_kernel(MoeRoute a) {
   }
 }
 
+__global__ __launch_bounds__(256) void moe_route_kernel(MoeRoute a) {
+  if (*a.done) return;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m < a.M) route_row(a, m, threadIdx.x & 63);
+}
+
 constexpr int NE_MAX = MOE_MAX_EXPERTS + MOE_MAX_SHARED;
 constexpr int EPL = (NE_MAX + 63) / 64;   // experts per lane in the offset scan
 
-__global__ __launch_bounds__(1024) void moe_bucket_kernel(MoeRoute a) {
-  if (*a.done) return;
+// Counts, offsets, tile table and placement; called by all 1024 threads of one workgroup.
+TD_DEV void bucket(const MoeRoute &a) {
   __shared__ int s_cnt[NE_MAX], s_seg[NE_MAX], s_tile[NE_MAX], s_cur[NE_MAX];
   const int tid = threadIdx.x;
   const int NE = a.E + a.n_shared, KS = a.top_k + a.n_shared;
@@ -200,6 +203,22 @@ __global__ __launch_bounds__(1024) void moe_bucket_kernel(MoeRoute a) {
     a.src_row[p] = m;
     a.slot_pos[(size_t)m * KS + a.top_k + sh] = p;
   }
+}
+
+__global__ __launch_bounds__(1024) void moe_bucket_kernel(MoeRoute a) {
+  if (*a.done) return;
+  bucket(a);
+}
+
+// Few rows: routing (16 waves, one row each in turn) and the bucket pass in one
+// workgroup, one launch instead of two.  The routing results reach the bucket pass
+// through the barrier (same workgroup: its stores are complete and visible).
+constexpr int MOE_FUSED_ROWS = 64;
+__global__ __launch_bounds__(1024) void moe_route_bucket_kernel(MoeRoute a) {
+  if (*a.done) return;
+  for (int m = threadIdx.x >> 6; m < a.M; m += 16) route_row(a, m, threadIdx.x & 63);
+  __syncthreads();
+  bucket(a);
 }
 
 // k-tiles in flight per wave: one activation fragment and NT weight fragments per
@@ -349,8 +368,12 @@ hipError_t launch_moe_route(const MoeRoute &a, hipStream_t s) {
       a.n_shared < 0 || a.n_shared > MOE_MAX_SHARED || a.Epad < a.E || a.d % 16 || !a.done || !a.seq_done ||
       a.B < 1 || a.M % a.B)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(moe_route_kernel, dim3((a.M + 3) / 4), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(1024), 0, s, a);
+  if (a.M <= MOE_FUSED_ROWS) {
+    hipLaunchKernelGGL(moe_route_bucket_kernel, dim3(1), dim3(1024), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(moe_route_kernel, dim3((a.M + 3) / 4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(1024), 0, s, a);
+  }
   return hipGetLastError();
 }
 

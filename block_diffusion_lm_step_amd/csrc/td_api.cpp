@@ -1133,8 +1133,15 @@ int32_t td_profile_end(td_ctx *c, float *ms_out, int32_t max) {
 
 int32_t td_kernels_per_step(const td_ctx *c) {
   if (!c) return -1;
-  // prep/init, embed, per layer 6 (10 with a mixture of experts), LM head, merge+commit
-  return 1 + 1 + (c->moe ? 10 : 6) * c->cfg.n_layers + 2;
+  // prep/init, embed; per layer the projections (a K-split one adds its reduction),
+  // attention and its merge, and the MLP or the mixture of experts (router GEMM, routing
+  // and bucketing in one launch up to 64 rows, else two, the expert up and down
+  // projections, the combine); the LM head and the merge + commit.
+  auto gemm = [](const GemmPlan &p) { return 1 + (p.splits > 1 ? 1 : 0); };
+  const int M = std::max(1, c->n_seqs) * c->cfg.block_size;
+  int layer = gemm(c->p_qkv) + 2 + gemm(c->p_wo);
+  layer += c->moe ? gemm(c->p_router) + (M <= 64 ? 1 : 2) + 3 : gemm(c->p_w1) + gemm(c->p_w2);
+  return 2 + layer * c->cfg.n_layers + 2;
 }
 
 void td_destroy(td_ctx *c) {

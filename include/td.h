@@ -279,7 +279,8 @@ td_status td_profile_begin(td_ctx *ctx, int32_t kind);
  * committed are included (they take a few microseconds). */
 int32_t td_profile_end(td_ctx *ctx, float *ms_out_host, int32_t max);
 
-/* Number of kernels one td_denoise_step enqueues (for profiling and launch accounting). */
+/* Number of kernels one td_denoise_step enqueues on the bound batch (for profiling and
+ * launch accounting; before a binding, for one sequence with the creation-time plans). */
 int32_t td_kernels_per_step(const td_ctx *ctx);
 
 void td_destroy(td_ctx *ctx);                  /* NULL-safe; waits for the stream */

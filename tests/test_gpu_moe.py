@@ -1,8 +1,9 @@
 """GPU parity of the mixture-of-experts denoiser (td_set_moe) against the float64 oracle.
 
 Small towers cover fp32 and bf16 storage, expert counts that are not a multiple of 32
-(padded router), top_k up to 8, no shared expert, several 16-row tiles per expert (M =
-144, the tiled router GEMM) and a single row per expert; the full-size tower is the
+(padded router), 256 experts, top_k up to 8 and top_k = E, no shared expert, several
+16-row tiles per expert (M = 144: the tiled router GEMM and separate routing and bucket
+kernels; the others route and bucket in one workgroup) and a single row per expert; the full-size tower is the
 batch-1 d 2048 tower with 128 experts, 6 routed + 2 shared of width 1024.
 
 Bars: logits per-row relative error (1e-4 fp32, 2e-2 bf16), decisions bit-exact outside
@@ -64,6 +65,12 @@ SMALL = {
     # top_k = 8 (the maximum), no shared expert, block 8.
     "bf16_e32_k8_s0_b8": dict(n=1, plen=("uniform", 1, 300), B=8, d=256, H=4, Hkv=4, hd=64, L=2, F=1024, V=4096,
                               dtype="bf16", moe=(32, 8, 0, 64)),
+    # 256 experts (the maximum: four router scores per lane), top 3.
+    "bf16_e256_k3_s0": dict(n=2, plen=("uniform", 0, 200), B=16, d=256, H=4, Hkv=4, hd=64, L=2, F=1024, V=4096,
+                            dtype="bf16", moe=(256, 3, 0, 64), seed=2),
+    # top_k = E: every expert chosen, routing decides only the gates.
+    "f32_e4_k4_s1": dict(n=2, plen=("uniform", 0, 200), B=8, d=256, H=4, Hkv=2, hd=64, L=2, F=1024, V=4096,
+                         dtype="f32", moe=(4, 4, 1, 64)),
 }
 
 
