@@ -34,11 +34,9 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kernel(GemmArgs a) {
   constexpr int ROWS = 16 * MT;
   constexpr int TPR = (64 * NW / ROWS) < 64 ? 64 * NW / ROWS : 64;   // threads per row (row scales)
   constexpr int SQB = 16;
-  // The loop-exit flag is loaded before any operand: issued behind the operand stream it
-  // would queue with it and hold back the first MFMAs; it is tested once the first
-  // operand loads are in flight.
-  const int stop = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // a vector load
-  __builtin_amdgcn_sched_barrier(0);
+  // The loop-exit flag decides before any operand is requested (a launch in a step after
+  // the block is adopted then reads nothing else).
+  if (__hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
   const int nrows = a.n_rows ? *a.n_rows : a.M;
   const int m0 = blockIdx.z * ROWS;
   if (m0 >= nrows) return;
@@ -83,8 +81,6 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kernel(GemmArgs a) {
   };
 #pragma unroll
   for (int i = 0; i < PASS; ++i) fill(i, i);
-  asm volatile("" ::: "memory");   // the loads above are issued before the test below
-  if (stop) return;
   {
     float s = 0.f;
 #pragma unroll
@@ -181,8 +177,7 @@ __global__ __launch_bounds__(64 * LDS_NW) void lmhead_lds_kernel(GemmArgs a) {
 
   // The loop-exit flag first (see lmhead_kernel), then the small per-row values, the
   // activation block and the first weights.
-  const int stop = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_sched_barrier(0);
+  if (__hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
   const int M = a.M, KT = a.K >> 5;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -216,8 +211,6 @@ __global__ __launch_bounds__(64 * LDS_NW) void lmhead_lds_kernel(GemmArgs a) {
   };
 #pragma unroll
   for (int i = 0; i < PASS; ++i) fill(i, i);
-  asm volatile("" ::: "memory");   // the loads above are issued before the test below
-  if (stop) return;
 
   // Waiting for the block waits for nothing issued after it: the weights stay in flight.
 #pragma unroll

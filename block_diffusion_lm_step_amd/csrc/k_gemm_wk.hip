@@ -57,11 +57,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
   constexpr int ROWS = 16 * MT;
   constexpr int TPR = (64 * NW / ROWS) < 64 ? 64 * NW / ROWS : 64;   // threads per row (row scales)
   constexpr int SQB = 16;                                             // partial sums loaded per batch
-  // The loop-exit flag is loaded before any operand: issued behind the operand stream it
-  // would queue with it and hold back the first MFMAs; it is tested once the first
-  // operand loads are in flight.
-  const int stop = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // a vector load
-  __builtin_amdgcn_sched_barrier(0);
+  // The loop-exit flag decides before any operand is requested.  Steps after the block is
+  // adopted still launch every kernel; requesting a PASS window of weights before the
+  // test made each such launch as long as a working one (measured at the batch-1 tower:
+  // 0.3 ms per such step; testing first costs a working launch about 0.2 us).
+  if (__hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
   const int M = a.M;
   const int m0 = blockIdx.z * ROWS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -102,9 +102,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
   // First PASS k-tiles of activations and weights.
 #pragma unroll
   for (int i = 0; i < PASS; ++i) fill(i, kw0 + i);
-  // (Reading the operands is harmless when the block is already adopted.)
-  asm volatile("" ::: "memory");   // the loads above are issued before the test below
-  if (stop) return;
   if constexpr (NORM) {
     float s = 0.f;
 #pragma unroll

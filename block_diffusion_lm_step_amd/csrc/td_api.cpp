@@ -626,7 +626,7 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   TD_HIP(c, hipGetDevice(&c->dev));
   c->elt = g.dtype == TD_BF16 ? 2 : 4;
   const size_t e = c->elt;
-  const size_t d = g.d_model, F = g.d_ff, V = g.vocab, L = g.n_layers;
+  const size_t d = g.d_model, F = g.d_ff, V = g.vocab;
   const size_t Hd = (size_t)g.n_heads * g.head_dim, KVd = (size_t)g.n_kv_heads * g.head_dim;
   c->Nqkv = (int)(Hd + 2 * KVd);
   c->Mmax = g.max_batch * g.block_size;
