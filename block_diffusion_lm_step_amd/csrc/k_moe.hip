@@ -12,7 +12,7 @@
 //   W1       per (tile, column group): the expert's up projection over the gathered
 //            input rows, GELU, stored in fragment layout for W2;
 //   W2       per (tile, column group): the expert's down projection, fp32;
-//   combine  per row: x += sum_j gate_j * y(slot j) + sum_s y(shared s), in slot order,
+//   combine  per row and column: x += sum_j gate_j * y(slot j) + sum_s y(shared s), in slot order,
 //            then the next RMSNorm's partial sums of squares and x * gain in fragment
 //            layout, as the dense MLP's down projection leaves them.
 //
@@ -64,10 +64,11 @@ TD_DEV void argmax_wave(float &v, int &i) {
 
 constexpr int SPL = MOE_MAX_EXPERTS / 64;   // router scores per lane
 
-// Routing of token row m by one wave.
-TD_DEV void route_row(const MoeRoute &a, int m, int lane) {
+// Routing of token row m by one wave; the chosen experts go to experts[m * top_k + j]
+// (global memory, or LDS in the fused kernel).
+TD_DEV void route_row(const MoeRoute &a, int m, int lane, int *experts) {
   if (a.seq_done[m / a.B]) {   // no routed expert for this row
-    if (lane < a.top_k) a.experts[(size_t)m * a.top_k + lane] = -1;
+    if (lane < a.top_k) experts[(size_t)m * a.top_k + lane] = -1;
     return;
   }
   float s[SPL];
@@ -110,7 +111,7 @@ TD_DEV void route_row(const MoeRoute &a, int m, int lane) {
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
       if (j < a.top_k) {
-        a.experts[(size_t)m * a.top_k + j] = ids[j];
+        experts[(size_t)m * a.top_k + j] = ids[j];
         a.gates[(size_t)m * a.top_k + j] = w[j] / z;
       }
     }
@@ -121,14 +122,15 @@ TD_DEV void route_row(const MoeRoute &a, int m, int lane) {
 __global__ __launch_bounds__(256) void moe_route_kernel(MoeRoute a) {
   if (*a.done) return;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m < a.M) route_row(a, m, threadIdx.x & 63);
+  if (m < a.M) route_row(a, m, threadIdx.x & 63, a.experts);
 }
 
 constexpr int NE_MAX = MOE_MAX_EXPERTS + MOE_MAX_SHARED;
 constexpr int EPL = (NE_MAX + 63) / 64;   // experts per lane in the offset scan
 
-// Counts, offsets, tile table and placement; called by all 1024 threads of one workgroup.
-TD_DEV void bucket(const MoeRoute &a) {
+// Counts, offsets, tile table and placement from the chosen experts [M][top_k]; called by
+// all 1024 threads of one workgroup.
+TD_DEV void bucket(const MoeRoute &a, const int *experts) {
   __shared__ int s_cnt[NE_MAX], s_seg[NE_MAX], s_tile[NE_MAX], s_cur[NE_MAX];
   const int tid = threadIdx.x;
   const int NE = a.E + a.n_shared, KS = a.top_k + a.n_shared;
@@ -139,7 +141,7 @@ TD_DEV void bucket(const MoeRoute &a) {
   }
   __syncthreads();
   for (int i = tid; i < MK; i += 1024) {
-    const int e = a.experts[i];
+    const int e = experts[i];
     if ((unsigned)e < (unsigned)a.E) atomicAdd(&s_cnt[e], 1);
   }
   __syncthreads();
@@ -190,7 +192,7 @@ TD_DEV void bucket(const MoeRoute &a) {
     for (int r = n; r < ((n + 15) & ~15); ++r) a.src_row[r0 + r] = 0;
   }
   for (int i = tid; i < MK; i += 1024) {
-    const int e = a.experts[i];
+    const int e = experts[i];
     if ((unsigned)e >= (unsigned)a.E) continue;
     const int m = i / a.top_k, j = i - m * a.top_k;
     const int p = s_seg[e] + atomicAdd(&s_cur[e], 1);
@@ -207,18 +209,18 @@ TD_DEV void bucket(const MoeRoute &a) {
 
 __global__ __launch_bounds__(1024) void moe_bucket_kernel(MoeRoute a) {
   if (*a.done) return;
-  bucket(a);
+  bucket(a, a.experts);
 }
 
 // Few rows: routing (16 waves, one row each in turn) and the bucket pass in one
-// workgroup, one launch instead of two.  The routing results reach the bucket pass
-// through the barrier (same workgroup: its stores are complete and visible).
+// workgroup, one launch instead of two; the chosen experts stay in LDS.
 constexpr int MOE_FUSED_ROWS = 64;
 __global__ __launch_bounds__(1024) void moe_route_bucket_kernel(MoeRoute a) {
+  __shared__ int s_exp[MOE_FUSED_ROWS * MOE_MAX_TOP_K];
   if (*a.done) return;
-  for (int m = threadIdx.x >> 6; m < a.M; m += 16) route_row(a, m, threadIdx.x & 63);
+  for (int m = threadIdx.x >> 6; m < a.M; m += 16) route_row(a, m, threadIdx.x & 63, s_exp);
   __syncthreads();
-  bucket(a);
+  bucket(a, s_exp);
 }
 
 // k-tiles in flight per wave: one activation fragment and NT weight fragments per
@@ -341,24 +343,34 @@ __global__ __launch_bounds__(64 * NW) void moe_gemm_kernel(MoeGemm a) {
   }
 }
 
+// One workgroup per (row, 256 columns), one column per thread.  The row's slot
+// positions and gates are workgroup-uniform (scalar loads, read once).
 template <typename T>
 __global__ __launch_bounds__(256) void moe_combine_kernel(MoeCombine a) {
   if (*a.done) return;
   const int m = blockIdx.x;
   if (a.seq_done[m / a.B]) return;
   const int KS = a.top_k + a.n_shared;
-  const int *pos = a.slot_pos + (size_t)m * KS;
-  const float *gt = a.gates + (size_t)m * a.top_k;
-  for (int c = threadIdx.x; c < a.d; c += 256) {
-    float acc = 0.f;
-    for (int j = 0; j < a.top_k; ++j) acc += gt[j] * a.y[(size_t)pos[j] * a.d + c];
-    for (int s = 0; s < a.n_shared; ++s) acc += a.y[(size_t)pos[a.top_k + s] * a.d + c];
-    const float xv = a.x[(size_t)m * a.d + c] + acc;
-    a.x[(size_t)m * a.d + c] = xv;
-    afl_put<T>(a.out_afl, a.d >> 5, m, c, xv * to_f32<T>(reinterpret_cast<const T *>(a.gain_next)[c]));
-    const float sq = sum16(xv * xv);
-    if ((threadIdx.x & 15) == 0) a.ssq_out[(size_t)(c >> 4) * a.M + m] = sq;
-  }
+  int pos[MOE_MAX_TOP_K + MOE_MAX_SHARED];
+  float gt[MOE_MAX_TOP_K];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOP_K + MOE_MAX_SHARED; ++j) pos[j] = j < KS ? a.slot_pos[(size_t)m * KS + j] : 0;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOP_K; ++j) gt[j] = j < a.top_k ? a.gates[(size_t)m * a.top_k + j] : 0.f;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c >= a.d) return;   // whole 16-column groups (d is a multiple of 64)
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOP_K; ++j)
+    if (j < a.top_k) acc += gt[j] * a.y[(size_t)pos[j] * a.d + c];
+#pragma unroll
+  for (int s = 0; s < MOE_MAX_SHARED; ++s)
+    if (s < a.n_shared) acc += a.y[(size_t)pos[a.top_k + s] * a.d + c];
+  const float xv = a.x[(size_t)m * a.d + c] + acc;
+  a.x[(size_t)m * a.d + c] = xv;
+  afl_put<T>(a.out_afl, a.d >> 5, m, c, xv * to_f32<T>(reinterpret_cast<const T *>(a.gain_next)[c]));
+  const float sq = sum16(xv * xv);
+  if ((threadIdx.x & 15) == 0) a.ssq_out[(size_t)(c >> 4) * a.M + m] = sq;
 }
 
 }  // namespace
@@ -396,8 +408,9 @@ hipError_t launch_moe_gemm(int dtype, bool up, const MoeGemm &a, hipStream_t s) 
 
 hipError_t launch_moe_combine(int dtype, const MoeCombine &a, hipStream_t s) {
   if (a.M <= 0 || a.d % 64 || !a.done || !a.seq_done || a.B < 1 || a.M % a.B) return hipErrorInvalidValue;
-  if (dtype == DT_BF16) hipLaunchKernelGGL(moe_combine_kernel<bf16_t>, dim3(a.M), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(moe_combine_kernel<float>, dim3(a.M), dim3(256), 0, s, a);
+  const dim3 grid(a.M, (a.d + 255) / 256);
+  if (dtype == DT_BF16) hipLaunchKernelGGL(moe_combine_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(moe_combine_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
