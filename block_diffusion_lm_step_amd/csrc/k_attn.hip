@@ -266,8 +266,10 @@ TD_DEV void static_for(F &&f) {
   }
 }
 
+// bf16 pages with one row tile fit two workgroups per CU (243 VGPRs when told so; left
+// alone the compiler also took 32 AGPRs and one); the others need the whole register file.
 template <typename T, int HD, int RT, int NW, int DEPTH>
-__global__ __launch_bounds__(64 * NW) void attn_direct_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void attn_direct_kernel(AttnArgs a) {
   constexpr int NT = 64 * NW, HC = HD / 32, OT = HD / 16, EPT = HD / 16, KPT = BMAX * HD / NT;
   constexpr int MERGE = (NW + 1) * RT * 16 * (HD + 2);   // waves' and the block's states
   constexpr int LDS = MERGE + block_item_lds<HD>();
