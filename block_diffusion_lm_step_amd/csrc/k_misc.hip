@@ -88,15 +88,25 @@ __global__ __launch_bounds__(256) void embed_kernel(const int *tokens, const T *
   const T *e = E + (size_t)tok * d;
   const T *p = Pos ? Pos + (size_t)(r % B) * d : nullptr;   // no table: the context tower
   for (int grp = threadIdx.x; grp < d / 16; grp += blockDim.x) {
+    // 16 consecutive columns per thread, moved as 16-byte vectors.
+    Frag<T> fe[2], fp[2], fg[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      fe[h].load(e + grp * 16 + 8 * h);
+      if (p) fp[h].load(p + grp * 16 + 8 * h);
+      else fp[h].zero();
+      fg[h].load(gain + grp * 16 + 8 * h);
+    }
     float s = 0.f, v[16], vg[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      const int k = grp * 16 + c;
-      v[c] = to_f32<T>(e[k]) + (p ? to_f32<T>(p[k]) : 0.f);
-      vg[c] = v[c] * to_f32<T>(gain[k]);
-      x[(size_t)r * d + k] = v[c];
+      v[c] = fe[c >> 3].get(c & 7) + fp[c >> 3].get(c & 7);
+      vg[c] = v[c] * fg[c >> 3].get(c & 7);
       s += v[c] * v[c];
     }
+    float4 *xr = reinterpret_cast<float4 *>(x + (size_t)r * d + grp * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xr[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
     ssq[(size_t)grp * M + r] = s;
     afl_put8<T>(x_afl, d / 32, r, grp * 16, vg);
     afl_put8<T>(x_afl, d / 32, r, grp * 16 + 8, vg + 8);
