@@ -345,9 +345,9 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int c = 0; c < HC; ++c) kf[b][h][c].load(kp + kpos(c, h, l16) + g * 8);
+        for (int c = 0; c < HC; ++c) kf[b][h][c].load_nt(kp + kpos(c, h, l16) + g * 8);
 #pragma unroll
-      for (int t = 0; t < OT; ++t) vf[b][t].load(vp + (16 * t + l16) * SUB + g * 8);
+      for (int t = 0; t < OT; ++t) vf[b][t].load_nt(vp + (16 * t + l16) * SUB + g * 8);
     }
   };
   auto consume = [&](auto bufc, int pg) __attribute__((always_inline)) {
@@ -542,9 +542,9 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
       const u32x4_t *kp = reinterpret_cast<const u32x4_t *>(Kp + base + (size_t)c * 8);
       const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(Vp + base + (size_t)c * 8);
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        kreg[r][i][w] = kp[w];
-        vreg[r][i][w] = vp[w];
+      for (int w = 0; w < W; ++w) {   // pages are read once per step: streaming loads
+        kreg[r][i][w] = __builtin_nontemporal_load(kp + w);
+        vreg[r][i][w] = __builtin_nontemporal_load(vp + w);
       }
     }
   };

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) xa[i][mt] = afl_get<T>(Al[mt] + (size_t)k * 2048);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) wb[i][j].load(Wl + ((size_t)j * KT + k) * 512);
+    for (int j = 0; j < NT; ++j) wb[i][j].load_nt(Wl + ((size_t)j * KT + k) * 512);
   };
 #pragma unroll
   for (int i = 0; i < PASS; ++i) fill(i, i);
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * LDS_NW) void lmhead_lds_kernel(GemmArgs a) {
   auto fill = [&](int i, int kt) __attribute__((always_inline)) {
     const int k = min(kt, KT - 1);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) wb[i][j].load(Wl + ((size_t)j * KT + k) * 512);
+    for (int j = 0; j < NT; ++j) wb[i][j].load_nt(Wl + ((size_t)j * KT + k) * 512);
   };
 #pragma unroll
   for (int i = 0; i < PASS; ++i) fill(i, i);

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_wk_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) xa[i][mt] = afl_get<T>(Al + ((size_t)mt * KT + k) * 2048);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) wb[i][j].load(Wl + ((size_t)j * KT + k) * 512);
+    for (int j = 0; j < NT; ++j) wb[i][j].load_nt(Wl + ((size_t)j * KT + k) * 512);
   };
 
   // Partial sums of squares of this thread's row first (TPR threads per row).

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(64 * NW) void moe_gemm_kernel(MoeGemm a) {
 #pragma unroll
     for (int i = 0; i < PASS; ++i)
 #pragma unroll
-      for (int j = 0; j < NT; ++j) wb[i][j].load(Wl + ((size_t)j * KT + clampk(kw0 + i)) * 512);
+      for (int j = 0; j < NT; ++j) wb[i][j].load_nt(Wl + ((size_t)j * KT + clampk(kw0 + i)) * 512);
     // Fragment (row, k-tile kt) of lane (g, l16) in fragment layout: ((row/16 * KT + kt)
     // * 64 + 16 g + row % 16) * 32 bytes.
     Al = reinterpret_cast<const char *>(a.A) + ((size_t)(srow >> 4) * KT * 64 + 16 * g + (srow & 15)) * 32;
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(64 * NW) void moe_gemm_kernel(MoeGemm a) {
         const int k = clampk(p0 + PASS + i);
         xa[i] = afl_get<T>(Al + (size_t)k * 2048);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) wb[i][j].load(Wl + ((size_t)j * KT + k) * 512);
+        for (int j = 0; j < NT; ++j) wb[i][j].load_nt(Wl + ((size_t)j * KT + k) * 512);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -46,6 +46,11 @@ template <> struct Frag<bf16_t> {
   uint4 raw;   // 8 bf16
   TD_DEV void zero() { raw = make_uint4(0, 0, 0, 0); }
   TD_DEV void load(const bf16_t *p) { raw = *reinterpret_cast<const uint4 *>(p); }
+  // Streaming load (nontemporal hint): data read once per step, larger than the caches
+  // (weights, K/V pages), is not kept where it would evict what is re-read.
+  TD_DEV void load_nt(const bf16_t *p) {
+    raw = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p)));
+  }
   TD_DEV float get(int j) const {
     uint32_t w = (&raw.x)[j >> 1];
     return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
@@ -64,6 +69,10 @@ template <> struct Frag<float> {
   TD_DEV void load(const float *p) {
     lo = reinterpret_cast<const float4 *>(p)[0];
     hi = reinterpret_cast<const float4 *>(p)[1];
+  }
+  TD_DEV void load_nt(const float *p) {
+    lo = __builtin_bit_cast(float4, __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p)));
+    hi = __builtin_bit_cast(float4, __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p) + 1));
   }
   TD_DEV float get(int j) const { return j < 4 ? (&lo.x)[j] : (&hi.x)[j - 4]; }
   TD_DEV void set8(const float *v) {
