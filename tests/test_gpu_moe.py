@@ -178,3 +178,31 @@ def test_moe_full_size_first_steps():
         _check_trace(case, steps=2)
     finally:
         case.dev.close()
+
+
+def test_moe_errors_without_experts():
+    """A tower created without dense MLP weights cannot step until td_set_moe; td_moe_stats
+    needs a mixture of experts."""
+    import torch
+    from block_diffusion_lm_step_amd import Denoiser, TdError
+    from synth import Workload, draw_prefix_lengths, draw_tower
+    from synth.device import prefix_to_device, tower_config, tower_to_device
+    w = Workload(name="moe_noexp", tower="moe_noexp", n=1, plen=("fixed", 40), B=8, d=256, H=4, Hkv=4, hd=64, L=1,
+                 F=1024, V=4096, dtype="bf16", moe=(8, 2, 0, 64))
+    dW = tower_to_device(draw_tower(w))
+    assert dW["w1"] is None and dW["w2"] is None
+    offsets, ks, vs = prefix_to_device(w, draw_prefix_lengths(w))
+    dev = Denoiser(tower_config(w, max_batch=1, max_prefix_tokens=offsets[-1]), dW)
+    try:
+        dev.set_prefix(offsets, ks, vs)
+        tok = torch.full((1, w.B), w.V, dtype=torch.int32, device="cuda")
+        com = torch.zeros((1, w.B), dtype=torch.uint8, device="cuda")
+        with pytest.raises(TdError, match="no MLP"):
+            dev.denoise_step(tok, com, None, w.gamma)
+        with pytest.raises(TdError, match="no MLP"):
+            dev.generate_block(tok, com, None, w.gamma)
+        with pytest.raises(TdError, match="mixture of experts"):
+            dev.moe_stats()
+        dev.sync()
+    finally:
+        dev.close()
