@@ -83,6 +83,14 @@ def test_null_ctx_calls_are_rejected(td):
     assert td.lib.td_profile_begin(None, 1) == td.TD_EINVAL
     assert td.lib.td_profile_end(None, None, 0) == -1
     assert td.lib.td_kernels_per_step(None) == -1
+    assert td.lib.td_set_commit_rule(None, 0, 1) == td.TD_EINVAL
+    assert td.lib.td_bind_cache(None, 1, None, None, None, None) == td.TD_EINVAL
+    assert td.lib.td_set_context_tower(None, None) == td.TD_EINVAL
+    assert td.lib.td_append_block(None, None) == td.TD_EINVAL
+    assert td.lib.td_ar_step(None, None) == td.TD_EINVAL
+    assert td.lib.td_set_moe(None, None, None) == td.TD_EINVAL
+    n, act = ctypes.c_int64(0), ctypes.c_int64(0)
+    assert td.lib.td_moe_stats(None, ctypes.byref(n), ctypes.byref(act)) == td.TD_EINVAL
     td.lib.td_destroy(None)
 
 
