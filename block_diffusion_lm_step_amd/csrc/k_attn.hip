@@ -477,24 +477,25 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
 // more rows take several workgroups per item).  Pages reach LDS through a ring of
 // DEPTH pages held in registers (every thread loads its share of page p + DEPTH while
 // page p is multiplied), then one 16-byte store per chunk into the double-buffered,
-// padded LDS stage of two pages (K in its page layout with 32-element rows, V^T rows);
-// one barrier per two pages (one per page measured 11% slower).  Each wave reads a page's K fragments from LDS once and reuses them for all of
+// padded LDS stage of PPS = 2 pages (K in its page layout with 32-element rows, V^T
+// rows); one barrier per two pages (one per page measured 11% slower, three 10%).  Each wave reads a page's K fragments from LDS once and reuses them for all of
 // its row tiles; V fragments are read at their use.
 template <typename T, int HD, int RTW>
 __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
   constexpr int NW = 8, NT = 64 * NW, HC = HD / 32, OT = HD / 16;
-  constexpr int DEPTH = 4;                 // pages in flight in registers (two stages of two)
+  constexpr int PPS = 2;                   // pages per LDS stage (measured: 1 and 3 slower)
+  constexpr int DEPTH = 2 * PPS;           // pages in flight in registers (two stages)
   constexpr int KR = 32 + Pad<T>::K;       // K row stride in LDS (elements)
   constexpr int VP = SUB + Pad<T>::V;      // V^T row stride in LDS (elements)
   constexpr int KCH = SUB * HD / 8;        // 8-element chunks of a K page (= of a V page)
   constexpr int CPT = (KCH + NT - 1) / NT; // chunks of each per thread
   constexpr int KBUF = HC * 2 * 16 * KR, VBUF = HD * VP;   // elements of one LDS page
-  constexpr int BYTES_PAGES = 4 * (KBUF + VBUF) * (int)sizeof(T);   // two stages of two pages
+  constexpr int BYTES_PAGES = DEPTH * (KBUF + VBUF) * (int)sizeof(T);   // two stages of PPS pages
   constexpr int BYTES_BLOCK = block_item_lds<HD>() * 4;
   constexpr int BYTES = BYTES_PAGES > BYTES_BLOCK ? BYTES_PAGES : BYTES_BLOCK;
   __shared__ __attribute__((aligned(16))) char smem[BYTES];
   T *s_k = reinterpret_cast<T *>(smem);          // [stage][page][KBUF]
-  T *s_vt = s_k + 4 * KBUF;                      // [stage][page][VBUF]
+  T *s_vt = s_k + DEPTH * KBUF;                  // [stage][page][VBUF]
 
   // Workgroup b takes row group b % YS of item b / YS: the row groups of an item are
   // neighbours in launch order, so its pages are read while still in the last-level cache.
@@ -580,33 +581,35 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
                            [&](int t) { return *reinterpret_cast<const Frag<T> *>(&sv[(16 * t + l16) * VP + g * 8]); },
                            qf[rt], a.scale, kvalid, g, m_run[rt], l_run[rt], o[rt]);
   };
-  // Two pages per stage and barrier: multiply pages p, p + 1 from LDS stage buffer b while
-  // pages p + 4, p + 5 are requested into their (now free) register slots and pages
-  // p + 2, p + 3 are staged into the other buffer; one barrier per two pages.
-  auto stage = [&](auto s0, auto s1, auto t0, auto t1, int p, int b) __attribute__((always_inline)) {
-    fetch(s0, p + DEPTH);
-    fetch(s1, p + 1 + DEPTH);
-    compute(2 * b, nkeys - p * SUB);
-    if (p + 1 < npg) compute(2 * b + 1, nkeys - (p + 1) * SUB);
-    if (p + 2 < npg) stash(t0, 2 * (b ^ 1), nkeys - (p + 2) * SUB);
-    if (p + 3 < npg) stash(t1, 2 * (b ^ 1) + 1, nkeys - (p + 3) * SUB);
+  // PPS pages per stage and barrier: stage h multiplies pages p .. p + PPS - 1 from LDS
+  // stage buffer h while the register slots of stage h (now free) take pages p + DEPTH ..,
+  // and the pages held in the other stage's slots are staged into the other buffer.
+  auto stage = [&](auto hc, int p) __attribute__((always_inline)) {
+    constexpr int h = decltype(hc)::value;
+    static_for<PPS>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      fetch(std::integral_constant<int, h * PPS + i>{}, p + i + DEPTH);
+    });
+#pragma unroll
+    for (int i = 0; i < PPS; ++i)
+      if (p + i < npg) compute(h * PPS + i, nkeys - (p + i) * SUB);
+    static_for<PPS>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (p + PPS + i < npg)
+        stash(std::integral_constant<int, (1 - h) * PPS + i>{}, (1 - h) * PPS + i, nkeys - (p + PPS + i) * SUB);
+    });
     __syncthreads();
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-  fetch(S0{}, 0);
-  fetch(S1{}, 1);
-  fetch(S2{}, 2);
-  fetch(S3{}, 3);
-  stash(S0{}, 0, nkeys);
-  if (npg > 1) stash(S1{}, 1, nkeys - SUB);
+  static_for<DEPTH>([&](auto ic) { fetch(ic, decltype(ic)::value); });
+  static_for<PPS>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if (i < npg) stash(ic, i, nkeys - i * SUB);
+  });
   __syncthreads();
-  for (int p = 0; p < npg; p += 4) {
-    stage(S0{}, S1{}, S2{}, S3{}, p, 0);
-    if (p + 2 >= npg) break;
-    stage(S2{}, S3{}, S0{}, S1{}, p + 2, 1);
+  for (int p = 0; p < npg; p += DEPTH) {
+    stage(std::integral_constant<int, 0>{}, p);
+    if (p + PPS >= npg) break;
+    stage(std::integral_constant<int, 1>{}, p + PPS);
   }
   float l_tot[RTW];
 #pragma unroll
