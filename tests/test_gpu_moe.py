@@ -154,6 +154,19 @@ def test_small_moe_generate(small):
     assert launches == w.L * int(sg.max())   # the layers of finished steps exit on the device flag
 
 
+def test_moe_determinism(small):
+    """Rows land in their expert's segment in an order set by LDS atomics, but every output
+    row is computed from its own input row only and the gated sum is in slot order: two
+    runs give bit-identical logits and decisions."""
+    w = small.w
+    tok = np.full((w.n, w.B), w.V, dtype=np.int64)
+    c = np.zeros((w.n, w.B), bool)
+    g1 = gpu_step(small, tok, c, w.gamma, want_logits=True)
+    g2 = gpu_step(small, tok, c, w.gamma, want_logits=True)
+    assert np.array_equal(g1["z"], g2["z"], equal_nan=True)
+    assert np.array_equal(g1["tok"], g2["tok"]) and np.array_equal(g1["conf"], g2["conf"], equal_nan=True)
+
+
 def test_moe_rejects_bad_configs(small):
     from block_diffusion_lm_step_amd import TdError
     w = small.w
