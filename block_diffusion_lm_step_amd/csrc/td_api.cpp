@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <new>
 #include <string>
@@ -1039,6 +1040,11 @@ td_status td_set_moe(td_ctx *c, const td_moe_config *mc, const td_moe_weights *w
     return fail(c, TD_EINVAL, "n_shared must be in [0, %d]", MOE_MAX_SHARED);
   if (m.d_expert < 64 || m.d_expert % 64 || m.d_expert > (1 << 20))
     return fail(c, TD_EINVAL, "d_expert must be a positive multiple of 64");
+  {  // the packed expert matrices are addressed with 32-bit row counts
+    const int64_t NE = (int64_t)m.n_experts + m.n_shared;
+    if (NE * m.d_expert > INT32_MAX || NE * c->cfg.d_model > INT32_MAX)
+      return fail(c, TD_EUNSUPPORTED, "experts x width too large");
+  }
   const void *const *lists[] = {w->router, w->w1, w->w2, w->shared_w1, w->shared_w2};
   for (int k = 0; k < 5; ++k) {
     if (k >= 3 && m.n_shared == 0) continue;
