@@ -189,7 +189,8 @@ typedef struct {
  * may free them once the stream has synchronised); the workspace for max_batch rows is
  * allocated here.  The context tower keeps its dense MLP.  Routing, the expert
  * products and their gated sum all run on the device inside every later step.
- * Errors: TD_EINVAL (NULL pointer, unsupported shape), TD_ENOMEM. */
+ * Errors: TD_EINVAL (NULL pointer, shape outside the supported ranges), TD_EUNSUPPORTED
+ * ((n_experts + n_shared) * max(d_expert, d_model) beyond 2^31 - 1), TD_ENOMEM. */
 td_status td_set_moe(td_ctx *ctx, const td_moe_config *cfg, const td_moe_weights *w);
 
 /* Expert counters of the MoE layers since the previous call (then reset): the number of
