@@ -1,5 +1,6 @@
 """The seeded input generator: determinism, chunk independence, bf16 encoding, ranges."""
 import numpy as np
+import pytest
 import torch
 
 from synth import (WORKLOADS, bf16_bits_from_f32, draw_inv_temp, draw_prefix_kv, draw_prefix_lengths,
@@ -67,6 +68,30 @@ def test_tower_shapes_and_storage():
     btw = draw_tower(bw)
     assert btw.wq[0].dtype == np.uint16
     assert (f32_from_bf16_bits(btw.attn_norm[0]) == 1).all()
+
+
+def test_moe_weights_shapes_streams_and_storage():
+    from synth import draw_moe
+    w = get_workload("tiny_fp32").with_(tower="tiny_moe", moe=(8, 2, 1, 64))
+    mi = draw_moe(w)
+    E, k, S, de = w.moe
+    assert len(mi.router) == w.L and mi.router[0].shape == (E, w.d)
+    assert mi.w1[0].shape == (E, de, w.d) and mi.w2[0].shape == (E, w.d, de)
+    assert mi.sw1[0].shape == (S, de, w.d) and mi.sw2[0].shape == (S, w.d, de)
+    assert abs(float(mi.w1[0].std()) - 0.02) < 2e-3
+    # keyed streams: the same draw twice, different tensors and layers differ
+    again = draw_moe(w)
+    assert np.array_equal(again.w1[1], mi.w1[1]) and np.array_equal(again.router[0], mi.router[0])
+    assert not np.array_equal(mi.w1[0][:, :, :64].reshape(-1)[:4096], mi.w2[0].reshape(-1)[:4096])
+    assert not np.array_equal(mi.router[0], mi.router[1])
+    # a mixture-of-experts tower has no dense MLP; the context tower keeps one
+    tw = draw_tower(w)
+    assert tw.w1 == [] and tw.w2 == []
+    assert draw_tower(w, context=True).w1[0].shape == (w.F, w.d)
+    bw = w.with_(dtype="bf16", tower="tiny_moe_bf16")
+    assert draw_moe(bw).w2[0].dtype == np.uint16
+    with pytest.raises(ValueError):
+        draw_moe(get_workload("tiny_fp32"))
 
 
 def test_prefix_kv_token_slices():
