@@ -233,7 +233,10 @@ hipError_t launch_nt(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
   if (a.nw == 4) return launch_nw<T, MT, NT, 4>(epi, norm, a, s);
   if (a.nw == 8) return launch_nw<T, MT, NT, 8>(epi, norm, a, s);
   // Four row tiles with 16 waves would spill (128 VGPRs per lane): 8 waves instead.
-  if (a.nw == 16) return MT == 4 ? launch_nw<T, MT, NT, 8>(epi, norm, a, s) : launch_nw<T, MT, NT, 16>(epi, norm, a, s);
+  if (a.nw == 16) {
+    if constexpr (MT == 4) return launch_nw<T, MT, NT, 8>(epi, norm, a, s);
+    else return launch_nw<T, MT, NT, 16>(epi, norm, a, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -242,9 +245,7 @@ hipError_t launch_mt(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
   if (a.nt == 1) return launch_nt<T, MT, 1>(epi, norm, a, s);
   if constexpr (sizeof(T) == 2) {   // several column tiles per workgroup: bf16 towers
     if (a.nt == 2) return launch_nt<T, MT, 2>(epi, norm, a, s);
-    if constexpr (MT == 1) {
-      if (a.nt == 4) return launch_nt<T, MT, 4>(epi, norm, a, s);
-    }
+    if (a.nt == 4) return launch_nt<T, MT, 4>(epi, norm, a, s);
   }
   return hipErrorInvalidValue;
 }

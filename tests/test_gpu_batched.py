@@ -131,6 +131,10 @@ SMALL = {
     # projection and the LM head.
     "bf16_n9_b16_tiled": dict(n=9, plen=("uniform", 0, 200), B=16, d=256, H=4, Hkv=2, hd=64, L=2, F=1024,
                               V=4096, dtype="bf16"),
+    # M = 48 (three row tiles, a four-tile group's last one empty), MLP 256 x 8192: four
+    # column tiles per wave over eight waves; the down projection also K-split.
+    "bf16_n3_b16_nt4": dict(n=3, plen=("uniform", 0, 200), B=16, d=256, H=4, Hkv=2, hd=64, L=2, F=8192,
+                            V=4096, dtype="bf16"),
     # M = 400, MLP up projection 400 x 8192: 256 tiles of 128 rows, so 64-row tiles (the
     # last one partial, 16 rows); the down projection K-split over 16 workgroups.
     "bf16_n25_b16_tiled64": dict(n=25, plen=("uniform", 0, 100), B=16, d=256, H=4, Hkv=2, hd=64, L=2, F=8192,
