@@ -11,7 +11,10 @@
 // Work items (built on the host per prefix binding): runs of prefix pages of one
 // (sequence, K/V head) pair, and one item per pair for the block's own keys.  Every
 // item writes a partial state per query row: running max m, sum l of exp(s - m), and
-// the unnormalised output o; attn_merge_kernel combines a pair's partials in item order.
+// the unnormalised output o, into its slot; a pair's slots are consecutive in key
+// order, and attn_merge_kernel combines them in that order.  Items are launched
+// longest first, so that the short ragged ends of the pairs fill the last wave of
+// workgroups instead of trailing it.
 //
 // Prefix items, flash-decoding style.  The cache is paged (32 tokens per page; per page
 // and K/V head one contiguous 8 KiB block of K and one of V for bf16), laid out so that
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
   // it once their first pages are requested.
   if (it.is_block == 1) {
     if (a.seq_done[it.seq]) return;
-    block_item<HD, NT>(a, it, blockIdx.x, smem);
+    block_item<HD, NT>(a, it, it.slot, smem);
     return;
   }
   const bool with_block = it.is_block == 2;
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
         for (int e = 0; e < EPT; ++e) acc[e] += s_o[w][rr][e0 + e] * f;
       }
     }
-    const size_t prow = (size_t)blockIdx.x * a.R + rr;
+    const size_t prow = (size_t)it.slot * a.R + rr;
     if (sub == 0) {
       a.part_ml[prow * 2 + 0] = Mx;
       a.part_ml[prow * 2 + 1] = L;
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
   if (a.done && *a.done) return;
   if (a.seq_done[it.seq]) return;   // block fully adopted: no attention needed
   if (it.is_block) {
-    if (ygrp == 0) block_item<HD, NT>(a, it, item, reinterpret_cast<float *>(smem));
+    if (ygrp == 0) block_item<HD, NT>(a, it, it.slot, reinterpret_cast<float *>(smem));
     return;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -614,7 +617,7 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
   float l_tot[RTW];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) l_tot[rt] = sum_groups(l_run[rt]);
-  store_partial<HD, RTW>(a, item, rt0, g, l16, m_run, l_tot, o);
+  store_partial<HD, RTW>(a, it.slot, rt0, g, l16, m_run, l_tot, o);
 }
 
 // Merge of a pair's partials in item order (prefix runs, then the block), one thread

@@ -751,18 +751,24 @@ td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const int64_t
   for (int i = 0; i < n_seqs; ++i) {
     const int64_t P = off[i + 1] - off[i];
     for (int h = 0; h < g.n_kv_heads; ++h) {
-      const int pair = i * g.n_kv_heads + h;
       pfirst.push_back((int)items.size());
-      if (few && P == 0) items.push_back(AttnItem{i, h, 0, 0, 2, pair, page_base});
+      if (few && P == 0) items.push_back(AttnItem{i, h, 0, 0, 2, 0, page_base});
       for (int64_t k0 = 0; k0 < P; k0 += tc)
-        items.push_back(AttnItem{i, h, (int)k0, (int)std::min<int64_t>(P, k0 + tc), (few && k0 == 0) ? 2 : 0, pair,
+        items.push_back(AttnItem{i, h, (int)k0, (int)std::min<int64_t>(P, k0 + tc), (few && k0 == 0) ? 2 : 0, 0,
                                  page_base + k0 / KV_PAGE});
-      if (!few) items.push_back(AttnItem{i, h, 0, 0, 1, pair, 0});
+      if (!few) items.push_back(AttnItem{i, h, 0, 0, 1, 0, 0});
       pcount.push_back((int)items.size() - pfirst.back());
     }
     page_base += cap[i];
   }
   if (items.size() > ((size_t)1 << 28)) return fail(c, TD_EINVAL, "too many attention work items");
+  // Slots in pair order (the merge reads them so); launch order longest first, ties in
+  // slot order: workgroups start roughly in launch order, so the short ragged ends of
+  // the pairs fill the last wave instead of trailing it (largest-first list scheduling).
+  for (size_t k = 0; k < items.size(); ++k) items[k].slot = (int)k;
+  std::stable_sort(items.begin(), items.end(), [](const AttnItem &x, const AttnItem &y) {
+    return x.k_end - x.k_begin > y.k_end - y.k_begin;
+  });
   auto grow = [&](auto **p, size_t &cap, size_t need, size_t elt) -> td_status {
     if (need <= cap) return TD_OK;
     if (*p) TD_HIP(c, hipFree(*p));

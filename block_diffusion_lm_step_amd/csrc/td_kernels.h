@@ -93,7 +93,8 @@ constexpr int ATTN_FEW_ROWS = 32;
 
 // One split-K work item of a (seq, kv head) pair: prefix tokens [k_begin, k_end)
 // (k_begin a multiple of the page size, first page page0 of the cache) and/or the
-// block's own keys.  The items of a pair are consecutive.  is_block:
+// block's own keys.  The slots of a pair's items are consecutive; the items array is in
+// launch order.  is_block:
 //   0  prefix keys only;
 //   1  the block's keys only (the pair's last item; grouped-query path);
 //   2  prefix keys and the block's keys (the pair's first item; few-row path; the
@@ -102,7 +103,7 @@ struct AttnItem {
   int seq, kvh;            // sequence and key/value head
   int k_begin, k_end;      // prefix key range (token index within the sequence)
   int is_block;            // 0, 1 or 2 as above
-  int pair;                // seq * Hkv + kvh
+  int slot;                // partial-state slot: the item's index in (pair, key range) order
   int64_t page0;           // cache page holding token k_begin (prefix items)
 };
 struct AttnArgs {
