@@ -76,7 +76,7 @@ struct td_ctx {
   // output, au = GELU output of the MLP up projection.
   void *ah = nullptr, *ao = nullptr, *au = nullptr;
   int *arg_row = nullptr;
-  int *state_ints = nullptr;    // rowlist | rowpos | n_rows, done, t, err, counter
+  int *state_ints = nullptr;    // rowlist | rowpos | n_rows, done, t, err
   StepState st{};
   GemmPlan p_qkv, p_wo, p_w1, p_w2, p_lm;
 
@@ -679,7 +679,6 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   c->st.done = si + 2 * M + 1;
   c->st.t = si + 2 * M + 2;
   c->st.err = si + 2 * M + 3;
-  c->st.counter = (unsigned *)(si + 2 * M + 4);
   TD_HIP(c, hipStreamSynchronize(c->stream));
   return TD_OK;
 }
@@ -1152,12 +1151,13 @@ int32_t td_kernels_per_step(const td_ctx *c) {
   // prep/init, embed; per layer the projections (a K-split one adds its reduction),
   // attention and its merge, and the MLP or the mixture of experts (router GEMM, routing
   // and bucketing in one launch up to 64 rows, else two, the expert up and down
-  // projections, the combine); the LM head and the merge + commit.
+  // projections, the combine); the LM head and the merge + commit (two launches above
+  // COMMIT_SMALL_ROWS rows).
   auto gemm = [](const GemmPlan &p) { return 1 + (p.splits > 1 ? 1 : 0); };
   const int M = std::max(1, c->n_seqs) * c->cfg.block_size;
   int layer = gemm(c->p_qkv) + 2 + gemm(c->p_wo);
   layer += c->moe ? gemm(c->p_router) + (M <= 64 ? 1 : 2) + 3 : gemm(c->p_w1) + gemm(c->p_w2);
-  return 2 + layer * c->cfg.n_layers + 2;
+  return 2 + layer * c->cfg.n_layers + 2 + (M > COMMIT_SMALL_ROWS ? 1 : 0);
 }
 
 void td_destroy(td_ctx *c) {

@@ -132,7 +132,6 @@ struct StepState {                 // device-resident loop state owned by the ct
   int *done;                       // 1 when no row is masked
   int *t;                          // step counter of td_generate_block
   int *err;                        // device-side input error flags
-  unsigned *counter;               // last-workgroup counter of the vocab merge
   int *seq_done;                   // [n] 1 when the sequence has no masked position left
 };
 hipError_t launch_prep(const int *tokens, const uint8_t *committed, int M, int B, int V, StepState st, hipStream_t s);
@@ -157,6 +156,8 @@ struct CommitArgs {
   int *steps; int8_t *commit_step; // nullable
   StepState st;
 };
+// Up to COMMIT_SMALL_ROWS rows one launch merges and commits; more rows take two.
+constexpr int COMMIT_SMALL_ROWS = 128;
 hipError_t launch_merge_commit(const CommitArgs &a, int max_rows, hipStream_t s);
 // K/V of the block rows of qkv ([n*B][Nqkv] fp32: q | k | v) appended to one layer's cache
 // (layout above; bf16 caches round to nearest even): row seq*B + p is token
