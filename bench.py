@@ -8,7 +8,9 @@ commit) that starts from an all-[MASK] block and ends when every position is ado
 
 Default workload: bf16 tower at batch 1 (prefix 4096, d 2048, 16 x 128 heads, 8 layers,
 MLP 8192, vocab 131072, block 16, gamma 0.8), inputs synthetic and resident in HBM
-before the timed region.  Prints one JSON line.
+before the timed region.  The loop is issued with a window of 2 steps
+(td_set_issue_window): steps after the device reports the block adopted are not
+enqueued; --issue-window 0 enqueues all B at once.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -40,6 +42,9 @@ def parse():
     p.add_argument("--gamma", type=float, default=None)
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--issue-window", type=int, default=2,
+                   help="td_set_issue_window: step s is enqueued once the device has finished step s - W, none "
+                        "after it reports the batch adopted (0: the whole block loop at once)")
     p.add_argument("--breakdown", action="store_true", help="also time each kernel class (extra blocks)")
     p.add_argument("--ar", type=int, default=0,
                    help="also time K steps of AR decoding (td_ar_step: the context tower with its own head, one "
@@ -337,6 +342,8 @@ def main():
         dev.set_moe(moe_config(w), dM)
         del dM
     dev.set_prefix(offsets, ks, vs)
+    if args.issue_window > 0:
+        dev.set_issue_window(args.issue_window)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM ({time.time() - t:.1f} s)")
 
@@ -390,7 +397,9 @@ def main():
         # Expert launches that did work: per working step, L layers x (up, down).  Each
         # reads the W1 (or W2) of every expert that holds a row, once: the counters give
         # the experts per layer-step.
-        lm = np.array(lm_ms).reshape(args.steps, w.B, w.L, 2)[:, :S]
+        issued = len(lm_ms) // (args.steps * w.L * 2)   # steps issued per block (fewer than B with a window)
+        assert issued * args.steps * w.L * 2 == len(lm_ms) and issued >= S, (len(lm_ms), args.steps, S)
+        lm = np.array(lm_ms).reshape(args.steps, issued, w.L, 2)[:, :S]
         assert moe_launches == args.steps * S * w.L, (moe_launches, args.steps, S)
         active_per_layer = moe_active / moe_launches
         lm_bytes = int(round(active_per_layer * w.moe[3] * w.d * elt))
@@ -398,8 +407,11 @@ def main():
                   f"{active_per_layer:.1f} experts (routed + shared) holding a row per layer")
         traffic = None
     else:
-        # LM-head launches that did work: the first S of every block's B launches.
-        lm = np.array(lm_ms).reshape(args.steps, w.B)[:, :S]
+        # LM-head launches that did work: the first S of every block's launches (B, or
+        # fewer with an issue window; every block is the same).
+        issued = len(lm_ms) // args.steps
+        assert issued * args.steps == len(lm_ms) and issued >= S, (len(lm_ms), args.steps, S)
+        lm = np.array(lm_ms).reshape(args.steps, issued)[:, :S]
         lm_bytes = w.V * w.d * elt
         kernel = lmhead_kernel_name(w)
         traffic = traffic_record(w.name)
@@ -411,6 +423,7 @@ def main():
         kinds = (("gemm", TD_PROF_GEMM), ("attention", TD_PROF_ATTENTION), ("step", TD_PROF_STEP))
         if w.moe:
             kinds += (("moe_experts", TD_PROF_MOE),)
+        dev.set_issue_window(0)   # B steps per block: launches per step are read off the record
         for name, kind in kinds:
             dev.profile_begin(kind)
             for _ in range(3):
@@ -419,6 +432,7 @@ def main():
             per = len(ms) // (3 * w.B)
             ms = ms.reshape(3, w.B, per)[:, :S, :]
             breakdown[name] = dict(ms_per_step=float(ms.sum(axis=2).mean()), launches_per_step=per)
+        dev.set_issue_window(args.issue_window)
         step_bytes = (w.weight_params(moe_active / max(1, moe_launches)) * elt
                       + int(plens.sum()) * w.L * 2 * w.Hkv * w.hd * elt)
         breakdown["step_alg_bytes"] = step_bytes
@@ -446,6 +460,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; random-init tower weights N(0,0.02), prefix K/V N(0,1))",
         "config": {"workload": w.name, "batch": w.n, "prefix_tokens": int(plens.sum()), "block": w.B, "gamma": w.gamma,
+                   "issue_window": args.issue_window,
                    "d_model": w.d, "heads": w.H, "kv_heads": w.Hkv, "head_dim": w.hd, "layers": w.L, "d_ff": w.F,
                    "vocab": w.V, **({"moe": {"experts": w.moe[0], "top_k": w.moe[1], "shared": w.moe[2],
                                               "d_expert": w.moe[3]}} if w.moe else {})},

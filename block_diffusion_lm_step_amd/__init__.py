@@ -59,6 +59,7 @@ try:
     lib.td_denoise_step.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.td_generate_block.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
     lib.td_set_commit_rule.argtypes = [_CTX, c_int32, c_int32]
+    lib.td_set_issue_window.argtypes = [_CTX, c_int32]
     lib.td_bind_cache.argtypes = [_CTX, c_int32, POINTER(c_int64), POINTER(c_int64), POINTER(c_void_p),
                                   POINTER(c_void_p)]
     lib.td_set_context_tower.argtypes = [_CTX, POINTER(TdWeights)]
@@ -80,16 +81,16 @@ try:
     lib.td_last_error.restype = c_char_p
     lib.td_version.restype = c_char_p
     for _f in ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_generate_block",
-               "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_ar_step", "td_set_moe",
-               "td_moe_stats", "td_debug_attention", "td_sync"):
+               "td_set_commit_rule", "td_set_issue_window", "td_set_context_tower", "td_append_block",
+               "td_ar_step", "td_set_moe", "td_moe_stats", "td_debug_attention", "td_sync"):
         getattr(lib, _f).restype = c_int
 except AttributeError as e:   # a library built from older sources
     raise ImportError(f"{LIB_PATH} is stale ({e}); rebuild with `python block_diffusion_lm_step_amd/build.py`") from e
 
 # Every symbol the C header declares.
 EXPORTED = ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_generate_block",
-            "td_set_commit_rule", "td_set_context_tower", "td_append_block", "td_ar_step", "td_set_moe", "td_moe_stats",
-            "td_debug_attention", "td_sync",
+            "td_set_commit_rule", "td_set_issue_window", "td_set_context_tower", "td_append_block", "td_ar_step",
+            "td_set_moe", "td_moe_stats", "td_debug_attention", "td_sync",
             "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_destroy", "td_last_error", "td_version")
 TD_PROF_OFF, TD_PROF_LMHEAD, TD_PROF_GEMM, TD_PROF_ATTENTION, TD_PROF_STEP, TD_PROF_MOE = range(6)
 TD_RULE_THRESHOLD, TD_RULE_LEFT_TO_RIGHT = range(2)
@@ -209,6 +210,9 @@ class Denoiser:
 
     def set_commit_rule(self, rule: int, min_adopt: int = 1) -> None:
         self._check(lib.td_set_commit_rule(self._ctx, int(rule), int(min_adopt)))
+
+    def set_issue_window(self, steps_ahead: int) -> None:
+        self._check(lib.td_set_issue_window(self._ctx, int(steps_ahead)))
 
     def debug_attention(self, layer: int, qkv, o) -> None:
         self._check(lib.td_debug_attention(self._ctx, int(layer), _ptr(qkv), _ptr(o)))

@@ -105,6 +105,9 @@ TD_DEV void commit_all(const CommitArgs &a, int *s_wave) {
     *a.st.n_rows = base;
     *a.st.done = base == 0 ? 1 : 0;
     *a.st.t = t + 1;
+    if (a.host_progress)   // one word, system scope: the host polls it while issuing steps
+      __hip_atomic_store(a.host_progress, (a.gen << 8) | ((unsigned)(t + 1) << 1) | (base == 0 ? 1u : 0u),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -93,6 +94,13 @@ struct td_ctx {
   float *part = nullptr;     // split-K partial products
   size_t part_cap = 0;       // floats
   size_t att_cap_rows = 0;   // capacity in partial rows (items * R)
+
+  // td_generate_block's issue window (td_set_issue_window): steps enqueued beyond the
+  // last one the device has reported finished; 0 = the whole loop at once.
+  int issue_window = 0;
+  unsigned *host_progress = nullptr;   // coherent pinned word written by the commit
+  unsigned gen = 0;                    // tag of the current windowed td_generate_block call
+  bool progress_armed = false;         // steps enqueued now report progress
 
   // profiling: event pairs around the launches of one kernel class
   int prof_kind = TD_PROF_OFF;
@@ -504,6 +512,8 @@ td_status enqueue_head_commit(td_ctx *c, const void *head, int *tokens, uint8_t 
   ca.steps = steps;
   ca.commit_step = commit_step;
   ca.st = c->st;
+  ca.host_progress = c->progress_armed ? c->host_progress : nullptr;
+  ca.gen = c->gen;
   TD_HIP(c, launch_merge_commit(ca, M, c->stream));
   return TD_OK;
 }
@@ -594,6 +604,8 @@ void free_all(td_ctx *c) {
   free_moe(c);
   for (hipEvent_t e : c->ev_start) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->ev_stop) (void)hipEventDestroy(e);
+  if (c->host_progress) (void)hipHostFree(c->host_progress);
+  c->host_progress = nullptr;
 }
 
 // Per-layer weights of a tower, packed into MFMA tiles (W_q, W_k, W_v fused).
@@ -873,6 +885,21 @@ td_status td_denoise_step(td_ctx *c, int32_t *tokens, uint8_t *committed, const 
                       nullptr);
 }
 
+// Spins on the progress word until the current call's first `need` steps have finished
+// on the device (returns 0) or its batch is adopted (1); -1 after a second without
+// either (the stream may be waiting on work the caller enqueues later).
+static int wait_progress(const td_ctx *c, int need) {
+  const auto t0 = std::chrono::steady_clock::now();
+  for (unsigned it = 0;; ++it) {
+    const unsigned w = __atomic_load_n(c->host_progress, __ATOMIC_ACQUIRE);
+    if ((w >> 8) == c->gen) {
+      if (w & 1u) return 1;
+      if ((int)((w >> 1) & 127u) >= need) return 0;
+    }
+    if ((it & 1023u) == 1023u && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(1)) return -1;
+  }
+}
+
 td_status td_generate_block(td_ctx *c, int32_t *tokens, uint8_t *committed, const float *inv_temp, float gamma,
                             int32_t *steps, int8_t *commit_step) {
   TD_TRY(check_ctx(c));
@@ -883,9 +910,42 @@ td_status td_generate_block(td_ctx *c, int32_t *tokens, uint8_t *committed, cons
   const td_config &g = c->cfg;
   TD_HIP(c, launch_init_block(tokens, committed, commit_step, steps, c->n_seqs, g.block_size, g.vocab, c->st,
                               c->stream));
-  for (int s = 0; s < g.block_size; ++s)
-    TD_TRY(enqueue_step(c, tokens, committed, inv_temp, gamma, nullptr, nullptr, nullptr, nullptr, steps,
-                        commit_step));
+  // With an issue window W, step s is enqueued once the device has finished step s - W
+  // (so W - 1 steps stay queued behind the running one), and no step is enqueued once
+  // the device reports the batch adopted: the launches that would only test the loop-exit
+  // flag are never issued.  The loop's decisions stay on the device either way.
+  const int W = c->issue_window;
+  bool wait = W > 0 && c->host_progress;
+  if (wait) {
+    c->gen = (c->gen + 1) & 0xFFFFFFu;
+    if (c->gen == 0) c->gen = 1;
+  }
+  c->progress_armed = wait;
+  td_status st = TD_OK;
+  for (int s = 0; s < g.block_size && st == TD_OK; ++s) {
+    if (wait && s >= W) {
+      const int r = wait_progress(c, s - W + 1);
+      if (r > 0) break;
+      if (r < 0) wait = false;   // issue the rest at once
+    }
+    st = enqueue_step(c, tokens, committed, inv_temp, gamma, nullptr, nullptr, nullptr, nullptr, steps, commit_step);
+  }
+  c->progress_armed = false;
+  return st;
+}
+
+td_status td_set_issue_window(td_ctx *c, int32_t steps_ahead) {
+  TD_TRY(check_ctx(c));
+  if (steps_ahead < 0) return fail(c, TD_EINVAL, "steps_ahead must be >= 0");
+  if (steps_ahead > 0 && !c->host_progress) {
+    TD_HIP(c, hipSetDevice(c->dev));
+    void *p = nullptr;
+    const hipError_t e = hipHostMalloc(&p, 256, hipHostMallocCoherent);
+    if (e != hipSuccess) return fail(c, TD_ENOMEM, "hipHostMalloc(256, coherent) failed: %s", hipGetErrorString(e));
+    std::memset(p, 0, 256);
+    c->host_progress = static_cast<unsigned *>(p);
+  }
+  c->issue_window = steps_ahead;
   return TD_OK;
 }
 

@@ -155,6 +155,10 @@ struct CommitArgs {
   float *conf_out; int *argmax_out;   // nullable [n*B]
   int *steps; int8_t *commit_step; // nullable
   StepState st;
+  // Nullable: a word in coherent pinned host memory that the commit overwrites with
+  // (gen << 8) | (steps finished << 1) | adopted, for a host issuing the loop's steps a
+  // few at a time.
+  unsigned *host_progress; unsigned gen;
 };
 // Up to COMMIT_SMALL_ROWS rows one launch merges and commits; more rows take two.
 constexpr int COMMIT_SMALL_ROWS = 128;

@@ -227,6 +227,19 @@ td_status td_denoise_step(td_ctx *ctx, int32_t *tokens, uint8_t *committed, cons
 td_status td_generate_block(td_ctx *ctx, int32_t *tokens, uint8_t *committed, const float *inv_temp,
                             float gamma, int32_t *steps, int8_t *commit_step);
 
+/* Issue window of td_generate_block.  0 (the default): the call enqueues all B steps and
+ * returns at once; steps after the batch is adopted still launch and return on the
+ * device's loop-exit flag (a few microseconds per launch).  steps_ahead = W > 0: the call
+ * enqueues step s only once the device has finished step s - W, and enqueues no step
+ * once the device reports the whole batch adopted; it then returns when the last step
+ * it needs is enqueued, close to the end of the block.  The device writes its progress
+ * to a word of coherent pinned host memory (allocated here, owned by the ctx) that the
+ * calling thread polls; results are identical for every W.  If the device reports
+ * nothing for a second (e.g. the stream waits on an event the caller records later),
+ * the call enqueues the remaining steps at once.  W = 2 keeps one step queued behind the
+ * running one.  Errors: TD_EINVAL (steps_ahead < 0), TD_ENOMEM. */
+td_status td_set_issue_window(td_ctx *ctx, int32_t steps_ahead);
+
 /* Adoption rules for td_set_commit_rule. */
 typedef enum {
   TD_RULE_THRESHOLD = 0,     /* conf >= gamma, plus the min_adopt most confident */

@@ -84,6 +84,7 @@ def test_null_ctx_calls_are_rejected(td):
     assert td.lib.td_profile_end(None, None, 0) == -1
     assert td.lib.td_kernels_per_step(None) == -1
     assert td.lib.td_set_commit_rule(None, 0, 1) == td.TD_EINVAL
+    assert td.lib.td_set_issue_window(None, 2) == td.TD_EINVAL
     assert td.lib.td_bind_cache(None, 1, None, None, None, None) == td.TD_EINVAL
     assert td.lib.td_set_context_tower(None, None) == td.TD_EINVAL
     assert td.lib.td_append_block(None, None) == td.TD_EINVAL
