@@ -5,6 +5,8 @@ the device's loop-exit flag.
 Compared bit for bit with window 0 (itself checked against the oracle's block loop in the
 tiny, batched and full-size tests) and, on the tiny tower, with the oracle's loop.
 """
+import time
+
 import numpy as np
 import pytest
 
@@ -84,3 +86,35 @@ def test_window_must_not_be_negative(tiny):
     with pytest.raises(TdError) as ei:
         tiny.dev.set_issue_window(-1)
     assert ei.value.status == TD_EINVAL
+
+
+def test_window_falls_back_when_the_device_reports_nothing(tiny):
+    """The stream is still busy with earlier work (a bounded spin kernel of about 3 s,
+    enqueued first), so no progress arrives: the first wait gives up after a second, the
+    call enqueues the remaining steps at once and returns, and the results are those of
+    the whole loop."""
+    torch, w = tiny.torch, tiny.w
+    ref = _run(tiny, w.gamma, 0)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 20_000_000
+    start.record()
+    torch.cuda._sleep(n)
+    stop.record()
+    stop.synchronize()
+    per_s = n / (start.elapsed_time(stop) * 1e-3)   # spin-kernel cycles per second
+    tok = torch.zeros((w.n, w.B), dtype=torch.int32, device="cuda")
+    com = torch.zeros((w.n, w.B), dtype=torch.uint8, device="cuda")
+    steps = torch.zeros(w.n, dtype=torch.int32, device="cuda")
+    cstep = torch.zeros((w.n, w.B), dtype=torch.int8, device="cuda")
+    tiny.dev.set_issue_window(2)
+    try:
+        torch.cuda._sleep(int(3.0 * per_s))
+        t0 = time.perf_counter()
+        tiny.dev.generate_block(tok, com, tiny.tau_d, w.gamma, steps=steps, commit_step=cstep)
+        returned = time.perf_counter() - t0
+        tiny.dev.sync()
+    finally:
+        tiny.dev.set_issue_window(0)
+    log(f"[window] busy stream: generate_block returned after {returned:.2f} s")
+    assert 0.9 <= returned < 2.5
+    assert _same(ref, tuple(x.cpu().numpy() for x in (tok, com, steps, cstep)))
