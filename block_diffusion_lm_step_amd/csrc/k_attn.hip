@@ -257,9 +257,8 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
 
 // Few-row shape (R <= 32, multi-head attention): the NW = 4 waves take pages w, w + 4,
 // ..., operands straight from HBM, each wave with DEPTH pages in flight (a ring).  (Eight waves
-// measured slower: at two workgroups per CU their registers spill, and at one workgroup
-// per CU, where one-workgroup-per-CU grids would gain waves, attention took 18% longer.)
-// The pair's first item also attends
+// measured slower: with two workgroups per CU their registers spill; with one, on a grid
+// of one item per CU (batch 1), attention took 18% longer.)  The pair's first item also attends
 // the block's own keys: their loads are issued before the first pages', so the fp32
 // block pass (block_item's arithmetic, into LDS) runs while the pages are in flight, and
 // its state is merged after the waves' in the fixed order waves 0..NW-1, block.
