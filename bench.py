@@ -310,7 +310,7 @@ def main():
         print(json.dumps(write_traffic(args.workload, *args.traffic_from, args.calibrate_copy_mb)))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU path; "
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the library has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -7,7 +7,7 @@ depend on how the work was split.  Values are drawn in float32 and, for bfloat16
 workloads, stored as bfloat16 bit patterns (round to nearest even); both the oracle
 and the HIP path read those stored values, never a re-draw.
 
-Workload shapes follow the problem statement of the block-diffusion denoiser: a
+Workload shapes follow the block-diffusion denoiser of the pages: a
 block of B [MASK] tokens refined by a denoiser tower that attends over a frozen
 context tower's prefix K/V (poko-everyday.com Nemotron-TwoTower news item, section
 技術/ビジネス面; dzen.guru "NVIDIA Nemotron 70B генерирует текст в 2,4 раза быстрее…",
