@@ -17,7 +17,10 @@
  * Conventions.
  *  - Every buffer pointer is a DEVICE pointer unless its name ends in _host.
  *  - All calls enqueue work on the stream given to td_create and return without
- *    waiting; results are valid once that stream has synchronised (td_sync).
+ *    waiting, except where a call's comment says it waits (the binding and setup
+ *    calls, td_append_block, td_ar_step, td_moe_stats, and td_generate_block under an
+ *    issue window, td_set_issue_window); results are valid once that stream has
+ *    synchronised (td_sync).
  *  - A ctx is bound to one device and one stream and is not thread-safe.
  *  - Every call returns td_status; no C++ exception crosses the ABI.  Arguments are
  *    validated on the host before anything is enqueued (TD_EINVAL, nothing runs).
