@@ -56,3 +56,17 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     assert abs(rec["hbm_bytes_per_launch"] - (262144.0 * 1024 * 2 + 64.0 * 1024)) < 1.0
     assert rec["source_sha256_16"] == bench.source_hash(*bench.LMHEAD_SOURCES)
     assert json.loads(out.read_text())["hbm_bytes_per_launch"] == rec["hbm_bytes_per_launch"]
+
+
+def test_cpu_baseline_repeats_whole_block_loops():
+    from synth import get_workload
+    w = get_workload("tiny_fp32")
+    r = bench.cpu_baseline(w, 0.3)       # floor min(0.3 s, 10 s): whole loops, none past 0.3 s
+    assert r["kind"] == "oracle" and r["unit"] == "committed tokens/s" and r["cores"] >= 1
+    assert r["seconds"] >= 0.3 or "cut at the time budget" in r["sample"]
+    blocks = int(r["sample"].split(": ")[1].split(" whole")[0])
+    adopted = int(r["sample"].split("), ")[1].split(" positions")[0])
+    assert blocks >= 1
+    cut = "cut at the time budget" in r["sample"]
+    assert adopted == blocks * w.B or (cut and blocks * w.B < adopted < (blocks + 1) * w.B)
+    assert abs(r["value"] - adopted / r["seconds"]) < 1e-6 * r["value"]
