@@ -395,6 +395,7 @@ class StepResult:
     tok: np.ndarray         # [S][B] tokens after the step
     committed: np.ndarray   # [S][B] bool after the step
     z: Optional[np.ndarray] = None   # [S][B][V] logits of masked rows (nan elsewhere) if kept
+    zmax: Optional[np.ndarray] = None   # [S][B] max_v |z| of masked rows (nan elsewhere): the scale of a row's logits
 
 
 def oracle_step(tower: OracleTower, tok: np.ndarray, committed: np.ndarray, tau: np.ndarray,
@@ -410,11 +411,13 @@ def oracle_step(tower: OracleTower, tok: np.ndarray, committed: np.ndarray, tau:
     conf = np.full(S * B, np.nan)
     arg = np.full(S * B, -1, dtype=np.int64)
     gap = np.full(S * B, np.nan)
+    zmax = np.full(S * B, np.nan)
     z_all = None
     if rows.size:
         z = tower.logits(hf.reshape(S * B, -1)[rows])
         c, a, g = vocab_reduce(z, tau.reshape(-1)[rows])
         conf[rows], arg[rows], gap[rows] = c, a, g
+        zmax[rows] = np.abs(z).max(axis=1)
         if keep_logits:
             z_all = np.full((S * B, tower.V), np.nan)
             z_all[rows] = z
@@ -425,7 +428,7 @@ def oracle_step(tower: OracleTower, tok: np.ndarray, committed: np.ndarray, tau:
         U[s] = commit_rule(conf[s], masked[s], gamma, rule, min_adopt)
     new_tok = np.where(U, arg, tok)
     new_c = committed.astype(bool) | U
-    return StepResult(conf, arg, gap, U, new_tok, new_c, z_all)
+    return StepResult(conf, arg, gap, U, new_tok, new_c, z_all, zmax.reshape(S, B))
 
 
 def oracle_generate_blocks(tower: OracleTower, context: OracleContextTower, n_blocks: int, S: int, B: int,

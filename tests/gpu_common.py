@@ -2,7 +2,15 @@
 
 Parity rules (decisions that rounding can flip are exempt, as listed):
 * logits: per row, max_v |z_gpu - z_oracle| / max_v |z_oracle| <= 1e-4 (fp32 towers) or
-  2e-2 (bf16 towers), against the plain float64 oracle;
+  2e-2 (bf16 towers), against the plain float64 oracle (the stated bars); and within the
+  precision the design carries, 1e-5 (fp32) or 1e-4 (bf16 towers, whose activations enter
+  the bf16 matrix cores as a high part plus a remainder: ~2^-17 relative each), so that
+  losing the remainder (~5e-3) fails;
+* confidences: per masked row, |conf_gpu - conf_oracle| <= conf_oracle * (exp(2 tau delta)
+  - 1) + 4e-6 conf_oracle + 1e-7, where delta bounds the row's absolute logit error (the
+  measured one where logits are captured, else the design bar times max |z_oracle|):
+  the largest scaled logit and the log-sum-exp each move by at most tau * delta, so
+  log conf moves by at most 2 tau delta; the last terms cover the fp32 exp and sums;
 * token ids and commit masks, each step from the oracle's state, are bit-exact except at
   positions whose oracle confidence is within 1e-3 of gamma or whose oracle top-2 gap
   (p1 - p2) is below 1e-3; a fallback choice is also exempt when the oracle's two most
@@ -18,6 +26,8 @@ from typing import List, Optional
 import numpy as np
 
 EXEMPT = 1e-3
+LOGIT_BAR = {"f32": 1e-4, "bf16": 2e-2}          # stated bars
+LOGIT_DESIGN_BAR = {"f32": 1e-5, "bf16": 1e-4}   # the precision the kernels carry
 
 
 def log(*a):
@@ -38,7 +48,9 @@ class Case:
     keep: object = None
 
 
-def build_case(w, plens=None, mode=None, device="cuda") -> Case:
+def build_case(w, plens=None, mode=None, device="cuda", zero_head: bool = False) -> Case:
+    """The tower of workload w on the device and in the oracle; zero_head replaces the LM
+    head by zeros on both sides (every logit exactly 0: the tie cases)."""
     import torch
 
     from block_diffusion_lm_step_amd import Denoiser
@@ -49,6 +61,8 @@ def build_case(w, plens=None, mode=None, device="cuda") -> Case:
 
     log(f"[case] building {w.name}: n={w.n} B={w.B} d={w.d} L={w.L} V={w.V} dtype={w.dtype} moe={w.moe}")
     tw = draw_tower(w)
+    if zero_head:
+        tw.lm_head[...] = 0   # +0.0 in float32 and in bf16 bits
     mi = None
     if w.moe:
         from synth import draw_moe
@@ -144,3 +158,31 @@ def conf_abs_err(g: dict, r, committed_in: np.ndarray) -> float:
     if not masked.any():
         return 0.0
     return float(np.abs(g["conf"][masked].astype(np.float64) - r.conf[masked]).max())
+
+
+def check_logits(err: np.ndarray, dtype: str, what: str = "") -> None:
+    """Per-row relative logit errors against the stated bar and the design bar."""
+    assert err.max() <= LOGIT_BAR[dtype], f"{what} logits rel err {err.max():.3e} > {LOGIT_BAR[dtype]}"
+    assert err.max() <= LOGIT_DESIGN_BAR[dtype], \
+        f"{what} logits rel err {err.max():.3e} > design bar {LOGIT_DESIGN_BAR[dtype]}"
+
+
+def conf_violations(g: dict, r, committed_in: np.ndarray, tau: np.ndarray, dtype: str,
+                    z_gpu: Optional[np.ndarray] = None, z_orc: Optional[np.ndarray] = None) -> List[str]:
+    """Masked rows whose GPU confidence is outside the bound derived from the logit error.
+
+    delta per row: the measured max |z_gpu - z_oracle| when both logit arrays ([S][B][V])
+    are given, else LOGIT_DESIGN_BAR * max |z_oracle| (r.zmax)."""
+    masked = ~committed_in.astype(bool)
+    if z_gpu is not None and z_orc is not None:
+        delta = np.where(masked, np.abs(np.nan_to_num(z_gpu.astype(np.float64) - z_orc)).max(axis=-1), np.nan)
+    else:
+        delta = LOGIT_DESIGN_BAR[dtype] * r.zmax
+    out = []
+    for s, p in zip(*np.nonzero(masked)):
+        co, cg = float(r.conf[s, p]), float(g["conf"][s, p])
+        bound = co * (np.expm1(2.0 * float(tau[s, p]) * float(delta[s, p])) + 4e-6) + 1e-7
+        if not abs(cg - co) <= bound:
+            out.append(f"seq {s} pos {p}: conf gpu {cg:.8f} oracle {co:.8f} (|d| {abs(cg - co):.2e} > {bound:.2e}, "
+                       f"tau {float(tau[s, p]):.2f}, delta {float(delta[s, p]):.2e})")
+    return out

@@ -14,7 +14,8 @@ exemptions, and the device-driven block loop equal to the oracle's loop.
 import numpy as np
 import pytest
 
-from tests.gpu_common import build_case, conf_abs_err, decision_mismatches, gpu_step, log, logits_rel_err
+from tests.gpu_common import (build_case, check_logits, conf_abs_err, conf_violations, decision_mismatches, gpu_step,
+                              log, logits_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +48,8 @@ def _check_step0(case, sample):
     log(f"[{w.name}] step0 sample {sample}: logits rel err max {err.max():.3e}; "
         f"conf abs err {conf_abs_err(gs, r, c[sample]):.2e}")
     assert err.max() <= TOL[w.dtype]
+    check_logits(err, w.dtype, f"{w.name} step 0")
+    assert conf_violations(gs, r, c[sample], case.tau[sample], w.dtype, g["z"][sample], r.z) == []
     bad = decision_mismatches(gs, r, c[sample], w.gamma)
     assert bad == [], bad
 
@@ -97,6 +100,8 @@ def _check_trace(case, sample, rule=0, min_adopt=1):
             log(f"[{w.name}] step {t} (rule {rule}, min_adopt {min_adopt}): commits oracle {int(r.U.sum())} gpu "
                 f"{int(gs['U'].sum())}, conf err {conf_abs_err(gs, r, c[sample]):.2e}")
             assert bad == [], f"step {t}: {bad}"
+            cbad = conf_violations(gs, r, c[sample], case.tau[sample], w.dtype)
+            assert cbad == [], f"step {t}: {cbad}"
             others = np.setdiff1d(np.arange(w.n), sample)
             assert not g["U"][others].any(), "a committed sequence adopted a position"
             tok[sample], c[sample] = r.tok, r.committed

@@ -8,7 +8,8 @@ loop against the oracle's loop.
 import numpy as np
 import pytest
 
-from tests.gpu_common import build_case, conf_abs_err, decision_mismatches, gpu_step, log, logits_rel_err
+from tests.gpu_common import (build_case, check_logits, conf_abs_err, conf_violations, decision_mismatches, gpu_step,
+                              log, logits_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +40,8 @@ def test_step0_logits(b1, b1_trace):
     log(f"[b1] step0 logits rel err: max {err.max():.3e} mean {err.mean():.3e}; "
         f"conf abs err {conf_abs_err(g, r, c):.3e}")
     assert err.max() <= TOL_BF16
+    check_logits(err, w.dtype, "b1 step 0")
+    assert conf_violations(g, r, c, b1.tau, w.dtype, g["z"], r.z) == []
     bad = decision_mismatches(g, r, c, w.gamma)
     assert bad == [], bad
 
@@ -54,6 +57,7 @@ def test_teacher_forced_trace(b1, b1_trace):
         log(f"[b1] step {t}: commits oracle {int(r.U.sum())} gpu {int(g['U'].sum())}, "
             f"conf abs err {conf_abs_err(g, r, c):.2e}, mismatches {len(bad)}")
         all_bad += [f"step {t}: {b}" for b in bad]
+        all_bad += [f"step {t}: {b}" for b in conf_violations(g, r, c, b1.tau, w.dtype)]
         tok, c = r.tok, r.committed
     assert all_bad == [], all_bad
 

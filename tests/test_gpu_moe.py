@@ -22,7 +22,8 @@ and at least half of a trace's steps must be checked.
 import numpy as np
 import pytest
 
-from tests.gpu_common import build_case, conf_abs_err, decision_mismatches, gpu_step, log, logits_rel_err
+from tests.gpu_common import (build_case, check_logits, conf_abs_err, conf_violations, decision_mismatches, gpu_step,
+                              log, logits_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,6 +109,9 @@ def _check_trace(case, steps=None):
         if margin > ROUTE_MARGIN:
             assert act_gpu == active
             assert err.max() <= TOL[w.dtype]
+            check_logits(err, w.dtype, f"{w.name} step {t}")
+            cbad = conf_violations(g, r, c, case.tau, w.dtype, g["z"], r.z)
+            assert cbad == [], f"step {t}: {cbad}"
             assert bad == [], f"step {t}: {bad}"
             checked += 1
         else:

@@ -6,7 +6,8 @@ relative per row; decisions bit-exact with the near-threshold / near-tie exempti
 import numpy as np
 import pytest
 
-from tests.gpu_common import EXEMPT, build_case, conf_abs_err, decision_mismatches, gpu_step, log, logits_rel_err
+from tests.gpu_common import (EXEMPT, build_case, check_logits, conf_abs_err, conf_violations, decision_mismatches,
+                              gpu_step, log, logits_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +30,8 @@ def test_step_from_all_mask(tiny):
     err = logits_rel_err(g["z"].reshape(-1, w.V), r.z.reshape(-1, w.V))
     log(f"[tiny] step0 logits rel err max {err.max():.3e}; conf abs err {conf_abs_err(g, r, c):.3e}")
     assert err.max() <= TOL_F32
+    check_logits(err, w.dtype, "tiny step 0")
+    assert conf_violations(g, r, c, tiny.tau, w.dtype, g["z"], r.z) == []
     assert decision_mismatches(g, r, c, w.gamma) == []
     assert np.array_equal(g["committed"], r.committed) or decision_mismatches(g, r, c, w.gamma) == []
 
@@ -44,6 +47,7 @@ def test_teacher_forced_trace(tiny):
         bad = decision_mismatches(g, r, c, w.gamma)
         log(f"[tiny] step {t}: commits oracle {r.U.sum()} gpu {g['U'].sum()}, conf err {conf_abs_err(g, r, c):.2e}")
         assert bad == [], bad
+        assert conf_violations(g, r, c, tiny.tau, w.dtype) == []
         tok, c = r.tok, r.committed
 
 
