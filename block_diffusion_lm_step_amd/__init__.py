@@ -71,7 +71,7 @@ try:
     lib.td_sync.argtypes = [_CTX]
     lib.td_profile_begin.argtypes = [_CTX, c_int32]
     lib.td_profile_begin.restype = c_int
-    lib.td_profile_end.argtypes = [_CTX, POINTER(c_float), c_int32]
+    lib.td_profile_end.argtypes = [_CTX, POINTER(c_float), POINTER(c_int32), c_int32]
     lib.td_profile_end.restype = c_int32
     lib.td_kernels_per_step.argtypes = [_CTX]
     lib.td_kernels_per_step.restype = c_int32
@@ -80,7 +80,11 @@ try:
     lib.td_last_error.argtypes = [_CTX]
     lib.td_last_error.restype = c_char_p
     lib.td_version.restype = c_char_p
-    for _f in ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_generate_block",
+    lib.td_measure_peaks.argtypes = [c_void_p, c_int64, c_void_p, POINTER(ctypes.c_double), POINTER(ctypes.c_double),
+                                     POINTER(ctypes.c_double)]
+    lib.td_measure_peaks.restype = c_int
+    for _f in ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step",
+               "td_generate_block",
                "td_set_commit_rule", "td_set_issue_window", "td_set_context_tower", "td_append_block",
                "td_ar_step", "td_set_moe", "td_moe_stats", "td_debug_attention", "td_sync"):
         getattr(lib, _f).restype = c_int
@@ -88,11 +92,15 @@ except AttributeError as e:   # a library built from older sources
     raise ImportError(f"{LIB_PATH} is stale ({e}); rebuild with `python block_diffusion_lm_step_amd/build.py`") from e
 
 # Every symbol the C header declares.
-EXPORTED = ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_generate_block",
+EXPORTED = ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step",
+            "td_generate_block",
             "td_set_commit_rule", "td_set_issue_window", "td_set_context_tower", "td_append_block", "td_ar_step",
             "td_set_moe", "td_moe_stats", "td_debug_attention", "td_sync",
-            "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_destroy", "td_last_error", "td_version")
-TD_PROF_OFF, TD_PROF_LMHEAD, TD_PROF_GEMM, TD_PROF_ATTENTION, TD_PROF_STEP, TD_PROF_MOE = range(6)
+            "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_measure_peaks", "td_destroy",
+            "td_last_error", "td_version")
+(TD_PROF_OFF, TD_PROF_LMHEAD, TD_PROF_GEMM, TD_PROF_ATTENTION, TD_PROF_STEP, TD_PROF_MOE, TD_PROF_ATTN_MERGE,
+ TD_PROF_COMMIT, TD_PROF_EMBED) = range(9)
+PROJ_QKV, PROJ_OUT, PROJ_UP, PROJ_DOWN, PROJ_ROUTER = range(5)   # sub tags of TD_PROF_GEMM
 TD_RULE_THRESHOLD, TD_RULE_LEFT_TO_RIGHT = range(2)
 
 
@@ -111,6 +119,20 @@ def _ptr_array(ts: Optional[Sequence]):
     if not ts:
         return None
     return (c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def measure_peaks(buf, stream=None) -> Dict[str, float]:
+    """td_measure_peaks over the device tensor buf (scratch, overwritten): HBM read stream
+    and copy in GB/s, bf16 matrix-core loop in TFLOP/s."""
+    import torch
+
+    st = stream if stream is not None else torch.cuda.current_stream()
+    r, c, m = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    status = lib.td_measure_peaks(c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(), c_void_p(st.cuda_stream),
+                                  ctypes.byref(r), ctypes.byref(c), ctypes.byref(m))
+    if status != TD_OK:
+        raise TdError(status, "td_measure_peaks failed")
+    return dict(hbm_read_gbs=r.value, copy_gbs=c.value, mfma_bf16_tflops=m.value)
 
 
 class Denoiser:
@@ -217,15 +239,26 @@ class Denoiser:
     def debug_attention(self, layer: int, qkv, o) -> None:
         self._check(lib.td_debug_attention(self._ctx, int(layer), _ptr(qkv), _ptr(o)))
 
-    def profile_begin(self, kind: int) -> None:
-        self._check(lib.td_profile_begin(self._ctx, int(kind)))
+    def profile_begin(self, *kinds: int) -> None:
+        """Bracket every launch of the given kernel classes (TD_PROF_*) with HIP events."""
+        mask = 0
+        for k in kinds:
+            mask |= 1 << int(k)
+        self._check(lib.td_profile_begin(self._ctx, mask))
 
-    def profile_end(self, max_launches: int = 65536):
+    def profile_end(self, max_launches: int = 65536, tags: bool = False):
+        """Durations (ms) of the bracketed launches in launch order; with tags=True also
+        their tags (class, sub, layer) as a list of triples."""
         buf = (c_float * max_launches)()
-        n = lib.td_profile_end(self._ctx, buf, max_launches)
+        tg = (c_int32 * max_launches)()
+        n = lib.td_profile_end(self._ctx, buf, tg, max_launches)
         if n < 0:
             raise TdError(TD_EDEVICE, lib.td_last_error(self._ctx).decode())
-        return [buf[i] for i in range(min(n, max_launches))]
+        m = min(n, max_launches)
+        ms = [buf[i] for i in range(m)]
+        if not tags:
+            return ms
+        return ms, [(tg[i] & 0xFF, (tg[i] >> 8) & 0xFF, tg[i] >> 16) for i in range(m)]
 
     def sync(self) -> None:
         self._check(lib.td_sync(self._ctx))

@@ -675,8 +675,9 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 }
 
 template <typename T, int HD>
-hipError_t launch_hd(const AttnArgs &a, hipStream_t s) {
-  if (a.R <= 16) {
+hipError_t launch_hd(const AttnArgs &a, int part, hipStream_t s) {
+  if (!(part & ATTN_SPLIT)) {
+  } else if (a.R <= 16) {
     hipLaunchKernelGGL((attn_direct_kernel<T, HD, 1, 4, DIRECT_DEPTH>), dim3(a.n_items), dim3(256), 0, s, a);
   } else if (a.R <= ATTN_FEW_ROWS) {
     hipLaunchKernelGGL((attn_direct_kernel<T, HD, 2, 4, DIRECT_DEPTH>), dim3(a.n_items), dim3(256), 0, s, a);
@@ -684,21 +685,21 @@ hipError_t launch_hd(const AttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((attn_group_kernel<T, HD, 1>), dim3(a.n_items * ((a.R + 127) / 128)), dim3(512), 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !(part & ATTN_MERGE)) return e;
   hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3(a.n_pairs, (a.R + 15) / 16, HD / 32), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attention(int dtype, const AttnArgs &a, hipStream_t s) {
+hipError_t launch_attention(int dtype, const AttnArgs &a, int part, hipStream_t s) {
   if (a.n_items <= 0 || a.n_pairs <= 0 || a.B > BMAX || a.seq_done == nullptr) return hipErrorInvalidValue;
   if (dtype == DT_BF16) {
-    if (a.hd == 128) return launch_hd<bf16_t, 128>(a, s);
-    if (a.hd == 64) return launch_hd<bf16_t, 64>(a, s);
+    if (a.hd == 128) return launch_hd<bf16_t, 128>(a, part, s);
+    if (a.hd == 64) return launch_hd<bf16_t, 64>(a, part, s);
   } else {
-    if (a.hd == 128) return launch_hd<float, 128>(a, s);
-    if (a.hd == 64) return launch_hd<float, 64>(a, s);
+    if (a.hd == 128) return launch_hd<float, 128>(a, part, s);
+    if (a.hd == 64) return launch_hd<float, 64>(a, part, s);
   }
   return hipErrorInvalidValue;
 }

@@ -22,6 +22,9 @@ namespace {
 
 thread_local std::string g_create_error;
 
+// Projection ids of the profiling tags of TD_PROF_GEMM.
+enum { PROJ_QKV = 0, PROJ_OUT = 1, PROJ_UP = 2, PROJ_DOWN = 3, PROJ_ROUTER = 4 };
+
 struct GemmPlan {
   int nt = 1, nw = 4;
   bool tile = false;   // many rows: the tiled MFMA kernel
@@ -93,6 +96,7 @@ struct td_ctx {
   float *att_o = nullptr, *att_ml = nullptr;
   float *part = nullptr;     // split-K partial products
   size_t part_cap = 0;       // floats
+  size_t part_need = 0;      // floats the bound batch's GEMM plans use
   size_t att_cap_rows = 0;   // capacity in partial rows (items * R)
 
   // td_generate_block's issue window (td_set_issue_window): steps enqueued beyond the
@@ -102,9 +106,13 @@ struct td_ctx {
   unsigned gen = 0;                    // tag of the current windowed td_generate_block call
   bool progress_armed = false;         // steps enqueued now report progress
 
-  // profiling: event pairs around the launches of one kernel class
-  int prof_kind = TD_PROF_OFF;
+  // profiling: event pairs around the launches of the kernel classes in prof_mask, each
+  // pair tagged kind | sub << 8 | layer << 16
+  unsigned prof_mask = 0;
+  int prof_layer = 0;                 // layer of the launches being enqueued
+  long prof_open[TD_PROF_KINDS] = {}; // slot of the open bracket of each kind, or -1
   std::vector<hipEvent_t> ev_start, ev_stop;
+  std::vector<int32_t> ev_tag;
   size_t prof_n = 0;
 };
 
@@ -261,9 +269,13 @@ int chunk_keys(int64_t total_pair_keys, int R) {
 
 constexpr size_t PROF_MAX = 65536;
 
-td_status prof_mark(td_ctx *c, int kind, bool start) {
-  if (c->prof_kind != kind || c->prof_n >= PROF_MAX) return TD_OK;
+// Opens (start) or closes the bracket of one launch of class `kind`; sub tells the
+// launches of a class apart (the layer projections).
+td_status prof_mark(td_ctx *c, int kind, bool start, int sub = 0) {
+  if (!(c->prof_mask & (1u << kind))) return TD_OK;
   if (start) {
+    c->prof_open[kind] = -1;
+    if (c->prof_n >= PROF_MAX) return TD_OK;
     if (c->ev_start.size() <= c->prof_n) {
       // Timing-only events: no system-scope fence, which would write back and invalidate
       // the L2 around every timed launch and slow the next kernel.
@@ -272,11 +284,16 @@ td_status prof_mark(td_ctx *c, int kind, bool start) {
       TD_HIP(c, hipEventCreateWithFlags(&b, hipEventDisableSystemFence));
       c->ev_start.push_back(a);
       c->ev_stop.push_back(b);
+      c->ev_tag.push_back(0);
     }
     TD_HIP(c, hipEventRecord(c->ev_start[c->prof_n], c->stream));
+    c->ev_tag[c->prof_n] = kind | (sub << 8) | (c->prof_layer << 16);
+    c->prof_open[kind] = (long)c->prof_n++;
   } else {
-    TD_HIP(c, hipEventRecord(c->ev_stop[c->prof_n], c->stream));
-    ++c->prof_n;
+    const long slot = c->prof_open[kind];
+    if (slot < 0) return TD_OK;
+    TD_HIP(c, hipEventRecord(c->ev_stop[slot], c->stream));
+    c->prof_open[kind] = -1;
   }
   return TD_OK;
 }
@@ -312,8 +329,11 @@ td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, vo
   // other passes skip nothing (flags that stay 0).
   a.seq_done = done && c->n_seqs > 1 ? c->st.seq_done : c->zero_seq;
   TD_TRY(prof_mark(c, TD_PROF_ATTENTION, true));
-  TD_HIP(c, launch_attention(g.dtype, a, c->stream));
+  TD_HIP(c, launch_attention(g.dtype, a, ATTN_SPLIT, c->stream));
   TD_TRY(prof_mark(c, TD_PROF_ATTENTION, false));
+  TD_TRY(prof_mark(c, TD_PROF_ATTN_MERGE, true));
+  TD_HIP(c, launch_attention(g.dtype, a, ATTN_MERGE, c->stream));
+  TD_TRY(prof_mark(c, TD_PROF_ATTN_MERGE, false));
   return TD_OK;
 }
 
@@ -321,7 +341,7 @@ td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, vo
 // RMSNorm whose row scale comes from the partial sums of squares in c->ssq.
 td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const void *A, const void *Wp,
                        const GemmPlan &p, float *out, void *out_afl, const void *gain_next,
-                       const GemmArgs *extra = nullptr) {
+                       const GemmArgs *extra = nullptr, int prof_sub = 0) {
   GemmArgs a{};
   if (extra) a = *extra;
   a.M = M;
@@ -346,13 +366,13 @@ td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const
   a.splits = epi == EPI_VSTAT ? 1 : p.splits;
   a.part = c->part;
   if (p.tile) {
-    if (epi != EPI_VSTAT) TD_TRY(prof_mark(c, TD_PROF_GEMM, true));
+    if (epi != EPI_VSTAT) TD_TRY(prof_mark(c, TD_PROF_GEMM, true, prof_sub));
     TD_HIP(c, launch_gemm_tile(epi, norm, a, c->stream));
     if (epi != EPI_VSTAT) TD_TRY(prof_mark(c, TD_PROF_GEMM, false));
   } else if (epi == EPI_VSTAT) {
     TD_HIP(c, launch_gemm(c->cfg.dtype, epi, norm, a, c->stream));
   } else {
-    TD_TRY(prof_mark(c, TD_PROF_GEMM, true));
+    TD_TRY(prof_mark(c, TD_PROF_GEMM, true, prof_sub));
     TD_HIP(c, launch_gemm_wk(c->cfg.dtype, epi, norm, a, c->stream));
     TD_TRY(prof_mark(c, TD_PROF_GEMM, false));
   }
@@ -373,7 +393,7 @@ td_status enqueue_moe(td_ctx *c, int l, int M, const void *gain_after) {
   const td_moe_config &mc = c->moe_cfg;
   const int d = g.d_model;
   TD_TRY(enqueue_gemm(c, EPI_STORE, true, M, c->moe_Epad, d, c->ah, c->moe_router[l], c->p_router, c->moe_scores,
-                      nullptr, nullptr));
+                      nullptr, nullptr, nullptr, PROJ_ROUTER));
   MoeRoute r{};
   r.M = M;
   r.E = mc.n_experts;
@@ -422,10 +442,10 @@ td_status enqueue_moe(td_ctx *c, int l, int M, const void *gain_after) {
   dn.out_afl = nullptr;
   dn.out = c->moe_y;
   (void)NE;
-  TD_TRY(prof_mark(c, TD_PROF_MOE, true));
+  TD_TRY(prof_mark(c, TD_PROF_MOE, true, 0));
   TD_HIP(c, launch_moe_gemm(g.dtype, true, up, c->stream));
   TD_TRY(prof_mark(c, TD_PROF_MOE, false));
-  TD_TRY(prof_mark(c, TD_PROF_MOE, true));
+  TD_TRY(prof_mark(c, TD_PROF_MOE, true, 1));
   TD_HIP(c, launch_moe_gemm(g.dtype, false, dn, c->stream));
   TD_TRY(prof_mark(c, TD_PROF_MOE, false));
   MoeCombine cb{};
@@ -454,20 +474,29 @@ td_status enqueue_step(td_ctx *c, int *tokens, uint8_t *committed, const float *
   const int M = c->n_seqs * g.block_size;
   const int d = g.d_model, Hd = g.n_heads * g.head_dim;
   TD_TRY(prof_mark(c, TD_PROF_STEP, true));
+  c->prof_layer = 0;
+  TD_TRY(prof_mark(c, TD_PROF_EMBED, true));
   TD_HIP(c, launch_embed(g.dtype, tokens, c->tok_emb, c->pos_emb, c->layers.attn_norm[0], c->x, c->ssq, c->ah, M,
                          g.block_size, d, g.vocab, c->st, c->stream));
+  TD_TRY(prof_mark(c, TD_PROF_EMBED, false));
   for (int l = 0; l < g.n_layers; ++l) {
+    c->prof_layer = l;
     const void *gain_after = l + 1 < g.n_layers ? c->layers.attn_norm[l + 1] : c->final_norm;
-    TD_TRY(enqueue_gemm(c, EPI_STORE, true, M, c->Nqkv, d, c->ah, c->layers.wqkv[l], c->p_qkv, c->qkv, nullptr, nullptr));
+    TD_TRY(enqueue_gemm(c, EPI_STORE, true, M, c->Nqkv, d, c->ah, c->layers.wqkv[l], c->p_qkv, c->qkv, nullptr, nullptr,
+                        nullptr, PROJ_QKV));
     TD_TRY(enqueue_attention(c, l, c->qkv, nullptr, c->ao, c->st.done));
-    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, Hd, c->ao, c->layers.wo[l], c->p_wo, c->x, c->ah, c->layers.mlp_norm[l]));
+    TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, Hd, c->ao, c->layers.wo[l], c->p_wo, c->x, c->ah, c->layers.mlp_norm[l],
+                        nullptr, PROJ_OUT));
     if (c->moe) {
       TD_TRY(enqueue_moe(c, l, M, gain_after));
     } else {
-      TD_TRY(enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, c->ah, c->layers.w1[l], c->p_w1, nullptr, c->au, nullptr));
-      TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->au, c->layers.w2[l], c->p_w2, c->x, c->ah, gain_after));
+      TD_TRY(enqueue_gemm(c, EPI_GELU, true, M, g.d_ff, d, c->ah, c->layers.w1[l], c->p_w1, nullptr, c->au, nullptr,
+                          nullptr, PROJ_UP));
+      TD_TRY(enqueue_gemm(c, EPI_RESID, false, M, d, g.d_ff, c->au, c->layers.w2[l], c->p_w2, c->x, c->ah, gain_after,
+                          nullptr, PROJ_DOWN));
     }
   }
+  c->prof_layer = 0;
   TD_TRY(enqueue_head_commit(c, c->lm_head, tokens, committed, inv_temp, gamma, c->rule, c->min_adopt, newly, conf_out,
                              argmax_out, logits, steps, commit_step));
   TD_TRY(prof_mark(c, TD_PROF_STEP, false));
@@ -514,7 +543,9 @@ td_status enqueue_head_commit(td_ctx *c, const void *head, int *tokens, uint8_t 
   ca.st = c->st;
   ca.host_progress = c->progress_armed ? c->host_progress : nullptr;
   ca.gen = c->gen;
+  TD_TRY(prof_mark(c, TD_PROF_COMMIT, true));
   TD_HIP(c, launch_merge_commit(ca, M, c->stream));
+  TD_TRY(prof_mark(c, TD_PROF_COMMIT, false));
   return TD_OK;
 }
 
@@ -697,6 +728,7 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
 
 }  // namespace
 
+
 extern "C" {
 
 td_status td_create(const td_config *cfg, const td_weights *w, void *stream, td_ctx **out) {
@@ -727,7 +759,7 @@ td_status td_create(const td_config *cfg, const td_weights *w, void *stream, td_
 
 // Binds caches whose sequence i holds len[i] tokens in cap[i] reserved pages, the pages
 // of sequence i starting after those of sequences 0..i-1.
-td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const int64_t *cap,
+static td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const int64_t *cap,
                     const void *const *k_cache_host, const void *const *v_cache_host) {
   const td_config &g = c->cfg;
   int64_t total = 0, pages = 0;
@@ -819,6 +851,7 @@ td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const int64_t
     for (int i = 0; i < 5; ++i)
       if (plans[i]->splits > 1) need = std::max(need, (size_t)plans[i]->splits * M * widths[i]);
     TD_TRY(grow(&c->part, c->part_cap, need, sizeof(float)));
+    c->part_need = need;
   }
   {  // per-sequence length and first page for the K/V append
     std::vector<int> lp(2 * n_seqs);
@@ -866,7 +899,7 @@ td_status td_bind_cache(td_ctx *c, int32_t n_seqs, const int64_t *lengths_host, 
   return bind_impl(c, n_seqs, lengths_host, page_capacity_host, k_cache_host, v_cache_host);
 }
 
-td_status check_mlp(td_ctx *c) {
+static td_status check_mlp(td_ctx *c) {
   if (!c->moe && (c->layers.w1.empty() || !c->layers.w1[0]))
     return fail(c, TD_EINVAL, "the denoiser has no MLP weights: pass w1/w2 to td_create or call td_set_moe");
   return TD_OK;
@@ -1037,7 +1070,7 @@ td_status td_ar_step(td_ctx *c, int32_t *tokens) {
   return bind_impl(c, c->n_seqs, len.data(), cap.data(), kc.data(), vc.data());
 }
 
-td_status set_moe_impl(td_ctx *c, const td_moe_config &m, const td_moe_weights &w) {
+static td_status set_moe_impl(td_ctx *c, const td_moe_config &m, const td_moe_weights &w) {
   const td_config &g = c->cfg;
   const size_t e = c->elt, d = g.d_model, de = m.d_expert, L = g.n_layers;
   const size_t E = m.n_experts, S = m.n_shared, NE = E + S;
@@ -1129,6 +1162,7 @@ td_status td_set_moe(td_ctx *c, const td_moe_config *mc, const td_moe_weights *w
     const int M = c->n_seqs * c->cfg.block_size;
     c->p_router = plan_gemm(M, c->moe_Epad, c->cfg.d_model, false, c->cfg.dtype);
     const size_t need = c->p_router.splits > 1 ? (size_t)c->p_router.splits * M * c->moe_Epad : 0;
+    c->part_need = std::max(c->part_need, need);
     if (need > c->part_cap) {
       if (c->part) (void)hipFree(c->part);
       c->part = nullptr;
@@ -1185,24 +1219,28 @@ td_status td_sync(td_ctx *c) {
   return TD_OK;
 }
 
-td_status td_profile_begin(td_ctx *c, int32_t kind) {
+td_status td_profile_begin(td_ctx *c, int32_t kinds_mask) {
   TD_TRY(check_ctx(c));
-  if (kind < TD_PROF_OFF || kind > TD_PROF_MOE) return fail(c, TD_EINVAL, "unknown profiling kind %d", kind);
-  c->prof_kind = kind;
+  if (kinds_mask & ~((1 << TD_PROF_KINDS) - 1)) return fail(c, TD_EINVAL, "unknown profiling kinds in mask 0x%x", kinds_mask);
+  c->prof_mask = (unsigned)kinds_mask & ~1u;   // bit 0 (TD_PROF_OFF) brackets nothing
+  for (long &o : c->prof_open) o = -1;
   return TD_OK;
 }
 
-int32_t td_profile_end(td_ctx *c, float *ms_out, int32_t max) {
+int32_t td_profile_end(td_ctx *c, float *ms_out, int32_t *tags_out, int32_t max) {
   if (!c) return -1;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return -1;
   const size_t n = c->prof_n;
-  for (size_t i = 0; i < n && (int64_t)i < max && ms_out; ++i) {
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, c->ev_start[i], c->ev_stop[i]) != hipSuccess) return -1;
-    ms_out[i] = ms;
-  }
   c->prof_n = 0;
-  c->prof_kind = TD_PROF_OFF;
+  c->prof_mask = 0;
+  for (size_t i = 0; i < n && (int64_t)i < max; ++i) {
+    float ms = 0.f;
+    if (ms_out) {
+      if (hipEventElapsedTime(&ms, c->ev_start[i], c->ev_stop[i]) != hipSuccess) return -1;
+      ms_out[i] = ms;
+    }
+    if (tags_out) tags_out[i] = c->ev_tag[i];
+  }
   return (int32_t)n;
 }
 

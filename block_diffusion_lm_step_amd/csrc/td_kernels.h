@@ -122,7 +122,9 @@ struct AttnArgs {
   float scale;                     // 1 / sqrt(hd)
   const int *done;
 };
-hipError_t launch_attention(int dtype, const AttnArgs &a, hipStream_t s);
+// part: ATTN_SPLIT (the split-K items), ATTN_MERGE (the merge of their partials), or both.
+enum { ATTN_SPLIT = 1, ATTN_MERGE = 2 };
+hipError_t launch_attention(int dtype, const AttnArgs &a, int part, hipStream_t s);
 
 // ---------------------------------------------------------------- embedding, step control
 struct StepState {                 // device-resident loop state owned by the ctx

@@ -275,30 +275,52 @@ td_status td_debug_attention(td_ctx *ctx, int32_t layer, const void *qkv, void *
  * errors recorded since the last td_sync. */
 td_status td_sync(td_ctx *ctx);
 
-/* Kernel classes for td_profile_begin. */
+/* Kernel classes for td_profile_begin (bit k of its mask brackets class k). */
 typedef enum {
   TD_PROF_OFF = 0,
   TD_PROF_LMHEAD = 1,     /* LM head + fused vocab statistics (one launch per step) */
-  TD_PROF_GEMM = 2,       /* the 4 L layer projections of a step */
-  TD_PROF_ATTENTION = 3,  /* split-K attention + merge, L per step */
+  TD_PROF_GEMM = 2,       /* each layer projection, with its K-split reduction when split: 4 L per
+                           * step (tag sub 0 fused QKV, 1 output, 2 MLP up, 3 MLP down, 4 MoE router) */
+  TD_PROF_ATTENTION = 3,  /* the split-K attention items (prefix pages and block keys), L per step */
   TD_PROF_STEP = 4,       /* one whole step, embedding to commit */
-  TD_PROF_MOE = 5         /* the expert up and down projections, 2 L per step (td_set_moe) */
+  TD_PROF_MOE = 5,        /* the expert up (sub 0) and down (sub 1) projections, 2 L per step */
+  TD_PROF_ATTN_MERGE = 6, /* the merge of the attention partials, L per step */
+  TD_PROF_COMMIT = 7,     /* vocabulary merge + adoption rule (one or two launches per step) */
+  TD_PROF_EMBED = 8,      /* the embedding (one launch per step) */
+  TD_PROF_KINDS = 9
 } td_prof_kind;
 
-/* Profiling: from now on bracket every launch of kernel class `kind` with a pair of HIP
- * events on the ctx's stream (at most 65536 launches are recorded; later ones are not).
- * TD_PROF_OFF stops recording. */
-td_status td_profile_begin(td_ctx *ctx, int32_t kind);
+/* Profiling: from now on bracket every launch of the kernel classes in kinds_mask
+ * (bit k = class k; 0 stops recording) with a pair of HIP events on the ctx's stream, at
+ * most 65536 brackets (later launches are not recorded).  Errors: TD_EINVAL for bits
+ * past TD_PROF_KINDS. */
+td_status td_profile_begin(td_ctx *ctx, int32_t kinds_mask);
 
 /* Wait for the stream, write the duration in ms of each bracketed launch, in launch order,
- * to ms_out_host[0 .. min(count, max)) and return the number recorded (or -1 on error);
- * then clear the record.  Launches skipped on the device because the block was already
- * committed are included (they take a few microseconds). */
-int32_t td_profile_end(td_ctx *ctx, float *ms_out_host, int32_t max);
+ * to ms_out_host[0 .. min(count, max)) and its tag (class | sub << 8 | layer << 16) to
+ * tags_out_host (either may be NULL), and return the number recorded (or -1 on error);
+ * then clear the record and stop recording.  Launches skipped on the device because the
+ * block was already committed are included (they take a few microseconds). */
+int32_t td_profile_end(td_ctx *ctx, float *ms_out_host, int32_t *tags_out_host, int32_t max);
 
 /* Number of kernels one td_denoise_step enqueues on the bound batch (for profiling and
  * launch accounting; before a binding, for one sequence with the creation-time plans). */
 int32_t td_kernels_per_step(const td_ctx *ctx);
+
+/* Measurement helper, not part of the step: the chip's own ceilings, to report achieved
+ * rates against measured as well as published peaks.  On the current device and the
+ * given stream (a hipStream_t, NULL = default), waiting for it; best of five launches
+ * each.
+ *  hbm_read_gbs      a read stream over buf: every 16-byte word read once (streaming loads);
+ *  copy_gbs          a copy of the first half of buf into the second, bytes read + written;
+ *  mfma_bf16_tflops  loops of bf16 matrix-core products (16x16x32 and 32x32x16, the better
+ *                    of the two), operands in registers, no memory traffic, four waves per
+ *                    SIMD.
+ * buf: DEVICE scratch of `bytes` bytes (>= 68 MiB, 16-byte aligned; use well over the
+ * 256 MiB last-level cache for an HBM figure), overwritten.  Errors: TD_EINVAL (NULL
+ * pointer, buffer too small or misaligned), TD_EDEVICE (a runtime error). */
+td_status td_measure_peaks(void *buf, int64_t bytes, void *stream, double *hbm_read_gbs, double *copy_gbs,
+                           double *mfma_bf16_tflops);
 
 void td_destroy(td_ctx *ctx);                  /* NULL-safe; waits for the stream */
 const char *td_last_error(const td_ctx *ctx);  /* ctx == NULL: this thread's last create error */
