@@ -57,6 +57,8 @@ try:
     lib.td_create.argtypes = [POINTER(TdConfig), POINTER(TdWeights), c_void_p, POINTER(_CTX)]
     lib.td_set_prefix.argtypes = [_CTX, c_int32, POINTER(c_int64), POINTER(c_void_p), POINTER(c_void_p)]
     lib.td_denoise_step.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.td_denoise_step_noalloc.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                            c_void_p, c_void_p]
     lib.td_generate_block.argtypes = [_CTX, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
     lib.td_set_commit_rule.argtypes = [_CTX, c_int32, c_int32]
     lib.td_set_issue_window.argtypes = [_CTX, c_int32]
@@ -83,7 +85,7 @@ try:
     lib.td_measure_peaks.argtypes = [c_void_p, c_int64, c_void_p, POINTER(ctypes.c_double), POINTER(ctypes.c_double),
                                      POINTER(ctypes.c_double)]
     lib.td_measure_peaks.restype = c_int
-    for _f in ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step",
+    for _f in ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_denoise_step_noalloc",
                "td_generate_block",
                "td_set_commit_rule", "td_set_issue_window", "td_set_context_tower", "td_append_block",
                "td_ar_step", "td_set_moe", "td_moe_stats", "td_debug_attention", "td_sync"):
@@ -92,7 +94,7 @@ except AttributeError as e:   # a library built from older sources
     raise ImportError(f"{LIB_PATH} is stale ({e}); rebuild with `python block_diffusion_lm_step_amd/build.py`") from e
 
 # Every symbol the C header declares.
-EXPORTED = ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step",
+EXPORTED = ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "td_denoise_step_noalloc",
             "td_generate_block",
             "td_set_commit_rule", "td_set_issue_window", "td_set_context_tower", "td_append_block", "td_ar_step",
             "td_set_moe", "td_moe_stats", "td_debug_attention", "td_sync",
@@ -225,6 +227,13 @@ class Denoiser:
                      logits=None) -> None:
         self._check(lib.td_denoise_step(self._ctx, _ptr(tokens), _ptr(committed), _ptr(inv_temp), float(gamma),
                                         _ptr(newly), _ptr(conf), _ptr(argmax), _ptr(logits)))
+
+    def denoise_step_noalloc(self, tokens, committed, inv_temp, gamma: float, newly=None, conf=None, argmax=None,
+                             logits=None) -> None:
+        """td_denoise_step_noalloc: the step with its partial results in the library's
+        file-scope device array (no allocation)."""
+        self._check(lib.td_denoise_step_noalloc(self._ctx, _ptr(tokens), _ptr(committed), _ptr(inv_temp),
+                                                float(gamma), _ptr(newly), _ptr(conf), _ptr(argmax), _ptr(logits)))
 
     def generate_block(self, tokens, committed, inv_temp, gamma: float, steps=None, commit_step=None) -> None:
         self._check(lib.td_generate_block(self._ctx, _ptr(tokens), _ptr(committed), _ptr(inv_temp), float(gamma),

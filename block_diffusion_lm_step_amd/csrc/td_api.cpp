@@ -1,6 +1,7 @@
 // Host runtime behind td.h: validation, workspace, weight packing, split-K planning,
 // and the launch sequence of one denoising step / one block loop on the ctx's stream.
 #include "../../include/td.h"
+#include "td_internal.h"
 #include "td_kernels.h"
 
 #include <hip/hip_runtime.h>
@@ -672,6 +673,7 @@ td_status pack_layers(td_ctx *c, const td_weights &w, Layers &t) {
 
 td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   TD_HIP(c, hipGetDevice(&c->dev));
+  TD_HIP(c, td::noalloc_scratch_init());   // the allocation-free step's array on this device
   c->elt = g.dtype == TD_BF16 ? 2 : 4;
   const size_t e = c->elt;
   const size_t d = g.d_model, F = g.d_ff, V = g.vocab;
@@ -728,6 +730,84 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
 
 }  // namespace
 
+// ---------------------------------------------------------------- steps on caller-side scratch
+static td_status check_mlp(td_ctx *c);
+
+namespace td {
+
+// The partial-result buffers of one step over the bound batch, carved from `base`
+// (256-byte aligned pieces): the vocabulary statistics of every (row, column group), the
+// per-row confidences and predictions, the attention items' partial states and the
+// K-split partial products.  Returns the bytes needed; fills *out only when they fit.
+int ctx_device(const td_ctx *c) { return c->dev; }
+
+size_t carve_step_scratch(const td_ctx *c, char *base, size_t bytes, StepScratch *out) {
+  const td_config &g = c->cfg;
+  const size_t M = (size_t)c->n_seqs * g.block_size;
+  const size_t nslices = c->p_lm.tile ? gemm_tile_slices(g.vocab) : lmhead_slices(g.vocab, c->p_lm.nt, c->p_lm.nw);
+  const size_t R = (size_t)(g.n_heads / g.n_kv_heads) * g.block_size;
+  const size_t rows = (size_t)c->n_items * R;
+  const size_t sizes[6] = {M * nslices * sizeof(VStat), M * 4, M * 4, rows * g.head_dim * 4, rows * 8,
+                           c->part_need * 4};
+  size_t off[6], total = 0;
+  for (int i = 0; i < 6; ++i) {
+    off[i] = total;
+    total += (sizes[i] + 255) / 256 * 256;
+  }
+  if (out && base && total <= bytes) {
+    out->vpart = reinterpret_cast<VStat *>(base + off[0]);
+    out->conf_row = reinterpret_cast<float *>(base + off[1]);
+    out->arg_row = reinterpret_cast<int *>(base + off[2]);
+    out->att_o = reinterpret_cast<float *>(base + off[3]);
+    out->att_ml = reinterpret_cast<float *>(base + off[4]);
+    out->part = sizes[5] ? reinterpret_cast<float *>(base + off[5]) : nullptr;
+  }
+  return total;
+}
+
+// td_denoise_step with the step's partial results in caller-side device scratch
+// [scratch, scratch + bytes) instead of the ctx's own buffers.  Nothing is allocated:
+// profiling brackets (whose events are created on first use) are not recorded.
+td_status denoise_step_on_scratch(td_ctx *c, int32_t *tokens, uint8_t *committed, const float *inv_temp, float gamma,
+                                  uint8_t *newly, float *conf_out, int32_t *argmax_out, float *logits_out,
+                                  char *scratch, size_t bytes) {
+  TD_TRY(check_ctx(c));
+  TD_TRY(check_mlp(c));
+  if (!tokens || !committed) return fail(c, TD_EINVAL, "tokens and committed must not be NULL");
+  if (!finite(gamma)) return fail(c, TD_EINVAL, "gamma must be finite");
+  if (c->n_seqs <= 0) return fail(c, TD_EINVAL, "no prefix bound: call td_set_prefix first");
+  StepScratch sc{};
+  const size_t need = carve_step_scratch(c, scratch, bytes, &sc);
+  if (!scratch || need > bytes)
+    return fail(c, TD_EINVAL, "the bound batch needs %zu bytes of step scratch; the allocation-free step holds %zu",
+                need, bytes);
+  TD_TRY(check_bound(c));
+  const StepScratch own{c->vpart, c->conf_row, c->arg_row, c->att_o, c->att_ml, c->part};
+  const unsigned mask = c->prof_mask;
+  c->prof_mask = 0;
+  c->vpart = sc.vpart;
+  c->conf_row = sc.conf_row;
+  c->arg_row = sc.arg_row;
+  c->att_o = sc.att_o;
+  c->att_ml = sc.att_ml;
+  c->part = sc.part;
+  const int M = c->n_seqs * c->cfg.block_size;
+  td_status st = TD_OK;
+  const hipError_t e = launch_prep(tokens, committed, M, c->cfg.block_size, c->cfg.vocab, c->st, c->stream);
+  if (e != hipSuccess) st = fail(c, TD_EDEVICE, "launch_prep: %s", hipGetErrorString(e));
+  if (st == TD_OK)
+    st = enqueue_step(c, tokens, committed, inv_temp, gamma, newly, conf_out, argmax_out, logits_out, nullptr, nullptr);
+  c->vpart = own.vpart;
+  c->conf_row = own.conf_row;
+  c->arg_row = own.arg_row;
+  c->att_o = own.att_o;
+  c->att_ml = own.att_ml;
+  c->part = own.part;
+  c->prof_mask = mask;
+  return st;
+}
+
+}  // namespace td
 
 extern "C" {
 

@@ -222,6 +222,25 @@ td_status td_denoise_step(td_ctx *ctx, int32_t *tokens, uint8_t *committed, cons
                           float gamma, uint8_t *newly_committed, float *conf_out, int32_t *argmax_out,
                           float *logits_out);
 
+/* Allocation-free step, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): td_denoise_step,
+ * same arguments and results, whose partial results -- the vocabulary statistics of
+ * every (row, column group), the per-row confidences and predictions, the attention
+ * items' partial states and the K-split partial products -- live in a file-scope device
+ * array of TD_NOALLOC_SCRATCH_MB MiB instead of buffers of the ctx.  The call makes no
+ * hipMalloc, hipFree or other allocating call (profiling brackets are not recorded by
+ * it).  Each device holds one such array, from the first td_create on it until the
+ * process ends; every call on a device uses that device's array and leaves its contents
+ * behind (each step writes every part it reads first), so calls that overlap on one GPU
+ * -- ctxs on different streams -- race.  Errors: as td_denoise_step, and TD_EINVAL when
+ * the bound batch needs more than the array holds (about 12 B per row and vocabulary
+ * column group, plus (head_dim + 2) * 4 B per attention query row and split-K item, plus
+ * the K-split partials). */
+#define TD_NOALLOC_SCRATCH_MB 64
+td_status td_denoise_step_noalloc(td_ctx *ctx, int32_t *tokens, uint8_t *committed, const float *inv_temp,
+                                  float gamma, uint8_t *newly_committed, float *conf_out, int32_t *argmax_out,
+                                  float *logits_out);
+
 /* The whole block loop on the device, without host round-trips: sets tokens to [MASK]
  * and committed to 0, then runs at most B steps; each sequence's loop ends when its
  * block is fully committed (a finished sequence is left unchanged).
