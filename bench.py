@@ -583,9 +583,13 @@ def bench_workload(args, w, peaks: dict, want_cpu: bool) -> dict:
     classes, empty_ms, nblk = summarize(w, plens, list(zip(ms, tags)), activity, w.B, moe_active)
     dominant = max((c for c in classes if classes[c]["bytes"] or classes[c]["flops"]), key=lambda c: classes[c]["ms"])
     dkind, dsub = class_kind(dominant)
-    per_step_launches = 1 if dkind == K_LMHEAD else w.L
 
-    # Timed region: blocks enqueued whole; events on the dominant class only.
+    # Timed region: blocks enqueued whole; events on the dominant class only, and for a
+    # per-layer class on its middle layer only (one pair of events per step, as for the
+    # LM head: more events between short launches would slow the loop they time).
+    per_step_launches = 1
+    if dkind != K_LMHEAD:
+        dev.profile_layer(w.L // 2)
     dev.profile_begin(dkind)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -594,6 +598,7 @@ def bench_workload(args, w, peaks: dict, want_cpu: bool) -> dict:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dms, dtags = dev.profile_end(tags=True)
+    dev.profile_layer(-1)
     dev.sync()
     elapsed = t1 - t0
     st, cs = steps.cpu().numpy(), cstep.cpu().numpy()

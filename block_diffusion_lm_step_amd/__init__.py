@@ -74,6 +74,8 @@ try:
     lib.td_profile_begin.argtypes = [_CTX, c_int32]
     lib.td_profile_begin.restype = c_int
     lib.td_profile_end.argtypes = [_CTX, POINTER(c_float), POINTER(c_int32), c_int32]
+    lib.td_profile_layer.argtypes = [_CTX, c_int32]
+    lib.td_profile_layer.restype = c_int
     lib.td_profile_end.restype = c_int32
     lib.td_kernels_per_step.argtypes = [_CTX]
     lib.td_kernels_per_step.restype = c_int32
@@ -98,7 +100,8 @@ EXPORTED = ("td_create", "td_set_prefix", "td_bind_cache", "td_denoise_step", "t
             "td_generate_block",
             "td_set_commit_rule", "td_set_issue_window", "td_set_context_tower", "td_append_block", "td_ar_step",
             "td_set_moe", "td_moe_stats", "td_debug_attention", "td_sync",
-            "td_profile_begin", "td_profile_end", "td_kernels_per_step", "td_measure_peaks", "td_destroy",
+            "td_profile_begin", "td_profile_layer", "td_profile_end", "td_kernels_per_step", "td_measure_peaks",
+            "td_destroy",
             "td_last_error", "td_version")
 (TD_PROF_OFF, TD_PROF_LMHEAD, TD_PROF_GEMM, TD_PROF_ATTENTION, TD_PROF_STEP, TD_PROF_MOE, TD_PROF_ATTN_MERGE,
  TD_PROF_COMMIT, TD_PROF_EMBED) = range(9)
@@ -254,6 +257,10 @@ class Denoiser:
         for k in kinds:
             mask |= 1 << int(k)
         self._check(lib.td_profile_begin(self._ctx, mask))
+
+    def profile_layer(self, layer: int) -> None:
+        """Bracket the per-layer classes on this layer only (-1: every layer)."""
+        self._check(lib.td_profile_layer(self._ctx, int(layer)))
 
     def profile_end(self, max_launches: int = 65536, tags: bool = False):
         """Durations (ms) of the bracketed launches in launch order; with tags=True also

@@ -47,6 +47,32 @@ struct alignas(16) StageLds {
 
 constexpr int EPI_PART = 100;   // split-K partial: store the raw accumulator tile
 
+// LM-head tile of the workgroup at (blockIdx.x, blockIdx.y), or false if the launch
+// index lies past the live row tiles (gy of them; the grid holds row tiles for every
+// row).  Workgroups are handed to the eight XCDs round-robin in launch order, each XCD
+// with its own L2, and the head matrix (V x d, larger than the last-level cache) must not
+// be fetched once per row tile.  So the workgroups an XCD runs together cover a block of
+// up to 8 row tiles x 8 column tiles (each k-slice of a column tile is then read once for
+// all of the block's row tiles, and of a row tile once for all 8 column tiles): launch
+// index i goes to XCD i % 8, and the XCD's j-th workgroup (j = i / 8) takes block
+// j / (gm * 8) of its column tiles (c == XCD mod 8), row tile j % gm of the block's rows.
+// The live tiles take the first launch indices, so they start first.  Needs
+// gridDim.x % 64 == 0 (else the tiles keep the launch order).
+TD_DEV bool lmhead_tile(int gy, int &tx, int &ty) {
+  const int gx = gridDim.x;
+  if (gx % 64) return true;
+  const int i = blockIdx.y * gx + blockIdx.x;
+  if (i >= gx * gy) return false;
+  int gm = gy < 8 ? gy : 8;
+  while (gy % gm) --gm;                       // row tiles per block: a divisor of gy
+  const int xcd = i & 7, j = i >> 3;
+  const int blk = j / (gm * 8), w = j % (gm * 8);
+  const int rblocks = gy / gm;
+  ty = (blk % rblocks) * gm + w % gm;
+  tx = ((blk / rblocks) * 8 + w / gm) * 8 + xcd;
+  return true;
+}
+
 template <int EPI, bool NORM, int BM>
 __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   constexpr int MTW = BM / 32;                     // MFMA row tiles per wave
@@ -64,7 +90,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   const int stop = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // a vector load
   __builtin_amdgcn_sched_barrier(0);
   const int nrows = a.n_rows ? *a.n_rows : a.M;   // live rows (LM head: masked rows)
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  int tx = blockIdx.x, ty = blockIdx.y;
+  if constexpr (EPI == EPI_VSTAT) {
+    if (!lmhead_tile((nrows + BM - 1) / BM, tx, ty)) return;
+  }
+  const int m0 = ty * BM, n0 = tx * BN;
   if (m0 >= nrows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -233,46 +263,77 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
       }
     __syncthreads();
     if (threadIdx.x < BM && m0 + threadIdx.x < nrows)
-      a.vpart[(size_t)(m0 + threadIdx.x) * gridDim.x + blockIdx.x] = vstat_merge(s_stat[0][threadIdx.x], s_stat[1][threadIdx.x]);
+      a.vpart[(size_t)(m0 + threadIdx.x) * gridDim.x + tx] = vstat_merge(s_stat[0][threadIdx.x], s_stat[1][threadIdx.x]);
   } else {
+    // STORE / GELU / RESID, a half of the wave's columns at a time: the wave parks its
+    // accumulators (row scale applied) in the now idle stage buffers, one padded row per
+    // tile row, and reads them back as 8 consecutive columns of one row per lane, so that
+    // every output is a whole 32-byte fragment-layout chunk (hi and lo parts of 8 columns)
+    // or a 32-byte run of a row-major fp32 row, instead of per-element stores.
+    // Output row of tile row ri: through the row list when one is given (the rows of the
+    // sequences still active), else m0 + ri; positions past the live count are not written.
+    constexpr int RW = MTW * 16;        // rows of the wave's tile
+    constexpr int EP = 32 + 4;          // padded row of 32 columns (floats)
+    static_assert(4 * RW * EP * 4 <= (int)sizeof(s_st), "epilogue staging fits the stage buffers");
+    float *ep = reinterpret_cast<float *>(&s_st[0]) + wave * RW * EP;
     const int M = a.M;
     const int KTo = a.N >> 5;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int col = n0 + (wn * NTW + j) * 16 + l16;
-      float gnext = 1.0f;
-      f32x16_t xold;   // [i * 4 + r]
-      if constexpr (EPI == EPI_RESID) {
-        gnext = to_f32<bf16_t>(reinterpret_cast<const bf16_t *>(a.gain_next)[col]);
-#pragma unroll
-        for (int i = 0; i < MTW; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            xold[i * 4 + r] = a.out[(size_t)min(m0 + (wm * MTW + i) * 16 + 4 * g + r, M - 1) * a.ldo + col];
-      }
+    for (int h = 0; h < NTW / 2; ++h) {
 #pragma unroll
       for (int i = 0; i < MTW; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ri = (wm * MTW + i) * 16 + 4 * g + r;
-          const int row = m0 + ri;
-          const bool ok = row < M;
-          float y = acc[i][j][r];
-          if constexpr (NORM) y *= s_rs[ri];
-          if constexpr (EPI == EPI_STORE) {
-            if (ok) a.out[(size_t)row * a.ldo + col] = y;
-          } else if constexpr (EPI == EPI_GELU) {
-            if (ok) afl_put<bf16_t>(a.out_afl, KTo, row, col, gelu_erf(y));
-          } else {
-            const float xv = ok ? xold[i * 4 + r] + y : 0.f;
-            if (ok) {
-              a.out[(size_t)row * a.ldo + col] = xv;
-              afl_put<bf16_t>(a.out_afl, KTo, row, col, xv * gnext);
-            }
-            const float sq16 = sum16(xv * xv);
-            if (ok && l16 == 0) a.ssq_out[(size_t)(col >> 4) * M + row] = sq16;
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rl = i * 16 + 4 * g + r;
+            float y = acc[i][2 * h + jj][r];
+            if constexpr (NORM) y *= s_rs[wm * RW + rl];
+            ep[rl * EP + jj * 16 + l16] = y;
+          }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < RW * 4 / 64; ++q) {
+        const int o = lane + 64 * q;               // octet: row o / 4, columns 8 (o % 4) ..
+        const int rl = o >> 2, c8 = (o & 3) * 8;
+        const int ri = wm * RW + rl;
+        const bool ok = m0 + ri < nrows;
+        const int row = a.rowlist ? s_row[ri] : m0 + ri;
+        const int col = n0 + (wn * NTW + 2 * h) * 16 + c8;
+        float v[8];
+        load8f(ep + rl * EP + c8, v);
+        if constexpr (EPI == EPI_STORE) {
+          if (ok) {
+            float4 *o4 = reinterpret_cast<float4 *>(a.out + (size_t)row * a.ldo + col);
+            o4[0] = make_float4(v[0], v[1], v[2], v[3]);
+            o4[1] = make_float4(v[4], v[5], v[6], v[7]);
+          }
+        } else if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
+          if (ok) afl_put8<bf16_t>(a.out_afl, KTo, row, col, v);
+        } else {
+          float xo[8], gn[8], sq = 0.f;
+          load8f(a.out + (size_t)(ok ? row : 0) * a.ldo + col, xo);
+          Frag<bf16_t> gf;
+          gf.load(reinterpret_cast<const bf16_t *>(a.gain_next) + col);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v[e] += xo[e];
+            sq += v[e] * v[e];
+            gn[e] = v[e] * gf.get(e);
+          }
+          sq += dpp_f<DPP_SWAP1>(sq);   // the neighbouring lane holds the other 8 columns of the 16
+          if (ok) {
+            float4 *x4 = reinterpret_cast<float4 *>(a.out + (size_t)row * a.ldo + col);
+            x4[0] = make_float4(v[0], v[1], v[2], v[3]);
+            x4[1] = make_float4(v[4], v[5], v[6], v[7]);
+            afl_put8<bf16_t>(a.out_afl, KTo, row, col, gn);
+            if ((o & 1) == 0) a.ssq_out[(size_t)(col >> 4) * M + row] = sq;
           }
         }
+      }
+      __syncthreads();
     }
   }
 }
@@ -283,16 +344,21 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
 template <int EPI, bool NORM>
 __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a) {
   __shared__ float s_red[4];
-  const int row = blockIdx.y;
+  // Partials are indexed by position (blockIdx.y); the output row is the row list's entry
+  // there when a row list is given (positions past the live count have nothing to do).
+  const int pos = blockIdx.y;
+  const int nrows = a.n_rows ? *a.n_rows : a.M;   // loaded with the loop-exit flag
+  const int row = a.rowlist ? a.rowlist[min(pos, a.M - 1)] : pos;
   const int col = blockIdx.x * 1024 + threadIdx.x * 4;
   const bool in = col < a.N;
+  if (a.done && *a.done) return;
+  if (pos >= nrows) return;
   f32x4_t y = zero4();
   if (in) {
 #pragma unroll 4
     for (int sp = 0; sp < a.splits; ++sp)
-      y += *reinterpret_cast<const f32x4_t *>(a.part + ((size_t)sp * a.M + row) * a.N + col);
+      y += *reinterpret_cast<const f32x4_t *>(a.part + ((size_t)sp * a.M + pos) * a.N + col);
   }
-  if (a.done && *a.done) return;
   if constexpr (NORM) {
     float s = 0.f;
     for (int p = threadIdx.x; p < a.norm_nparts; p += 256) s += a.ssq[(size_t)p * a.ld_ssq + row];
@@ -307,18 +373,21 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a) {
   if constexpr (EPI == EPI_STORE) {
     *reinterpret_cast<f32x4_t *>(a.out + (size_t)row * a.ldo + col) = y;
   } else if constexpr (EPI == EPI_GELU) {
+    float u[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) afl_put<bf16_t>(a.out_afl, KTo, row, col + e, gelu_erf(y[e]));
+    for (int e = 0; e < 4; ++e) u[e] = gelu_erf(y[e]);
+    afl_put4<bf16_t>(a.out_afl, KTo, row, col, u);
   } else {
     f32x4_t *xp = reinterpret_cast<f32x4_t *>(a.out + (size_t)row * a.ldo + col);
     const f32x4_t xv = *xp + y;
     *xp = xv;
-    float sq = 0.f;
+    float sq = 0.f, gx[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      afl_put<bf16_t>(a.out_afl, KTo, row, col + e, xv[e] * to_f32<bf16_t>(reinterpret_cast<const bf16_t *>(a.gain_next)[col + e]));
+      gx[e] = xv[e] * to_f32<bf16_t>(reinterpret_cast<const bf16_t *>(a.gain_next)[col + e]);
       sq += xv[e] * xv[e];
     }
+    afl_put4<bf16_t>(a.out_afl, KTo, row, col, gx);
     sq = sum_lanes<4>(sq);
     if ((threadIdx.x & 3) == 0) a.ssq_out[(size_t)(col >> 4) * a.M + row] = sq;
   }
@@ -327,14 +396,17 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a) {
 }  // namespace
 
 // Rows per workgroup tile: 64 for a layer projection with between a half and one
-// 128-row tile per CU (the 64-row tiles then fill the chip without a K split), else 128,
-// and always 128 for the LM head (its statistics come in 128-column groups of 128-row
-// tiles).  Measured: with 1.5-2 tiles of 128 rows per CU the 64-row tiles were slower,
-// bound by LDS bandwidth at their lower reuse, and fewer tiles are better split in K.
-static int tile_bm(int epi, int M, int N) {
+// 128-row tile per CU (the 64-row tiles then fill the chip without a K split), except a
+// deep contraction (K >= 4 N, the MLP down projection), which keeps 128-row tiles and
+// splits K in two instead (measured at 2048 x 2048 x 8192: 151 us against 194 us in
+// 64-row tiles); else 128, and always 128 for the LM head (its statistics come in
+// 128-column groups of 128-row tiles).  Measured: with 1.5-2 tiles of 128 rows per CU the
+// 64-row tiles were slower, bound by LDS bandwidth at their lower reuse, and fewer tiles
+// are better split in K.
+static int tile_bm(int epi, int M, int N, int K) {
   if (epi == EPI_VSTAT) return 128;
   const int t128 = (N / BN) * ((M + 127) / 128);
-  return t128 > 128 && t128 <= 256 ? 64 : 128;
+  return t128 > 128 && t128 <= 256 && K < 4 * N ? 64 : 128;
 }
 
 bool gemm_tile_supported(int dtype, int M, int N, int K) {
@@ -347,10 +419,10 @@ int gemm_tile_slices(int N) { return N / BN; }
 // split): measured, a grid of 256 tiles runs faster whole than split in two.  (For the
 // layer projections, the only ones split.)
 int gemm_tile_splits(int M, int N, int K) {
-  const int bm = tile_bm(EPI_STORE, M, N);
+  const int bm = tile_bm(EPI_STORE, M, N, K);
   const int tiles = (N / BN) * ((M + bm - 1) / bm);
   int s = 1;
-  if (tiles >= 256) return s;
+  if (tiles >= 512 || (tiles >= 256 && K < 4 * N)) return s;
   while (tiles * s < 512 && (K / 32) / (2 * s) >= 8) s *= 2;
   return s;
 }
@@ -375,9 +447,10 @@ hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a, hipStream_t s
   if (a.done == nullptr) return hipErrorInvalidValue;
   if (norm && (a.ssq == nullptr || a.norm_nparts <= 0)) return hipErrorInvalidValue;
   if ((epi == EPI_GELU || epi == EPI_RESID) && a.out_afl == nullptr) return hipErrorInvalidValue;
-  const int bm = tile_bm(epi, a.M, a.N);
+  const int bm = tile_bm(epi, a.M, a.N, a.K);
+  if ((a.n_rows == nullptr) != (a.rowlist == nullptr)) return hipErrorInvalidValue;
   if (a.splits > 1) {
-    if (epi == EPI_VSTAT || a.part == nullptr || a.n_rows != nullptr) return hipErrorInvalidValue;
+    if (epi == EPI_VSTAT || a.part == nullptr) return hipErrorInvalidValue;
     const dim3 pgrid(a.N / BN, (a.M + bm - 1) / bm, a.splits);
     if (bm == 64) hipLaunchKernelGGL((gemm_tile_kernel<EPI_PART, false, 64>), pgrid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((gemm_tile_kernel<EPI_PART, false, 128>), pgrid, dim3(256), 0, s, a);

@@ -94,15 +94,18 @@ TD_DEV void commit_all(const CommitArgs &a, int *s_wave) {
     if (in && p == 0) a.st.seq_done[r / a.B] = rem ? 0 : 1;
   }
   __syncthreads();
-  // Rows still masked, in row order, for the next step.
-  int base = 0;
+  // Rows still masked, in row order, for the next step, and the rows of the sequences
+  // still active (the next step's layer GEMMs compute only those).
+  int base = 0, act = 0;
   for (int r0 = 0; r0 < M; r0 += blockDim.x) {
     const int r = r0 + threadIdx.x;
     const bool masked = r < M && !a.committed[r];
     base = block_compact(masked, base, a.st.rowlist, a.st.rowpos, r < M ? r : -1, s_wave);
+    act = block_compact(r < M && !a.st.seq_done[r / a.B], act, a.st.act_rows, nullptr, r < M ? r : -1, s_wave);
   }
   if (threadIdx.x == 0) {
     *a.st.n_rows = base;
+    *a.st.n_act = act;
     *a.st.done = base == 0 ? 1 : 0;
     *a.st.t = t + 1;
     if (a.host_progress)   // one word, system scope: the host polls it while issuing steps

@@ -25,7 +25,7 @@ __global__ void pack_weight_kernel(const T *__restrict__ W, T *__restrict__ Wp, 
 __global__ __launch_bounds__(1024) void prep_kernel(const int *tokens, const uint8_t *committed, int M, int B,
                                                     int V, StepState st) {
   __shared__ int s_wave[16];
-  int base = 0, err = 0;
+  int base = 0, act = 0, err = 0;
   for (int r0 = 0; r0 < M; r0 += 1024) {
     const int r = r0 + threadIdx.x;
     bool masked = false;
@@ -43,10 +43,13 @@ __global__ __launch_bounds__(1024) void prep_kernel(const int *tokens, const uin
     for (int o = 1; o < B; o <<= 1) any |= __shfl_xor(any, o);
     if (r < M && r % B == 0) st.seq_done[r / B] = any ? 0 : 1;
     base = block_compact(masked, base, st.rowlist, st.rowpos, r < M ? r : -1, s_wave);
+    // rows of the sequences still active (the layer GEMMs compute only these)
+    act = block_compact(r < M && any, act, st.act_rows, nullptr, r < M ? r : -1, s_wave);
   }
   if (err) atomicOr(st.err, 1);
   if (threadIdx.x == 0) {
     *st.n_rows = base;
+    *st.n_act = act;
     *st.done = base == 0 ? 1 : 0;
   }
 }
@@ -60,6 +63,7 @@ __global__ __launch_bounds__(1024) void init_block_kernel(int *tokens, uint8_t *
     if (commit_step) commit_step[r] = -1;
     st.rowlist[r] = r;
     st.rowpos[r] = r;
+    st.act_rows[r] = r;
   }
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     if (steps) steps[i] = 0;
@@ -67,6 +71,7 @@ __global__ __launch_bounds__(1024) void init_block_kernel(int *tokens, uint8_t *
   }
   if (threadIdx.x == 0) {
     *st.n_rows = M;
+    *st.n_act = M;
     *st.done = M == 0 ? 1 : 0;
     *st.t = 0;
   }
@@ -132,7 +137,26 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const float *qkv, int Nq
   vc[((page * Hkv + h) * hd + e) * KV_PAGE + slot] = from_f32<T>(vv);
 }
 
+__global__ __launch_bounds__(256) void advance_kernel(AttnItem *items, const int *grow_idx, int n_pairs, int *seq_len,
+                                                     int n_seqs, int add) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_pairs) {
+    const int k = grow_idx[i];
+    if (k >= 0) items[k].k_end += add;
+  }
+  if (i < n_seqs) seq_len[i] += add;
+}
+
 }  // namespace
+
+hipError_t launch_advance(AttnItem *items, const int *grow_idx, int n_pairs, int *seq_len, int n_seqs, int add,
+                          hipStream_t s) {
+  const int n = n_pairs > n_seqs ? n_pairs : n_seqs;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(advance_kernel, dim3((n + 255) / 256), dim3(256), 0, s, items, grow_idx, n_pairs, seq_len, n_seqs,
+                     add);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(int dtype, const float *qkv, int Nqkv, int H, int Hkv, int hd, void *kc, void *vc,
                             const int *seq_len, const int *seq_page, int n, int B, hipStream_t s) {

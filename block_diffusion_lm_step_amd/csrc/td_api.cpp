@@ -81,7 +81,7 @@ struct td_ctx {
   // output, au = GELU output of the MLP up projection.
   void *ah = nullptr, *ao = nullptr, *au = nullptr;
   int *arg_row = nullptr;
-  int *state_ints = nullptr;    // rowlist | rowpos | n_rows, done, t, err
+  int *state_ints = nullptr;    // rowlist | rowpos | act_rows | n_rows, done, t, err, n_act
   StepState st{};
   GemmPlan p_qkv, p_wo, p_w1, p_w2, p_lm;
 
@@ -92,6 +92,14 @@ struct td_ctx {
   std::vector<const void *> kc, vc;
   AttnItem *items_d = nullptr;
   int *pair_first_d = nullptr, *pair_count_d = nullptr;
+  // Appending tokens (td_append_block, td_ar_step) extends each pair's last prefix item on
+  // the device (grow_idx_d: its index in items_d, or -1 if the pair has none); the host
+  // follows the lengths and rebuilds the list only when such an item has grown past
+  // twice the chunk size.
+  int *grow_idx_d = nullptr;
+  std::vector<int> grow_len;            // tokens of each pair's growing item
+  std::vector<char> grow_ok;            // the pair has an item that can grow
+  int chunk = 0;                        // tokens per split-K item of the binding
   int n_items = 0, n_pairs = 0;
   size_t items_cap = 0, pairs_cap = 0;
   float *att_o = nullptr, *att_ml = nullptr;
@@ -111,6 +119,7 @@ struct td_ctx {
   // pair tagged kind | sub << 8 | layer << 16
   unsigned prof_mask = 0;
   int prof_layer = 0;                 // layer of the launches being enqueued
+  int prof_only_layer = -1;           // >= 0: per-layer classes bracketed on this layer only
   long prof_open[TD_PROF_KINDS] = {}; // slot of the open bracket of each kind, or -1
   std::vector<hipEvent_t> ev_start, ev_stop;
   std::vector<int32_t> ev_tag;
@@ -274,6 +283,9 @@ constexpr size_t PROF_MAX = 65536;
 // launches of a class apart (the layer projections).
 td_status prof_mark(td_ctx *c, int kind, bool start, int sub = 0) {
   if (!(c->prof_mask & (1u << kind))) return TD_OK;
+  const bool per_layer = kind == TD_PROF_GEMM || kind == TD_PROF_ATTENTION || kind == TD_PROF_ATTN_MERGE ||
+                         kind == TD_PROF_MOE;
+  if (per_layer && c->prof_only_layer >= 0 && c->prof_layer != c->prof_only_layer) return TD_OK;
   if (start) {
     c->prof_open[kind] = -1;
     if (c->prof_n >= PROF_MAX) return TD_OK;
@@ -366,6 +378,13 @@ td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const
   a.done = c->gemm_done ? c->gemm_done : c->st.done;
   a.splits = epi == EPI_VSTAT ? 1 : p.splits;
   a.part = c->part;
+  // A denoising step over several sequences computes only the rows of the sequences that
+  // still have a masked position (a finished sequence's rows are never read again); the
+  // context pass (its own loop-exit flag) computes every row.
+  if (p.tile && epi != EPI_VSTAT && !c->gemm_done && c->n_seqs > 1 && !a.rowlist) {
+    a.rowlist = c->st.act_rows;
+    a.n_rows = c->st.n_act;
+  }
   if (p.tile) {
     if (epi != EPI_VSTAT) TD_TRY(prof_mark(c, TD_PROF_GEMM, true, prof_sub));
     TD_HIP(c, launch_gemm_tile(epi, norm, a, c->stream));
@@ -597,6 +616,12 @@ td_status check_ctx(td_ctx *c) {
   return TD_OK;
 }
 
+td_status check_mlp(td_ctx *c) {
+  if (!c->moe && (c->layers.w1.empty() || !c->layers.w1[0]))
+    return fail(c, TD_EINVAL, "the denoiser has no MLP weights: pass w1/w2 to td_create or call td_set_moe");
+  return TD_OK;
+}
+
 td_status check_bound(td_ctx *c) {
   if (c->n_seqs <= 0) return fail(c, TD_EINVAL, "no prefix bound: call td_set_prefix first");
   TD_HIP(c, hipSetDevice(c->dev));
@@ -632,7 +657,7 @@ void free_all(td_ctx *c) {
   f(c->ctx_tok_emb); f(c->ctx_final_norm); f(c->ctx_lm_head); f(c->ar_committed); f(c->st.seq_done); f(c->zero_seq); f(c->zero_flag); f(c->seq_lp_d);
   f(c->x); f(c->ssq); f(c->conf_row); f(c->vpart); f(c->qkv); f(c->ah); f(c->ao); f(c->au);
   f(c->arg_row); f(c->state_ints); f(c->items_d); f(c->pair_first_d);
-  f(c->pair_count_d); f(c->att_o); f(c->att_ml); f(c->part);
+  f(c->pair_count_d); f(c->grow_idx_d); f(c->att_o); f(c->att_ml); f(c->part);
   free_moe(c);
   for (hipEvent_t e : c->ev_start) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->ev_stop) (void)hipEventDestroy(e);
@@ -715,15 +740,17 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
   TD_HIP(c, hipMemsetAsync(c->zero_seq, 0, g.max_batch * sizeof(int), c->stream));
   TD_TRY(dmalloc(c, &c->zero_flag, sizeof(int)));
   TD_HIP(c, hipMemsetAsync(c->zero_flag, 0, sizeof(int), c->stream));
-  TD_TRY(dmalloc(c, &c->state_ints, (2 * M + 8) * sizeof(int)));
-  TD_HIP(c, hipMemsetAsync(c->state_ints, 0, (2 * M + 8) * sizeof(int), c->stream));
+  TD_TRY(dmalloc(c, &c->state_ints, (3 * M + 8) * sizeof(int)));
+  TD_HIP(c, hipMemsetAsync(c->state_ints, 0, (3 * M + 8) * sizeof(int), c->stream));
   int *si = c->state_ints;
   c->st.rowlist = si;
   c->st.rowpos = si + M;
-  c->st.n_rows = si + 2 * M;
-  c->st.done = si + 2 * M + 1;
-  c->st.t = si + 2 * M + 2;
-  c->st.err = si + 2 * M + 3;
+  c->st.act_rows = si + 2 * M;
+  c->st.n_rows = si + 3 * M;
+  c->st.done = si + 3 * M + 1;
+  c->st.t = si + 3 * M + 2;
+  c->st.err = si + 3 * M + 3;
+  c->st.n_act = si + 3 * M + 4;
   TD_HIP(c, hipStreamSynchronize(c->stream));
   return TD_OK;
 }
@@ -731,7 +758,6 @@ td_status create_impl(td_ctx *c, const td_config &g, const td_weights &w) {
 }  // namespace
 
 // ---------------------------------------------------------------- steps on caller-side scratch
-static td_status check_mlp(td_ctx *c);
 
 namespace td {
 
@@ -869,16 +895,23 @@ static td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const 
   // so the item count is the prefix pages' alone); grouped-query path: a block item last.
   const bool few = R <= ATTN_FEW_ROWS;
   std::vector<AttnItem> items;
-  std::vector<int> pfirst, pcount;
+  std::vector<int> pfirst, pcount, grow_slot;
+  std::vector<int> grow_len;
   int64_t page_base = 0;   // first cache page of sequence i
   for (int i = 0; i < n_seqs; ++i) {
     const int64_t P = off[i + 1] - off[i];
     for (int h = 0; h < g.n_kv_heads; ++h) {
       pfirst.push_back((int)items.size());
       if (few && P == 0) items.push_back(AttnItem{i, h, 0, 0, 2, 0, page_base});
+      // A grouped-query pair with no prefix but room to grow gets an empty prefix item,
+      // which appended tokens extend.
+      if (!few && P == 0 && cap[i] > 0) items.push_back(AttnItem{i, h, 0, 0, 0, 0, page_base});
       for (int64_t k0 = 0; k0 < P; k0 += tc)
         items.push_back(AttnItem{i, h, (int)k0, (int)std::min<int64_t>(P, k0 + tc), (few && k0 == 0) ? 2 : 0, 0,
                                  page_base + k0 / KV_PAGE});
+      const bool has_prefix_item = (int)items.size() > pfirst.back();
+      grow_slot.push_back(has_prefix_item ? (int)items.size() - 1 : -1);
+      grow_len.push_back(has_prefix_item ? items.back().k_end - items.back().k_begin : 0);
       if (!few) items.push_back(AttnItem{i, h, 0, 0, 1, 0, 0});
       pcount.push_back((int)items.size() - pfirst.back());
     }
@@ -892,6 +925,9 @@ static td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const 
   std::stable_sort(items.begin(), items.end(), [](const AttnItem &x, const AttnItem &y) {
     return x.k_end - x.k_begin > y.k_end - y.k_begin;
   });
+  std::vector<int> at_slot(items.size()), grow_idx(grow_slot.size());
+  for (size_t k = 0; k < items.size(); ++k) at_slot[items[k].slot] = (int)k;
+  for (size_t p = 0; p < grow_slot.size(); ++p) grow_idx[p] = grow_slot[p] >= 0 ? at_slot[grow_slot[p]] : -1;
   auto grow = [&](auto **p, size_t &cap, size_t need, size_t elt) -> td_status {
     if (need <= cap) return TD_OK;
     if (*p) TD_HIP(c, hipFree(*p));
@@ -904,10 +940,11 @@ static td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const 
   size_t cap_items = c->items_cap;
   TD_TRY(grow(&c->items_d, cap_items, items.size(), sizeof(AttnItem)));
   c->items_cap = cap_items;
-  size_t cap_pairs = c->pairs_cap, cap_pairs2 = c->pairs_cap;
+  size_t cap_pairs = c->pairs_cap, cap_pairs2 = c->pairs_cap, cap_pairs3 = c->pairs_cap;
   TD_TRY(grow(&c->pair_first_d, cap_pairs, pfirst.size(), sizeof(int)));
   TD_TRY(grow(&c->pair_count_d, cap_pairs2, pcount.size(), sizeof(int)));
-  c->pairs_cap = std::min(cap_pairs, cap_pairs2);
+  TD_TRY(grow(&c->grow_idx_d, cap_pairs3, grow_idx.size(), sizeof(int)));
+  c->pairs_cap = std::min(cap_pairs, std::min(cap_pairs2, cap_pairs3));
   const size_t rows = items.size() * (size_t)R;
   size_t cap_o = c->att_cap_rows, cap_ml = c->att_cap_rows;
   TD_TRY(grow(&c->att_o, cap_o, rows, (size_t)g.head_dim * 4));
@@ -916,6 +953,7 @@ static td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const 
   TD_HIP(c, hipMemcpy(c->items_d, items.data(), items.size() * sizeof(AttnItem), hipMemcpyHostToDevice));
   TD_HIP(c, hipMemcpy(c->pair_first_d, pfirst.data(), pfirst.size() * sizeof(int), hipMemcpyHostToDevice));
   TD_HIP(c, hipMemcpy(c->pair_count_d, pcount.data(), pcount.size() * sizeof(int), hipMemcpyHostToDevice));
+  TD_HIP(c, hipMemcpy(c->grow_idx_d, grow_idx.data(), grow_idx.size() * sizeof(int), hipMemcpyHostToDevice));
   {  // GEMM plans for this batch size
     const int M = n_seqs * g.block_size;
     const int d = g.d_model, F = g.d_ff, Hd = g.n_heads * g.head_dim;
@@ -950,6 +988,32 @@ static td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const 
   c->n_items = (int)items.size();
   c->n_pairs = (int)pfirst.size();
   c->n_seqs = n_seqs;
+  c->grow_len = grow_len;
+  c->grow_ok.assign(grow_idx.size(), 0);
+  for (size_t p = 0; p < grow_idx.size(); ++p) c->grow_ok[p] = grow_idx[p] >= 0;
+  c->chunk = tc;
+  return TD_OK;
+}
+
+// Every bound sequence grew by `add` tokens (appended to the caches by the work already
+// enqueued).  Extends each pair's last prefix item and the device lengths with one small
+// kernel, without waiting; rebuilds the binding (which waits for the stream) only when a
+// pair has no item that can grow or an item would exceed twice the chunk size.
+static td_status advance_binding(td_ctx *c, int add) {
+  bool rebuild = false;
+  for (size_t p = 0; p < c->grow_len.size(); ++p) {
+    if (!c->grow_ok[p] || c->grow_len[p] + add > 2 * c->chunk) rebuild = true;
+  }
+  std::vector<int64_t> len = c->lengths;
+  for (auto &v : len) v += add;
+  if (rebuild) {
+    const std::vector<int64_t> cap = c->caps;
+    const std::vector<const void *> kc = c->kc, vc = c->vc;
+    return bind_impl(c, c->n_seqs, len.data(), cap.data(), kc.data(), vc.data());
+  }
+  TD_HIP(c, launch_advance(c->items_d, c->grow_idx_d, c->n_pairs, c->seq_lp_d, c->n_seqs, add, c->stream));
+  for (auto &v : c->grow_len) v += add;
+  c->lengths = len;
   return TD_OK;
 }
 
@@ -977,12 +1041,6 @@ td_status td_bind_cache(td_ctx *c, int32_t n_seqs, const int64_t *lengths_host, 
   if (!lengths_host || !page_capacity_host || !k_cache_host || !v_cache_host)
     return fail(c, TD_EINVAL, "NULL lengths, capacities or cache array");
   return bind_impl(c, n_seqs, lengths_host, page_capacity_host, k_cache_host, v_cache_host);
-}
-
-static td_status check_mlp(td_ctx *c) {
-  if (!c->moe && (c->layers.w1.empty() || !c->layers.w1[0]))
-    return fail(c, TD_EINVAL, "the denoiser has no MLP weights: pass w1/w2 to td_create or call td_set_moe");
-  return TD_OK;
 }
 
 td_status td_denoise_step(td_ctx *c, int32_t *tokens, uint8_t *committed, const float *inv_temp, float gamma,
@@ -1120,9 +1178,7 @@ td_status td_append_block(td_ctx *c, const int32_t *tokens) {
     len[i] += B;
   }
   TD_TRY(enqueue_context_pass(c, tokens));
-  const std::vector<int64_t> cap = c->caps;
-  const std::vector<const void *> kc = c->kc, vc = c->vc;
-  return bind_impl(c, c->n_seqs, len.data(), cap.data(), kc.data(), vc.data());
+  return advance_binding(c, B);
 }
 
 td_status td_ar_step(td_ctx *c, int32_t *tokens) {
@@ -1145,9 +1201,7 @@ td_status td_ar_step(td_ctx *c, int32_t *tokens) {
   TD_HIP(c, launch_init_block(tokens, c->ar_committed, nullptr, nullptr, c->n_seqs, 1, g.vocab, c->st, c->stream));
   TD_TRY(enqueue_head_commit(c, c->ctx_lm_head, tokens, c->ar_committed, nullptr, 0.f, RULE_THRESHOLD, 1, nullptr,
                              nullptr, nullptr, nullptr, nullptr, nullptr));
-  const std::vector<int64_t> cap = c->caps;
-  const std::vector<const void *> kc = c->kc, vc = c->vc;
-  return bind_impl(c, c->n_seqs, len.data(), cap.data(), kc.data(), vc.data());
+  return advance_binding(c, 1);
 }
 
 static td_status set_moe_impl(td_ctx *c, const td_moe_config &m, const td_moe_weights &w) {
@@ -1304,6 +1358,13 @@ td_status td_profile_begin(td_ctx *c, int32_t kinds_mask) {
   if (kinds_mask & ~((1 << TD_PROF_KINDS) - 1)) return fail(c, TD_EINVAL, "unknown profiling kinds in mask 0x%x", kinds_mask);
   c->prof_mask = (unsigned)kinds_mask & ~1u;   // bit 0 (TD_PROF_OFF) brackets nothing
   for (long &o : c->prof_open) o = -1;
+  return TD_OK;
+}
+
+td_status td_profile_layer(td_ctx *c, int32_t layer) {
+  TD_TRY(check_ctx(c));
+  if (layer < -1 || layer >= c->cfg.n_layers) return fail(c, TD_EINVAL, "layer must be in [-1, n_layers)");
+  c->prof_only_layer = layer;
   return TD_OK;
 }
 

@@ -180,6 +180,24 @@ template <> TD_DEV void afl_put8<float>(void *buf, int KT, int row, int k, const
   p[0] = make_float4(v[0], v[1], v[2], v[3]);
   p[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
+// Elements k .. k+3 (k a multiple of 4) of one row: half of a fragment's columns.
+template <typename T> TD_DEV void afl_put4(void *buf, int KT, int row, int k, const float *v);
+template <> TD_DEV void afl_put4<bf16_t>(void *buf, int KT, int row, int k, const float *v) {
+  uint32_t hi[2], lo[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const bf16_t h0 = f2bf(v[2 * e]), h1 = f2bf(v[2 * e + 1]);
+    hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lo[e] = (uint32_t)f2bf(v[2 * e] - bf2f(h0)) | ((uint32_t)f2bf(v[2 * e + 1] - bf2f(h1)) << 16);
+  }
+  char *f = reinterpret_cast<char *>(buf) + afl_frag(row, k, KT) + (k & 7) * 2;
+  *reinterpret_cast<uint2 *>(f) = make_uint2(hi[0], hi[1]);
+  *reinterpret_cast<uint2 *>(f + 16) = make_uint2(lo[0], lo[1]);
+}
+template <> TD_DEV void afl_put4<float>(void *buf, int KT, int row, int k, const float *v) {
+  *reinterpret_cast<float4 *>(reinterpret_cast<char *>(buf) + afl_frag(row, k, KT) + (k & 7) * 4) =
+      make_float4(v[0], v[1], v[2], v[3]);
+}
 template <typename T> TD_DEV AFrag<T> afl_get(const void *frag);
 template <> TD_DEV AFrag<bf16_t> afl_get<bf16_t>(const void *frag) {
   AFrag<bf16_t> f;
@@ -280,7 +298,8 @@ TD_DEV float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.7071067811
 
 // Exclusive position of each flagged row among the flagged rows, in row order.
 // Called by every thread of one workgroup, once per chunk of blockDim.x rows; `row` < 0
-// marks a thread past the end.  s_wave holds blockDim.x / 64 ints of LDS.
+// marks a thread past the end.  s_wave holds blockDim.x / 64 ints of LDS.  rowpos may be
+// null (no inverse map kept).
 TD_DEV int block_compact(bool flag, int base, int *rowlist, int *rowpos, int row, int *s_wave) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const unsigned long long mask = __ballot(flag);
@@ -293,8 +312,8 @@ TD_DEV int block_compact(bool flag, int base, int *rowlist, int *rowpos, int row
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) total += s_wave[w];
   if (flag) {
     rowlist[off + before] = row;
-    rowpos[row] = off + before;
-  } else if (row >= 0) {
+    if (rowpos) rowpos[row] = off + before;
+  } else if (row >= 0 && rowpos) {
     rowpos[row] = -1;
   }
   __syncthreads();

@@ -91,6 +91,7 @@ constexpr int KV_PAGE = 32;
 // waves per item straight from HBM); more rows take the grouped-query path.
 constexpr int ATTN_FEW_ROWS = 32;
 
+
 // One split-K work item of a (seq, kv head) pair: prefix tokens [k_begin, k_end)
 // (k_begin a multiple of the page size, first page page0 of the cache) and/or the
 // block's own keys.  The slots of a pair's items are consecutive; the items array is in
@@ -131,6 +132,8 @@ struct StepState {                 // device-resident loop state owned by the ct
   int *rowlist;                    // [M] rows (seq*B + p) still masked, ascending
   int *rowpos;                     // [M] index of each row in rowlist, or -1
   int *n_rows;                     // number of masked rows
+  int *act_rows;                   // [M] rows of the sequences that still have a masked position, ascending
+  int *n_act;                      // number of such rows (the layer GEMMs' live rows)
   int *done;                       // 1 when no row is masked
   int *t;                          // step counter of td_generate_block
   int *err;                        // device-side input error flags
@@ -168,6 +171,10 @@ hipError_t launch_merge_commit(const CommitArgs &a, int max_rows, hipStream_t s)
 // K/V of the block rows of qkv ([n*B][Nqkv] fp32: q | k | v) appended to one layer's cache
 // (layout above; bf16 caches round to nearest even): row seq*B + p is token
 // seq_len[seq] + p of sequence seq, whose pages start at seq_page[seq].
+// Every bound sequence grew by `add` appended tokens: items[grow_idx[p]].k_end += add for
+// each pair p with grow_idx[p] >= 0, and seq_len[s] += add for each sequence.
+hipError_t launch_advance(AttnItem *items, const int *grow_idx, int n_pairs, int *seq_len, int n_seqs, int add,
+                          hipStream_t s);
 hipError_t launch_kv_append(int dtype, const float *qkv, int Nqkv, int H, int Hkv, int hd, void *kc, void *vc,
                             const int *seq_len, const int *seq_page, int n, int B, hipStream_t s);
 

@@ -18,9 +18,9 @@
  *  - Every buffer pointer is a DEVICE pointer unless its name ends in _host.
  *  - All calls enqueue work on the stream given to td_create and return without
  *    waiting, except where a call's comment says it waits (the binding and setup
- *    calls, td_append_block, td_ar_step, td_moe_stats, and td_generate_block under an
- *    issue window, td_set_issue_window); results are valid once that stream has
- *    synchronised (td_sync).
+ *    calls, td_moe_stats, td_generate_block under an issue window, and td_append_block /
+ *    td_ar_step when they rebuild the work lists); results are valid once that stream
+ *    has synchronised (td_sync).
  *  - A ctx is bound to one device and one stream and is not thread-safe.
  *  - Every call returns td_status; no C++ exception crosses the ABI.  Arguments are
  *    validated on the host before anything is enqueued (TD_EINVAL, nothing runs).
@@ -148,7 +148,8 @@ td_status td_set_context_tower(td_ctx *ctx, const td_weights *w);
  * the bound lengths advance by 1, and tokens receives the prediction: the lowest id of
  * the largest logit (greedy).  Needs a ctx created with block_size 1, a context tower
  * with final_norm and lm_head, and a binding with room for one more token per sequence;
- * otherwise TD_EINVAL and nothing is enqueued.  Waits for the ctx's stream. */
+ * otherwise TD_EINVAL and nothing is enqueued.  Returns without waiting, like
+ * td_append_block (the same work-list growth and rebuild rule, for one token). */
 td_status td_ar_step(td_ctx *ctx, int32_t *tokens);
 
 /* Append a committed block to the prefix (the loop of multi-block generation): run the
@@ -159,8 +160,11 @@ td_status td_ar_step(td_ctx *ctx, int32_t *tokens);
  * to nearest even), then advance every bound length by B and rebuild the work lists.
  * The next td_generate_block then continues after the appended block.  Needs
  * td_set_context_tower and a binding with room for B more tokens per sequence
- * (td_bind_cache); otherwise TD_EINVAL and nothing is enqueued.  Waits for the ctx's
- * stream before returning (the work lists are rebuilt on the host). */
+ * (td_bind_cache); otherwise TD_EINVAL and nothing is enqueued.  Returns without waiting:
+ * each (sequence, K/V head)'s last split-K item of the prefix is extended on the device.
+ * Only when such an item would exceed twice the binding's chunk size (or a pair has no
+ * prefix item to extend) are the work lists rebuilt on the host, which waits for the
+ * stream. */
 td_status td_append_block(td_ctx *ctx, const int32_t *tokens);
 
 /* Mixture-of-experts MLP of the denoiser (dzen.guru, section "Что нового": the tower's
@@ -314,6 +318,12 @@ typedef enum {
  * most 65536 brackets (later launches are not recorded).  Errors: TD_EINVAL for bits
  * past TD_PROF_KINDS. */
 td_status td_profile_begin(td_ctx *ctx, int32_t kinds_mask);
+
+/* Bracket the per-layer classes (projections, attention, merge, experts) on one layer
+ * only (layer in [0, n_layers)), or on every layer (-1, the default): fewer events on the
+ * stream where they would perturb short launches.  Errors: TD_EINVAL (layer out of range,
+ * NULL ctx). */
+td_status td_profile_layer(td_ctx *ctx, int32_t layer);
 
 /* Wait for the stream, write the duration in ms of each bracketed launch, in launch order,
  * to ms_out_host[0 .. min(count, max)) and its tag (class | sub << 8 | layer << 16) to

@@ -81,6 +81,7 @@ def test_null_ctx_calls_are_rejected(td):
     assert td.lib.td_debug_attention(None, 0, None, None) == td.TD_EINVAL
     assert td.lib.td_sync(None) == td.TD_EINVAL
     assert td.lib.td_profile_begin(None, 1) == td.TD_EINVAL
+    assert td.lib.td_profile_layer(None, 0) == td.TD_EINVAL
     assert td.lib.td_profile_end(None, None, None, 0) == -1
     assert td.lib.td_kernels_per_step(None) == -1
     assert td.lib.td_set_commit_rule(None, 0, 1) == td.TD_EINVAL

@@ -24,6 +24,13 @@ CASES = {
     # R = G * B = 128 query rows per K/V head: the grouped-query attention path, causal block item.
     "bf16_n2_b32_gqa": dict(n=2, plen=("uniform", 1, 50), B=32, d=256, H=8, Hkv=2, hd=64, L=2, F=1024, V=4096,
                             dtype="bf16"),
+    # Grouped-query pairs with no prefix at all: the empty prefix item that appended blocks extend.
+    "bf16_n2_b32_gqa_empty": dict(n=2, plen=("fixed", 0), B=32, d=256, H=8, Hkv=2, hd=64, L=2, F=1024, V=4096,
+                                  dtype="bf16"),
+    # Prefixes of ~490 tokens (split-K chunks of 256): the last chunk grows by 32 per block and
+    # passes twice the chunk size at the ninth block, where the work lists are rebuilt.
+    "bf16_n2_b32_grow": dict(n=2, plen=("uniform", 480, 500), B=32, d=256, H=4, Hkv=4, hd=64, L=2, F=1024, V=4096,
+                             dtype="bf16", blocks=10),
 }
 
 
@@ -44,8 +51,9 @@ def mb(request):
     from synth import get_workload
     m = MB()
     if request.param in CASES:
-        m.w = w = Workload(name=request.param, tower="mb_" + request.param, weight_std=0.02, **CASES[request.param])
-        m.blocks = N_BLOCKS
+        kw = dict(CASES[request.param])
+        m.blocks = kw.pop("blocks", N_BLOCKS)
+        m.w = w = Workload(name=request.param, tower="mb_" + request.param, weight_std=0.02, **kw)
     else:   # full size: the single-sequence 4096-prefix workload, two blocks
         m.w = w = get_workload(request.param)
         m.blocks = 2
