@@ -53,7 +53,7 @@ namespace {
 
 constexpr int SUB = KV_PAGE;   // keys per page
 // Pages in flight per wave in the few-row kernel (measured: three were slower at every
-// shape, batch 1 to 64 x 4096).
+// shape, batch 1 to 64 x 4096, with one row tile and with two).
 constexpr int DIRECT_DEPTH = 2;
 constexpr int BMAX = 32;       // largest block size
 
@@ -76,49 +76,138 @@ TD_DEV void mask_v(Frag<T> &f, int g, int kvalid) {
   f.set8(v);
 }
 
-// Online-softmax update of one 16-row tile with one page: S^T from the key fragments,
-// probabilities, P.V into o.
+// The queries enter the page products pre-scaled by scale * log2(e), so that the scores
+// and the running maxima of the prefix pages are in base-2 units and the probabilities
+// are single exp2 instructions; a partial's maximum is turned back into natural units
+// (times ln 2) where it leaves the kernel or meets the block pass's state.
+constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+
+// Online-softmax update of one 16-row tile with one page of 32 keys, from its scores
+// S^T (lane group g holding keys 8g .. 8g + 7; vis(key): the key is visible to this
+// lane's query row, at least one per row) and pv(pf, o), which adds V^T . P^T for the
+// probability fragment pf into o.  The running state is rescaled only when the maximum
+// of some row of the wave grew: the factor is exactly 1 for every other row, so skipping
+// it changes no bit.
+template <typename T, int OT, typename VIS, typename PV>
+TD_DEV void softmax_page(const f32x4_t (&st)[2], int g, VIS &&vis, float &m_run, float &l_run, f32x4_t (&o)[OT],
+                         PV &&pv) {
+  float sc[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = vis(8 * g + 4 * h + r) ? st[h][r] : -INFINITY;
+      sc[4 * h + r] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = max_groups(mx);
+  // m_new is finite (a visible key per row), so exp2(-inf - m_new) = 0 covers both the
+  // hidden keys and the first page (m_run = -inf).
+  const float m_new = fmaxf(m_run, mx);
+  float p[8], psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = __builtin_amdgcn_exp2f(sc[j] - m_new);
+    psum += p[j];
+  }
+  if (__ballot(m_new > m_run)) {   // wave-uniform
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < OT; ++t) o[t] *= alpha;
+  }
+  l_run += psum;
+  m_run = m_new;
+  AFrag<T> pf;
+  pf.set8(p);
+  pv(pf, o);
+}
+
+// A prefix page: S^T from the bf16 key fragments, P.V from the value fragments.  FULL:
+// all SUB keys of the page are valid.
 template <typename T, int HD>
 struct PageMath {
   static constexpr int HC = HD / 32, OT = HD / 16;
-  template <typename KF, typename VF>
-  TD_DEV static void run(const KF &kfrag, const VF &vfrag, const AFrag<T> (&qf)[HC], float scale, int kvalid,
-                         int g, float &m_run, float &l_run, f32x4_t (&o)[OT]) {
+  template <bool FULL, typename KF, typename VF>
+  TD_DEV static void run(const KF &kfrag, const VF &vfrag, const AFrag<T> (&qf)[HC], int kvalid, int g,
+                         float &m_run, float &l_run, f32x4_t (&o)[OT]) {
     f32x4_t st[2] = {zero4(), zero4()};
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int c = 0; c < HC; ++c) st[h] = mma_b(kfrag(h, c), qf[c], st[h]);
-    float sc[8];
-    float mx = -INFINITY;
+    softmax_page<T>(st, g, [&](int key) { return FULL || key < kvalid; }, m_run, l_run, o,
+                    [&](const AFrag<T> &pf, f32x4_t(&oo)[OT]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = 8 * g + 4 * h + r;
-        const float v = key < kvalid ? st[h][r] * scale : -INFINITY;
-        sc[4 * h + r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = max_groups(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - m_new);
-    float pv[8], psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pv[j] = (sc[j] == -INFINITY) ? 0.f : __expf(sc[j] - m_new);
-      psum += pv[j];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < OT; ++t) o[t] *= alpha;
-    AFrag<T> pf;
-    pf.set8(pv);
-#pragma unroll
-    for (int t = 0; t < OT; ++t) o[t] = mma_b(vfrag(t), pf, o[t]);
+                      for (int t = 0; t < OT; ++t) oo[t] = mma_b(vfrag(t), pf, oo[t]);
+                    });
   }
 };
+
+// Product of two split operands: high x high + high x low + low x high (the dropped
+// low x low term is below 2^-16 of the product); fp32 operands multiply as they are.
+TD_DEV f32x4_t mma_ab(const AFrag<bf16_t> &a, const AFrag<bf16_t> &b, f32x4_t acc) {
+  acc = mma(a.hi, b.hi, acc);
+  acc = mma(a.hi, b.lo, acc);
+  return mma(a.lo, b.hi, acc);
+}
+TD_DEV f32x4_t mma_ab(const AFrag<float> &a, const AFrag<float> &b, f32x4_t acc) { return mma(a.f, b.f, acc); }
+
+// Row strides (floats) of the block's keys [BMAX][BKS] and transposed values [HD][BVS]
+// staged in LDS: 16-byte aligned rows, so that a lane's eight consecutive elements are
+// two 16-byte reads.
+template <int HD> constexpr int bks() { return HD + 4; }
+constexpr int BVS = BMAX + 4;
+template <int HD> constexpr int block_page_lds() { return BMAX * bks<HD>() + HD * BVS; }   // floats
+
+// The block's own nb keys as one more page of the online softmax, on the matrix cores:
+// keys and values are fp32 activations, split into bf16 high and low parts (three
+// products per operand pair) and multiplied against the pre-scaled queries.  MFMA row i
+// of half h is key 8 (i / 4) + 4 h + i % 4, as in the prefix pages.  causal_p >= 0: the
+// row sees block keys 0..causal_p only (the frozen context tower's pass).
+template <typename T, int HD>
+TD_DEV void block_page(const float *s_k, const float *s_vt, const AFrag<T> (&qf)[HD / 32], int nb, int causal_p, int g,
+                       int l16, float &m_run, float &l_run, f32x4_t (&o)[HD / 16]) {
+  constexpr int HC = HD / 32, OT = HD / 16;
+  f32x4_t st[2] = {zero4(), zero4()};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float *kr = s_k + (8 * (l16 >> 2) + 4 * h + (l16 & 3)) * bks<HD>() + 8 * g;
+#pragma unroll
+    for (int c = 0; c < HC; ++c) {
+      float v[8];
+      const f32x4_t a = *reinterpret_cast<const f32x4_t *>(kr + 32 * c);
+      const f32x4_t b = *reinterpret_cast<const f32x4_t *>(kr + 32 * c + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = a[j];
+        v[4 + j] = b[j];
+      }
+      AFrag<T> kf;
+      kf.set8(v);
+      st[h] = mma_ab(kf, qf[c], st[h]);
+    }
+  }
+  softmax_page<T>(st, g, [&](int key) { return key < nb && (causal_p < 0 || key <= causal_p); }, m_run, l_run, o,
+                  [&](const AFrag<T> &pf, f32x4_t(&oo)[OT]) {
+#pragma unroll
+                    for (int t = 0; t < OT; ++t) {
+                      const float *vr = s_vt + (16 * t + l16) * BVS + 8 * g;
+                      float v[8];
+                      const f32x4_t a = *reinterpret_cast<const f32x4_t *>(vr);
+                      const f32x4_t b = *reinterpret_cast<const f32x4_t *>(vr + 4);
+#pragma unroll
+                      for (int j = 0; j < 4; ++j) {
+                        v[j] = a[j];
+                        v[4 + j] = b[j];
+                      }
+                      AFrag<T> vf;
+                      vf.set8(v);
+                      oo[t] = mma_ab(vf, pf, oo[t]);
+                    }
+                  });
+}
 
 // Query values of rows (rt0 + rt) * 16 + l16, dimensions c * 32 + g * 8 .. + 7, as fp32:
 // loads only, no branch (rows past R read row 0 and are zeroed by q_frags), so that
@@ -138,6 +227,7 @@ TD_DEV void load_q_raw(const AttnArgs &a, const AttnItem &it, int rt0, int g, in
 
 template <typename T, int HD, int RT>
 TD_DEV void q_frags(const AttnArgs &a, int rt0, int l16, const float (&v)[RT][HD / 32][8], AFrag<T> (&qf)[RT][HD / 32]) {
+  const float qs = a.scale * LOG2E;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const bool valid = (rt0 + rt) * 16 + l16 < a.R;
@@ -145,7 +235,7 @@ TD_DEV void q_frags(const AttnArgs &a, int rt0, int l16, const float (&v)[RT][HD
     for (int c = 0; c < HD / 32; ++c) {
       float w[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = valid ? v[rt][c][e] : 0.f;
+      for (int e = 0; e < 8; ++e) w[e] = valid ? v[rt][c][e] * qs : 0.f;
       qf[rt][c].set8(w);
     }
   }
@@ -153,6 +243,7 @@ TD_DEV void q_frags(const AttnArgs &a, int rt0, int l16, const float (&v)[RT][HD
 
 template <typename T, int HD, int RT>
 TD_DEV void load_q(const AttnArgs &a, const AttnItem &it, int rt0, int g, int l16, AFrag<T> (&qf)[RT][HD / 32]) {
+  const float qs = a.scale * LOG2E;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int rho = (rt0 + rt) * 16 + l16;
@@ -162,6 +253,8 @@ TD_DEV void load_q(const AttnArgs &a, const AttnItem &it, int rt0, int g, int l1
         const int j = rho / a.B, p = rho % a.B;
         float v[8];
         load8f(a.qkv + (size_t)(it.seq * a.B + p) * a.Nqkv + (size_t)(it.kvh * a.G + j) * HD + c * 32 + g * 8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= qs;
         qf[rt][c].set8(v);
       } else {
         qf[rt][c].zero();
@@ -170,7 +263,8 @@ TD_DEV void load_q(const AttnArgs &a, const AttnItem &it, int rt0, int g, int l1
   }
 }
 
-// Partial state of rows (rt0 + rt) * 16 + l16 -> the item's slot.
+// Partial state of rows (rt0 + rt) * 16 + l16 -> the item's slot (the maximum in natural
+// units).
 template <int HD, int RT>
 TD_DEV void store_partial(const AttnArgs &a, int item, int rt0, int g, int l16, const float (&m_run)[RT],
                           const float (&l_tot)[RT], const f32x4_t (&o)[RT][HD / 16]) {
@@ -180,7 +274,7 @@ TD_DEV void store_partial(const AttnArgs &a, int item, int rt0, int g, int l16, 
     if (rho < a.R) {
       const size_t prow = (size_t)item * a.R + rho;
       if (g == 0) {
-        a.part_ml[prow * 2 + 0] = m_run[rt];
+        a.part_ml[prow * 2 + 0] = m_run[rt] * LN2;
         a.part_ml[prow * 2 + 1] = l_tot[rt];
       }
 #pragma unroll
@@ -193,8 +287,10 @@ TD_DEV void store_partial(const AttnArgs &a, int item, int rt0, int g, int l16, 
 template <int HD> constexpr int block_item_lds() { return 2 * BMAX * (HD + 1); }   // floats
 
 // The block's own keys of one (sequence, K/V head) pair, fp32 on the VALU: 16 threads
-// per query row (HD/16 dimensions each), 16 rows at a time.  sm: block_item_lds floats
-// of LDS.  Writes the pair's block partial (m, l, o) to the item's slot.
+// per query row, thread `sub` of the row taking dimensions sub, sub + 16, ... (so that the
+// 16 threads read 16 consecutive LDS words: no bank conflict), NT/16 rows at a time.
+// sm: block_item_lds floats of LDS.  Writes the pair's block partial (m, l, o) to the
+// item's slot.
 template <int HD, int NT = 256>
 TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *sm) {
   constexpr int EPT = HD / 16, KPT = BMAX * HD / NT;
@@ -210,15 +306,15 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
     }
   }
   __syncthreads();
-  const int sub = threadIdx.x & 15, e0 = sub * EPT;
+  const int sub = threadIdx.x & 15;
   for (int rho0 = 0; rho0 < a.R; rho0 += NT / 16) {
     const int rho = rho0 + (threadIdx.x >> 4);
     if (rho >= a.R) break;   // whole 16-lane groups leave together
     const int j = rho / a.B, p = rho % a.B;
-    const float *q = base + (size_t)p * a.Nqkv + (size_t)(it.kvh * a.G + j) * HD + e0;
+    const float *q = base + (size_t)p * a.Nqkv + (size_t)(it.kvh * a.G + j) * HD + sub;
     float qv[EPT];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) qv[e] = q[e];
+    for (int e = 0; e < EPT; ++e) qv[e] = q[16 * e];
     const int kmax = a.causal ? min(a.B, p + 1) : a.B;   // causal: block keys 0..p
     float sc[BMAX];
     float m = -INFINITY;
@@ -227,7 +323,7 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
       if (key < a.B) {
         float dsum = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) dsum += qv[e] * s_k[key * (HD + 1) + e0 + e];
+        for (int e = 0; e < EPT; ++e) dsum += qv[e] * s_k[key * (HD + 1) + sub + 16 * e];
         sc[key] = key < kmax ? sum16(dsum) * a.scale : -INFINITY;
         m = fmaxf(m, sc[key]);
       }
@@ -241,7 +337,7 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
         const float pk = __expf(sc[key] - m);
         l += pk;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) ov[e] += pk * s_v[key * (HD + 1) + e0 + e];
+        for (int e = 0; e < EPT; ++e) ov[e] += pk * s_v[key * (HD + 1) + sub + 16 * e];
       }
     }
     const size_t prow = (size_t)item * a.R + rho;
@@ -250,8 +346,7 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
       a.part_ml[prow * 2 + 1] = l;
     }
 #pragma unroll
-    for (int e = 0; e < EPT; e += 4)
-      *reinterpret_cast<float4 *>(&a.part_o[prow * HD + e0 + e]) = make_float4(ov[e], ov[e + 1], ov[e + 2], ov[e + 3]);
+    for (int e = 0; e < EPT; ++e) a.part_o[prow * HD + sub + 16 * e] = ov[e];
   }
 }
 
@@ -259,9 +354,11 @@ TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *s
 // ..., operands straight from HBM, each wave with DEPTH pages in flight (a ring).  (Eight waves
 // measured slower: with two workgroups per CU their registers spill; with one, on a grid
 // of one item per CU (batch 1), attention took 18% longer.)  The pair's first item also attends
-// the block's own keys: their loads are issued before the first pages', so the fp32
-// block pass (block_item's arithmetic, into LDS) runs while the pages are in flight, and
-// its state is merged after the waves' in the fixed order waves 0..NW-1, block.
+// the block's own keys: their loads are issued before the first pages', the keys and
+// values are staged in LDS, and wave rt < RT takes them (block_page, on the matrix
+// cores) as the first page of its row tile rt while its prefix pages are in flight.  (An
+// fp32 pass over them on the VALU, 16 threads per row, took 15 us of the item's 49 at
+// the batch-64 block-32 sweep, with the CU streaming no pages meanwhile.)
 template <int N, typename F>
 TD_DEV void static_for(F &&f) {
   if constexpr (N > 0) {
@@ -274,13 +371,17 @@ TD_DEV void static_for(F &&f) {
 // alone the compiler also took 32 AGPRs and one); the others need the whole register file.
 template <typename T, int HD, int RT, int NW, int DEPTH>
 __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void attn_direct_kernel(AttnArgs a) {
-  constexpr int NT = 64 * NW, HC = HD / 32, OT = HD / 16, EPT = HD / 16, KPT = BMAX * HD / NT;
-  constexpr int MERGE = (NW + 1) * RT * 16 * (HD + 2);   // waves' and the block's states
-  constexpr int LDS = MERGE + block_item_lds<HD>();
-  __shared__ float smem[LDS];
-  float(*s_o)[RT * 16][HD] = reinterpret_cast<float(*)[RT * 16][HD]>(smem);
-  float(*s_ml)[RT * 16][2] = reinterpret_cast<float(*)[RT * 16][2]>(smem + (NW + 1) * RT * 16 * HD);
-  float *s_bk = smem + MERGE, *s_bv = s_bk + BMAX * (HD + 1);
+  constexpr int NT = 64 * NW, HC = HD / 32, OT = HD / 16, KPT = BMAX * HD / NT;
+  // The states' rows are padded by 4 words, so that the 16 rows of an MFMA tile store
+  // their 16-byte pieces into distinct banks.
+  constexpr int HS = HD + 4;
+  constexpr int MERGE = NW * RT * 16 * (HS + 2);   // the waves' states
+  constexpr int BLK = block_page_lds<HD>() > block_item_lds<HD>() ? block_page_lds<HD>() : block_item_lds<HD>();
+  constexpr int LDS = MERGE + BLK;
+  __shared__ __attribute__((aligned(16))) float smem[LDS];
+  float(*s_o)[RT * 16][HS] = reinterpret_cast<float(*)[RT * 16][HS]>(smem);
+  float(*s_ml)[RT * 16][2] = reinterpret_cast<float(*)[RT * 16][2]>(smem + NW * RT * 16 * HS);
+  float *s_bk = smem + MERGE, *s_bvt = s_bk + BMAX * bks<HD>();
 
   const AttnItem it = a.items[blockIdx.x];   // loaded together with the loop-exit flag
   if (a.done && *a.done) return;
@@ -302,12 +403,10 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
   const T *Kp = reinterpret_cast<const T *>(a.kc) + ((size_t)it.page0 * a.Hkv + it.kvh) * SUB * HD;
   const T *Vp = reinterpret_cast<const T *>(a.vc) + ((size_t)it.page0 * a.Hkv + it.kvh) * HD * SUB;
 
-  // Block keys/values (fp32, this thread's KPT elements) and the block pass's query
-  // values (16 threads per row, EPT dimensions each): issued first.
-  constexpr int BPASS = (RT * 16 + NT / 16 - 1) / (NT / 16);
-  const int sub = threadIdx.x & 15, e0 = sub * EPT;
+  // Block keys/values (fp32, this thread's KPT elements; slots past the block's B keys
+  // read key 0, finite and never visible): issued first.
   const float *bbase = a.qkv + (size_t)it.seq * a.B * a.Nqkv;
-  float bk[KPT], bv[KPT], bq[BPASS][EPT];
+  float bk[KPT], bv[KPT];
   if (with_block) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -315,14 +414,6 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
       const int kk = key < a.B ? key : 0;
       bk[i] = bbase[(size_t)kk * a.Nqkv + (size_t)(a.H + it.kvh) * HD + e];
       bv[i] = bbase[(size_t)kk * a.Nqkv + (size_t)(a.H + a.Hkv + it.kvh) * HD + e];
-    }
-#pragma unroll
-    for (int ps = 0; ps < BPASS; ++ps) {
-      const int rho = ps * (NT / 16) + (threadIdx.x >> 4);
-      const int rr = rho < a.R ? rho : 0;
-      const float *q = bbase + (size_t)(rr % a.B) * a.Nqkv + (size_t)(it.kvh * a.G + rr / a.B) * HD + e0;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) bq[ps][e] = q[e];
     }
   }
 
@@ -357,15 +448,22 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
   auto consume = [&](auto bufc, int pg) __attribute__((always_inline)) {
     constexpr int b = decltype(bufc)::value;
     const int kvalid = nkeys - pg * SUB;
-    if (kvalid < SUB) {
+    auto tiles = [&](auto fullc) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        PageMath<T, HD>::template run<decltype(fullc)::value>(
+            [&](int h, int c) -> const Frag<T> & { return kf[b][h][c]; },
+            [&](int t) -> const Frag<T> & { return vf[b][t]; }, qf[rt], kvalid, g, m_run[rt], l_run[rt], o[rt]);
+    };
+    // Workgroup-uniform: only a sequence's last page is partial.  (fp32 pages keep the one
+    // masked path: two copies of their page code overflow the register file.)
+    if (sizeof(T) == 2 && kvalid >= SUB) {
+      tiles(std::true_type{});
+    } else {
 #pragma unroll
       for (int t = 0; t < OT; ++t) mask_v<T>(vf[b][t], g, kvalid);
+      tiles(std::false_type{});
     }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-      PageMath<T, HD>::run([&](int h, int c) -> const Frag<T> & { return kf[b][h][c]; },
-                           [&](int t) -> const Frag<T> & { return vf[b][t]; }, qf[rt], a.scale, kvalid, g,
-                           m_run[rt], l_run[rt], o[rt]);
   };
   const int pg0 = wave;
   __builtin_amdgcn_sched_barrier(0);   // the block and query loads stay ahead of the pages'
@@ -375,50 +473,22 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
   q_frags<T, HD, RT>(a, 0, l16, qraw, qf);
 
   if (with_block) {   // workgroup-uniform
-    // The block pass: scores over the B block keys in fp32, one softmax, into slot NW.
+    // The block's keys (rows) and values (transposed) into LDS; wave rt < RT then takes
+    // them as the first page of row tile rt, while its prefix pages are in flight.
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = threadIdx.x + NT * i, key = idx / HD, e = idx % HD;
-      s_bk[key * (HD + 1) + e] = bk[i];
-      s_bv[key * (HD + 1) + e] = bv[i];
+      s_bk[key * bks<HD>() + e] = bk[i];
+      s_bvt[e * BVS + key] = bv[i];
     }
     __syncthreads();
-#pragma unroll
-    for (int ps = 0; ps < BPASS; ++ps) {
-      const int rho = ps * (NT / 16) + (threadIdx.x >> 4);
-      float sc[BMAX];
-      float m = -INFINITY;
-      const int kmax = a.causal ? min(a.B, rho % a.B + 1) : a.B;   // causal: block keys 0..p
-#pragma unroll
-      for (int key = 0; key < BMAX; ++key) {
-        if (key < a.B) {
-          float dsum = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPT; ++e) dsum += bq[ps][e] * s_bk[key * (HD + 1) + e0 + e];
-          sc[key] = key < kmax ? sum16(dsum) * a.scale : -INFINITY;
-          m = fmaxf(m, sc[key]);
-        }
-      }
-      float l = 0.f, ov[EPT];
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) ov[e] = 0.f;
-#pragma unroll
-      for (int key = 0; key < BMAX; ++key) {
-        if (key < kmax) {
-          const float pk = __expf(sc[key] - m);
-          l += pk;
-#pragma unroll
-          for (int e = 0; e < EPT; ++e) ov[e] += pk * s_bv[key * (HD + 1) + e0 + e];
-        }
-      }
-      if (rho < RT * 16) {
-        if (sub == 0) {
-          s_ml[NW][rho][0] = m;
-          s_ml[NW][rho][1] = l;
-        }
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) s_o[NW][rho][e0 + e] = ov[e];
-      }
+    if (wave < RT) {
+      const int rho = wave * 16 + l16;
+      static_for<RT>([&](auto rc) {   // register arrays indexed by constants only
+        constexpr int rt = decltype(rc)::value;
+        if (rt == wave)
+          block_page<T, HD>(s_bk, s_bvt, qf[rt], a.B, a.causal ? rho % a.B : -1, g, l16, m_run[rt], l_run[rt], o[rt]);
+      });
     }
   }
 
@@ -433,37 +503,39 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
     });
   }
 
-  // Merge the waves' states (wave order), then the block's, through LDS.
+  // Merge the waves' states in wave order through LDS (the block's keys are in the states
+  // of waves 0 .. RT - 1).
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float l_tot = sum_groups(l_run[rt]);
     const int rr = rt * 16 + l16;
     if (g == 0) {
-      s_ml[wave][rr][0] = m_run[rt];
+      s_ml[wave][rr][0] = m_run[rt] * LN2;
       s_ml[wave][rr][1] = l_tot;
     }
 #pragma unroll
     for (int t = 0; t < OT; ++t) *reinterpret_cast<f32x4_t *>(&s_o[wave][rr][16 * t + 4 * g]) = o[rt][t];
   }
   __syncthreads();
-  const int nst = with_block ? NW + 1 : NW;
+  // Thread `sub` of a row merges the 16-byte pieces at words 4 sub + 64 k: the 16 threads
+  // of the row read 256 consecutive bytes per piece.
+  constexpr int KC = HD / 64;
+  const int sub = threadIdx.x & 15;
   for (int rr = threadIdx.x >> 4; rr < RT * 16 && rr < a.R; rr += 4 * NW) {
     float Mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w <= NW; ++w)
-      if (w < nst) Mx = fmaxf(Mx, s_ml[w][rr][0]);
-    float L = 0.f, acc[EPT];
+    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_ml[w][rr][0]);
+    float L = 0.f;
+    f32x4_t acc[KC];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
+    for (int k = 0; k < KC; ++k) acc[k] = zero4();
 #pragma unroll
-    for (int w = 0; w <= NW; ++w) {
-      if (w < nst) {
-        const float mw = s_ml[w][rr][0];
-        const float f = (mw == -INFINITY) ? 0.f : __expf(mw - Mx);
-        L += s_ml[w][rr][1] * f;
+    for (int w = 0; w < NW; ++w) {
+      const float mw = s_ml[w][rr][0];
+      const float f = (mw == -INFINITY) ? 0.f : __expf(mw - Mx);
+      L += s_ml[w][rr][1] * f;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) acc[e] += s_o[w][rr][e0 + e] * f;
-      }
+      for (int k = 0; k < KC; ++k) acc[k] += *reinterpret_cast<const f32x4_t *>(&s_o[w][rr][4 * sub + 64 * k]) * f;
     }
     const size_t prow = (size_t)it.slot * a.R + rr;
     if (sub == 0) {
@@ -471,8 +543,7 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
       a.part_ml[prow * 2 + 1] = L;
     }
 #pragma unroll
-    for (int e = 0; e < EPT; e += 4)
-      *reinterpret_cast<float4 *>(&a.part_o[prow * HD + e0 + e]) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    for (int k = 0; k < KC; ++k) *reinterpret_cast<f32x4_t *>(&a.part_o[prow * HD + 4 * sub + 64 * k]) = acc[k];
   }
 }
 
@@ -588,11 +659,18 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
       for (int c = 0; c < HC; ++c) kf[h][c] = *reinterpret_cast<const Frag<T> *>(&sk[((c * 2 + h) * 16 + l16) * KR + g * 8]);
     // V fragments are read from LDS at their use (once per row tile): holding them too
     // would exceed the 256 registers of a wave at two waves per SIMD.
+    auto tiles = [&](auto fullc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt)
-      PageMath<T, HD>::run([&](int h, int c) -> const Frag<T> & { return kf[h][c]; },
-                           [&](int t) { return *reinterpret_cast<const Frag<T> *>(&sv[(16 * t + l16) * VP + g * 8]); },
-                           qf[rt], a.scale, kvalid, g, m_run[rt], l_run[rt], o[rt]);
+      for (int rt = 0; rt < RTW; ++rt)
+        PageMath<T, HD>::template run<decltype(fullc)::value>(
+            [&](int h, int c) -> const Frag<T> & { return kf[h][c]; },
+            [&](int t) { return *reinterpret_cast<const Frag<T> *>(&sv[(16 * t + l16) * VP + g * 8]); }, qf[rt],
+            kvalid, g, m_run[rt], l_run[rt], o[rt]);
+    };
+    if (sizeof(T) == 2 && kvalid >= SUB)   // workgroup-uniform (fp32: one masked path, as above)
+      tiles(std::true_type{});
+    else
+      tiles(std::false_type{});
   };
   // Barrier over LDS only: this wave's LDS reads and writes are complete (lgkmcnt 0), the
   // ring's global loads may stay in flight.
