@@ -9,7 +9,8 @@
 // refined).  Query head j reads K/V head j / (H / Hkv).
 //
 // Work items (built on the host per prefix binding): runs of prefix pages of one
-// (sequence, K/V head) pair, and one item per pair for the block's own keys.  Every
+// (sequence, K/V head) pair; the pair's first item also takes the block's own keys (a
+// pair with no prefix has one item of no pages).  Every
 // item writes a partial state per query row: running max m, sum l of exp(s - m), and
 // the unnormalised output o, into its slot; a pair's slots are consecutive in key
 // order, and attn_merge_kernel combines them in that order.  Items are launched
@@ -31,17 +32,18 @@
 //     in the key loop (the next page in flight while the current one is consumed), and
 //     merge their states in LDS at the end;
 //   * many rows (grouped-query heads): each page is staged once into LDS through a
-//     three-page register ring and the eight waves, each owning RTW 16-row tiles, read
+//     four-page register ring and the eight waves, each owning RTW 16-row tiles, read
 //     it from there.
 // Queries are fp32 activations; against bf16 keys each query fragment enters the MFMA
 // as a bf16 high part plus a bf16 remainder, and the probabilities are split the same
 // way for P.V, so q and P keep ~16 significant bits.  Key slots past the end of a
 // sequence's last page are masked (scores to -inf, values to 0).
 //
-// Block items: the B block keys/values are fp32 activations from the QKV projection and
-// few, so they are attended in fp32 on the VALU (16 threads per query row).  For the
-// frozen context tower's pass (causal) block query p sees block keys 0..p only; the
-// prefix is always seen whole.
+// The block's own keys: the B block keys/values are fp32 activations from the QKV
+// projection.  Staged in LDS (values transposed), each split into a bf16 high part and
+// remainder, they are one more page of the online softmax on the matrix cores
+// (block_page).  For the frozen context tower's pass (causal) block query p sees block
+// keys 0..p only; the prefix is always seen whole.
 #include "td_device.h"
 #include "td_kernels.h"
 
@@ -284,72 +286,6 @@ TD_DEV void store_partial(const AttnArgs &a, int item, int rt0, int g, int l16, 
   }
 }
 
-template <int HD> constexpr int block_item_lds() { return 2 * BMAX * (HD + 1); }   // floats
-
-// The block's own keys of one (sequence, K/V head) pair, fp32 on the VALU: 16 threads
-// per query row, thread `sub` of the row taking dimensions sub, sub + 16, ... (so that the
-// 16 threads read 16 consecutive LDS words: no bank conflict), NT/16 rows at a time.
-// sm: block_item_lds floats of LDS.  Writes the pair's block partial (m, l, o) to the
-// item's slot.
-template <int HD, int NT = 256>
-TD_DEV void block_item(const AttnArgs &a, const AttnItem &it, int item, float *sm) {
-  constexpr int EPT = HD / 16, KPT = BMAX * HD / NT;
-  float *s_k = sm, *s_v = sm + BMAX * (HD + 1);
-  const float *base = a.qkv + (size_t)it.seq * a.B * a.Nqkv;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {   // all of the pair's block keys and values in flight at once
-    const int idx = threadIdx.x + NT * i;
-    const int key = idx / HD, e = idx % HD;
-    if (key < a.B) {
-      s_k[key * (HD + 1) + e] = base[(size_t)key * a.Nqkv + (size_t)(a.H + it.kvh) * HD + e];
-      s_v[key * (HD + 1) + e] = base[(size_t)key * a.Nqkv + (size_t)(a.H + a.Hkv + it.kvh) * HD + e];
-    }
-  }
-  __syncthreads();
-  const int sub = threadIdx.x & 15;
-  for (int rho0 = 0; rho0 < a.R; rho0 += NT / 16) {
-    const int rho = rho0 + (threadIdx.x >> 4);
-    if (rho >= a.R) break;   // whole 16-lane groups leave together
-    const int j = rho / a.B, p = rho % a.B;
-    const float *q = base + (size_t)p * a.Nqkv + (size_t)(it.kvh * a.G + j) * HD + sub;
-    float qv[EPT];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) qv[e] = q[16 * e];
-    const int kmax = a.causal ? min(a.B, p + 1) : a.B;   // causal: block keys 0..p
-    float sc[BMAX];
-    float m = -INFINITY;
-#pragma unroll
-    for (int key = 0; key < BMAX; ++key) {
-      if (key < a.B) {
-        float dsum = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) dsum += qv[e] * s_k[key * (HD + 1) + sub + 16 * e];
-        sc[key] = key < kmax ? sum16(dsum) * a.scale : -INFINITY;
-        m = fmaxf(m, sc[key]);
-      }
-    }
-    float l = 0.f, ov[EPT];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) ov[e] = 0.f;
-#pragma unroll
-    for (int key = 0; key < BMAX; ++key) {
-      if (key < kmax) {
-        const float pk = __expf(sc[key] - m);
-        l += pk;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) ov[e] += pk * s_v[key * (HD + 1) + sub + 16 * e];
-      }
-    }
-    const size_t prow = (size_t)item * a.R + rho;
-    if (sub == 0) {
-      a.part_ml[prow * 2 + 0] = m;
-      a.part_ml[prow * 2 + 1] = l;
-    }
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) a.part_o[prow * HD + sub + 16 * e] = ov[e];
-  }
-}
-
 // Few-row shape (R <= 32, multi-head attention): the NW = 4 waves take pages w, w + 4,
 // ..., operands straight from HBM, each wave with DEPTH pages in flight (a ring).  (Eight waves
 // measured slower: with two workgroups per CU their registers spill; with one, on a grid
@@ -376,8 +312,7 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
   // their 16-byte pieces into distinct banks.
   constexpr int HS = HD + 4;
   constexpr int MERGE = NW * RT * 16 * (HS + 2);   // the waves' states
-  constexpr int BLK = block_page_lds<HD>() > block_item_lds<HD>() ? block_page_lds<HD>() : block_item_lds<HD>();
-  constexpr int LDS = MERGE + BLK;
+  constexpr int LDS = MERGE + block_page_lds<HD>();
   __shared__ __attribute__((aligned(16))) float smem[LDS];
   float(*s_o)[RT * 16][HS] = reinterpret_cast<float(*)[RT * 16][HS]>(smem);
   float(*s_ml)[RT * 16][2] = reinterpret_cast<float(*)[RT * 16][2]>(smem + NW * RT * 16 * HS);
@@ -389,11 +324,6 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
   // scalar load (nothing in the kernel writes it, and the kernel's start invalidates the
   // scalar cache), whose wait does not hold the vector loads back; the pages' items test
   // it once their first pages are requested.
-  if (it.is_block == 1) {
-    if (a.seq_done[it.seq]) return;
-    block_item<HD, NT>(a, it, it.slot, smem);
-    return;
-  }
   const bool with_block = it.is_block == 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -559,7 +489,9 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
 // 4 x 65536 grouped-query workload).  Each wave reads a page's K fragments from LDS once
 // and reuses them for all of its row tiles; V fragments are read at their use.  (Four
 // waves of two row tiles each, one wave per SIMD, measured 281 us; four row tiles per
-// wave spill.)
+// wave spill.)  The pair's first item also takes the block's own keys: staged in LDS
+// beside the pages' stages, they are every wave's first page (block_page), as in the
+// few-row kernel.
 template <typename T, int HD, int RTW>
 __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
   constexpr int NW = 8, NT = 64 * NW, HC = HD / 32, OT = HD / 16;
@@ -571,11 +503,17 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
   constexpr int CPT = (KCH + NT - 1) / NT; // chunks of each per thread
   constexpr int KBUF = HC * 2 * 16 * KR, VBUF = HD * VP;   // elements of one LDS page
   constexpr int BYTES_PAGES = DEPTH * (KBUF + VBUF) * (int)sizeof(T);   // two stages of PPS pages
-  constexpr int BYTES_BLOCK = block_item_lds<HD>() * 4;
-  constexpr int BYTES = BYTES_PAGES > BYTES_BLOCK ? BYTES_PAGES : BYTES_BLOCK;
+  constexpr int BYTES_BLOCK = block_page_lds<HD>() * 4;
+  // The block's keys get LDS of their own beside the stages; where both do not fit (fp32
+  // pages at head size 128) they share the stages' first bytes and are used up before the
+  // first pages are staged.
+  constexpr bool SHARE = BYTES_PAGES + BYTES_BLOCK > 160 * 1024;
+  constexpr int BYTES = SHARE ? (BYTES_PAGES > BYTES_BLOCK ? BYTES_PAGES : BYTES_BLOCK) : BYTES_PAGES + BYTES_BLOCK;
+  constexpr int KPT = BMAX * HD / NT;      // block key / value elements per thread
   __shared__ __attribute__((aligned(16))) char smem[BYTES];
   T *s_k = reinterpret_cast<T *>(smem);          // [stage][page][KBUF]
   T *s_vt = s_k + DEPTH * KBUF;                  // [stage][page][VBUF]
+  float *s_bk = reinterpret_cast<float *>(smem + (SHARE ? 0 : BYTES_PAGES)), *s_bvt = s_bk + BMAX * bks<HD>();
 
   // Workgroup b takes row group b % YS of item b / YS: the row groups of an item are
   // neighbours in launch order, so its pages are read while still in the last-level cache.
@@ -584,10 +522,7 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
   const AttnItem it = a.items[item];   // loaded together with the loop-exit flag
   if (a.done && *a.done) return;
   if (a.seq_done[it.seq]) return;   // block fully adopted: no attention needed
-  if (it.is_block) {
-    if (ygrp == 0) block_item<HD, NT>(a, it, it.slot, reinterpret_cast<float *>(smem));
-    return;
-  }
+  const bool with_block = it.is_block == 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int nkeys = it.k_end - it.k_begin;
@@ -606,12 +541,49 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < OT; ++t) o[rt][t] = zero4();
   }
-  if (npg == 0) {   // an empty prefix item (room bound for appended tokens, none yet): the empty state
-    store_partial<HD, RTW>(a, it.slot, rt0, g, l16, m_run, l_run, o);
-    return;
+  // Block keys/values (fp32; slots past the block's B keys read key 0, never visible).
+  const float *bbase = a.qkv + (size_t)it.seq * a.B * a.Nqkv;
+  float bk[KPT], bv[KPT];
+  if (with_block) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int idx = threadIdx.x + NT * i, key = idx / HD, e = idx % HD;
+      const int kk = key < a.B ? key : 0;
+      bk[i] = bbase[(size_t)kk * a.Nqkv + (size_t)(a.H + it.kvh) * HD + e];
+      bv[i] = bbase[(size_t)kk * a.Nqkv + (size_t)(a.H + a.Hkv + it.kvh) * HD + e];
+    }
   }
   AFrag<T> qf[RTW][HC];
   load_q<T, HD, RTW>(a, it, rt0, g, l16, qf);
+  // The block's keys as each wave's first page (its state is then merged with the
+  // pages' in the same running softmax).
+  auto block_first = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int idx = threadIdx.x + NT * i, key = idx / HD, e = idx % HD;
+      s_bk[key * bks<HD>() + e] = bk[i];
+      s_bvt[e * BVS + key] = bv[i];
+    }
+  };
+  auto block_pass = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int rho = (rt0 + rt) * 16 + l16;
+      block_page<T, HD>(s_bk, s_bvt, qf[rt], a.B, a.causal ? rho % a.B : -1, g, l16, m_run[rt], l_run[rt], o[rt]);
+    }
+  };
+  if (npg == 0) {   // no prefix pages (yet): the block's keys alone, or the empty state
+    if (with_block) {
+      block_first();
+      __syncthreads();
+      block_pass();
+    }
+    float l_tot[RTW];   // each lane group summed its own keys
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) l_tot[rt] = sum_groups(l_run[rt]);
+    store_partial<HD, RTW>(a, it.slot, rt0, g, l16, m_run, l_tot, o);
+    return;
+  }
 
   // Register ring: slot r holds this thread's chunks of one page.  Loads are
   // unconditional (pages past the end reread the last page) so that the waits before
@@ -698,11 +670,20 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
     lds_barrier();
   };
   static_for<DEPTH>([&](auto ic) { fetch(ic, decltype(ic)::value); });
+  if (with_block) {   // workgroup-uniform
+    block_first();
+    if constexpr (SHARE) {
+      __syncthreads();
+      block_pass();
+      __syncthreads();
+    }
+  }
   static_for<PPS>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     if (i < npg) stash(ic, i, nkeys - i * SUB);
   });
   lds_barrier();
+  if (!SHARE && with_block) block_pass();
   for (int p = 0; p < npg; p += DEPTH) {
     stage(std::integral_constant<int, 0>{}, p);
     if (p + PPS >= npg) break;

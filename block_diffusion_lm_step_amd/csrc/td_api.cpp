@@ -891,9 +891,9 @@ static td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const 
   for (int i = 0; i < n_seqs; ++i) off[i + 1] = off[i] + len[i];
   const int G = g.n_heads / g.n_kv_heads, R = G * g.block_size;
   const int tc = chunk_keys(off[n_seqs] * g.n_kv_heads, R);
-  // Few-row path: the pair's first item also takes the block's keys (no item of its own,
-  // so the item count is the prefix pages' alone); grouped-query path: a block item last.
-  const bool few = R <= ATTN_FEW_ROWS;
+  // The pair's first item also takes the block's keys (no item of its own, so the item
+  // count is the prefix pages' alone: a block-only item made a second round of
+  // workgroups at batch 1).
   std::vector<AttnItem> items;
   std::vector<int> pfirst, pcount, grow_slot;
   std::vector<int> grow_len;
@@ -902,17 +902,14 @@ static td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const 
     const int64_t P = off[i + 1] - off[i];
     for (int h = 0; h < g.n_kv_heads; ++h) {
       pfirst.push_back((int)items.size());
-      if (few && P == 0) items.push_back(AttnItem{i, h, 0, 0, 2, 0, page_base});
-      // A grouped-query pair with no prefix but room to grow gets an empty prefix item,
-      // which appended tokens extend.
-      if (!few && P == 0 && cap[i] > 0) items.push_back(AttnItem{i, h, 0, 0, 0, 0, page_base});
+      // A pair with no prefix gets one item of no pages, which appended tokens extend.
+      if (P == 0) items.push_back(AttnItem{i, h, 0, 0, 2, 0, page_base});
       for (int64_t k0 = 0; k0 < P; k0 += tc)
-        items.push_back(AttnItem{i, h, (int)k0, (int)std::min<int64_t>(P, k0 + tc), (few && k0 == 0) ? 2 : 0, 0,
+        items.push_back(AttnItem{i, h, (int)k0, (int)std::min<int64_t>(P, k0 + tc), k0 == 0 ? 2 : 0, 0,
                                  page_base + k0 / KV_PAGE});
       const bool has_prefix_item = (int)items.size() > pfirst.back();
       grow_slot.push_back(has_prefix_item ? (int)items.size() - 1 : -1);
       grow_len.push_back(has_prefix_item ? items.back().k_end - items.back().k_begin : 0);
-      if (!few) items.push_back(AttnItem{i, h, 0, 0, 1, 0, 0});
       pcount.push_back((int)items.size() - pfirst.back());
     }
     page_base += cap[i];

@@ -97,13 +97,12 @@ constexpr int ATTN_FEW_ROWS = 32;
 // block's own keys.  The slots of a pair's items are consecutive; the items array is in
 // launch order.  is_block:
 //   0  prefix keys only;
-//   1  the block's keys only (the pair's last item; grouped-query path);
-//   2  prefix keys and the block's keys (the pair's first item; few-row path; the
-//      prefix range is empty when the sequence has no prefix).
+//   2  prefix keys and the block's keys (the pair's first item; the prefix range is
+//      empty when the sequence has no prefix).
 struct AttnItem {
   int seq, kvh;            // sequence and key/value head
   int k_begin, k_end;      // prefix key range (token index within the sequence)
-  int is_block;            // 0, 1 or 2 as above
+  int is_block;            // 0 or 2 as above
   int slot;                // partial-state slot: the item's index in (pair, key range) order
   int64_t page0;           // cache page holding token k_begin (prefix items)
 };

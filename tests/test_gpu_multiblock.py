@@ -21,7 +21,7 @@ CASES = {
                        dtype="f32"),
     "bf16_n3_b16": dict(n=3, plen=("uniform", 0, 70), B=16, d=256, H=4, Hkv=2, hd=64, L=2, F=1024, V=4096,
                         dtype="bf16"),
-    # R = G * B = 128 query rows per K/V head: the grouped-query attention path, causal block item.
+    # R = G * B = 128 query rows per K/V head: the grouped-query attention path, causal block keys in the first item.
     "bf16_n2_b32_gqa": dict(n=2, plen=("uniform", 1, 50), B=32, d=256, H=8, Hkv=2, hd=64, L=2, F=1024, V=4096,
                             dtype="bf16"),
     # Grouped-query pairs with no prefix at all: the empty prefix item that appended blocks extend.
