@@ -222,7 +222,7 @@ def roofline_of(w, cls: str, r: dict, peaks: dict) -> dict:
 # ----------------------------------------------------------------------------- HBM traffic records
 
 TRAFFIC_SOURCES = {
-    "attention": ("k_attn.hip", "td_device.h", "td_kernels.h"),
+    "attention": ("k_attn.hip", "td_device.h", "td_kernels.h", "td_api.cpp"),   # td_api: the work items
     "lm_head": ("k_gemm.hip", "k_gemm_tile.hip", "td_device.h", "td_kernels.h"),
     "gemm": ("k_gemm_tile.hip", "k_gemm_wk.hip", "td_device.h", "td_kernels.h"),
 }

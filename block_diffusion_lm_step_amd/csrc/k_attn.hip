@@ -467,13 +467,25 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
 #pragma unroll
       for (int k = 0; k < KC; ++k) acc[k] += *reinterpret_cast<const f32x4_t *>(&s_o[w][rr][4 * sub + 64 * k]) * f;
     }
-    const size_t prow = (size_t)it.slot * a.R + rr;
-    if (sub == 0) {
-      a.part_ml[prow * 2 + 0] = Mx;
-      a.part_ml[prow * 2 + 1] = L;
-    }
+    if (a.single) {   // the pair's only item: the normalised output (the merge's arithmetic for one partial)
+      const float inv = 1.0f / L;
+      const int orow = it.seq * a.B + rr % a.B, ocol = (it.kvh * a.G + rr / a.B) * HD + 4 * sub;
 #pragma unroll
-    for (int k = 0; k < KC; ++k) *reinterpret_cast<f32x4_t *>(&a.part_o[prow * HD + 4 * sub + 64 * k]) = acc[k];
+      for (int k = 0; k < KC; ++k) {
+        const f32x4_t v = acc[k] * inv;
+        const float vv[4] = {v[0], v[1], v[2], v[3]};
+        if (a.o) *reinterpret_cast<f32x4_t *>(a.o + (size_t)orow * a.ldo + ocol + 64 * k) = v;
+        if (a.o_afl) afl_put4<T>(a.o_afl, a.H * HD / 32, orow, ocol + 64 * k, vv);
+      }
+    } else {
+      const size_t prow = (size_t)it.slot * a.R + rr;
+      if (sub == 0) {
+        a.part_ml[prow * 2 + 0] = Mx;
+        a.part_ml[prow * 2 + 1] = L;
+      }
+#pragma unroll
+      for (int k = 0; k < KC; ++k) *reinterpret_cast<f32x4_t *>(&a.part_o[prow * HD + 4 * sub + 64 * k]) = acc[k];
+    }
   }
 }
 
@@ -759,7 +771,7 @@ hipError_t launch_hd(const AttnArgs &a, int part, hipStream_t s) {
     hipLaunchKernelGGL((attn_group_kernel<T, HD, 1>), dim3(a.n_items * ((a.R + 127) / 128)), dim3(512), 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !(part & ATTN_MERGE)) return e;
+  if (e != hipSuccess || !(part & ATTN_MERGE) || a.single) return e;
   hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3(a.n_pairs, (a.R + 15) / 16, HD / 32), dim3(64), 0, s, a);
   return hipGetLastError();
 }
@@ -768,6 +780,7 @@ hipError_t launch_hd(const AttnArgs &a, int part, hipStream_t s) {
 
 hipError_t launch_attention(int dtype, const AttnArgs &a, int part, hipStream_t s) {
   if (a.n_items <= 0 || a.n_pairs <= 0 || a.B > BMAX || a.seq_done == nullptr) return hipErrorInvalidValue;
+  if (a.single && (a.R > ATTN_FEW_ROWS || a.n_items != a.n_pairs)) return hipErrorInvalidValue;
   if (dtype == DT_BF16) {
     if (a.hd == 128) return launch_hd<bf16_t, 128>(a, part, s);
     if (a.hd == 64) return launch_hd<bf16_t, 64>(a, part, s);

@@ -101,6 +101,7 @@ struct td_ctx {
   std::vector<char> grow_ok;            // the pair has an item that can grow
   int chunk = 0;                        // tokens per split-K item of the binding
   int n_items = 0, n_pairs = 0;
+  bool attn_single = false;   // every pair has one attention item (few-row path): no merge launch
   size_t items_cap = 0, pairs_cap = 0;
   float *att_o = nullptr, *att_ml = nullptr;
   float *part = nullptr;     // split-K partial products
@@ -264,14 +265,17 @@ int moe_max_tiles(int M, const td_moe_config &mc) {
 
 // Prefix keys per split-K item: a multiple of the page size (at least eight pages)
 // chosen from the whole batch's prefix keys summed over K/V heads.  Multi-head items
-// (memory-bound) aim at about four workgroups per CU: that keeps the work balanced when
-// the prefix lengths of a batch differ (one item per pair would vary 16-fold) while long
-// prefixes still take long items and the merge sees few partials.  Grouped-query items
+// (memory-bound) aim at about two workgroups per CU: each item's start (its first loads,
+// the block's keys) leaves its CU partly idle, while the ragged ends of the pairs still
+// spread over the last round (longest first).  Measured against about four per CU:
+// attention per block 47.1 -> 45.2 ms at the batch-64 block-32 sweep (two row tiles, one
+// workgroup per CU; one item per pair there), 23.1 -> 22.5 ms at block 16, 19.9 ms at
+// the ragged batch of 32 either way; six per CU was slower everywhere.  Grouped-query items
 // (matrix-core-bound pages, split into row groups of 128 query rows) aim at about one
 // workgroup per CU, counting the row groups (measured: more items were slower).
 int chunk_keys(int64_t total_pair_keys, int R) {
   const int64_t row_groups = R <= ATTN_FEW_ROWS ? 1 : (R + 127) / 128;
-  const int64_t target = R <= ATTN_FEW_ROWS ? 1024 : std::max<int64_t>(1, 256 / row_groups);
+  const int64_t target = R <= ATTN_FEW_ROWS ? 512 : std::max<int64_t>(1, 256 / row_groups);
   int64_t tc = (total_pair_keys + target - 1) / target;
   tc = (tc + KV_PAGE - 1) / KV_PAGE * KV_PAGE;
   return (int)std::min<int64_t>(std::max<int64_t>(tc, 8 * KV_PAGE), (int64_t)1 << 30);
@@ -341,12 +345,15 @@ td_status enqueue_attention(td_ctx *c, int layer, const float *qkv, float *o, vo
   // The denoiser's step skips finished sequences (one sequence: the step's own flag does);
   // other passes skip nothing (flags that stay 0).
   a.seq_done = done && c->n_seqs > 1 ? c->st.seq_done : c->zero_seq;
+  a.single = c->attn_single ? 1 : 0;
   TD_TRY(prof_mark(c, TD_PROF_ATTENTION, true));
   TD_HIP(c, launch_attention(g.dtype, a, ATTN_SPLIT, c->stream));
   TD_TRY(prof_mark(c, TD_PROF_ATTENTION, false));
-  TD_TRY(prof_mark(c, TD_PROF_ATTN_MERGE, true));
-  TD_HIP(c, launch_attention(g.dtype, a, ATTN_MERGE, c->stream));
-  TD_TRY(prof_mark(c, TD_PROF_ATTN_MERGE, false));
+  if (!a.single) {   // pairs of one item normalise their output themselves
+    TD_TRY(prof_mark(c, TD_PROF_ATTN_MERGE, true));
+    TD_HIP(c, launch_attention(g.dtype, a, ATTN_MERGE, c->stream));
+    TD_TRY(prof_mark(c, TD_PROF_ATTN_MERGE, false));
+  }
   return TD_OK;
 }
 
@@ -984,6 +991,7 @@ static td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const 
   c->vc.assign(v_cache_host, v_cache_host + g.n_layers);
   c->n_items = (int)items.size();
   c->n_pairs = (int)pfirst.size();
+  c->attn_single = R <= ATTN_FEW_ROWS && items.size() == pfirst.size();
   c->n_seqs = n_seqs;
   c->grow_len = grow_len;
   c->grow_ok.assign(grow_idx.size(), 0);

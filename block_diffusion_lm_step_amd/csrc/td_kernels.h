@@ -121,8 +121,11 @@ struct AttnArgs {
   void *o_afl;                     // optional output [n*B][H*hd] in fragment layout
   float scale;                     // 1 / sqrt(hd)
   const int *done;
+  int single;                      // 1: every pair has one item (few-row path): the items write
+                                   // the normalised output (o, o_afl) themselves, no merge runs
 };
-// part: ATTN_SPLIT (the split-K items), ATTN_MERGE (the merge of their partials), or both.
+// part: ATTN_SPLIT (the split-K items), ATTN_MERGE (the merge of their partials; nothing
+// when a.single), or both.
 enum { ATTN_SPLIT = 1, ATTN_MERGE = 2 };
 hipError_t launch_attention(int dtype, const AttnArgs &a, int part, hipStream_t s);
 
