@@ -5,10 +5,12 @@
 // BM x 128 output tile; wave (wm, wn) owns a (BM/2) x 64 quarter ((BM/32) x 4 MFMA tiles
 // of 16 x 16).  BM = 128, or 64 for layer projections whose 128-row tiles would give
 // about one workgroup per CU: that leaves each SIMD a single wave, whose LDS and barrier
-// latencies nothing overlaps (measured: the MFMA pipes were busy 22% of such a launch).  K advances one 32-wide k-tile per stage through double-buffered LDS (48 KiB,
-// so two workgroups share a CU and one's LDS traffic overlaps the other's MFMAs), one
-// barrier per stage: the next stage is loaded from memory into registers while the
-// current one is multiplied, then written to the other buffer.
+// latencies nothing overlaps (measured: the MFMA pipes were busy 22% of such a launch).
+// K advances one 32-wide k-tile per stage through double-buffered LDS (48 KiB of stages;
+// with 141 registers per lane three workgroups share a CU, and one's LDS traffic and
+// barrier overlap the others' MFMAs), one barrier per stage: the next stage is loaded
+// from memory into registers while the current one is multiplied, then written to the
+// other buffer.
 // Both operands are already in MFMA fragment order in memory (weights packed at
 // creation, activations written in fragment layout by their producers), so staging is
 // a straight 16-byte copy; the activation fragments' bf16 high and low halves go to two
