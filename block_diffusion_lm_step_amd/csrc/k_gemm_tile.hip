@@ -49,6 +49,33 @@ struct alignas(16) StageLds {
 
 constexpr int EPI_PART = 100;   // split-K partial: store the raw accumulator tile
 
+// K split of a tiled layer GEMM: the static split a.splits, grown (a.dyn) when the live
+// row tiles times the column tiles fill less than one workgroup per CU, as happens late in
+// a batched block loop once most sequences are adopted (their rows leave the row list):
+// then about two workgroups per CU, never more than the grid holds, at least 8 k-tiles
+// per split, and no more partials than the workspace holds.  The GEMM and its reduction
+// both derive it from the same live row count, so they agree.  Partials are laid out
+// [split][live tiles * BM][N] (position in the row list, then column).
+constexpr int DYN_MIN_WG = 256, DYN_TARGET_WG = 512;
+struct SplitPlan {
+  int live, S, pstride;
+};
+TD_DEV SplitPlan split_plan(const GemmArgs &a, int nrows, int bm, int tiles_x, int grid_y) {
+  SplitPlan p;
+  p.live = (nrows + bm - 1) / bm;
+  p.pstride = p.live * bm;
+  p.S = a.splits;
+  const int per = p.live * tiles_x;   // workgroups per split
+  if (a.dyn && per > 0 && per * a.splits < DYN_MIN_WG) {
+    int s = (DYN_TARGET_WG + per - 1) / per;
+    s = min(s, grid_y * a.splits / p.live);
+    s = min(s, (a.K >> 5) / 8);
+    s = (int)min((size_t)s, a.part_cap / ((size_t)p.pstride * a.N));
+    p.S = max(s, a.splits);
+  }
+  return p;
+}
+
 // LM-head tile of the workgroup at (blockIdx.x, blockIdx.y), or false if the launch
 // index lies past the live row tiles (gy of them; the grid holds row tiles for every
 // row).  Workgroups are handed to the eight XCDs round-robin in launch order, each XCD
@@ -92,18 +119,28 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   const int stop = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // a vector load
   __builtin_amdgcn_sched_barrier(0);
   const int nrows = a.n_rows ? *a.n_rows : a.M;   // live rows (LM head: masked rows)
-  int tx = blockIdx.x, ty = blockIdx.y;
+  int tx = blockIdx.x, ty = blockIdx.y, sp = blockIdx.z, S = a.splits, pstride = 0;
   if constexpr (EPI == EPI_VSTAT) {
     if (!lmhead_tile((nrows + BM - 1) / BM, tx, ty)) return;
+  } else {
+    const SplitPlan pl = split_plan(a, nrows, BM, gridDim.x, gridDim.y);
+    pstride = pl.pstride;
+    if (pl.S != a.splits) {   // grown split: workgroup (y, z) -> live row tile, split
+      S = pl.S;
+      const int idx = blockIdx.z * gridDim.y + blockIdx.y;
+      ty = idx % pl.live;
+      sp = idx / pl.live;
+      if (sp >= S) return;
+    }
   }
   const int m0 = ty * BM, n0 = tx * BN;
   if (m0 >= nrows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;
-  // K range of this workgroup: split blockIdx.z of a.splits (whole k-tiles).
+  // K range of this workgroup: split sp of S (whole k-tiles).
   const int KTall = a.K >> 5;
-  const int kt0 = (int)((int64_t)KTall * blockIdx.z / a.splits), kt1 = (int)((int64_t)KTall * (blockIdx.z + 1) / a.splits);
+  const int kt0 = (int)((int64_t)KTall * sp / S), kt1 = (int)((int64_t)KTall * (sp + 1) / S);
   const int KT = KTall, nstage = (kt1 - kt0) / KS;
 
   // Activation rows of this tile (gathered through the row list for the LM head);
@@ -221,8 +258,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
 #undef TD_STORE_STAGE
 
   // ---------------------------------------------------------------- epilogues
-  if constexpr (EPI == EPI_PART) {
-    float *part = a.part + (size_t)blockIdx.z * a.M * a.N;
+  // Split partial: the raw accumulator tile at (split, position in the row list).
+  auto store_part = [&]() __attribute__((always_inline)) {
+    float *part = a.part + (size_t)sp * pstride * a.N;
 #pragma unroll
     for (int i = 0; i < MTW; ++i)
 #pragma unroll
@@ -230,10 +268,13 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
         const int col = n0 + (wn * NTW + j) * 16 + l16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = m0 + (wm * MTW + i) * 16 + 4 * g + r;
-          if (row < a.M) part[(size_t)row * a.N + col] = acc[i][j][r];
+          const int pos = m0 + (wm * MTW + i) * 16 + 4 * g + r;   // < pstride
+          part[(size_t)pos * a.N + col] = acc[i][j][r];
         }
       }
+  };
+  if constexpr (EPI == EPI_PART) {
+    store_part();
   } else if constexpr (EPI == EPI_VSTAT) {
 #pragma unroll
     for (int i = 0; i < MTW; ++i)
@@ -267,6 +308,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
     if (threadIdx.x < BM && m0 + threadIdx.x < nrows)
       a.vpart[(size_t)(m0 + threadIdx.x) * gridDim.x + tx] = vstat_merge(s_stat[0][threadIdx.x], s_stat[1][threadIdx.x]);
   } else {
+    if (S > 1) {   // a grown split (workgroup-uniform): split_reduce applies the epilogue
+      store_part();
+      return;
+    }
     // STORE / GELU / RESID, a half of the wave's columns at a time: the wave parks its
     // accumulators (row scale applied) in the now idle stage buffers, one padded row per
     // tile row, and reads them back as 8 consecutive columns of one row per lane, so that
@@ -340,58 +385,68 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   }
 }
 
-// Split-K reduction and epilogue: one workgroup per (row, 1024 columns); thread t holds
-// 4 consecutive columns, sums the partials in split order, applies the row scale and
-// the epilogue.  Four threads cover a 16-column group (partial sums of squares).
+// Split-K reduction and epilogue: a workgroup per (row position, 1024 columns), rows
+// taken with a stride of gridDim.y; thread t holds 4 consecutive columns, sums the
+// partials in split order, applies the row scale and the epilogue.  Four threads cover a
+// 16-column group (partial sums of squares).  After a tiled GEMM the split is the one it
+// used (split_plan: possibly grown, or none, in which case there is nothing to do).
 template <int EPI, bool NORM>
 __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a) {
   __shared__ float s_red[4];
-  // Partials are indexed by position (blockIdx.y); the output row is the row list's entry
-  // there when a row list is given (positions past the live count have nothing to do).
-  const int pos = blockIdx.y;
   const int nrows = a.n_rows ? *a.n_rows : a.M;   // loaded with the loop-exit flag
-  const int row = a.rowlist ? a.rowlist[min(pos, a.M - 1)] : pos;
+  int S = a.splits, pstride = a.M;
+  if (a.tile_rows > 0) {
+    const SplitPlan pl = split_plan(a, nrows, a.tile_rows, a.N / BN, (a.M + a.tile_rows - 1) / a.tile_rows);
+    S = pl.S;
+    pstride = pl.pstride;
+  }
+  if (a.done && *a.done) return;
+  if (S < 2) return;
   const int col = blockIdx.x * 1024 + threadIdx.x * 4;
   const bool in = col < a.N;
-  if (a.done && *a.done) return;
-  if (pos >= nrows) return;
-  f32x4_t y = zero4();
-  if (in) {
+  // Partials are indexed by position; the output row is the row list's entry there when
+  // a row list is given (positions past the live count have nothing to do).
+  for (int pos = blockIdx.y; pos < nrows; pos += gridDim.y) {   // workgroup-uniform
+    const int row = a.rowlist ? a.rowlist[min(pos, a.M - 1)] : pos;
+    f32x4_t y = zero4();
+    if (in) {
 #pragma unroll 4
-    for (int sp = 0; sp < a.splits; ++sp)
-      y += *reinterpret_cast<const f32x4_t *>(a.part + ((size_t)sp * a.M + pos) * a.N + col);
-  }
-  if constexpr (NORM) {
-    float s = 0.f;
-    for (int p = threadIdx.x; p < a.norm_nparts; p += 256) s += a.ssq[(size_t)p * a.ld_ssq + row];
-    s = sum_lanes<64>(s);
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = s;
-    __syncthreads();
-    const float rs = 1.0f / sqrtf((s_red[0] + s_red[1] + s_red[2] + s_red[3]) / (float)a.K + a.norm_eps);
-    y *= rs;
-  }
-  if (!in) return;
-  const int KTo = a.N >> 5;
-  if constexpr (EPI == EPI_STORE) {
-    *reinterpret_cast<f32x4_t *>(a.out + (size_t)row * a.ldo + col) = y;
-  } else if constexpr (EPI == EPI_GELU) {
-    float u[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = gelu_erf(y[e]);
-    afl_put4<bf16_t>(a.out_afl, KTo, row, col, u);
-  } else {
-    f32x4_t *xp = reinterpret_cast<f32x4_t *>(a.out + (size_t)row * a.ldo + col);
-    const f32x4_t xv = *xp + y;
-    *xp = xv;
-    float sq = 0.f, gx[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      gx[e] = xv[e] * to_f32<bf16_t>(reinterpret_cast<const bf16_t *>(a.gain_next)[col + e]);
-      sq += xv[e] * xv[e];
+      for (int sp = 0; sp < S; ++sp)
+        y += *reinterpret_cast<const f32x4_t *>(a.part + ((size_t)sp * pstride + pos) * a.N + col);
     }
-    afl_put4<bf16_t>(a.out_afl, KTo, row, col, gx);
-    sq = sum_lanes<4>(sq);
-    if ((threadIdx.x & 3) == 0) a.ssq_out[(size_t)(col >> 4) * a.M + row] = sq;
+    if constexpr (NORM) {
+      float s = 0.f;
+      for (int p = threadIdx.x; p < a.norm_nparts; p += 256) s += a.ssq[(size_t)p * a.ld_ssq + row];
+      s = sum_lanes<64>(s);
+      if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = s;
+      __syncthreads();
+      const float rs = 1.0f / sqrtf((s_red[0] + s_red[1] + s_red[2] + s_red[3]) / (float)a.K + a.norm_eps);
+      y *= rs;
+      __syncthreads();   // s_red is rewritten for the next position
+    }
+    if (!in) continue;
+    const int KTo = a.N >> 5;
+    if constexpr (EPI == EPI_STORE) {
+      *reinterpret_cast<f32x4_t *>(a.out + (size_t)row * a.ldo + col) = y;
+    } else if constexpr (EPI == EPI_GELU) {
+      float u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = gelu_erf(y[e]);
+      afl_put4<bf16_t>(a.out_afl, KTo, row, col, u);
+    } else {
+      f32x4_t *xp = reinterpret_cast<f32x4_t *>(a.out + (size_t)row * a.ldo + col);
+      const f32x4_t xv = *xp + y;
+      *xp = xv;
+      float sq = 0.f, gx[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gx[e] = xv[e] * to_f32<bf16_t>(reinterpret_cast<const bf16_t *>(a.gain_next)[col + e]);
+        sq += xv[e] * xv[e];
+      }
+      afl_put4<bf16_t>(a.out_afl, KTo, row, col, gx);
+      sq = sum_lanes<4>(sq);
+      if ((threadIdx.x & 3) == 0) a.ssq_out[(size_t)(col >> 4) * a.M + row] = sq;
+    }
   }
 }
 
@@ -430,8 +485,12 @@ int gemm_tile_splits(int M, int N, int K) {
 }
 
 hipError_t launch_split_reduce(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
-  if (a.splits < 2 || a.part == nullptr || a.N % 16 || a.M <= 0) return hipErrorInvalidValue;
-  const dim3 rgrid((a.N + 1023) / 1024, a.M);
+  if (a.part == nullptr || a.N % 16 || a.M <= 0) return hipErrorInvalidValue;
+  if (a.splits < 2 && !(a.dyn && a.tile_rows > 0)) return hipErrorInvalidValue;
+  // A static split covers every row, one workgroup per row; after a GEMM whose split only
+  // grows at few live rows, 128 row positions per column chunk (nothing to do, and cheap,
+  // at full batch).
+  const dim3 rgrid((a.N + 1023) / 1024, a.splits > 1 ? a.M : std::min(a.M, 128));
 #define TD_R(E, NRM)                                                                \
   if (epi == E && norm == NRM) {                                                \
     hipLaunchKernelGGL((split_reduce_kernel<E, NRM>), rgrid, dim3(256), 0, s, a); \
@@ -444,13 +503,16 @@ hipError_t launch_split_reduce(int epi, bool norm, const GemmArgs &a, hipStream_
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a, hipStream_t s) {
+hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a_in, hipStream_t s) {
+  GemmArgs a = a_in;
   if (a.N % BN || a.K % (32 * KS) || a.M <= 0 || a.splits < 1) return hipErrorInvalidValue;
   if (a.done == nullptr) return hipErrorInvalidValue;
   if (norm && (a.ssq == nullptr || a.norm_nparts <= 0)) return hipErrorInvalidValue;
   if ((epi == EPI_GELU || epi == EPI_RESID) && a.out_afl == nullptr) return hipErrorInvalidValue;
   const int bm = tile_bm(epi, a.M, a.N, a.K);
   if ((a.n_rows == nullptr) != (a.rowlist == nullptr)) return hipErrorInvalidValue;
+  if (a.dyn && (epi == EPI_VSTAT || a.part == nullptr || a.n_rows == nullptr)) return hipErrorInvalidValue;
+  a.tile_rows = bm;
   if (a.splits > 1) {
     if (epi == EPI_VSTAT || a.part == nullptr) return hipErrorInvalidValue;
     const dim3 pgrid(a.N / BN, (a.M + bm - 1) / bm, a.splits);
@@ -465,7 +527,9 @@ hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a, hipStream_t s
   if (epi == E && norm == NRM) {                                                        \
     if (bm == 64) hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 64>), grid, dim3(256), 0, s, a); \
     else hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 128>), grid, dim3(256), 0, s, a);         \
-    return hipGetLastError();                                                           \
+    hipError_t e = hipGetLastError();                                                   \
+    if (e != hipSuccess || !a.dyn) return e;                                            \
+    return launch_split_reduce(epi, norm, a, s);                                        \
   }
   TD_L(EPI_STORE, true)
   TD_L(EPI_GELU, true)

@@ -385,12 +385,18 @@ td_status enqueue_gemm(td_ctx *c, int epi, bool norm, int M, int N, int K, const
   a.done = c->gemm_done ? c->gemm_done : c->st.done;
   a.splits = epi == EPI_VSTAT ? 1 : p.splits;
   a.part = c->part;
+  a.part_cap = c->part_need;
   // A denoising step over several sequences computes only the rows of the sequences that
   // still have a masked position (a finished sequence's rows are never read again); the
-  // context pass (its own loop-exit flag) computes every row.
+  // context pass (its own loop-exit flag) computes every row.  A projection already split
+  // in K (the MLP down projection) grows its split on the device once those rows get few:
+  // its reduction is launched anyway.  (Growing the others too needs a reduction launch
+  // after each of them in every step; at the batch-64 block-32 sweep those launches, idle
+  // at full batch, cost 2.3 ms per block, about what their late steps saved.)
   if (p.tile && epi != EPI_VSTAT && !c->gemm_done && c->n_seqs > 1 && !a.rowlist) {
     a.rowlist = c->st.act_rows;
     a.n_rows = c->st.n_act;
+    a.dyn = p.splits > 1 ? 1 : 0;
   }
   if (p.tile) {
     if (epi != EPI_VSTAT) TD_TRY(prof_mark(c, TD_PROF_GEMM, true, prof_sub));
@@ -970,8 +976,14 @@ static td_status bind_impl(td_ctx *c, int32_t n_seqs, const int64_t *len, const 
     c->p_router = plan_gemm(M, std::max(c->moe_Epad, 32), d, false, g.dtype);
     const GemmPlan *plans[] = {&c->p_qkv, &c->p_wo, &c->p_w1, &c->p_w2, &c->p_router};
     const int widths[] = {c->Nqkv, d, F, d, c->moe_Epad};
-    for (int i = 0; i < 5; ++i)
-      if (plans[i]->splits > 1) need = std::max(need, (size_t)plans[i]->splits * M * widths[i]);
+    const size_t Mpad = (size_t)(M + 127) / 128 * 128;   // the tiled kernel's rows, whole tiles
+    for (int i = 0; i < 5; ++i) {
+      if (plans[i]->splits > 1) need = std::max(need, (size_t)plans[i]->splits * Mpad * widths[i]);
+      // A split tiled layer GEMM of a batched step grows its split at few live rows (up
+      // to the workspace: here at least 1024 rows' worth of partials at its width).
+      if (i < 4 && plans[i]->tile && plans[i]->splits > 1 && n_seqs > 1)
+        need = std::max(need, (size_t)1024 * widths[i]);
+    }
     TD_TRY(grow(&c->part, c->part_cap, need, sizeof(float)));
     c->part_need = need;
   }
@@ -1300,7 +1312,7 @@ td_status td_set_moe(td_ctx *c, const td_moe_config *mc, const td_moe_weights *w
   if (s == TD_OK && c->n_seqs > 0) {   // the router's GEMM plan for the bound batch
     const int M = c->n_seqs * c->cfg.block_size;
     c->p_router = plan_gemm(M, c->moe_Epad, c->cfg.d_model, false, c->cfg.dtype);
-    const size_t need = c->p_router.splits > 1 ? (size_t)c->p_router.splits * M * c->moe_Epad : 0;
+    const size_t need = c->p_router.splits > 1 ? (size_t)c->p_router.splits * ((size_t)(M + 127) / 128 * 128) * c->moe_Epad : 0;
     c->part_need = std::max(c->part_need, need);
     if (need > c->part_cap) {
       if (c->part) (void)hipFree(c->part);

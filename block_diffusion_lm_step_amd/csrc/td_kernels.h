@@ -52,7 +52,13 @@ struct GemmArgs {
   float *logits;           // VSTAT: optional capture [rows][N] of the raw logits
   const int *done;         // skip the launch when *done != 0 (required: read before the operands)
   int splits;              // K split over this many workgroups (1: none; not VSTAT)
-  float *part;             // splits > 1: [splits][M][N] fp32 partial products (workspace)
+  float *part;             // K-split partial products, fp32 (workspace): [splits][M][N] for the
+                           // weight-streaming kernels, [S][live tiles * tile_rows][N] for the tiled one
+  int dyn;                 // tiled layer GEMM over live rows (*n_rows): the K split grows on the
+                           // device when the live row tiles fill less than one workgroup per CU;
+                           // split_reduce then sums the partials (it does nothing when none grew)
+  int tile_rows;           // tiled kernel: rows per workgroup tile (set by launch_gemm_tile)
+  size_t part_cap;         // floats of `part` a grown split may use
 };
 // The LM head (EPI_VSTAT): nw waves x nt column tiles per workgroup, each wave streaming
 // its own columns over the whole K range.
