@@ -127,23 +127,18 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kernel(GemmArgs a) {
       const int row = s_row[ri];
       const float rs = s_rs[ri];
       const float tau = (row >= 0 && a.inv_temp) ? a.inv_temp[row] : 1.0f;
-      VStat v{-INFINITY, 0.f, 0x7FFFFFFF};
+      const int col0 = ntw * 16 + l16;
+      float sv[NT];
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int col = (ntw + j) * 16 + l16;
         const float z = acc[mt][j][r] * rs;
-        float sv = -INFINITY;
+        sv[j] = -INFINITY;
         if (row >= 0) {
-          if (a.logits) a.logits[(size_t)row * a.N + col] = z;
-          sv = tau * z;
+          if (a.logits) a.logits[(size_t)row * a.N + col0 + 16 * j] = z;
+          sv[j] = tau * z;
         }
-        float mx = sv;
-        mx = max16(mx);
-        const float se = sum16(row >= 0 ? __expf(sv - mx) : 0.f);
-        int am = (row >= 0 && sv == mx) ? col : 0x7FFFFFFF;
-        am = min16(am);
-        v = vstat_merge(v, VStat{mx, se, am});
       }
+      const VStat v = vstat_row16<NT>(sv, col0, row >= 0);
       if (l16 == 0) s_stat[wave][ri] = v;
     }
   __syncthreads();
@@ -266,21 +261,18 @@ __global__ __launch_bounds__(64 * LDS_NW) void lmhead_lds_kernel(GemmArgs a) {
     const int row = 4 * g + r;
     const bool live = s_pos[row] >= 0;
     const float rs = s_rs[row], tr = s_tau[row];
-    VStat v{-INFINITY, 0.f, 0x7FFFFFFF};
+    const int col0 = ntw * 16 + l16;
+    float sv[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int col = (ntw + j) * 16 + l16;
       const float z = acc[j][r] * rs;
-      float sv = -INFINITY;
+      sv[j] = -INFINITY;
       if (live) {
-        if (a.logits) a.logits[(size_t)row * a.N + col] = z;
-        sv = tr * z;
+        if (a.logits) a.logits[(size_t)row * a.N + col0 + 16 * j] = z;
+        sv[j] = tr * z;
       }
-      const float mx = max16(sv);
-      const float se = sum16(live ? __expf(sv - mx) : 0.f);
-      const int am = min16((live && sv == mx) ? col : 0x7FFFFFFF);
-      v = vstat_merge(v, VStat{mx, se, am});
     }
+    const VStat v = vstat_row16<NT>(sv, col0, live);
     if (l16 == 0) s_stat[wave][row] = v;
   }
   __syncthreads();

@@ -285,23 +285,20 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
         const int row = s_row[ri];
         const float rs = s_rs[ri];
         const float tau = (live && a.inv_temp) ? a.inv_temp[row] : 1.0f;
-        VStat v{-INFINITY, 0.f, 0x7FFFFFFF};
+        // The row's statistics over the wave's 16 NTW columns (a row past the live count
+        // gives the empty set).
+        const int col0 = n0 + wn * NTW * 16 + l16;
+        float sv[NTW];
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          const int col = n0 + (wn * NTW + j) * 16 + l16;
           const float z = acc[i][j][r] * rs;
-          float sv = -INFINITY;
+          sv[j] = -INFINITY;
           if (live) {
-            if (a.logits) a.logits[(size_t)row * a.N + col] = z;
-            sv = tau * z;
+            if (a.logits) a.logits[(size_t)row * a.N + col0 + 16 * j] = z;
+            sv[j] = tau * z;
           }
-          float mx = sv;
-          mx = max16(mx);
-          const float se = sum16(live ? __expf(sv - mx) : 0.f);
-          int am = (live && sv == mx) ? col : 0x7FFFFFFF;
-          am = min16(am);
-          v = vstat_merge(v, VStat{mx, se, am});
         }
+        const VStat v = vstat_row16<NTW>(sv, col0, live);
         if (l16 == 0) s_stat[wn][ri] = v;
       }
     __syncthreads();

@@ -294,6 +294,29 @@ TD_DEV VStat vstat_merge(VStat x, VStat y) {
   return r;
 }
 
+// Vocabulary statistics of one row over the NT column tiles its 16-lane group holds: lane
+// l16 holds scaled score sv[j] of column col0 + 16 j.  The lane's own columns first, then
+// one reduction each over the 16 lanes: the max, the sum of exp(sv - max), and the lowest
+// column holding the max.  Every lane of the group takes part (live is uniform in it); a
+// row that is not live gives the empty set (-inf, 0, none).
+template <int NT>
+TD_DEV VStat vstat_row16(const float (&sv)[NT], int col0, bool live) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) mx = fmaxf(mx, sv[j]);
+  mx = max16(mx);
+  float se = 0.f;
+  int am = 0x7FFFFFFF;
+#pragma unroll
+  for (int j = NT - 1; j >= 0; --j) {   // descending: the lowest matching column wins
+    if (live) {
+      se += __expf(sv[j] - mx);
+      if (sv[j] == mx) am = col0 + 16 * j;
+    }
+  }
+  return VStat{mx, sum16(se), min16(am)};
+}
+
 TD_DEV float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
 // Exclusive position of each flagged row among the flagged rows, in row order.
