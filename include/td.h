@@ -245,7 +245,8 @@ td_status td_denoise_step_noalloc(td_ctx *ctx, int32_t *tokens, uint8_t *committ
                                   float gamma, uint8_t *newly_committed, float *conf_out, int32_t *argmax_out,
                                   float *logits_out);
 
-/* The whole block loop on the device, without host round-trips: sets tokens to [MASK]
+/* The whole block loop on the device, with no host round-trip at the default issue
+ * window 0 (td_set_issue_window; W > 0 paces it from the host): sets tokens to [MASK]
  * and committed to 0, then runs at most B steps; each sequence's loop ends when its
  * block is fully committed (a finished sequence is left unchanged).
  *  steps        int32 [n] or NULL: steps in which the sequence still had a masked position.
