@@ -64,9 +64,20 @@ constexpr int BMAX = 32;       // largest block size
 // receives the scores of keys 8g .. 8g+7.
 TD_DEV int kpos(int c, int h, int i) { return ((c * 2 + h) * 16 + i) * 32; }
 
-template <typename T> struct Pad;
-template <> struct Pad<bf16_t> { static constexpr int K = 8, V = 8; };
-template <> struct Pad<float> { static constexpr int K = 4, V = 4; };
+// A page fragment staged in LDS as frag_words<T>() planes of 64 lane-ordered 16-byte
+// words (1 KiB per plane): every wave instruction that reads or writes it touches one
+// contiguous KiB, which the LDS serves without bank conflicts.  (Rows padded to 80 bytes
+// instead measured one conflict cycle per active cycle.)
+TD_DEV void lds_frag_put(char *f, int lane, const Frag<bf16_t> &v) { reinterpret_cast<uint4 *>(f)[lane] = v.raw; }
+TD_DEV void lds_frag_put(char *f, int lane, const Frag<float> &v) {
+  reinterpret_cast<float4 *>(f)[lane] = v.lo;
+  reinterpret_cast<float4 *>(f + 1024)[lane] = v.hi;
+}
+TD_DEV void lds_frag_get(const char *f, int lane, Frag<bf16_t> &v) { v.raw = reinterpret_cast<const uint4 *>(f)[lane]; }
+TD_DEV void lds_frag_get(const char *f, int lane, Frag<float> &v) {
+  v.lo = reinterpret_cast<const float4 *>(f)[lane];
+  v.hi = reinterpret_cast<const float4 *>(f + 1024)[lane];
+}
 
 // Zero the value slots of a V^T fragment (keys 8g .. 8g+7 of the page) at or past kvalid.
 template <typename T>
@@ -493,9 +504,10 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && RT == 1) ? 2 : 1) void 
 // owning RTW 16-row tiles of the pair's query rows (RTW = 1: 128 rows per workgroup;
 // more rows take several workgroups per item).  Pages reach LDS through a ring of
 // DEPTH pages held in registers (every thread loads its share of page p + DEPTH while
-// page p is multiplied), then one 16-byte store per chunk into the double-buffered,
-// padded LDS stage of PPS = 2 pages (K in its page layout with 32-element rows, V^T
-// rows); one barrier per two pages (one per page measured 11% slower, three 10%).  The
+// page p is multiplied), then stored into the double-buffered LDS stage of PPS = 2
+// pages, each MFMA fragment of the page (16 K rows or V^T rows of 32 keys) in lane
+// order: thread t of a wave loads the 8-element chunk that lane t reads, so that the
+// stores and the reads are contiguous; one barrier per two pages (one per page measured 11% slower, three 10%).  The
 // barrier waits for this wave's LDS operations only, not for the ring's page loads still
 // in flight (a full fence would wait for those too: 216 -> 204 us per launch at the
 // 4 x 65536 grouped-query workload).  Each wave reads a page's K fragments from LDS once
@@ -509,12 +521,11 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
   constexpr int NW = 8, NT = 64 * NW, HC = HD / 32, OT = HD / 16;
   constexpr int PPS = 2;                   // pages per LDS stage (measured: 1 and 3 slower)
   constexpr int DEPTH = 2 * PPS;           // pages in flight in registers (two stages)
-  constexpr int KR = 32 + Pad<T>::K;       // K row stride in LDS (elements)
-  constexpr int VP = SUB + Pad<T>::V;      // V^T row stride in LDS (elements)
   constexpr int KCH = SUB * HD / 8;        // 8-element chunks of a K page (= of a V page)
   constexpr int CPT = (KCH + NT - 1) / NT; // chunks of each per thread
-  constexpr int KBUF = HC * 2 * 16 * KR, VBUF = HD * VP;   // elements of one LDS page
-  constexpr int BYTES_PAGES = DEPTH * (KBUF + VBUF) * (int)sizeof(T);   // two stages of PPS pages
+  constexpr int FB = frag_words<T>() * 1024;              // bytes of one staged fragment
+  constexpr int KBUF = 2 * HC * FB, VBUF = OT * FB;       // bytes of one staged page
+  constexpr int BYTES_PAGES = DEPTH * (KBUF + VBUF);      // two stages of PPS pages
   constexpr int BYTES_BLOCK = block_page_lds<HD>() * 4;
   // The block's keys get LDS of their own beside the stages; where both do not fit (fp32
   // pages at head size 128) they share the stages' first bytes and are used up before the
@@ -523,14 +534,18 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
   constexpr int BYTES = SHARE ? (BYTES_PAGES > BYTES_BLOCK ? BYTES_PAGES : BYTES_BLOCK) : BYTES_PAGES + BYTES_BLOCK;
   constexpr int KPT = BMAX * HD / NT;      // block key / value elements per thread
   __shared__ __attribute__((aligned(16))) char smem[BYTES];
-  T *s_k = reinterpret_cast<T *>(smem);          // [stage][page][KBUF]
-  T *s_vt = s_k + DEPTH * KBUF;                  // [stage][page][VBUF]
+  char *s_k = smem;                              // [stage][page][fragment 2c + h][plane][lane]
+  char *s_vt = smem + DEPTH * KBUF;              // [stage][page][fragment t][plane][lane]
   float *s_bk = reinterpret_cast<float *>(smem + (SHARE ? 0 : BYTES_PAGES)), *s_bvt = s_bk + BMAX * bks<HD>();
 
-  // Workgroup b takes row group b % YS of item b / YS: the row groups of an item are
-  // neighbours in launch order, so its pages are read while still in the last-level cache.
+  // The row groups of an item run on one XCD, launched close together: workgroup b
+  // (XCD b % 8 in the round-robin dispatch) takes row group (b / 8) % YS of item
+  // 8 ((b / 8) / YS) + b % 8, so the later groups read the item's pages from that XCD's
+  // L2.  The grid is rounded up to whole groups of 8 items.
   const int YS = (a.R + NW * RTW * 16 - 1) / (NW * RTW * 16);
-  const int item = blockIdx.x / YS, ygrp = blockIdx.x % YS;
+  const int xslot = blockIdx.x >> 3;
+  const int item = (xslot / YS) * 8 + (blockIdx.x & 7), ygrp = xslot % YS;
+  if (item >= a.n_items) return;
   const AttnItem it = a.items[item];   // loaded together with the loop-exit flag
   if (a.done && *a.done) return;
   if (a.seq_done[it.seq]) return;   // block fully adopted: no attention needed
@@ -599,48 +614,51 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
 
   // Register ring: slot r holds this thread's chunks of one page.  Loads are
   // unconditional (pages past the end reread the last page) so that the waits before
-  // each store are exact.
+  // each store are exact.  Chunk index u = 64 f + lane of this thread (fragment f) takes
+  // the page's chunk 64 f + 4 (lane % 16) + lane / 16: K row or V^T row lane % 16 of
+  // the fragment, keys or dimensions 8 (lane / 16) .. + 7, the operand of that lane.
   constexpr int W = frag_words<T>();
   u32x4_t kreg[DEPTH][CPT][W], vreg[DEPTH][CPT][W];
+  auto chunk_of = [](int u) { return (u & ~63) + 4 * (u & 15) + ((u >> 4) & 3); };
   auto fetch = [&](auto slotc, int pg) __attribute__((always_inline)) {
     constexpr int r = decltype(slotc)::value;
     const size_t base = (size_t)min(pg, npg - 1) * pstride;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = min((int)threadIdx.x + NT * i, KCH - 1);
+      const int c = chunk_of(min((int)threadIdx.x + NT * i, KCH - 1));
       const u32x4_t *kp = reinterpret_cast<const u32x4_t *>(Kp + base + (size_t)c * 8);
       const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(Vp + base + (size_t)c * 8);
 #pragma unroll
-      for (int w = 0; w < W; ++w) {   // pages are read once per step: streaming loads
-        kreg[r][i][w] = __builtin_nontemporal_load(kp + w);
-        vreg[r][i][w] = __builtin_nontemporal_load(vp + w);
+      for (int w = 0; w < W; ++w) {   // plain loads: the item's other row groups re-read them
+        kreg[r][i][w] = kp[w];
+        vreg[r][i][w] = vp[w];
       }
     }
   };
   auto stash = [&](auto slotc, int buf, int kvalid) __attribute__((always_inline)) {
     constexpr int r = decltype(slotc)::value;
-    T *sk = s_k + buf * KBUF;
-    T *sv = s_vt + buf * VBUF;
+    char *sk = s_k + buf * KBUF;
+    char *sv = s_vt + buf * VBUF;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + NT * i;
-      if (c < KCH) {
-        *reinterpret_cast<Frag<T> *>(&sk[(c >> 2) * KR + (c & 3) * 8]) = frag_of(kreg[r][i], T{});
-        const int vrow = c / (SUB / 8), vpart = c % (SUB / 8);
+      const int u = threadIdx.x + NT * i;
+      if (u < KCH) {
+        const int f = u >> 6, ln = u & 63;
+        lds_frag_put(sk + f * FB, ln, frag_of(kreg[r][i], T{}));
         Frag<T> v = frag_of(vreg[r][i], T{});
-        mask_v<T>(v, vpart, kvalid);
-        *reinterpret_cast<Frag<T> *>(&sv[vrow * VP + vpart * 8]) = v;
+        mask_v<T>(v, ln >> 4, kvalid);   // keys 8 (ln / 16) .. + 7 of the page
+        lds_frag_put(sv + f * FB, ln, v);
       }
     }
   };
   auto compute = [&](int buf, int kvalid) __attribute__((always_inline)) {
-    const T *sk = s_k + buf * KBUF;
-    const T *sv = s_vt + buf * VBUF;
+    const char *sk = s_k + buf * KBUF;
+    const char *sv = s_vt + buf * VBUF;
     Frag<T> kf[2][HC];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int c = 0; c < HC; ++c) kf[h][c] = *reinterpret_cast<const Frag<T> *>(&sk[((c * 2 + h) * 16 + l16) * KR + g * 8]);
+      for (int c = 0; c < HC; ++c) lds_frag_get(sk + (c * 2 + h) * FB, lane, kf[h][c]);
     // V fragments are read from LDS at their use (once per row tile): holding them too
     // would exceed the 256 registers of a wave at two waves per SIMD.
     auto tiles = [&](auto fullc) __attribute__((always_inline)) {
@@ -648,7 +666,12 @@ __global__ __launch_bounds__(512) void attn_group_kernel(AttnArgs a) {
       for (int rt = 0; rt < RTW; ++rt)
         PageMath<T, HD>::template run<decltype(fullc)::value>(
             [&](int h, int c) -> const Frag<T> & { return kf[h][c]; },
-            [&](int t) { return *reinterpret_cast<const Frag<T> *>(&sv[(16 * t + l16) * VP + g * 8]); }, qf[rt],
+            [&](int t) {
+              Frag<T> v;
+              lds_frag_get(sv + t * FB, lane, v);
+              return v;
+            },
+            qf[rt],
             kvalid, g, m_run[rt], l_run[rt], o[rt]);
     };
     if (sizeof(T) == 2 && kvalid >= SUB)   // workgroup-uniform (fp32: one masked path, as above)
@@ -768,7 +791,8 @@ hipError_t launch_hd(const AttnArgs &a, int part, hipStream_t s) {
   } else if (a.R <= ATTN_FEW_ROWS) {
     hipLaunchKernelGGL((attn_direct_kernel<T, HD, 2, 4, DIRECT_DEPTH>), dim3(a.n_items), dim3(256), 0, s, a);
   } else {   // one 16-row tile per wave, 128 rows per workgroup (more would spill)
-    hipLaunchKernelGGL((attn_group_kernel<T, HD, 1>), dim3(a.n_items * ((a.R + 127) / 128)), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_group_kernel<T, HD, 1>), dim3((a.n_items + 7) / 8 * 8 * ((a.R + 127) / 128)), dim3(512), 0,
+                       s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(part & ATTN_MERGE) || a.single) return e;

@@ -84,6 +84,12 @@ def test_bf16_shapes(H, Hkv, B, plens):
     _run("bf16", H=H, Hkv=Hkv, hd=128, B=B, plens=plens, qscale=0.5)
 
 
+@pytest.mark.parametrize("H,Hkv,B,plens", [(8, 2, 16, [777, 40, 0]), (16, 1, 16, [300, 1])])
+def test_bf16_gqa_head_dim_64(H, Hkv, B, plens):
+    """Grouped-query rows at head size 64: half of the workgroup's threads stage no chunk."""
+    _run("bf16", H=H, Hkv=Hkv, hd=64, B=B, plens=plens, qscale=0.5)
+
+
 def test_bf16_long_context_gqa_full_size():
     """4 sequences x 65536 prefix keys, 32 query heads over 2 K/V heads (layer 0)."""
     _run("bf16", H=32, Hkv=2, hd=128, B=16, plens=[65536] * 4, qscale=0.5)
