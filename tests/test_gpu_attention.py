@@ -79,7 +79,7 @@ def test_fp32_gqa_and_block_sizes(H, Hkv, B):
 
 
 @pytest.mark.parametrize("H,Hkv,B,plens", [(16, 16, 16, [4096]), (16, 16, 8, [1000, 3]), (16, 16, 32, [2047, 0]),
-                                           (32, 2, 16, [5000, 1])])
+                                           (32, 2, 16, [5000, 1]), (12, 1, 16, [700, 33, 0])])
 def test_bf16_shapes(H, Hkv, B, plens):
     _run("bf16", H=H, Hkv=Hkv, hd=128, B=B, plens=plens, qscale=0.5)
 
