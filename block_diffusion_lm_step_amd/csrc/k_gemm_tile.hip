@@ -10,7 +10,8 @@
 // with 141 registers per lane three workgroups share a CU, and one's LDS traffic and
 // barrier overlap the others' MFMAs), one barrier per stage: the next stage is loaded
 // from memory into registers while the current one is multiplied, then written to the
-// other buffer.
+// other buffer.  A projection with about one 128-row tile per CU runs two such groups of
+// four waves per workgroup, each over one half of the k-tiles (KG = 2).
 // Both operands are already in MFMA fragment order in memory (weights packed at
 // creation, activations written in fragment layout by their producers), so staging is
 // a straight 16-byte copy; the activation fragments' bf16 high and low halves go to two
@@ -102,12 +103,18 @@ TD_DEV bool lmhead_tile(int gy, int &tx, int &ty) {
   return true;
 }
 
-template <int EPI, bool NORM, int BM>
-__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
+// KG = 2: eight waves in two groups of four; each group takes one half of the
+// workgroup's k-tiles through its own pair of stage buffers, and the second group's
+// accumulators are added to the first's through LDS (first half + second half, one
+// rounding) before the first group's epilogue.  Twice the waves on a tile without a
+// split-K reduction launch.
+template <int EPI, bool NORM, int BM, int KG = 1>
+__global__ __launch_bounds__(256 * KG, KG == 1 ? 2 : 1) void gemm_tile_kernel(GemmArgs a) {
+  static_assert(KG == 1 || (KG == 2 && EPI != EPI_VSTAT && EPI != EPI_PART), "two K groups: layer epilogues only");
   constexpr int MTW = BM / 32;                     // MFMA row tiles per wave
   constexpr int NFA = (BM / 16) * KS * 64 / 256;   // activation fragments staged per thread
   constexpr int NPAR = 256 / BM;                   // threads per row summing squares
-  __shared__ StageLds<BM> s_st[2];
+  __shared__ StageLds<BM> s_st[KG][2];
   __shared__ int s_row[BM];
   __shared__ float s_rs[BM];
   __shared__ float s_part[NPAR][BM];
@@ -135,13 +142,19 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   }
   const int m0 = ty * BM, n0 = tx * BN;
   if (m0 >= nrows) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x & 255;                      // thread within its K group
+  const int kg = KG == 1 ? 0 : (int)(threadIdx.x >> 8);  // K group (wave-uniform)
+  const bool lead = kg == 0;                              // the group that finishes the tile
+  const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;
   // K range of this workgroup: split sp of S (whole k-tiles).
   const int KTall = a.K >> 5;
-  const int kt0 = (int)((int64_t)KTall * sp / S), kt1 = (int)((int64_t)KTall * (sp + 1) / S);
-  const int KT = KTall, nstage = (kt1 - kt0) / KS;
+  const int kw0 = (int)((int64_t)KTall * sp / S), kw1 = (int)((int64_t)KTall * (sp + 1) / S);
+  // This K group's k-tiles [kt0, kt1); the first group takes the larger half.
+  const int kmid = KG == 1 ? kw1 : kw0 + (kw1 - kw0 + 1) / 2;
+  const int kt0 = lead ? kw0 : kmid, kt1 = lead ? kmid : kw1;
+  const int KT = KTall, nstage = (kt1 - kt0) / KS, nmax = (kmid - kw0) / KS;
 
   // Activation rows of this tile (gathered through the row list for the LM head);
   // rows past the live count read a valid row and are never written.
@@ -159,19 +172,19 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   u64x4_t aoff, woff;
 #pragma unroll
   for (int i = 0; i < NFA; ++i) {
-    const int f = threadIdx.x + 256 * i;
+    const int f = tid + 256 * i;
     const int fl = f & 63, kt = (f >> 6) % KS, t = f / (64 * KS);
     const int row = s_row[t * 16 + (fl & 15)];
     aoff[i] = (((size_t)(row >> 4) * KT + kt0 + kt) * 64 + (fl >> 4) * 16 + (row & 15)) * 32;
   }
 #pragma unroll
   for (int i = 0; i < NFW; ++i) {
-    const int f = threadIdx.x + 256 * i;
+    const int f = tid + 256 * i;
     const int fl = f & 63, kt = (f >> 6) % KS, t = f / (64 * KS);
     woff[i] = (((size_t)(n0 / 16 + t) * KT + kt0 + kt) * 64 + fl) * 8;
   }
   // (tile, k-tile) of fragment i = 0; fragment i is 4 / KS tiles further.
-  const int ft = threadIdx.x / (64 * KS), fkt = (threadIdx.x >> 6) % KS;
+  const int ft = tid / (64 * KS), fkt = (tid >> 6) % KS;
   u32x4_t ra_hi[NFA], ra_lo[NFA], rw[NFW];
 #define TD_LOAD_STAGE(S)                                                                        \
   _Pragma("unroll") for (int i = 0; i < NFA; ++i) {                                             \
@@ -183,18 +196,21 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
     rw[i] = *reinterpret_cast<const u32x4_t *>(Wb + woff[i] + (size_t)(S) * KS * 512);
 #define TD_STORE_STAGE(B)                                                                       \
   _Pragma("unroll") for (int i = 0; i < NFA; ++i) {                                             \
-    s_st[B].a_hi[ft + (4 / KS) * i][fkt][lane] = ra_hi[i];                                      \
-    s_st[B].a_lo[ft + (4 / KS) * i][fkt][lane] = ra_lo[i];                                      \
+    s_st[kg][B].a_hi[ft + (4 / KS) * i][fkt][lane] = ra_hi[i];                                  \
+    s_st[kg][B].a_lo[ft + (4 / KS) * i][fkt][lane] = ra_lo[i];                                  \
   }                                                                                             \
-  _Pragma("unroll") for (int i = 0; i < NFW; ++i) s_st[B].w[ft + (4 / KS) * i][fkt][lane] = rw[i];
+  _Pragma("unroll") for (int i = 0; i < NFW; ++i) s_st[kg][B].w[ft + (4 / KS) * i][fkt][lane] = rw[i];
 
-  TD_LOAD_STAGE(0)
+  if (nstage > 0) {   // (a second K group can have no k-tile)
+    TD_LOAD_STAGE(0)
+  }
   asm volatile("" ::: "memory");   // the loads above are issued before the test below
   if (stop) return;
   if constexpr (NORM && EPI != EPI_PART) {
     // Row scales from the producer's partial sums of squares: thread t sums the parts
     // p = t / BM (mod NPAR) of row t % BM (consecutive threads read consecutive rows).
-    const int r = threadIdx.x & (BM - 1), par = threadIdx.x / BM;
+    const int r = tid & (BM - 1), par = tid / BM;
+    if (lead) {
     const int row = s_row[r];
     float sacc = 0.f;
     for (int p0 = par; p0 < a.norm_nparts; p0 += NPAR * 16) {
@@ -205,8 +221,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
       for (int j = 0; j < 16; ++j) sacc += (p0 + NPAR * j < a.norm_nparts) ? v[j] : 0.f;
     }
     s_part[par][r] = sacc;
+    }
   }
-  TD_STORE_STAGE(0)
+  if (nstage > 0) {
+    TD_STORE_STAGE(0)
+  }
   __syncthreads();
   if constexpr (NORM && EPI != EPI_PART) {
     if (threadIdx.x < BM) {
@@ -223,22 +242,25 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = zero4();
 
-  for (int s = 0; s < nstage; ++s) {
+  // Both K groups pass the same barriers: nmax stages, the second group idle in the last
+  // one when its half is the shorter.
+  for (int s = 0; s < nmax; ++s) {
     const int b = s & 1;
     if (s + 1 < nstage) {
       TD_LOAD_STAGE(s + 1)
     }
 #pragma unroll
     for (int kt = 0; kt < KS; ++kt) {
+      if (KG > 1 && s >= nstage) break;
       AFrag<bf16_t> af[MTW];
       Frag<bf16_t> wf[NTW];
 #pragma unroll
       for (int i = 0; i < MTW; ++i) {
-        af[i].hi.raw = __builtin_bit_cast(uint4, s_st[b].a_hi[wm * MTW + i][kt][lane]);
-        af[i].lo.raw = __builtin_bit_cast(uint4, s_st[b].a_lo[wm * MTW + i][kt][lane]);
+        af[i].hi.raw = __builtin_bit_cast(uint4, s_st[kg][b].a_hi[wm * MTW + i][kt][lane]);
+        af[i].lo.raw = __builtin_bit_cast(uint4, s_st[kg][b].a_lo[wm * MTW + i][kt][lane]);
       }
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) wf[j].raw = __builtin_bit_cast(uint4, s_st[b].w[wn * NTW + j][kt][lane]);
+      for (int j = 0; j < NTW; ++j) wf[j].raw = __builtin_bit_cast(uint4, s_st[kg][b].w[wn * NTW + j][kt][lane]);
 #pragma unroll
       for (int i = 0; i < MTW; ++i)
 #pragma unroll
@@ -256,6 +278,25 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
 
 #undef TD_LOAD_STAGE
 #undef TD_STORE_STAGE
+
+  if constexpr (KG == 2) {   // the second group's sums into the first's, through the idle stages
+    static_assert(4 * MTW * NTW * 64 * 16 <= (int)sizeof(s_st), "accumulators fit the stage buffers");
+    f32x4_t *xf = reinterpret_cast<f32x4_t *>(&s_st[0][0]) + wave * MTW * NTW * 64 + lane;
+    if (!lead) {
+#pragma unroll
+      for (int i = 0; i < MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) xf[(i * NTW + j) * 64] = acc[i][j];
+    }
+    __syncthreads();
+    if (lead) {
+#pragma unroll
+      for (int i = 0; i < MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[i][j] += xf[(i * NTW + j) * 64];
+    }
+    __syncthreads();
+  }
 
   // ---------------------------------------------------------------- epilogues
   // Split partial: the raw accumulator tile at (split, position in the row list).
@@ -306,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
       a.vpart[(size_t)(m0 + threadIdx.x) * gridDim.x + tx] = vstat_merge(s_stat[0][threadIdx.x], s_stat[1][threadIdx.x]);
   } else {
     if (S > 1) {   // a grown split (workgroup-uniform): split_reduce applies the epilogue
-      store_part();
+      if (lead) store_part();
       return;
     }
     // STORE / GELU / RESID, a half of the wave's columns at a time: the wave parks its
@@ -319,11 +360,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
     constexpr int RW = MTW * 16;        // rows of the wave's tile
     constexpr int EP = 32 + 4;          // padded row of 32 columns (floats)
     static_assert(4 * RW * EP * 4 <= (int)sizeof(s_st), "epilogue staging fits the stage buffers");
-    float *ep = reinterpret_cast<float *>(&s_st[0]) + wave * RW * EP;
+    float *ep = reinterpret_cast<float *>(&s_st[0][0]) + wave * RW * EP;
     const int M = a.M;
     const int KTo = a.N >> 5;
 #pragma unroll
     for (int h = 0; h < NTW / 2; ++h) {
+      // (With two K groups the first one does the epilogue; the second passes the
+      // barriers.)
+      if (lead) {
 #pragma unroll
       for (int i = 0; i < MTW; ++i)
 #pragma unroll
@@ -335,9 +379,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
             if constexpr (NORM) y *= s_rs[wm * RW + rl];
             ep[rl * EP + jj * 16 + l16] = y;
           }
+      }
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < RW * 4 / 64; ++q) {
+        if (!lead) break;
         const int o = lane + 64 * q;               // octet: row o / 4, columns 8 (o % 4) ..
         const int rl = o >> 2, c8 = (o & 3) * 8;
         const int ri = wm * RW + rl;
@@ -449,18 +495,31 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a) {
 
 }  // namespace
 
-// Rows per workgroup tile: 64 for a layer projection with between a half and one
-// 128-row tile per CU (the 64-row tiles then fill the chip without a K split), except a
-// deep contraction (K >= 4 N, the MLP down projection), which keeps 128-row tiles and
-// splits K in two instead (measured at 2048 x 2048 x 8192: 151 us against 194 us in
-// 64-row tiles); else 128, and always 128 for the LM head (its statistics come in
-// 128-column groups of 128-row tiles).  Measured: with 1.5-2 tiles of 128 rows per CU the
-// 64-row tiles were slower, bound by LDS bandwidth at their lower reuse, and fewer tiles
-// are better split in K.
+// Rows per workgroup tile: 64 for a layer projection with between a half and three
+// quarters of a 128-row tile per CU (the 64-row tiles then fill the chip without a K
+// split), except a deep contraction (K >= 4 N, the MLP down projection), which keeps
+// 128-row tiles and splits K in two instead (measured at 2048 x 2048 x 8192: 151 us
+// against 194 us in 64-row tiles); else 128, and always 128 for the LM head (its
+// statistics come in 128-column groups of 128-row tiles).  Measured: with 1.5-2 tiles of
+// 128 rows per CU the 64-row tiles were slower, bound by LDS bandwidth at their lower
+// reuse, and fewer tiles are better split in K.
 static int tile_bm(int epi, int M, int N, int K) {
   if (epi == EPI_VSTAT) return 128;
   const int t128 = (N / BN) * ((M + 127) / 128);
-  return t128 > 128 && t128 <= 256 && K < 4 * N ? 64 : 128;
+  return t128 > 128 && t128 <= 192 && K < 4 * N ? 64 : 128;
+}
+
+// K groups per workgroup: two (eight waves, 128-row tiles) for a layer projection with
+// between three quarters of and one 128-row tile per CU, which 64-row tiles used to
+// cover (bound by LDS bandwidth at their lower reuse).  Measured: the output projection
+// of 2048 rows 55.7 -> 49.1 us, the MLP up projection of 512 rows 54.5 -> 51.5 us.  The
+// MLP down projection keeps its two-way K split: as two K groups with its split grown on
+// the device only at few rows it took 137.8 us against 132.5 (the two halves of a
+// 256-k-tile range in one workgroup).
+static int tile_kg(int epi, int M, int N, int K) {
+  if (epi == EPI_VSTAT) return 1;
+  const int t128 = (N / BN) * ((M + 127) / 128);
+  return t128 > 192 && t128 <= 256 && K < 4 * N ? 2 : 1;
 }
 
 bool gemm_tile_supported(int dtype, int M, int N, int K) {
@@ -520,9 +579,11 @@ hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a_in, hipStream_
     return launch_split_reduce(epi, norm, a, s);
   }
   const dim3 grid(a.N / BN, (a.M + bm - 1) / bm);
+  const int kg = tile_kg(epi, a.M, a.N, a.K);
 #define TD_L(E, NRM)                                                                        \
   if (epi == E && norm == NRM) {                                                        \
     if (bm == 64) hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 64>), grid, dim3(256), 0, s, a); \
+    else if (kg == 2) hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 128, 2>), grid, dim3(512), 0, s, a); \
     else hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 128>), grid, dim3(256), 0, s, a);         \
     hipError_t e = hipGetLastError();                                                   \
     if (e != hipSuccess || !a.dyn) return e;                                            \
