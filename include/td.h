@@ -88,7 +88,9 @@ typedef struct {
   const void *lm_head;                 /* [vocab][d], untied; never predicts [MASK] */
 } td_weights;
 
-/* Create a ctx on the current HIP device.  `stream` is a hipStream_t (NULL = default
+/* Create a ctx on the current HIP device for the denoiser tower of the two-tower model
+ * (poko-everyday.com Nemotron-TwoTower news item, section 技術/ビジネス面: a diffusion
+ * tower that reads the context tower's cache).  `stream` is a hipStream_t (NULL = default
  * stream).  Validates cfg/w (TD_EINVAL), allocates the workspace for max_batch and
  * max_prefix_tokens (TD_ENOMEM), packs the weights (TD_EDEVICE on runtime failure,
  * e.g. no device).  On failure *out is NULL and the message is in td_last_error(NULL). */
@@ -209,7 +211,12 @@ td_status td_set_moe(td_ctx *ctx, const td_moe_config *cfg, const td_moe_weights
  * Waits for the stream.  Errors: TD_EINVAL (no MoE set, NULL pointer). */
 td_status td_moe_stats(td_ctx *ctx, int64_t *launches_host, int64_t *active_experts_host);
 
-/* One denoising step over the bound batch.
+/* One denoising step over the bound batch: one forward pass of the denoiser over every
+ * position of the block, the confidence and prediction of each masked position, and the
+ * adoption of those at or above gamma (the single most confident one if none is); the
+ * rest stay [MASK] (PredNext "人工知能は拡散言語モデルの夢を見るか？", section
+ * 拡散言語モデルで推論するには, steps 2-4).  A finished sequence (no masked position)
+ * is left unchanged.
  *  tokens     int32 [n][B] in/out: a token id, or vocab ([MASK]) exactly where
  *             committed == 0.
  *  committed  uint8 [n][B] in/out.
@@ -245,8 +252,11 @@ td_status td_denoise_step_noalloc(td_ctx *ctx, int32_t *tokens, uint8_t *committ
                                   float gamma, uint8_t *newly_committed, float *conf_out, int32_t *argmax_out,
                                   float *logits_out);
 
-/* The whole block loop on the device, with no host round-trip at the default issue
- * window 0 (td_set_issue_window; W > 0 paces it from the host): sets tokens to [MASK]
+/* The whole block loop on the device (PredNext, section 拡散言語モデルで推論するには,
+ * steps 1-5: start from an all-[MASK] block and repeat the step until no [MASK] is left;
+ * dzen.guru, section "Как попробовать?": blocks of 16 at threshold 0.8), with no host
+ * round-trip at the default issue window 0 (td_set_issue_window; W > 0 paces it from the
+ * host polling a pinned progress word): sets tokens to [MASK]
  * and committed to 0, then runs at most B steps; each sequence's loop ends when its
  * block is fully committed (a finished sequence is left unchanged).
  *  steps        int32 [n] or NULL: steps in which the sequence still had a masked position.
