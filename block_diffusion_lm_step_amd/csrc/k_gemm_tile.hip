@@ -2,8 +2,11 @@
 //
 // At M >= 128 every weight element is used by many rows and the projections are bound
 // by the matrix cores, not by the weight stream.  A workgroup of 4 waves computes a
-// BM x 128 output tile; wave (wm, wn) owns a (BM/2) x 64 quarter ((BM/32) x 4 MFMA tiles
-// of 16 x 16).  BM = 128, or 64 for layer projections whose 128-row tiles would give
+// BM x BNT output tile (BNT = 128, or 256 for the LM head and the widest projections);
+// wave (wm, wn) owns a (BM/2) x (BNT/2) quarter ((BM/32) x (BNT/32) MFMA tiles of
+// 16 x 16).  The 256-column tiles read a third fewer LDS bytes per product (the
+// activations' two planes are loaded once for twice the columns), which is what these
+// loops are short of: at 128 columns the matrix cores issue about half of the time.  BM = 128, or 64 for layer projections whose 128-row tiles would give
 // about one workgroup per CU: that leaves each SIMD a single wave, whose LDS and barrier
 // latencies nothing overlaps (measured: the MFMA pipes were busy 22% of such a launch).
 // K advances one 32-wide k-tile per stage through double-buffered LDS (48 KiB of stages;
@@ -16,8 +19,9 @@
 // creation, activations written in fragment layout by their producers), so staging is
 // a straight 16-byte copy; the activation fragments' bf16 high and low halves go to two
 // separate LDS planes so that a wave's 16-byte LDS reads are contiguous (no bank
-// conflicts).  Per k-tile and wave: 8 activation + 4 weight fragment reads from LDS,
-// 32 MFMAs (high and low parts of the activations against the bf16 weights).
+// conflicts).  Per k-tile and wave: 8 activation + 4 (BNT = 256: 8) weight fragment
+// reads from LDS, 32 (64) MFMAs (high and low parts of the activations against the bf16
+// weights).
 //
 // Epilogues as in the weight-streaming kernels (the RMSNorm row scale multiplies the
 // accumulator): STORE (q/k/v), GELU and RESID (fragment-layout outputs, partial sums of
@@ -32,8 +36,6 @@ namespace {
 
 constexpr int BN = 128;             // workgroup tile columns
 constexpr int KS = 1;               // k-tiles per stage
-constexpr int NTW = 4;              // MFMA column tiles per wave
-constexpr int NFW = (BN / 16) * KS * 64 / 256;   // weight fragments staged per thread
 
 // Small per-thread tables are vector values, not arrays: arrays indexed in loops are
 // turned into LDS or scratch copies before the loops are unrolled.
@@ -41,11 +43,11 @@ typedef unsigned long long u64x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-template <int BM>
+template <int BM, int BNT>
 struct alignas(16) StageLds {
   u32x4_t a_hi[BM / 16][KS][64];   // activation fragments, bf16 high parts
   u32x4_t a_lo[BM / 16][KS][64];   // ... bf16 remainders
-  u32x4_t w[BN / 16][KS][64];      // weight fragments
+  u32x4_t w[BNT / 16][KS][64];     // weight fragments
 };
 
 constexpr int EPI_PART = 100;   // split-K partial: store the raw accumulator tile
@@ -108,13 +110,16 @@ TD_DEV bool lmhead_tile(int gy, int &tx, int &ty) {
 // accumulators are added to the first's through LDS (first half + second half, one
 // rounding) before the first group's epilogue.  Twice the waves on a tile without a
 // split-K reduction launch.
-template <int EPI, bool NORM, int BM, int KG = 1>
+template <int EPI, bool NORM, int BM, int KG = 1, int BNT = BN>
 __global__ __launch_bounds__(256 * KG, KG == 1 ? 2 : 1) void gemm_tile_kernel(GemmArgs a) {
   static_assert(KG == 1 || (KG == 2 && EPI != EPI_VSTAT && EPI != EPI_PART), "two K groups: layer epilogues only");
+  static_assert(BNT == BN || (BNT == 256 && KG == 1 && BM == 128 && EPI != EPI_PART), "256-column tiles");
+  constexpr int NTW = BNT / 32;                    // 16-column MFMA tiles per wave
+  constexpr int NFW = (BNT / 16) * KS * 64 / 256;  // weight fragments staged per thread
   constexpr int MTW = BM / 32;                     // MFMA row tiles per wave
   constexpr int NFA = (BM / 16) * KS * 64 / 256;   // activation fragments staged per thread
   constexpr int NPAR = 256 / BM;                   // threads per row summing squares
-  __shared__ StageLds<BM> s_st[KG][2];
+  __shared__ StageLds<BM, BNT> s_st[KG][2];
   __shared__ int s_row[BM];
   __shared__ float s_rs[BM];
   __shared__ float s_part[NPAR][BM];
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(256 * KG, KG == 1 ? 2 : 1) void gemm_tile_kernel(Ge
       if (sp >= S) return;
     }
   }
-  const int m0 = ty * BM, n0 = tx * BN;
+  const int m0 = ty * BM, n0 = tx * BNT;
   if (m0 >= nrows) return;
   const int tid = threadIdx.x & 255;                      // thread within its K group
   const int kg = KG == 1 ? 0 : (int)(threadIdx.x >> 8);  // K group (wave-uniform)
@@ -526,7 +531,19 @@ bool gemm_tile_supported(int dtype, int M, int N, int K) {
   return dtype == DT_BF16 && M >= 128 && N % BN == 0 && K % (32 * KS) == 0;
 }
 
-int gemm_tile_slices(int N) { return N / BN; }
+// The LM head runs 256-column tiles whenever the vocabulary allows: one statistics
+// triple per row and 256 columns.  Measured at 2048 rows x 131072 x 2048: 1.80-1.85 ms
+// against 2.22 in 128-column tiles (logits bit-identical).
+static int lmhead_bn(int N) { return N % 256 == 0 ? 256 : BN; }
+int gemm_tile_slices(int N) { return N / lmhead_bn(N); }
+
+// 256-column tiles for an unsplit layer projection whose 128 x 256 tiles still number at
+// least two per CU (two workgroups of 233 registers and 66 KiB of LDS share a CU).
+// Measured at 2048 rows: the MLP up projection 141-144 us against 147-148 in 128-column
+// tiles; the QKV projection (384 such tiles) keeps 128 columns.
+static bool tile_wide(int M, int N, int bm, int kg, const GemmArgs &a) {
+  return bm == 128 && kg == 1 && a.splits == 1 && !a.dyn && N % 256 == 0 && (N / 256) * ((M + 127) / 128) >= 512;
+}
 
 // Split only grids of less than one workgroup per CU (up to ~2 per CU, >= 8 k-tiles per
 // split): measured, a grid of 256 tiles runs faster whole than split in two.  (For the
@@ -580,10 +597,13 @@ hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a_in, hipStream_
   }
   const dim3 grid(a.N / BN, (a.M + bm - 1) / bm);
   const int kg = tile_kg(epi, a.M, a.N, a.K);
+  const bool wide = tile_wide(a.M, a.N, bm, kg, a);
+  const dim3 wgrid(a.N / 256, (a.M + bm - 1) / bm);
 #define TD_L(E, NRM)                                                                        \
   if (epi == E && norm == NRM) {                                                        \
     if (bm == 64) hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 64>), grid, dim3(256), 0, s, a); \
     else if (kg == 2) hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 128, 2>), grid, dim3(512), 0, s, a); \
+    else if (wide) hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 128, 1, 256>), wgrid, dim3(256), 0, s, a); \
     else hipLaunchKernelGGL((gemm_tile_kernel<E, NRM, 128>), grid, dim3(256), 0, s, a);         \
     hipError_t e = hipGetLastError();                                                   \
     if (e != hipSuccess || !a.dyn) return e;                                            \
@@ -594,7 +614,10 @@ hipError_t launch_gemm_tile(int epi, bool norm, const GemmArgs &a_in, hipStream_
   TD_L(EPI_RESID, false)
 #undef TD_L
   if (epi == EPI_VSTAT && norm) {
-    hipLaunchKernelGGL((gemm_tile_kernel<EPI_VSTAT, true, 128>), grid, dim3(256), 0, s, a);
+    if (lmhead_bn(a.N) == 256)
+      hipLaunchKernelGGL((gemm_tile_kernel<EPI_VSTAT, true, 128, 1, 256>), dim3(a.N / 256, (a.M + bm - 1) / bm),
+                         dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_tile_kernel<EPI_VSTAT, true, 128>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;
