@@ -6,12 +6,14 @@
 // wave (wm, wn) owns a (BM/2) x (BNT/2) quarter ((BM/32) x (BNT/32) MFMA tiles of
 // 16 x 16).  The 256-column tiles read a third fewer LDS bytes per product (the
 // activations' two planes are loaded once for twice the columns), which is what these
-// loops are short of: at 128 columns the matrix cores issue about half of the time.  BM = 128, or 64 for layer projections whose 128-row tiles would give
-// about one workgroup per CU: that leaves each SIMD a single wave, whose LDS and barrier
-// latencies nothing overlaps (measured: the MFMA pipes were busy 22% of such a launch).
-// K advances one 32-wide k-tile per stage through double-buffered LDS (48 KiB of stages;
-// with 141 registers per lane three workgroups share a CU, and one's LDS traffic and
-// barrier overlap the others' MFMAs), one barrier per stage: the next stage is loaded
+// loops are short of: at 128 columns the matrix cores issue about half of the time.
+// BM = 128, or 64 for layer projections whose 128-row tiles would give about one
+// workgroup per CU: that leaves each SIMD a single wave, whose LDS and barrier latencies
+// nothing overlaps (measured: the MFMA pipes were busy 22% of such a launch).
+// K advances one 32-wide k-tile per stage through double-buffered LDS (48 KiB of stages
+// at 128 columns; with 141 registers per lane three workgroups share a CU, and one's LDS
+// traffic and barrier overlap the others' MFMAs; two at 256 columns), one barrier per
+// stage: the next stage is loaded
 // from memory into registers while the current one is multiplied, then written to the
 // other buffer.  A projection with about one 128-row tile per CU runs two such groups of
 // four waves per workgroup, each over one half of the k-tiles (KG = 2).
@@ -26,7 +28,7 @@
 // Epilogues as in the weight-streaming kernels (the RMSNorm row scale multiplies the
 // accumulator): STORE (q/k/v), GELU and RESID (fragment-layout outputs, partial sums of
 // squares per 16 columns), and VSTAT for the LM head (rows gathered through the row
-// list; per row one (max, sum of exp, argmax) triple per 128-column group).
+// list; per row one (max, sum of exp, argmax) triple per BNT-column group).
 #include "td_device.h"
 #include "td_kernels.h"
 
