@@ -507,7 +507,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a) {
 // split), except a deep contraction (K >= 4 N, the MLP down projection), which keeps
 // 128-row tiles and splits K in two instead (measured at 2048 x 2048 x 8192: 151 us
 // against 194 us in 64-row tiles); else 128, and always 128 for the LM head (its
-// statistics come in 128-column groups of 128-row tiles).  Measured: with 1.5-2 tiles of
+// statistics come per column group of 128-row tiles).  Measured: with 1.5-2 tiles of
 // 128 rows per CU the 64-row tiles were slower, bound by LDS bandwidth at their lower
 // reuse, and fewer tiles are better split in K.
 static int tile_bm(int epi, int M, int N, int K) {
