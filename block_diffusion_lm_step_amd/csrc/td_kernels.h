@@ -65,10 +65,8 @@ struct GemmArgs {
 hipError_t launch_gemm(int dtype, int epi, bool norm, const GemmArgs &a, hipStream_t s);
 // Column groups of the LM head, i.e. vocabulary-statistics triples per row.
 int lmhead_slices(int N, int nt, int nw);
-// Many rows (bf16, M >= 128, N % 128 == 0, K % 32 == 0): 128 x 128 tiles (128 x 256 for
-// the LM head when N % 256 == 0 and for the widest unsplit projections) through
-// double-buffered LDS, every epilogue (VSTAT: one statistics triple per row and tile
-// width; gemm_tile_slices gives their count per row).
+// Many rows (bf16, M >= 128, N % 128 == 0, K % 32 == 0): 128 x 128 tiles through
+// double-buffered LDS, every epilogue (VSTAT: one statistics triple per 128 columns).
 // With a.splits > 1 (not VSTAT) the K range is split over that many workgroups, which
 // store fp32 partials to a.part, and a second kernel sums them in split order and
 // applies the epilogue.
